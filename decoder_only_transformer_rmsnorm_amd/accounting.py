@@ -1,0 +1,44 @@
+"""Work accounting for the decoder forward: FLOPs per GEMM family and HBM bytes per kernel.
+
+Matmul FLOPs follow the rule on "从零实现一个完整的 LLM（CS336）——Transformer 篇" (dujian.net),
+parameter and FLOP accounting section: an (m x n) by (n x p) product costs 2mnp. That page
+counts attention as two full T x T products per head; the causal path only needs the visible
+(query, key) pairs, so ``attention="causal"`` counts 4 * d_head per visible pair, i.e.
+4 * d_head * Hq * B * S(S+1)/2, and ``attention="full"`` reproduces the page's convention.
+"""
+from __future__ import annotations
+
+
+def forward_flops(cfg, batch: int | None = None, seq: int | None = None,
+                  attention: str = "causal") -> dict:
+    B = cfg.batch if batch is None else batch
+    S = cfg.seq if seq is None else seq
+    M = B * S
+    D, F, V, L = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_layers
+    qd, kvd = cfg.n_heads * cfg.d_head, cfg.n_kv_heads * cfg.d_head
+    qkv = 2 * M * D * (qd + 2 * kvd)
+    out = 2 * M * qd * D
+    ffn = 2 * M * D * 2 * F + 2 * M * F * D
+    if attention == "causal":
+        att = 4 * cfg.d_head * cfg.n_heads * B * S * (S + 1) // 2
+    elif attention == "full":
+        att = 4 * cfg.d_head * cfg.n_heads * B * S * S
+    else:
+        raise ValueError(attention)
+    lm = 2 * M * D * V
+    per = {"qkv": qkv * L, "out": out * L, "proj": (qkv + out) * L, "ffn": ffn * L,
+           "attn": att * L, "lm_head": lm}
+    per["total"] = per["proj"] + per["ffn"] + per["attn"] + lm
+    per["gemm"] = per["proj"] + per["ffn"] + lm
+    return per
+
+
+def rmsnorm_bytes(rows: int, d: int, in_bytes: int = 4, out_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one RMSNorm call: read each input element once, write each
+    output element once (the gain vector is negligible and counted too)."""
+    return rows * d * (in_bytes + out_bytes) + d * out_bytes
+
+
+def model_rmsnorm_bytes(cfg) -> int:
+    w = 4 if cfg.dtype == "f32" else 2
+    return (2 * cfg.n_layers + 1) * rmsnorm_bytes(cfg.tokens, cfg.d_model, 4, w)

@@ -1,0 +1,208 @@
+"""ctypes binding of the plain fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check and by the
+benchmark's CPU-baseline leg, never by the HIP library or its binding. Inputs are numpy
+arrays; weights are passed as float32 (already bf16-rounded for bf16 models) and every
+result comes back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+c_int, c_i64, c_double = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+_p = ctypes.c_void_p
+
+
+class OracleCfg(ctypes.Structure):
+    _fields_ = [("n_layers", c_int), ("d_model", c_int), ("n_heads", c_int),
+                ("n_kv_heads", c_int), ("d_head", c_int), ("d_ff", c_int), ("vocab", c_int),
+                ("eps", c_double), ("theta", c_double)]
+
+
+class OracleLayer(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, -O2, OpenMP, strict IEEE double)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-ffp-contract=off", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.oracle_embedding.restype = c_int
+        L.oracle_embedding.argtypes = [_p, c_i64, _p, c_int, c_int, _p]
+        L.oracle_rmsnorm.argtypes = [_p, c_i64, c_int, _p, c_double, _p]
+        L.oracle_linear.argtypes = [_p, c_i64, c_int, _p, c_int, _p]
+        L.oracle_rope.argtypes = [_p, c_int, c_int, c_int, c_int, c_i64, _p, c_double]
+        L.oracle_softmax.argtypes = [_p, c_i64, c_int, _p]
+        L.oracle_attention.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int, c_int,
+                                       c_int, _p, _p]
+        L.oracle_silu.restype = c_double
+        L.oracle_silu.argtypes = [c_double]
+        L.oracle_swiglu.argtypes = [_p, c_i64, c_int, c_int, _p, _p, _p, _p, _p]
+        L.oracle_block.argtypes = [ctypes.POINTER(OracleCfg), ctypes.POINTER(OracleLayer), _p,
+                                   _p, c_int, c_int]
+        L.oracle_model.restype = c_int
+        L.oracle_model.argtypes = [ctypes.POINTER(OracleCfg), _p, ctypes.POINTER(OracleLayer),
+                                   _p, _p, _p, _p, c_int, c_int, _p, _p, c_i64, _p]
+        L.oracle_num_threads.restype = c_int
+        _lib = L
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a) -> int | None:
+    return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def embedding(ids, E) -> np.ndarray:
+    ids, E = _i32(ids), _f32(E)
+    n = ids.size
+    x = np.empty((n, E.shape[1]), dtype=np.float64)
+    if lib().oracle_embedding(_ptr(ids), n, _ptr(E), E.shape[0], E.shape[1], _ptr(x)) != 0:
+        raise IndexError("token id outside the vocabulary")
+    return x.reshape(ids.shape + (E.shape[1],))
+
+
+def rmsnorm(x, g, eps: float = 1e-5) -> np.ndarray:
+    x, g = _f64(x), _f64(g)
+    d = x.shape[-1]
+    y = np.empty_like(x)
+    lib().oracle_rmsnorm(_ptr(x), x.size // d, d, _ptr(g), eps, _ptr(y))
+    return y
+
+
+def linear(x, W) -> np.ndarray:
+    x, W = _f64(x), _f32(W)
+    n_out, n_in = W.shape
+    assert x.shape[-1] == n_in
+    y = np.empty(x.shape[:-1] + (n_out,), dtype=np.float64)
+    lib().oracle_linear(_ptr(x), x.size // n_in, n_in, _ptr(W), n_out, _ptr(y))
+    return y
+
+
+def rope(x, n_heads: int, theta: float = 10000.0, pos=None) -> np.ndarray:
+    """RoPE on x of shape (B, S, n_heads*dh); returns a new array."""
+    x = _f64(x).copy()
+    B, S, F = x.shape
+    dh = F // n_heads
+    pos = None if pos is None else _i32(np.broadcast_to(pos, (B, S)))
+    lib().oracle_rope(_ptr(x), B, S, n_heads, dh, F, _ptr(pos), theta)
+    return x
+
+
+def softmax(s) -> np.ndarray:
+    s = _f64(s)
+    n = s.shape[-1]
+    p = np.empty_like(s)
+    lib().oracle_softmax(_ptr(s), s.size // n, n, _ptr(p))
+    return p
+
+
+def attention(q, k, v, n_heads: int, n_kv_heads: int, want_probs: bool = False):
+    """Causal attention on q (B, S, Hq*dh), k and v (B, S, Hkv*dh)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S, qd = q.shape
+    dh = qd // n_heads
+    assert k.shape == v.shape == (B, S, n_kv_heads * dh)
+    o = np.empty((B, S, qd), dtype=np.float64)
+    probs = np.empty((B, n_heads, S, S), dtype=np.float64) if want_probs else None
+    lib().oracle_attention(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
+                           n_kv_heads, dh, _ptr(o), _ptr(probs))
+    return (o, probs) if want_probs else o
+
+
+def silu(u: float) -> float:
+    return lib().oracle_silu(float(u))
+
+
+def swiglu(h, w1, w3, w2, want_hidden: bool = False):
+    h, w1, w3, w2 = _f64(h), _f32(w1), _f32(w3), _f32(w2)
+    d_ff, d = w1.shape
+    rows = h.size // d
+    out = np.empty(h.shape, dtype=np.float64)
+    u = np.empty(h.shape[:-1] + (d_ff,), dtype=np.float64) if want_hidden else None
+    lib().oracle_swiglu(_ptr(h), rows, d, d_ff, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), _ptr(u))
+    return (out, u) if want_hidden else out
+
+
+def _cfg(cfg) -> OracleCfg:
+    return OracleCfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
+                     cfg.d_ff, cfg.vocab, cfg.eps, cfg.rope_theta)
+
+
+def _layer(lw, keep: list) -> OracleLayer:
+    arrs = [_f32(getattr(lw, n)) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1",
+                                            "w3", "w2")]
+    keep.extend(arrs)
+    return OracleLayer(*[a.ctypes.data for a in arrs])
+
+
+def block(cfg, lw, x, pos=None) -> np.ndarray:
+    """One pre-norm block on the residual x of shape (B, S, D); returns a new array."""
+    x = _f64(x).copy()
+    B, S, _ = x.shape
+    keep: list = []
+    L = _layer(lw, keep)
+    pos = None if pos is None else _i32(np.broadcast_to(pos, (B, S)))
+    c = _cfg(cfg)
+    lib().oracle_block(ctypes.byref(c), ctypes.byref(L), _ptr(x), _ptr(pos), B, S)
+    return x
+
+
+def model(cfg, inputs, ids=None, pos=None, rows=None, want_hidden: bool = False):
+    """Forward of the whole model. ``ids`` defaults to ``inputs.ids``; ``rows`` (flat indices
+    b*S + s) restricts which logits rows are produced. Returns logits (and x_final)."""
+    ids = _i32(inputs.ids if ids is None else ids)
+    B, S = ids.shape
+    keep: list = []
+    arr = (OracleLayer * max(1, cfg.n_layers))(*[_layer(lw, keep) for lw in inputs.layers])
+    embed, g_final, lm = _f32(inputs.embed), _f32(inputs.g_final), _f32(inputs.lm_head)
+    pos = None if pos is None else _i32(np.broadcast_to(pos, (B, S)))
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n_rows = B * S if rows_a is None else rows_a.size
+    logits = np.empty((n_rows, cfg.vocab), dtype=np.float64)
+    xf = np.empty((B * S, cfg.d_model), dtype=np.float64) if want_hidden else None
+    c = _cfg(cfg)
+    rc = lib().oracle_model(ctypes.byref(c), _ptr(embed), arr, _ptr(g_final), _ptr(lm),
+                            _ptr(ids), _ptr(pos), B, S, _ptr(xf), _ptr(rows_a), n_rows,
+                            _ptr(logits))
+    if rc != 0:
+        raise IndexError("token id outside the vocabulary")
+    if rows_a is None:
+        logits = logits.reshape(B, S, cfg.vocab)
+    return (logits, xf) if want_hidden else logits
