@@ -1,0 +1,324 @@
+// extern "C" entry points of libtfm.so (declared and documented in include/tfm.h).
+// Host side only: argument validation, workspace planning and the launch sequence of the
+// pre-norm decoder block ("Transformer 篇" (dujian.net) 5.7; "LLM 2" FFN & PreNorm).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+#include "tfm.h"
+
+using namespace tfm;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TFM_OK;
+  g_last_hip = (int)e;
+  return TFM_ERR_HIP;
+}
+
+#define TFM_TRY(expr)                 \
+  do {                                \
+    int _st = (expr);                 \
+    if (_st != TFM_OK) return _st;    \
+  } while (0)
+
+#define TFM_HIP(expr) TFM_TRY(hip_status(expr))
+
+bool valid_dt(int dt) { return dt == TFM_F32 || dt == TFM_BF16; }
+size_t elt(int dt) { return dt == TFM_BF16 ? 2 : 4; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace regions of the block and model forward.
+struct WsPlan {
+  size_t flag, x, xn, qkv, o, u, total;
+};
+
+WsPlan plan_ws(const tfm_config *c, int B, int S) {
+  const size_t M = (size_t)B * S, e = elt(c->dtype);
+  const size_t qd = (size_t)c->n_heads * c->d_head, kvd = (size_t)c->n_kv_heads * c->d_head;
+  WsPlan p;
+  size_t off = 0;
+  p.flag = off; off += 256;
+  p.x = off; off += round256(M * c->d_model * 4);
+  p.xn = off; off += round256(M * c->d_model * e);
+  p.qkv = off; off += round256(M * (qd + 2 * kvd) * e);
+  p.o = off; off += round256(M * qd * e);
+  p.u = off; off += round256(M * c->d_ff * e);
+  p.total = off;
+  return p;
+}
+
+int check_config(const tfm_config *c, int B, int S) {
+  if (!c) return TFM_ERR_NULL;
+  if (!valid_dt(c->dtype)) return TFM_ERR_DTYPE;
+  if (c->n_layers < 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->d_head <= 0 || c->d_ff <= 0 || c->vocab <= 0 || c->max_seq_len <= 0)
+    return TFM_ERR_SHAPE;
+  if (c->n_heads % c->n_kv_heads != 0) return TFM_ERR_SHAPE;
+  if (c->d_head % 4 != 0) return TFM_ERR_SHAPE;  // RoPE pairs, 4-wide vectors
+  if (!(c->eps >= 0.f) || !std::isfinite(c->rope_theta) || !(c->rope_theta > 0.f))
+    return TFM_ERR_SHAPE;
+  if (B < 0 || S < 0 || S > c->max_seq_len) return TFM_ERR_SHAPE;
+  const int kalign = c->dtype == TFM_BF16 ? 8 : 4;
+  if (c->d_model % kalign != 0 || c->d_ff % kalign != 0 ||
+      (c->n_heads * c->d_head) % kalign != 0)
+    return TFM_ERR_SHAPE;
+  if (!attention_supported(c->dtype, c->d_head)) return TFM_ERR_UNSUPPORTED;
+  return TFM_OK;
+}
+
+int check_layer(const tfm_layer_weights *w) {
+  if (!w) return TFM_ERR_NULL;
+  const void *ps[] = {w->g_attn, w->wq, w->wk, w->wv, w->wo, w->g_ffn, w->w1, w->w3, w->w2};
+  for (const void *p : ps) {
+    if (!p) return TFM_ERR_NULL;
+    if (!aligned16(p)) return TFM_ERR_ALIGN;
+  }
+  return TFM_OK;
+}
+
+// Enqueue one block; arguments already validated.
+int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
+                  const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *ws,
+                  const WsPlan &p, hipStream_t s) {
+  const int64_t M = (int64_t)B * S;
+  const int D = c->d_model, dt = c->dtype;
+  const int qd = c->n_heads * c->d_head, kvd = c->n_kv_heads * c->d_head;
+  const int qkv_w = qd + 2 * kvd;
+  const size_t e = elt(dt);
+  void *xn = ws + p.xn;
+  uint8_t *qkv = ws + p.qkv;
+  void *o = ws + p.o;
+  void *u = ws + p.u;
+
+  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
+
+  GemmArgs g{};
+  g.a = xn; g.lda = D; g.w0 = w->wq; g.w1 = w->wk; g.w2 = w->wv; g.n0 = qd; g.n1 = kvd;
+  g.M = M; g.N = qkv_w; g.K = D; g.y = qkv; g.ldy = qkv_w; g.y_dt = dt;
+  g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = c->d_head;
+  g.max_seq = c->max_seq_len;
+  TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
+
+  TFM_HIP(launch_attention(qkv, qkv_w, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e,
+                           qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt, s));
+
+  g = GemmArgs{};
+  g.a = o; g.lda = qd; g.w0 = w->wo; g.M = M; g.N = D; g.K = qd; g.y = x; g.ldy = D;
+  g.y_dt = DT_F32; g.residual = x;
+  TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
+
+  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_ffn, dt, xn, dt, M, D, c->eps, s));
+
+  g = GemmArgs{};
+  g.a = xn; g.lda = D; g.w0 = w->w1; g.w1 = w->w3; g.n0 = c->d_ff; g.M = M; g.N = c->d_ff;
+  g.K = D; g.y = u; g.ldy = c->d_ff; g.y_dt = dt;
+  TFM_HIP(launch_gemm(EPI_SWIGLU, dt, g, s));
+
+  g = GemmArgs{};
+  g.a = u; g.lda = c->d_ff; g.w0 = w->w2; g.M = M; g.N = D; g.K = c->d_ff; g.y = x; g.ldy = D;
+  g.y_dt = DT_F32; g.residual = x;
+  TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
+  return TFM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tfm_status_string(int status) {
+  switch (status) {
+    case TFM_OK: return "ok";
+    case TFM_ERR_NULL: return "required pointer is NULL";
+    case TFM_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case TFM_ERR_DTYPE: return "unknown or unsupported dtype";
+    case TFM_ERR_WORKSPACE: return "workspace too small";
+    case TFM_ERR_ALIGN: return "pointer or stride misaligned";
+    case TFM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TFM_ERR_HIP: return "HIP launch or copy failed";
+    case TFM_ERR_TOKEN: return "token id outside the vocabulary";
+  }
+  return "unknown status";
+}
+
+int tfm_last_hip_error(void) { return g_last_hip; }
+
+const char *tfm_version(void) { return "tfm 0.1 gfx950"; }
+
+int tfm_rope_table_init(float *cos_sin, int max_seq, int d_head, double theta, void *stream) {
+  if (!cos_sin) return TFM_ERR_NULL;
+  if (!aligned16(cos_sin)) return TFM_ERR_ALIGN;
+  if (max_seq <= 0 || d_head <= 0 || d_head % 2 != 0 || !(theta > 0.0) || !std::isfinite(theta))
+    return TFM_ERR_SHAPE;
+  return hip_status(launch_rope_table(cos_sin, max_seq, d_head, theta, (hipStream_t)stream));
+}
+
+int tfm_embed(const int32_t *ids, int64_t n, const void *table, int table_dt, int vocab, int d,
+              float *x, int32_t *err_flag, void *stream) {
+  if (!valid_dt(table_dt)) return TFM_ERR_DTYPE;
+  if (n < 0 || vocab <= 0 || d <= 0 || d % 4 != 0) return TFM_ERR_SHAPE;
+  if (n == 0) return TFM_OK;
+  if (!ids || !table || !x) return TFM_ERR_NULL;
+  if (!aligned16(table) || !aligned16(x)) return TFM_ERR_ALIGN;
+  return hip_status(launch_embed(ids, n, table, table_dt, vocab, d, x, err_flag,
+                                 (hipStream_t)stream));
+}
+
+int tfm_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,
+                int64_t rows, int d, float eps, void *stream) {
+  if (!valid_dt(x_dt) || !valid_dt(g_dt) || !valid_dt(y_dt)) return TFM_ERR_DTYPE;
+  if (rows < 0 || d <= 0 || d % 4 != 0 || !(eps >= 0.f)) return TFM_ERR_SHAPE;
+  if (rows == 0) return TFM_OK;
+  if (!x || !g || !y) return TFM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(y)) return TFM_ERR_ALIGN;
+  if (x == y) return TFM_ERR_SHAPE;
+  return hip_status(launch_rmsnorm(x, x_dt, g, g_dt, y, y_dt, rows, d, eps, (hipStream_t)stream));
+}
+
+int tfm_rope(void *x, int x_dt, int64_t row_stride, const int32_t *positions, int B, int S,
+             int H, int d_head, const float *cos_sin, int max_seq, void *stream) {
+  if (!valid_dt(x_dt)) return TFM_ERR_DTYPE;
+  if (B < 0 || S < 0 || H < 0 || d_head <= 0 || d_head % 4 != 0 || max_seq <= 0 ||
+      row_stride < (int64_t)H * d_head)
+    return TFM_ERR_SHAPE;
+  if ((int64_t)B * S * H == 0) return TFM_OK;
+  if (!x || !cos_sin) return TFM_ERR_NULL;
+  if (row_stride % 4 != 0 || !aligned16(cos_sin) || ((uintptr_t)x & 7u) != 0) return TFM_ERR_ALIGN;
+  if (!positions && S > max_seq) return TFM_ERR_SHAPE;
+  return hip_status(launch_rope(x, x_dt, row_stride, positions, B, S, H, d_head, cos_sin, max_seq,
+                                (hipStream_t)stream));
+}
+
+int tfm_linear(const void *x, const void *w, int dt, const float *residual, void *y, int y_dt,
+               int64_t M, int N, int K, int64_t ldy, void *stream) {
+  if (!valid_dt(dt) || !valid_dt(y_dt)) return TFM_ERR_DTYPE;
+  if (residual && y_dt != TFM_F32) return TFM_ERR_DTYPE;
+  if (M < 0 || N <= 0 || K <= 0 || ldy < N) return TFM_ERR_SHAPE;
+  if (K % (dt == TFM_BF16 ? 8 : 4) != 0) return TFM_ERR_SHAPE;
+  if (M == 0) return TFM_OK;
+  if (!x || !w || !y) return TFM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)))
+    return TFM_ERR_ALIGN;
+  GemmArgs g{};
+  g.a = x; g.lda = K; g.w0 = w; g.M = M; g.N = N; g.K = K; g.y = y; g.ldy = ldy; g.y_dt = y_dt;
+  g.residual = residual;
+  return hip_status(launch_gemm(residual ? EPI_RESIDUAL : EPI_STORE, dt, g, (hipStream_t)stream));
+}
+
+int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
+                         int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
+                         int Hkv, int d_head, int dt, void *stream) {
+  if (!valid_dt(dt)) return TFM_ERR_DTYPE;
+  if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || Hq % Hkv != 0) return TFM_ERR_SHAPE;
+  if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head ||
+      kv_stride < (int64_t)Hkv * d_head)
+    return TFM_ERR_SHAPE;
+  if (!attention_supported(dt, d_head)) return TFM_ERR_UNSUPPORTED;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!q || !k || !v || !o) return TFM_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || q_stride % 8 != 0 ||
+      kv_stride % 8 != 0 || o_stride % 8 != 0)
+    return TFM_ERR_ALIGN;
+  return hip_status(launch_attention(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv,
+                                     d_head, dt, (hipStream_t)stream));
+}
+
+size_t tfm_swiglu_workspace_bytes(int64_t rows, int d_ff, int dt) {
+  if (rows < 0 || d_ff < 0 || !valid_dt(dt)) return 0;
+  return round256((size_t)rows * d_ff * elt(dt));
+}
+
+int tfm_swiglu_ffn(const void *xn, const void *w1, const void *w3, const void *w2,
+                   const float *residual, float *out, int64_t rows, int d, int d_ff, int dt,
+                   void *ws, size_t ws_bytes, void *stream) {
+  if (!valid_dt(dt)) return TFM_ERR_DTYPE;
+  const int kalign = dt == TFM_BF16 ? 8 : 4;
+  if (rows < 0 || d <= 0 || d_ff <= 0 || d % kalign != 0 || d_ff % kalign != 0)
+    return TFM_ERR_SHAPE;
+  if (rows == 0) return TFM_OK;
+  if (!xn || !w1 || !w3 || !w2 || !out || !ws) return TFM_ERR_NULL;
+  if (ws_bytes < tfm_swiglu_workspace_bytes(rows, d_ff, dt)) return TFM_ERR_WORKSPACE;
+  if (!aligned16(xn) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(out) ||
+      !aligned16(ws) || (residual && !aligned16(residual)))
+    return TFM_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g{};
+  g.a = xn; g.lda = d; g.w0 = w1; g.w1 = w3; g.n0 = d_ff; g.M = rows; g.N = d_ff; g.K = d;
+  g.y = ws; g.ldy = d_ff; g.y_dt = dt;
+  TFM_HIP(launch_gemm(EPI_SWIGLU, dt, g, s));
+  g = GemmArgs{};
+  g.a = ws; g.lda = d_ff; g.w0 = w2; g.M = rows; g.N = d; g.K = d_ff; g.y = out; g.ldy = d;
+  g.y_dt = DT_F32; g.residual = residual;
+  return hip_status(launch_gemm(residual ? EPI_RESIDUAL : EPI_STORE, dt, g, s));
+}
+
+size_t tfm_workspace_bytes(const tfm_config *cfg, int B, int S) {
+  if (check_config(cfg, B, S) != TFM_OK) return 0;
+  return plan_ws(cfg, B, S).total;
+}
+
+int tfm_block_forward(const tfm_config *cfg, const tfm_layer_weights *w, float *x,
+                      const int32_t *positions, int B, int S, const float *cos_sin, void *ws,
+                      size_t ws_bytes, void *stream) {
+  TFM_TRY(check_config(cfg, B, S));
+  TFM_TRY(check_layer(w));
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!x || !cos_sin || !ws) return TFM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(cos_sin) || !aligned16(ws)) return TFM_ERR_ALIGN;
+  const WsPlan p = plan_ws(cfg, B, S);
+  if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
+  return enqueue_block(cfg, w, x, positions, B, S, cos_sin, (uint8_t *)ws, p, (hipStream_t)stream);
+}
+
+int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                      const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                      int B, int S, const float *cos_sin, void *ws, size_t ws_bytes,
+                      void *stream) {
+  TFM_TRY(check_config(cfg, B, S));
+  if (!valid_dt(logits_dt)) return TFM_ERR_DTYPE;
+  if (!w) return TFM_ERR_NULL;
+  if (ld_logits < cfg->vocab) return TFM_ERR_SHAPE;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!ids || !logits || !cos_sin || !ws || !w->embed || !w->g_final || !w->lm_head ||
+      (cfg->n_layers > 0 && !w->layers))
+    return TFM_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(cos_sin) || !aligned16(ws) || !aligned16(w->embed) ||
+      !aligned16(w->g_final) || !aligned16(w->lm_head))
+    return TFM_ERR_ALIGN;
+  for (int l = 0; l < cfg->n_layers; ++l) TFM_TRY(check_layer(&w->layers[l]));
+  const WsPlan p = plan_ws(cfg, B, S);
+  if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *wsb = (uint8_t *)ws;
+  const int64_t M = (int64_t)B * S;
+  float *x = (float *)(wsb + p.x);
+  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 1, 0, s));
+  TFM_HIP(launch_embed(ids, M, w->embed, cfg->dtype, cfg->vocab, cfg->d_model, x,
+                       (int32_t *)(wsb + p.flag), s));
+  for (int l = 0; l < cfg->n_layers; ++l)
+    TFM_TRY(enqueue_block(cfg, &w->layers[l], x, positions, B, S, cos_sin, wsb, p, s));
+  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, cfg->dtype, wsb + p.xn, cfg->dtype, M,
+                         cfg->d_model, cfg->eps, s));
+  GemmArgs g{};
+  g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = M; g.N = cfg->vocab;
+  g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
+  TFM_HIP(launch_gemm(EPI_STORE, cfg->dtype, g, s));
+  return TFM_OK;
+}
+
+int tfm_check_device_flags(const void *ws, void *stream) {
+  if (!ws) return TFM_ERR_NULL;
+  TFM_HIP(hipStreamSynchronize((hipStream_t)stream));
+  int32_t flag = 0;
+  TFM_HIP(hipMemcpy(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost));
+  return flag ? TFM_ERR_TOKEN : TFM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the tfm kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tfm {
+
+typedef uint16_t bf16_t;  // bfloat16 storage word
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA bf16 operand
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;   // 32x32 MFMA accumulator
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static constexpr int bytes = 4;
+  __device__ __forceinline__ static float load(const float *p) { return *p; }
+  __device__ __forceinline__ static void store(float *p, float v) { *p = v; }
+};
+template <> struct Elt<bf16_t> {
+  static constexpr int bytes = 2;
+  __device__ __forceinline__ static float load(const bf16_t *p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Load 4 consecutive elements as floats (16-byte or 8-byte aligned vector load).
+__device__ __forceinline__ f32x4_t load4(const float *p) { return *(const f32x4_t *)p; }
+__device__ __forceinline__ f32x4_t load4(const bf16_t *p) {
+  uint2 u = *(const uint2 *)p;
+  f32x4_t r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xffff0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+__device__ __forceinline__ void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v; }
+__device__ __forceinline__ void store4(bf16_t *p, f32x4_t v) {
+  uint2 u;
+  u.x = pack_bf16x2(v[0], v[1]);
+  u.y = pack_bf16x2(v[2], v[3]);
+  *(uint2 *)p = u;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace tfm

@@ -1,0 +1,196 @@
+// Memory-bound kernels of the decoder forward: RoPE table, embedding gather, RMSNorm,
+// standalone RoPE, and a small fill kernel (used instead of hipMemsetAsync so the forward
+// stays safe to capture in a HIP graph).
+#include "common.h"
+#include "internal.h"
+
+namespace tfm {
+namespace {
+
+// RoPE table ("Transformer 篇" (dujian.net) 5.5; "LLM 2" RoPE): angle p * theta^(-2i/d)
+// formed in double precision, cos and sin stored interleaved as float.
+__global__ void rope_table_kernel(float *cs, int max_seq, int half, double theta, int d_head) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)max_seq * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double omega = pow(theta, -2.0 * (double)i / (double)d_head);
+  const double a = (double)p * omega;
+  cs[2 * idx] = (float)cos(a);
+  cs[2 * idx + 1] = (float)sin(a);
+}
+
+// Embedding ("Transformer 篇" 5.2): x[r, :] = table[ids[r], :], 4 elements per thread.
+template <typename T>
+__global__ void embed_kernel(const int32_t *ids, int64_t n, const T *table, int vocab, int d,
+                             float *x, int32_t *err) {
+  const int groups = d >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * groups) return;
+  const int64_t r = idx / groups;
+  const int c = (int)(idx % groups) * 4;
+  const int id = ids[r];
+  f32x4_t val;
+  if (id >= 0 && id < vocab) {
+    val = load4(table + (int64_t)id * d + c);
+  } else {
+    const float nan = __builtin_nanf("");
+    val = f32x4_t{nan, nan, nan, nan};
+    if (err) *err = 1;
+  }
+  store4(x + r * d + c, val);
+}
+
+// RMSNorm ("Transformer 篇" 5.6; "LLM 2" RMSNorm): one wave per row. Each lane reads
+// 4 consecutive elements per step (the wave covers 256 contiguous elements per step, so
+// every load is a full, coalesced 1 KiB (fp32) or 512 B (bf16) transaction); up to
+// kCache steps stay in registers so the row is read from HBM exactly once for
+// d <= 256 * kCache. Sum of squares and scaling in fp32, one rounding at the store.
+constexpr int kCache = 8;
+
+template <typename TX, typename TG, typename TY>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TX *__restrict__ x,
+                                                      const TG *__restrict__ g,
+                                                      TY *__restrict__ y, int64_t rows, int d,
+                                                      float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TX *xr = x + row * d;
+  TY *yr = y + row * d;
+  const int ng = d >> 2;
+  f32x4_t c[kCache];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCache; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < ng) {
+      c[i] = load4(xr + 4 * gi);
+      ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
+    }
+  }
+  for (int gi = lane + 64 * kCache; gi < ng; gi += 64) {
+    const f32x4_t v = load4(xr + 4 * gi);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < kCache; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < ng) store4(yr + 4 * gi, c[i] * inv * load4(g + 4 * gi));
+  }
+  for (int gi = lane + 64 * kCache; gi < ng; gi += 64)
+    store4(yr + 4 * gi, load4(xr + 4 * gi) * inv * load4(g + 4 * gi));
+}
+
+// RoPE in place ("Transformer 篇" 5.5; "Transformer篇" (fengye404.top) 7): each thread
+// rotates two adjacent pairs (4 elements) of one head of one token.
+template <typename T>
+__global__ void rope_kernel(T *x, int64_t row_stride, const int32_t *pos, int B, int S, int H,
+                            int d_head, const float *cs, int max_seq) {
+  const int gph = d_head >> 2;  // 4-element groups per head
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * S * H * gph;
+  if (idx >= total) return;
+  const int gi = (int)(idx % gph);
+  const int64_t rh = idx / gph;
+  const int hh = (int)(rh % H);
+  const int64_t r = rh / H;  // token row b*S + s
+  const int p = pos ? pos[r] : (int)(r % S);
+  T *px = x + r * row_stride + (int64_t)hh * d_head + 4 * gi;
+  f32x4_t v = load4(px);
+  if (p >= 0 && p < max_seq) {
+    const f32x4_t c = *(const f32x4_t *)(cs + ((int64_t)p * (d_head >> 1) + 2 * gi) * 2);
+    const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+    v[0] = x0 * c[0] - x1 * c[1];
+    v[1] = x0 * c[1] + x1 * c[0];
+    v[2] = x2 * c[2] - x3 * c[3];
+    v[3] = x2 * c[3] + x3 * c[2];
+  } else {
+    const float nan = __builtin_nanf("");
+    v = f32x4_t{nan, nan, nan, nan};
+  }
+  store4(px, v);
+}
+
+__global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
+
+template <typename TX, typename TG, typename TY>
+hipError_t rms3(const void *x, const void *g, void *y, int64_t rows, int d, float eps,
+                hipStream_t s) {
+  rmsnorm_kernel<TX, TG, TY><<<blocks_for(rows, 4), 256, 0, s>>>(
+      (const TX *)x, (const TG *)g, (TY *)y, rows, d, eps);
+  return hipGetLastError();
+}
+
+template <typename TX, typename TG>
+hipError_t rms2(const void *x, const void *g, void *y, int y_dt, int64_t rows, int d, float eps,
+                hipStream_t s) {
+  return y_dt == DT_BF16 ? rms3<TX, TG, bf16_t>(x, g, y, rows, d, eps, s)
+                         : rms3<TX, TG, float>(x, g, y, rows, d, eps, s);
+}
+
+template <typename TX>
+hipError_t rms1(const void *x, const void *g, int g_dt, void *y, int y_dt, int64_t rows, int d,
+                float eps, hipStream_t s) {
+  return g_dt == DT_BF16 ? rms2<TX, bf16_t>(x, g, y, y_dt, rows, d, eps, s)
+                         : rms2<TX, float>(x, g, y, y_dt, rows, d, eps, s);
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float *cos_sin, int max_seq, int d_head, double theta,
+                             hipStream_t s) {
+  const int64_t n = (int64_t)max_seq * (d_head / 2);
+  if (n == 0) return hipSuccess;
+  rope_table_kernel<<<blocks_for(n, 256), 256, 0, s>>>(cos_sin, max_seq, d_head / 2, theta,
+                                                       d_head);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t *ids, int64_t n, const void *table, int table_dt,
+                        int vocab, int d, float *x, int32_t *err_flag, hipStream_t s) {
+  const int64_t total = n * (d / 4);
+  if (total == 0) return hipSuccess;
+  if (table_dt == DT_BF16)
+    embed_kernel<bf16_t><<<blocks_for(total, 256), 256, 0, s>>>(ids, n, (const bf16_t *)table,
+                                                                vocab, d, x, err_flag);
+  else
+    embed_kernel<float><<<blocks_for(total, 256), 256, 0, s>>>(ids, n, (const float *)table,
+                                                               vocab, d, x, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,
+                          int64_t rows, int d, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  return x_dt == DT_BF16 ? rms1<bf16_t>(x, g, g_dt, y, y_dt, rows, d, eps, s)
+                         : rms1<float>(x, g, g_dt, y, y_dt, rows, d, eps, s);
+}
+
+hipError_t launch_rope(void *x, int x_dt, int64_t row_stride, const int32_t *positions, int B,
+                       int S, int H, int d_head, const float *cos_sin, int max_seq,
+                       hipStream_t s) {
+  const int64_t total = (int64_t)B * S * H * (d_head / 4);
+  if (total == 0) return hipSuccess;
+  if (x_dt == DT_BF16)
+    rope_kernel<bf16_t><<<blocks_for(total, 256), 256, 0, s>>>(
+        (bf16_t *)x, row_stride, positions, B, S, H, d_head, cos_sin, max_seq);
+  else
+    rope_kernel<float><<<blocks_for(total, 256), 256, 0, s>>>(
+        (float *)x, row_stride, positions, B, S, H, d_head, cos_sin, max_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fill_i32_kernel<<<blocks_for(n, 256), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace tfm

@@ -1,0 +1,55 @@
+// Host-side launch interface between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tfm {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---- elementwise / normalisation kernels (elementwise.hip)
+hipError_t launch_rope_table(float *cos_sin, int max_seq, int d_head, double theta,
+                             hipStream_t s);
+hipError_t launch_embed(const int32_t *ids, int64_t n, const void *table, int table_dt,
+                        int vocab, int d, float *x, int32_t *err_flag, hipStream_t s);
+hipError_t launch_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,
+                          int64_t rows, int d, float eps, hipStream_t s);
+hipError_t launch_rope(void *x, int x_dt, int64_t row_stride, const int32_t *positions, int B,
+                       int S, int H, int d_head, const float *cos_sin, int max_seq,
+                       hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+
+// ---- GEMM family (gemm.hip): y = a w^T with a fused epilogue.
+enum GemmEpi {
+  EPI_STORE = 0,     // y = acc (y_dt)
+  EPI_RESIDUAL = 1,  // y = residual + acc (float32)
+  EPI_QKV_ROPE = 2,  // weight rows from wq | wk | wv; RoPE on the q and k columns
+  EPI_SWIGLU = 3     // gate rows from w1, up rows from w3; y = SiLU(gate) * up
+};
+
+struct GemmArgs {
+  const void *a;           // (M, K) activations of dt, row stride lda
+  int64_t lda;
+  const void *w0, *w1, *w2;// weight row sources (see GemmEpi)
+  int n0, n1;              // QKV: rows of wq and of wk (= rows of wv); SwiGLU: d_ff
+  int64_t M;
+  int N;                   // output columns (QKV: n0 + 2 n1; SwiGLU: d_ff)
+  int K;
+  void *y;
+  int64_t ldy;
+  int y_dt;
+  const float *residual;   // EPI_RESIDUAL
+  const int32_t *positions;// EPI_QKV_ROPE: (M) or NULL -> row % S
+  const float *cos_sin;
+  int S, d_head, max_seq;
+};
+
+hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
+
+// ---- attention (attention.hip)
+hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, const void *v,
+                            int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
+                            int Hkv, int d_head, int dt, hipStream_t s);
+bool attention_supported(int dt, int d_head);
+
+}  // namespace tfm

@@ -1,0 +1,311 @@
+"""Thin ctypes binding of libtfm.so (include/tfm.h).
+
+Argument marshalling only: every function takes torch tensors that already live on the
+GPU, checks their dtype/contiguity, and passes raw device pointers plus the current HIP
+stream to the library. No computation happens here, and there is no fallback: if the
+library is missing or the GPU is absent, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtfm.so")
+
+F32, BF16 = 0, 1
+STATUS = {0: "TFM_OK", -1: "TFM_ERR_NULL", -2: "TFM_ERR_SHAPE", -3: "TFM_ERR_DTYPE",
+          -4: "TFM_ERR_WORKSPACE", -5: "TFM_ERR_ALIGN", -6: "TFM_ERR_UNSUPPORTED",
+          -7: "TFM_ERR_HIP", -8: "TFM_ERR_TOKEN"}
+
+EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_table_init",
+           "tfm_embed", "tfm_rmsnorm", "tfm_rope", "tfm_linear", "tfm_causal_attention",
+           "tfm_swiglu_workspace_bytes", "tfm_swiglu_ffn", "tfm_workspace_bytes",
+           "tfm_block_forward", "tfm_model_forward", "tfm_check_device_flags"]
+
+
+class TfmError(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == -7:
+            msg += f" (hipError {hip})"
+        super().__init__(msg)
+
+
+c_int, c_i64, c_size, c_p = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_layers", c_int), ("d_model", c_int), ("n_heads", c_int),
+                ("n_kv_heads", c_int), ("d_head", c_int), ("d_ff", c_int), ("vocab", c_int),
+                ("max_seq_len", c_int), ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("dtype", c_int)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, c_p) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")]
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = [("embed", c_p), ("layers", ctypes.POINTER(LayerWeights)), ("g_final", c_p),
+                ("lm_head", c_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtfm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(the HIP path has no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "tfm_status_string": (ctypes.c_char_p, [c_int]),
+            "tfm_last_hip_error": (c_int, []),
+            "tfm_version": (ctypes.c_char_p, []),
+            "tfm_rope_table_init": (c_int, [c_p, c_int, c_int, ctypes.c_double, c_p]),
+            "tfm_embed": (c_int, [c_p, c_i64, c_p, c_int, c_int, c_int, c_p, c_p, c_p]),
+            "tfm_rmsnorm": (c_int, [c_p, c_int, c_p, c_int, c_p, c_int, c_i64, c_int,
+                                    ctypes.c_float, c_p]),
+            "tfm_rope": (c_int, [c_p, c_int, c_i64, c_p, c_int, c_int, c_int, c_int, c_p, c_int,
+                                 c_p]),
+            "tfm_linear": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_i64, c_int, c_int, c_i64,
+                                   c_p]),
+            "tfm_causal_attention": (c_int, [c_p, c_i64, c_p, c_p, c_i64, c_p, c_i64, c_int,
+                                             c_int, c_int, c_int, c_int, c_int, c_p]),
+            "tfm_swiglu_workspace_bytes": (c_size, [c_i64, c_int, c_int]),
+            "tfm_swiglu_ffn": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_int, c_int, c_int,
+                                       c_p, c_size, c_p]),
+            "tfm_workspace_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
+            "tfm_block_forward": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
+                                          c_p, c_p, c_int, c_int, c_p, c_p, c_size, c_p]),
+            "tfm_model_forward": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
+                                          c_p, c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p,
+                                          c_size, c_p]),
+            "tfm_check_device_flags": (c_int, [c_p, c_p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise TfmError(st, where, lib().tfm_last_hip_error())
+
+
+# ------------------------------------------------------------------ tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def dt_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def torch_dtype(code: int):
+    torch = _torch()
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _dev(t):
+    """Device pointer of a contiguous GPU tensor, or None."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ entry points
+def tfm_rope_table_init(max_seq: int, d_head: int, theta: float = 10000.0, device="cuda",
+                        stream=None):
+    torch = _torch()
+    t = torch.empty(max_seq * d_head, dtype=torch.float32, device=device)
+    _check(lib().tfm_rope_table_init(_dev(t), max_seq, d_head, float(theta), _stream(stream)),
+           "tfm_rope_table_init")
+    return t
+
+
+def tfm_embed(ids, table, x=None, err_flag=None, stream=None):
+    torch = _torch()
+    n = ids.numel()
+    vocab, d = table.shape
+    if x is None:
+        x = torch.empty(ids.shape + (d,), dtype=torch.float32, device=table.device)
+    _check(lib().tfm_embed(_dev(ids), n, _dev(table), dt_code(table), vocab, d, _dev(x),
+                           _dev(err_flag), _stream(stream)), "tfm_embed")
+    return x
+
+
+def tfm_rmsnorm(x, g, eps: float = 1e-5, out_dtype=None, y=None, stream=None):
+    torch = _torch()
+    d = x.shape[-1]
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().tfm_rmsnorm(_dev(x), dt_code(x), _dev(g), dt_code(g), _dev(y), dt_code(y),
+                             x.numel() // d, d, float(eps), _stream(stream)), "tfm_rmsnorm")
+    return y
+
+
+def tfm_rope(x, n_heads: int, d_head: int, cos_sin, max_seq: int, positions=None,
+             row_stride: int | None = None, stream=None):
+    """In-place RoPE on x of shape (B, S, row) (heads at offsets h*d_head)."""
+    B, S = x.shape[0], x.shape[1]
+    rs = x.stride(1) if row_stride is None else row_stride
+    _check(lib().tfm_rope(_dev(x), dt_code(x), rs, _dev(positions), B, S, n_heads, d_head,
+                          _dev(cos_sin), max_seq, _stream(stream)), "tfm_rope")
+    return x
+
+
+def tfm_linear(x, w, residual=None, out_dtype=None, y=None, ldy: int | None = None, stream=None):
+    torch = _torch()
+    N, K = w.shape
+    M = x.numel() // K
+    if y is None:
+        y = torch.empty((M, N if ldy is None else ldy), dtype=out_dtype or x.dtype, device=x.device)
+    ld = y.shape[-1] if ldy is None else ldy
+    _check(lib().tfm_linear(_dev(x), _dev(w), dt_code(x), _dev(residual), _dev(y), dt_code(y), M,
+                            N, K, ld, _stream(stream)), "tfm_linear")
+    return y
+
+
+def tfm_causal_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head: int, o=None,
+                         q_stride=None, kv_stride=None, o_stride=None, stream=None):
+    """q (B, S, >=Hq*dh) rows; k, v (B, S, >=Hkv*dh) rows (may be strided column views)."""
+    torch = _torch()
+    B, S = q.shape[0], q.shape[1]
+    if o is None:
+        o = torch.empty((B, S, n_heads * d_head), dtype=q.dtype, device=q.device)
+    qs = q.stride(1) if q_stride is None else q_stride
+    kvs = k.stride(1) if kv_stride is None else kv_stride
+    os_ = o.stride(1) if o_stride is None else o_stride
+    _check(lib().tfm_causal_attention(_dev(q), qs, _dev(k), _dev(v), kvs, _dev(o), os_, B, S,
+                                      n_heads, n_kv_heads, d_head, dt_code(q), _stream(stream)),
+           "tfm_causal_attention")
+    return o
+
+
+def tfm_swiglu_ffn(xn, w1, w3, w2, residual=None, out=None, stream=None):
+    torch = _torch()
+    d_ff, d = w1.shape
+    rows = xn.numel() // d
+    dt = dt_code(xn)
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=xn.device)
+    nbytes = lib().tfm_swiglu_workspace_bytes(rows, d_ff, dt)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=xn.device)
+    _check(lib().tfm_swiglu_ffn(_dev(xn), _dev(w1), _dev(w3), _dev(w2), _dev(residual), _dev(out),
+                                rows, d, d_ff, dt, _dev(ws), nbytes, _stream(stream)),
+           "tfm_swiglu_ffn")
+    return out
+
+
+def make_config(cfg, max_seq: int | None = None) -> Config:
+    return Config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.d_head, cfg.d_ff,
+                  cfg.vocab, max_seq or cfg.seq, cfg.eps, cfg.rope_theta,
+                  BF16 if cfg.dtype == "bf16" else F32)
+
+
+def tfm_workspace_bytes(ccfg: Config, B: int, S: int) -> int:
+    return lib().tfm_workspace_bytes(ctypes.byref(ccfg), B, S)
+
+
+class DeviceModel:
+    """Model weights resident in GPU memory plus the RoPE table and a workspace.
+
+    Holds torch tensors (device memory only); every forward runs through the C ABI.
+    """
+
+    LAYER_FIELDS = ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")
+
+    def __init__(self, inputs, device="cuda", max_seq: int | None = None, batch: int | None = None,
+                 seq: int | None = None):
+        torch = _torch()
+        cfg = inputs.cfg
+        self.cfg = cfg
+        self.dtype = torch_dtype(BF16 if cfg.dtype == "bf16" else F32)
+        self.max_seq = max_seq or cfg.seq
+        self.ccfg = make_config(cfg, self.max_seq)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=self.dtype)
+        self.embed = up(inputs.embed)
+        self.lm_head = self.embed if inputs.lm_head is inputs.embed else up(inputs.lm_head)
+        self.g_final = up(inputs.g_final)
+        self.layers = [{f: up(getattr(lw, f)) for f in self.LAYER_FIELDS} for lw in inputs.layers]
+        self._layer_structs = (LayerWeights * max(1, len(self.layers)))(
+            *[LayerWeights(*[t.data_ptr() for t in (L[f] for f in self.LAYER_FIELDS)])
+              for L in self.layers])
+        self.weights = ModelWeights(self.embed.data_ptr(), self._layer_structs,
+                                    self.g_final.data_ptr(), self.lm_head.data_ptr())
+        self.cos_sin = tfm_rope_table_init(self.max_seq, cfg.d_head, cfg.rope_theta, device)
+        self.ids = torch.from_numpy(inputs.ids).to(device)
+        self._ws = None
+        self._ws_shape = None
+        self.device = device
+
+    def workspace(self, B: int, S: int):
+        torch = _torch()
+        if self._ws_shape != (B, S):
+            n = tfm_workspace_bytes(self.ccfg, B, S)
+            if n == 0:
+                raise TfmError(-2, "tfm_workspace_bytes")
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+            self._ws_shape = (B, S)
+        return self._ws
+
+    def layer_struct(self, i: int) -> LayerWeights:
+        return self._layer_structs[i]
+
+    def forward(self, ids=None, positions=None, logits=None, logits_dtype=None, ld_logits=None,
+                stream=None):
+        torch = _torch()
+        ids = self.ids if ids is None else ids
+        B, S = ids.shape
+        V = self.cfg.vocab
+        ld = V if ld_logits is None else ld_logits
+        if logits is None:
+            logits = torch.empty((B * S, ld), dtype=logits_dtype or self.dtype, device=self.device)
+        ws = self.workspace(B, S)
+        _check(lib().tfm_model_forward(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                       _dev(ids), _dev(positions), _dev(logits), dt_code(logits),
+                                       ld, B, S, _dev(self.cos_sin), _dev(ws), ws.numel(),
+                                       _stream(stream)), "tfm_model_forward")
+        return logits
+
+    def check_flags(self, stream=None) -> None:
+        _check(lib().tfm_check_device_flags(_dev(self._ws), _stream(stream)), "tfm_check_device_flags")
+
+
+def tfm_block_forward(dm: DeviceModel, layer: int, x, positions=None, stream=None):
+    """One block of ``dm`` on the fp32 residual x (B, S, D), in place."""
+    B, S = x.shape[0], x.shape[1]
+    ws = dm.workspace(B, S)
+    _check(lib().tfm_block_forward(ctypes.byref(dm.ccfg), ctypes.byref(dm.layer_struct(layer)),
+                                   _dev(x), _dev(positions), B, S, _dev(dm.cos_sin), _dev(ws),
+                                   ws.numel(), _stream(stream)), "tfm_block_forward")
+    return x
+
+
+def tfm_model_forward(dm: DeviceModel, ids=None, positions=None, **kw):
+    return dm.forward(ids=ids, positions=positions, **kw)

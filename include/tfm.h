@@ -1,0 +1,166 @@
+/* tfm — forward pass of a pre-norm decoder-only Transformer on AMD MI355X (gfx950).
+ *
+ * C ABI of libtfm.so. Every compute step runs in hand-written HIP kernels on the caller's
+ * stream. The library allocates no device memory and keeps no pointer after a call
+ * returns; the caller owns every buffer and keeps it alive until the stream has drained.
+ *
+ * Sources, by page title and section:
+ *  [T1] "从零实现一个完整的 LLM（CS336）——Transformer 篇" (dujian.net): 5.2 Embedding,
+ *       5.3 Linear and SwiGLU, 5.4 Attention, 5.5 RoPE, 5.6 RMSNorm, 5.7 assembly.
+ *  [T2] "LLM 2: Transformer 原理与实现" (juejin.cn): RMSNorm, SwiGLU FFN, RoPE, GQA/MQA.
+ *  [T3] "从零实现一个完整的LLM（CS336）——Transformer篇" (fengye404.top): 7 RoPE, 8 Attention.
+ *
+ * Common conventions
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *  - Device pointers are marked [dev]; host pointers [host]. All pointers to device data
+ *    must be 16-byte aligned unless stated otherwise (TFM_ERR_ALIGN).
+ *  - dtype codes: TFM_F32 (IEEE float) and TFM_BF16 (bfloat16, stored as 16-bit words).
+ *  - Weight matrices are (out_features, in_features), row-major: y = x W^T  [T1 5.3].
+ *  - Activations are (rows, features), row-major; for sequence data rows are (b, s) with
+ *    s fastest. The residual stream is float32 for both dtypes.
+ *  - Every argument check (null, shape, dtype, alignment, workspace size) runs on the host
+ *    before anything is enqueued; on failure nothing is launched and a negative status is
+ *    returned. TFM_ERR_HIP means a launch failed; tfm_last_hip_error() gives the code.
+ *  - All calls are asynchronous with respect to the host.
+ */
+#ifndef TFM_H
+#define TFM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TFM_F32 = 0, TFM_BF16 = 1 } tfm_dtype;
+
+typedef enum {
+  TFM_OK = 0,
+  TFM_ERR_NULL = -1,        /* a required pointer is NULL */
+  TFM_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  TFM_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+  TFM_ERR_WORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes() figure */
+  TFM_ERR_ALIGN = -5,       /* pointer or stride not aligned as required */
+  TFM_ERR_UNSUPPORTED = -6, /* valid request this build does not implement (e.g. d_head) */
+  TFM_ERR_HIP = -7,         /* a HIP launch or copy failed */
+  TFM_ERR_TOKEN = -8        /* a token id was outside [0, vocab) (device-side check) */
+} tfm_status;
+
+/* Model hyper-parameters. n_heads * d_head need not equal d_model; n_heads % n_kv_heads
+ * must be 0 (contiguous query-head groups share a KV head  [T2 GQA]). */
+typedef struct {
+  int n_layers, d_model, n_heads, n_kv_heads, d_head, d_ff, vocab, max_seq_len;
+  float eps;        /* RMSNorm epsilon, inside the square root  [T1 5.6] */
+  float rope_theta; /* RoPE base  [T1 5.5] */
+  int dtype;        /* tfm_dtype of weights, GEMM operands and activations */
+} tfm_config;
+
+/* [dev] pointers of one block's weights, all of the model dtype.
+ * g_*: (d_model); wq: (n_heads*d_head, d_model); wk, wv: (n_kv_heads*d_head, d_model);
+ * wo: (d_model, n_heads*d_head); w1 (gate), w3 (up): (d_ff, d_model); w2: (d_model, d_ff). */
+typedef struct {
+  const void *g_attn, *wq, *wk, *wv, *wo, *g_ffn, *w1, *w3, *w2;
+} tfm_layer_weights;
+
+/* embed: [dev] (vocab, d_model); layers: [host] array of n_layers; g_final: [dev] (d_model);
+ * lm_head: [dev] (vocab, d_model), may equal embed (tied weights). */
+typedef struct {
+  const void *embed;
+  const tfm_layer_weights *layers;
+  const void *g_final;
+  const void *lm_head;
+} tfm_model_weights;
+
+const char *tfm_status_string(int status);
+/* hipError_t behind the last TFM_ERR_HIP returned on this thread (0 if none). */
+int tfm_last_hip_error(void);
+/* Library version string. */
+const char *tfm_version(void);
+
+/* RoPE table  [T1 5.5; T2 RoPE]: for p in [0, max_seq) and pair i in [0, d_head/2),
+ * angle = p * theta^(-2i/d_head) formed in double precision;
+ * cos_sin[(p*(d_head/2) + i)*2 + 0] = cos(angle), [... + 1] = sin(angle), stored as float.
+ * cos_sin: [dev] max_seq*d_head floats. d_head must be even and > 0. */
+int tfm_rope_table_init(float *cos_sin, int max_seq, int d_head, double theta, void *stream);
+
+/* Token embedding  [T1 5.2]: x[r, :] = table[ids[r], :] widened to float32.
+ * ids: [dev] int32 (n); table: [dev] (vocab, d) of table_dt; x: [dev] float32 (n, d).
+ * An id outside [0, vocab) writes a NaN row and sets *err_flag = 1 ([dev] int32, may be
+ * NULL); the caller clears the flag. d % 4 == 0. */
+int tfm_embed(const int32_t *ids, int64_t n, const void *table, int table_dt, int vocab, int d,
+              float *x, int32_t *err_flag, void *stream);
+
+/* RMSNorm  [T1 5.6; T2 RMSNorm]: y = x / sqrt(mean(x^2) + eps) * g per row of d elements.
+ * Sum of squares, scaling and gain are float32; one rounding to y_dt at the store.
+ * x: [dev] (rows, d) of x_dt; g: [dev] (d) of g_dt; y: [dev] (rows, d) of y_dt; y may not
+ * alias x. d % 4 == 0, rows >= 0 (0 enqueues nothing). */
+int tfm_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,
+                int64_t rows, int d, float eps, void *stream);
+
+/* RoPE in place  [T1 5.5; T2 RoPE; T3 7]: x viewed as (B, S, H, d_head) with consecutive
+ * tokens `row_stride` elements apart and head h at element offset h*d_head of a row.
+ * Adjacent pairs (2i, 2i+1) turn counter-clockwise by pos * theta^(-2i/d_head), using the
+ * table from tfm_rope_table_init (max_seq rows). positions: [dev] int32 (B, S) or NULL for
+ * 0..S-1 in every sequence; a position outside [0, max_seq) yields NaN for that token.
+ * x_dt is TFM_F32 or TFM_BF16; row_stride % 4 == 0, d_head % 4 == 0. */
+int tfm_rope(void *x, int x_dt, int64_t row_stride, const int32_t *positions, int B, int S,
+             int H, int d_head, const float *cos_sin, int max_seq, void *stream);
+
+/* Linear  [T1 5.3]: y[m, n] = sum_k x[m, k] w[n, k] (+ residual[m, n]).
+ * x: [dev] (M, K) of dt, row stride K; w: [dev] (N, K) of dt; y: [dev] (M, ldy) of y_dt.
+ * residual: [dev] float32 (M, ldy) or NULL; when given, y_dt must be TFM_F32 and y may
+ * equal residual (in-place accumulate). fp32 accumulation. K % 8 == 0 (bf16) or
+ * K % 4 == 0 (f32); ldy >= N. ldy need not be a multiple of anything (odd vocab sizes). */
+int tfm_linear(const void *x, const void *w, int dt, const float *residual, void *y, int y_dt,
+               int64_t M, int N, int K, int64_t ldy, void *stream);
+
+/* Causal multi-head attention  [T1 5.4; T3 8; T2 GQA]:
+ * o[b,s,h,:] = sum_{t<=s} softmax_t(q[b,s,h,:] . k[b,t,g,:] / sqrt(d_head)) v[b,t,g,:]
+ * with g = h / (Hq/Hkv). Masking follows token order within a sequence (not positions).
+ * q: [dev] rows of q_stride elements, head h at offset h*d_head; k, v: rows of kv_stride
+ * elements with Hkv heads; o: [dev] rows of o_stride elements, Hq heads. All of dtype dt.
+ * Softmax state is float32; for bf16 the probabilities are rounded to bf16 before the PV
+ * product. bf16 supports d_head in {32, 64, 128}; f32 supports d_head in {16, 32, 64, 128}.
+ * Strides % 8 == 0. */
+int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
+                         int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
+                         int Hkv, int d_head, int dt, void *stream);
+
+/* SwiGLU FFN  [T1 5.3; T2 SwiGLU FFN]:
+ * out = (residual +) W2 ( SiLU(xn W1^T) * (xn W3^T) ), W1 the gate, W3 the up branch.
+ * xn: [dev] (rows, d) of dt; w1, w3: [dev] (d_ff, d); w2: [dev] (d, d_ff); residual: [dev]
+ * float32 (rows, d) or NULL (may equal out); out: [dev] float32 (rows, d).
+ * ws: [dev] workspace of at least tfm_swiglu_workspace_bytes(rows, d_ff, dt) bytes. */
+size_t tfm_swiglu_workspace_bytes(int64_t rows, int d_ff, int dt);
+int tfm_swiglu_ffn(const void *xn, const void *w1, const void *w3, const void *w2,
+                   const float *residual, float *out, int64_t rows, int d, int d_ff, int dt,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace of tfm_block_forward / tfm_model_forward for B sequences of S tokens. */
+size_t tfm_workspace_bytes(const tfm_config *cfg, int B, int S);
+
+/* One pre-norm block  [T1 5.7; T2 FFN & PreNorm] on the float32 residual x (B*S, d_model),
+ * in place:  x <- x + W_O attn(RoPE(RMSNorm(x) W_{Q,K,V}^T));  x <- x + SwiGLU(RMSNorm(x)).
+ * positions: [dev] int32 (B, S) or NULL; cos_sin: table of cfg->max_seq_len rows. */
+int tfm_block_forward(const tfm_config *cfg, const tfm_layer_weights *w, float *x,
+                      const int32_t *positions, int B, int S, const float *cos_sin, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Whole forward  [T1 5.7]: x = embed[ids]; n_layers blocks; RMSNorm(g_final); logits =
+ * x_f lm_head^T for every position, no softmax. ids: [dev] int32 (B, S); logits: [dev]
+ * (B*S, ld_logits) of logits_dt, ld_logits >= vocab (any value; odd is allowed).
+ * An out-of-range id is reported by tfm_check_device_flags (NaN logits for that row). */
+int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                      const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                      int B, int S, const float *cos_sin, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Waits for `stream`, then returns TFM_ERR_TOKEN if the last tfm_model_forward that used
+ * this workspace saw an out-of-range token id, else TFM_OK. */
+int tfm_check_device_flags(const void *ws, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_softmax.argtypes = [_p, c_i64, c_int, _p]
         L.oracle_attention.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int, c_int,
                                        c_int, _p, _p]
+        L.oracle_attention_rows.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int,
+                                            c_int, c_int, _p, c_i64, _p]
         L.oracle_silu.restype = c_double
         L.oracle_silu.argtypes = [c_double]
         L.oracle_swiglu.argtypes = [_p, c_i64, c_int, c_int, _p, _p, _p, _p, _p]
@@ -144,6 +146,18 @@ def attention(q, k, v, n_heads: int, n_kv_heads: int, want_probs: bool = False):
     lib().oracle_attention(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
                            n_kv_heads, dh, _ptr(o), _ptr(probs))
     return (o, probs) if want_probs else o
+
+
+def attention_rows(q, k, v, n_heads: int, n_kv_heads: int, rows):
+    """Causal attention output at the listed rows (b*S + s) only: (len(rows), Hq*dh)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, S, qd = q.shape
+    dh = qd // n_heads
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, qd), dtype=np.float64)
+    lib().oracle_attention_rows(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
+                                n_kv_heads, dh, _ptr(rows), rows.size, _ptr(o))
+    return o
 
 
 def silu(u: float) -> float:

@@ -97,40 +97,60 @@ void oracle_softmax(const double *s, int64_t rows, int n, double *p) {
 /* [T1 5.4 Attention; T3 8]: scores q.k / sqrt(dh) over the visible keys t <= s (the causal
  * mask gives the others weight exactly 0), a max-subtracted softmax over them, then the
  * probability-weighted sum of the value rows. [T2 GQA]: a contiguous group of Hq/Hkv query
- * heads shares one KV head. */
+ * heads shares one KV head. One query row of one head; sc is scratch of >= s+1 doubles. */
+static void attend_one(const double *q, int64_t q_stride, const double *k, const double *v,
+                       int64_t kv_stride, int S, int Hq, int Hkv, int dh, int b, int h, int s,
+                       double *os, double *prow, double *sc) {
+  const int g = h / (Hq / Hkv);
+  const double scale = 1.0 / sqrt((double)dh);
+  const double *qs = q + ((int64_t)b * S + s) * q_stride + (int64_t)h * dh;
+  double m = -INFINITY;
+  for (int t = 0; t <= s; ++t) {
+    const double *kt = k + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
+    double dot = 0.0;
+    for (int e = 0; e < dh; ++e) dot += qs[e] * kt[e];
+    sc[t] = dot * scale;
+    if (sc[t] > m) m = sc[t];
+  }
+  double sum = 0.0;
+  for (int t = 0; t <= s; ++t) sum += exp(sc[t] - m);
+  for (int e = 0; e < dh; ++e) os[e] = 0.0;
+  for (int t = 0; t <= s; ++t) {
+    double pt = exp(sc[t] - m) / sum;
+    if (prow) prow[t] = pt;
+    const double *vt = v + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
+    for (int e = 0; e < dh; ++e) os[e] += pt * vt[e];
+  }
+  if (prow)
+    for (int t = s + 1; t < S; ++t) prow[t] = 0.0;
+}
+
 void oracle_attention(const double *q, int64_t q_stride, const double *k, const double *v,
                       int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, double *o,
                       double *probs) {
-  const int group = Hq / Hkv;
-  const double scale = 1.0 / sqrt((double)dh);
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < Hq; ++h) {
-      const int g = h / group;
       double *sc = (double *)malloc(sizeof(double) * (size_t)S);
-      for (int s = 0; s < S; ++s) {
-        const double *qs = q + ((int64_t)b * S + s) * q_stride + (int64_t)h * dh;
-        double m = -INFINITY;
-        for (int t = 0; t <= s; ++t) {
-          const double *kt = k + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
-          double dot = 0.0;
-          for (int e = 0; e < dh; ++e) dot += qs[e] * kt[e];
-          sc[t] = dot * scale;
-          if (sc[t] > m) m = sc[t];
-        }
-        double sum = 0.0;
-        for (int t = 0; t <= s; ++t) sum += exp(sc[t] - m);
-        double *os = o + ((int64_t)b * S + s) * ((int64_t)Hq * dh) + (int64_t)h * dh;
-        for (int e = 0; e < dh; ++e) os[e] = 0.0;
-        for (int t = 0; t <= s; ++t) {
-          double pt = exp(sc[t] - m) / sum;
-          if (probs) probs[(((int64_t)b * Hq + h) * S + s) * S + t] = pt;
-          const double *vt = v + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
-          for (int e = 0; e < dh; ++e) os[e] += pt * vt[e];
-        }
-        if (probs)
-          for (int t = s + 1; t < S; ++t) probs[(((int64_t)b * Hq + h) * S + s) * S + t] = 0.0;
-      }
+      for (int s = 0; s < S; ++s)
+        attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s,
+                   o + ((int64_t)b * S + s) * ((int64_t)Hq * dh) + (int64_t)h * dh,
+                   probs ? probs + (((int64_t)b * Hq + h) * S + s) * S : NULL, sc);
+      free(sc);
+    }
+}
+
+void oracle_attention_rows(const double *q, int64_t q_stride, const double *k, const double *v,
+                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh,
+                           const int64_t *rows, int64_t n_rows, double *o) {
+  (void)B;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t i = 0; i < n_rows; ++i)
+    for (int h = 0; h < Hq; ++h) {
+      const int b = (int)(rows[i] / S), s = (int)(rows[i] % S);
+      double *sc = (double *)malloc(sizeof(double) * (size_t)S);
+      attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s,
+                 o + i * ((int64_t)Hq * dh) + (int64_t)h * dh, NULL, sc);
       free(sc);
     }
 }

@@ -68,6 +68,12 @@ void oracle_attention(const double *q, int64_t q_stride, const double *k, const 
                       int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, double *o,
                       double *probs);
 
+/* The rows of oracle_attention listed in `rows` (row = b*S + s), every head; o is
+ * (n_rows, Hq*dh). Same definition, for sampled checks at sizes where all rows would be slow. */
+void oracle_attention_rows(const double *q, int64_t q_stride, const double *k, const double *v,
+                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh,
+                           const int64_t *rows, int64_t n_rows, double *o);
+
 /* SiLU(u) = u * sigmoid(u)  [T1 5.3; T2 SiLU]. */
 double oracle_silu(double u);
 

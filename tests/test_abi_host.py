@@ -1,0 +1,189 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every function
+include/tfm.h declares, and every argument check returns its status before any launch.
+Pointers passed here are never dereferenced (validation fails first), so nothing runs on a
+device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decoder_only_transformer_rmsnorm_amd import synth, tfm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "tfm.h")
+
+OK, NULL, SHAPE, DTYPE, WS, ALIGN, UNSUP = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000  # a 16-byte aligned fake device address (never dereferenced here)
+PM = 0x10004  # misaligned
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tfm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tfm.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", tfm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L, n)
+    assert set(tfm.EXPORTS) == set(names)
+
+
+def test_status_strings(L):
+    for code in range(0, -9, -1):
+        s = L.tfm_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.tfm_status_string(5).decode() == "unknown status"
+    assert b"gfx950" in L.tfm_version()
+
+
+def test_rope_table_validation(L):
+    assert L.tfm_rope_table_init(None, 8, 16, 1e4, None) == NULL
+    assert L.tfm_rope_table_init(PM, 8, 16, 1e4, None) == ALIGN
+    assert L.tfm_rope_table_init(P, 8, 15, 1e4, None) == SHAPE
+    assert L.tfm_rope_table_init(P, 0, 16, 1e4, None) == SHAPE
+    assert L.tfm_rope_table_init(P, 8, 16, -1.0, None) == SHAPE
+
+
+def test_rmsnorm_validation(L):
+    f = L.tfm_rmsnorm
+    assert f(P, 2, P, 1, P + 64, 1, 4, 8, 1e-5, None) == DTYPE
+    assert f(P, 0, P, 1, P + 64, 1, 4, 6, 1e-5, None) == SHAPE
+    assert f(P, 0, P, 1, P + 64, 1, -1, 8, 1e-5, None) == SHAPE
+    assert f(P, 0, P, 1, P + 64, 1, 4, 8, -1.0, None) == SHAPE
+    assert f(None, 0, P, 1, P + 64, 1, 4, 8, 1e-5, None) == NULL
+    assert f(PM, 0, P, 1, P + 64, 1, 4, 8, 1e-5, None) == ALIGN
+    assert f(P, 0, P, 1, P, 1, 4, 8, 1e-5, None) == SHAPE       # y aliases x
+    assert f(None, 0, None, 1, None, 1, 0, 8, 1e-5, None) == OK  # empty: nothing launched
+
+
+def test_embed_and_rope_validation(L):
+    assert L.tfm_embed(P, 4, P, 3, 10, 8, P, None, None) == DTYPE
+    assert L.tfm_embed(P, 4, P, 1, 10, 6, P, None, None) == SHAPE
+    assert L.tfm_embed(None, 4, P, 1, 10, 8, P, None, None) == NULL
+    assert L.tfm_embed(P, 0, None, 1, 10, 8, None, None, None) == OK
+    assert L.tfm_rope(P, 1, 64, None, 2, 4, 2, 30, P, 8, None) == SHAPE   # d_head % 4
+    assert L.tfm_rope(P, 1, 60, None, 2, 4, 2, 32, P, 8, None) == SHAPE   # stride < H*dh
+    assert L.tfm_rope(P, 1, 66, None, 2, 4, 2, 32, P, 8, None) == ALIGN   # stride % 4
+    assert L.tfm_rope(P, 1, 64, None, 2, 9, 2, 32, P, 8, None) == SHAPE   # S > max_seq, no pos
+    assert L.tfm_rope(None, 1, 64, None, 2, 4, 2, 32, P, 8, None) == NULL
+
+
+def test_linear_validation(L):
+    f = L.tfm_linear
+    assert f(P, P, 1, None, P, 1, 16, 8, 12, 8, None) == SHAPE      # bf16 K % 8
+    assert f(P, P, 0, None, P, 0, 16, 8, 10, 8, None) == SHAPE      # f32 K % 4
+    assert f(P, P, 1, P, P, 1, 16, 8, 16, 8, None) == DTYPE         # residual needs f32 out
+    assert f(P, P, 1, None, P, 1, 16, 8, 16, 7, None) == SHAPE      # ldy < N
+    assert f(P, P, 1, None, None, 1, 16, 8, 16, 8, None) == NULL
+    assert f(P, PM, 1, None, P, 1, 16, 8, 16, 8, None) == ALIGN
+    assert f(None, None, 1, None, None, 1, 0, 8, 16, 8, None) == OK  # M == 0
+
+
+def test_attention_validation(L):
+    f = L.tfm_causal_attention
+    args = lambda **kw: dict(dict(q=P, qs=256, k=P, v=P, kvs=128, o=P, os=256, B=2, S=8, Hq=4,
+                                  Hkv=2, dh=64, dt=1), **kw)
+    call = lambda a: f(a["q"], a["qs"], a["k"], a["v"], a["kvs"], a["o"], a["os"], a["B"],
+                       a["S"], a["Hq"], a["Hkv"], a["dh"], a["dt"], None)
+    assert call(args(Hkv=3)) == SHAPE
+    assert call(args(qs=128)) == SHAPE
+    assert call(args(dh=16)) == UNSUP            # bf16 supports 32/64/128
+    assert call(args(dh=48, qs=192, os=192, kvs=96)) == UNSUP
+    assert call(args(dt=7)) == DTYPE
+    assert call(args(q=None)) == NULL
+    assert call(args(qs=260)) == ALIGN
+    assert call(args(k=PM)) == ALIGN
+    assert call(args(S=0)) == OK
+
+
+def _cfg(**kw):
+    c = tfm.make_config(synth.SMALL_BF16)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes_plan(L):
+    c = _cfg()
+    B, S = 32, 256
+    n = L.tfm_workspace_bytes(ctypes.byref(c), B, S)
+    M, D, F, e = B * S, 512, 1344, 2
+    expect = 256 + M * D * 4 + M * D * e + M * 3 * D * e + M * D * e + M * F * e
+    assert n == expect
+    assert L.tfm_workspace_bytes(ctypes.byref(_cfg(n_kv_heads=5)), B, S) == 0
+    assert L.tfm_workspace_bytes(ctypes.byref(c), B, 257) == 0    # S > max_seq_len
+    assert L.tfm_workspace_bytes(None, B, S) == 0
+    assert L.tfm_swiglu_workspace_bytes(100, 704, 1) == -(-100 * 704 * 2 // 256) * 256
+
+
+def _layer():
+    return tfm.LayerWeights(*([P] * 9))
+
+
+def test_block_and_model_validation(L):
+    c = _cfg()
+    lw = _layer()
+    ws_need = L.tfm_workspace_bytes(ctypes.byref(c), 2, 16)
+    blk = lambda cfg=c, w=lw, x=P, B=2, S=16, cs=P, ws=P, nb=ws_need: L.tfm_block_forward(
+        ctypes.byref(cfg) if cfg is not None else None, ctypes.byref(w) if w is not None else None,
+        x, None, B, S, cs, ws, nb, None)
+    assert blk(nb=ws_need - 1) == WS
+    assert blk(x=None) == NULL
+    assert blk(x=PM) == ALIGN
+    assert blk(cfg=_cfg(d_head=30)) == SHAPE
+    assert blk(cfg=_cfg(dtype=4)) == DTYPE
+    assert blk(cfg=_cfg(d_head=16, n_heads=32)) == UNSUP
+    assert blk(S=300) == SHAPE
+    assert blk(w=None) == NULL
+    bad = _layer(); bad.w3 = None
+    assert blk(w=bad) == NULL
+    bad = _layer(); bad.wo = PM
+    assert blk(w=bad) == ALIGN
+
+    layers = (tfm.LayerWeights * 4)(*[_layer() for _ in range(4)])
+    mw = tfm.ModelWeights(P, layers, P, P)
+    mdl = lambda cfg=c, w=mw, ld=10000, nb=ws_need, dtl=1: L.tfm_model_forward(
+        ctypes.byref(cfg), ctypes.byref(w) if w is not None else None, P, None, P, dtl, ld, 2, 16,
+        P, P, nb, None)
+    assert mdl(ld=9999) == SHAPE
+    assert mdl(nb=100) == WS
+    assert mdl(w=None) == NULL
+    assert mdl(dtl=2) == DTYPE
+    mw2 = tfm.ModelWeights(P, None, P, P)
+    assert mdl(w=mw2) == NULL
+    layers[2].g_ffn = None
+    assert mdl() == NULL
+
+
+def test_swiglu_validation(L):
+    f = L.tfm_swiglu_ffn
+    need = L.tfm_swiglu_workspace_bytes(64, 704, 1)
+    assert f(P, P, P, P, None, P, 64, 256, 704, 1, P, need - 1, None) == WS
+    assert f(P, P, P, P, None, P, 64, 250, 704, 1, P, need, None) == SHAPE
+    assert f(P, P, P, None, None, P, 64, 256, 704, 1, P, need, None) == NULL
+    assert f(P, P, P, P, PM, P, 64, 256, 704, 1, P, need, None) == ALIGN
+    assert f(P, P, P, P, None, P, 64, 256, 704, 9, P, need, None) == DTYPE
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The binding and the library never load the oracle; a missing library raises."""
+    src = open(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd", "tfm.py")).read()
+    assert "oracle" not in src.replace("oracle_", "")
+    for f in os.listdir(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd",
+                                                 "csrc", f)).read()

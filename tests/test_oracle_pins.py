@@ -397,3 +397,10 @@ def test_bf16_rounding_is_nearest_even():
     b = synth.round_to_bf16(a)
     assert b[0] == 1.0 and b[1] == 1.0 and b[2] == 1.0 + 4 * 2 ** -8 and b[3] == -2.5
     assert np.all((b.view(np.uint32) & 0xFFFF) == 0)
+
+
+def test_attention_rows_equal_full_rows():
+    q, k, v = _qkv(23, 2, 11, 4, 2, 8)
+    full = oracle.attention(q, k, v, 4, 2).reshape(22, 32)
+    rows = np.array([0, 5, 10, 11, 21])
+    np.testing.assert_array_equal(oracle.attention_rows(q, k, v, 4, 2, rows), full[rows])
