@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the decoder forward on one MI355X.
+
+A step is one tfm_model_forward over a batch of synthetic token ids: embedding, 12 pre-norm
+blocks (RMSNorm, QKV GEMM + RoPE, causal flash attention, out projection + residual,
+RMSNorm, SwiGLU up GEMM, down projection + residual), final RMSNorm and the LM-head GEMM,
+with weights, ids and the RoPE table already resident in HBM. Prints one JSON line.
+
+Besides the step time it reports:
+  roofline      the dominant kernel (the LM-head GEMM) timed alone through its entry point
+                on the same stream with HIP events: algorithmic FLOPs per launch divided by
+                the average launch duration, against the bf16 dense MFMA peak.
+  kernels       the same measurement for each kernel family of the step.
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15       # dense bf16 MFMA FLOP/s (MI355X published)
+PEAK_HBM = 8.0e12        # HBM3E bytes/s (MI355X published)
+METRIC = "decoder forward tokens/sec + attention/GEMM MFMA util, d768 L12 seq1024"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_launches(fn, n: int, stream) -> float:
+    """Average duration (ms) of fn() over n back-to-back launches on `stream`."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inputs, budget_s: float):
+    """The fp64 oracle on a bounded sample of the workload: whole sequences (all positions,
+    all logits) until about `budget_s` seconds of CPU work; tokens/s = tokens / wall time."""
+    import numpy as np
+    import oracle
+    threads = oracle.num_threads()
+    # calibrate on a short prefix, then pick the largest prefix that fits the budget
+    t0 = time.perf_counter()
+    oracle.model(cfg, inputs, ids=inputs.ids[:1, :64])
+    t64 = time.perf_counter() - t0
+    prefix = cfg.seq
+    est = t64 * (cfg.seq / 64) * 1.15
+    if est > budget_s:
+        prefix = max(64, int(64 * budget_s / max(t64, 1e-9) / 1.15) // 64 * 64)
+    t0 = time.perf_counter()
+    logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :prefix])
+    dt = time.perf_counter() - t0
+    assert np.isfinite(logits).all()
+    sample = (f"sequence 0 of {cfg.batch}, positions 0..{prefix - 1} ({prefix} tokens), all "
+              f"{cfg.vocab} logits per token, fp64 oracle with {threads} OpenMP threads")
+    return {"value": prefix / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
+    ap.add_argument("--logits", choices=["bf16", "f32"], default="bf16")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward shards by sequence with no exchange, "
+              "so a multi-GPU figure is not produced by this build (run with --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from decoder_only_transformer_rmsnorm_amd import accounting, synth, tfm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    cfg = synth.GPT2S_BF16
+    B, S, M = cfg.batch, cfg.seq, cfg.tokens
+    log(f"workload {cfg.name}: B={B} S={S} L={cfg.n_layers} d={cfg.d_model} V={cfg.vocab}")
+    inputs = synth.make_inputs(cfg, seed=0)
+    dm = tfm.DeviceModel(inputs)
+    stream = torch.cuda.current_stream()
+    logits_dtype = torch.float32 if args.logits == "f32" else torch.bfloat16
+    logits = torch.empty((M, cfg.vocab), dtype=logits_dtype, device="cuda")
+
+    def step():
+        dm.forward(logits=logits)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    dm.check_flags()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(logits[:: max(1, M // 64)]).all())
+
+    log(f"timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tok_s = M / (ms / 1e3)
+    flops = accounting.forward_flops(cfg)
+    log(f"{ms:.3f} ms/step, {tok_s / 1e6:.3f} M tokens/s, "
+        f"{flops['total'] / (ms / 1e3) / 1e12:.1f} TFLOP/s end to end (wall {wall:.2f} s)")
+
+    # ---- per-kernel timing through each entry point, same shapes as inside the step
+    kernels = {}
+    roofline = None
+    if not args.no_kernels:
+        D, F, V = cfg.d_model, cfg.d_ff, cfg.vocab
+        qd = cfg.n_heads * cfg.d_head
+        bf = torch.bfloat16
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        xres = torch.randn((M, D), device="cuda", generator=gen)
+        xn = torch.randn((M, D), device="cuda", generator=gen).to(bf)
+        L0 = dm.layers[0]
+        qkv = torch.randn((M, qd * 3), device="cuda", generator=gen).to(bf)
+        o = torch.empty((M, qd), dtype=bf, device="cuda")
+        u = torch.randn((M, F), device="cuda", generator=gen).to(bf)
+        tmp = torch.empty((M, max(3 * qd, D)), dtype=bf, device="cuda")
+        ws_ffn = torch.empty(tfm.lib().tfm_swiglu_workspace_bytes(M, F, 1), dtype=torch.uint8, device="cuda")
+        xout = torch.empty((M, D), device="cuda")
+        n = args.kernel_reps
+        flops_gemm = lambda N, K: 2.0 * M * N * K
+
+        def rec(name, ms_k, work, bound, unit_work):
+            if bound == "hbm":
+                ach = work / (ms_k / 1e3)
+                kernels[name] = {"ms": round(ms_k, 4), "GB/s": round(ach / 1e9, 1),
+                                 "frac_hbm": round(ach / PEAK_HBM, 4), "bytes": int(work)}
+            else:
+                ach = work / (ms_k / 1e3)
+                kernels[name] = {"ms": round(ms_k, 4), "TFLOP/s": round(ach / 1e12, 1),
+                                 "frac_mfma": round(ach / PEAK_BF16, 4), "flops": int(work)}
+            log(f"kernel {name}: {ms_k * 1e3:.1f} us, {kernels[name]}")
+
+        rec("rmsnorm", time_launches(lambda: tfm.tfm_rmsnorm(xres, L0["g_attn"], cfg.eps, y=xn), n, stream),
+            accounting.rmsnorm_bytes(M, D, 4, 2), "hbm", None)
+        # Q, K and V weights stacked so the timed GEMM has the QKV shape (N = 3*768).
+        wqkv = torch.cat([L0["wq"], L0["wk"], L0["wv"]]).contiguous()
+        rec("gemm_qkv", time_launches(lambda: tfm.tfm_linear(xn, wqkv, y=tmp[:, :3 * qd], ldy=tmp.shape[1]), n, stream),
+            flops_gemm(3 * qd, D), "mfma", None)
+        att_flops = accounting.forward_flops(cfg)["attn"] / cfg.n_layers
+        rec("attention", time_launches(lambda: tfm.tfm_causal_attention(
+            qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),
+            cfg.n_heads, cfg.n_kv_heads, cfg.d_head, o=o.view(B, S, qd),
+            q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd), n, stream), att_flops, "mfma", None)
+        rec("gemm_out_residual", time_launches(lambda: tfm.tfm_linear(o, L0["wo"], residual=xres, y=xres), n, stream),
+            flops_gemm(D, qd), "mfma", None)
+        rec("swiglu_ffn", time_launches(lambda: tfm.lib().tfm_swiglu_ffn(
+            xn.data_ptr(), L0["w1"].data_ptr(), L0["w3"].data_ptr(), L0["w2"].data_ptr(), xres.data_ptr(),
+            xout.data_ptr(), M, D, F, 1, ws_ffn.data_ptr(), ws_ffn.numel(), tfm._stream()), n, stream),
+            flops_gemm(2 * F, D) + flops_gemm(D, F), "mfma", None)
+        rec("gemm_down_residual", time_launches(lambda: tfm.tfm_linear(u, L0["w2"], residual=xres, y=xres), n, stream),
+            flops_gemm(D, F), "mfma", None)
+        lm_ms = time_launches(lambda: tfm.tfm_linear(xn, dm.lm_head, y=logits), n, stream)
+        rec("gemm_lm_head", lm_ms, flops_gemm(V, D), "mfma", None)
+        lm_flops = flops_gemm(V, D)
+        ach = lm_flops / (lm_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "gemm_kernel<bf16, EPI_STORE> (LM head, M=8192 N=50257 K=768)",
+                    "achieved": round(ach, 1), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                    "frac": round(ach * 1e12 / PEAK_BF16, 4), "flops_per_launch": int(lm_flops),
+                    "avg_launch_ms": round(lm_ms, 4), "traffic": traffic_from_profiles("gemm_lm_head")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle, budget {args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(cfg, inputs, args.cpu_budget)
+        log(f"cpu baseline {cpu['value']:.2f} tokens/s ({cpu['sample']}, {cpu['seconds']} s)")
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded uniform ids, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "batch": B, "seq_len": S, "n_layers": cfg.n_layers,
+                   "d_model": cfg.d_model, "n_heads": cfg.n_heads, "d_ff": cfg.d_ff,
+                   "vocab": cfg.vocab, "logits_dtype": args.logits, "parallelism": "single GPU"},
+        "end_to_end": {"flops_per_step_causal": int(flops["total"]),
+                       "TFLOP/s": round(flops["total"] / (ms / 1e3) / 1e12, 1),
+                       "frac_mfma": round(flops["total"] / (ms / 1e3) / PEAK_BF16, 4)},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
