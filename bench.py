@@ -34,12 +34,27 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_launches(fn, n: int, stream) -> float:
-    """Average duration (ms) of fn() over n back-to-back launches on `stream`."""
+def time_launches(fn, n: int, stream, graph: bool = True) -> float:
+    """Average duration (ms) of fn() over n back-to-back launches on `stream`.
+
+    With `graph`, the n launches are captured once in a HIP graph and the replay is timed,
+    so host-side launch overhead (Python, ctypes) does not inflate short kernels."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
     torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        end.synchronize()
+        return start.elapsed_time(end) / n
     with torch.cuda.stream(stream):
         start.record(stream)
         for _ in range(n):
@@ -170,7 +185,6 @@ def main() -> int:
         qkv = torch.randn((M, qd * 3), device="cuda", generator=gen).to(bf)
         o = torch.empty((M, qd), dtype=bf, device="cuda")
         u = torch.randn((M, F), device="cuda", generator=gen).to(bf)
-        tmp = torch.empty((M, max(3 * qd, D)), dtype=bf, device="cuda")
         ws_ffn = torch.empty(tfm.lib().tfm_swiglu_workspace_bytes(M, F, 1), dtype=torch.uint8, device="cuda")
         xout = torch.empty((M, D), device="cuda")
         n = args.kernel_reps
@@ -189,10 +203,10 @@ def main() -> int:
 
         rec("rmsnorm", time_launches(lambda: tfm.tfm_rmsnorm(xres, L0["g_attn"], cfg.eps, y=xn), n, stream),
             accounting.rmsnorm_bytes(M, D, 4, 2), "hbm", None)
-        # Q, K and V weights stacked so the timed GEMM has the QKV shape (N = 3*768).
-        wqkv = torch.cat([L0["wq"], L0["wk"], L0["wv"]]).contiguous()
-        rec("gemm_qkv", time_launches(lambda: tfm.tfm_linear(xn, wqkv, y=tmp[:, :3 * qd], ldy=tmp.shape[1]), n, stream),
-            flops_gemm(3 * qd, D), "mfma", None)
+        qkv_out = torch.empty((B, S, 3 * qd), dtype=bf, device="cuda")
+        rec("gemm_qkv_rope", time_launches(lambda: tfm.tfm_qkv_rope(
+            xn.view(B, S, D), L0["wq"], L0["wk"], L0["wv"], cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
+            dm.cos_sin, dm.max_seq, qkv=qkv_out), n, stream), flops_gemm(3 * qd, D), "mfma", None)
         att_flops = accounting.forward_flops(cfg)["attn"] / cfg.n_layers
         rec("attention", time_launches(lambda: tfm.tfm_causal_attention(
             qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),

@@ -211,6 +211,28 @@ int tfm_linear(const void *x, const void *w, int dt, const float *residual, void
   return hip_status(launch_gemm(residual ? EPI_RESIDUAL : EPI_STORE, dt, g, (hipStream_t)stream));
 }
 
+int tfm_qkv_rope(const void *xn, const void *wq, const void *wk, const void *wv, void *qkv,
+                 const int32_t *positions, int B, int S, int d, int Hq, int Hkv, int d_head,
+                 const float *cos_sin, int max_seq, int dt, void *stream) {
+  if (!valid_dt(dt)) return TFM_ERR_DTYPE;
+  const int kalign = dt == TFM_BF16 ? 8 : 4;
+  if (B < 0 || S < 0 || d <= 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || d_head % 4 != 0 ||
+      d % kalign != 0 || max_seq <= 0)
+    return TFM_ERR_SHAPE;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!xn || !wq || !wk || !wv || !qkv || !cos_sin) return TFM_ERR_NULL;
+  if (!aligned16(xn) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) || !aligned16(qkv) ||
+      !aligned16(cos_sin))
+    return TFM_ERR_ALIGN;
+  if (!positions && S > max_seq) return TFM_ERR_SHAPE;
+  const int qd = Hq * d_head, kvd = Hkv * d_head;
+  GemmArgs g{};
+  g.a = xn; g.lda = d; g.w0 = wq; g.w1 = wk; g.w2 = wv; g.n0 = qd; g.n1 = kvd;
+  g.M = (int64_t)B * S; g.N = qd + 2 * kvd; g.K = d; g.y = qkv; g.ldy = qd + 2 * kvd; g.y_dt = dt;
+  g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = d_head; g.max_seq = max_seq;
+  return hip_status(launch_gemm(EPI_QKV_ROPE, dt, g, (hipStream_t)stream));
+}
+
 int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                          int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                          int Hkv, int d_head, int dt, void *stream) {

@@ -11,6 +11,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA bf16 oper
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;   // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;   // buffer load/store data
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 constexpr int kWave = 64;
 

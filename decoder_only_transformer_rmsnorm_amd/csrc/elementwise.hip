@@ -41,13 +41,14 @@ __global__ void embed_kernel(const int32_t *ids, int64_t n, const T *table, int 
 }
 
 // RMSNorm ("Transformer 篇" 5.6; "LLM 2" RMSNorm): one wave per row. Each lane reads
-// 4 consecutive elements per step (the wave covers 256 contiguous elements per step, so
-// every load is a full, coalesced 1 KiB (fp32) or 512 B (bf16) transaction); up to
-// kCache steps stay in registers so the row is read from HBM exactly once for
-// d <= 256 * kCache. Sum of squares and scaling in fp32, one rounding at the store.
-constexpr int kCache = 8;
+// 4 consecutive elements per step (a wave covers 256 contiguous elements per step, so every
+// load is a full, coalesced 1 KiB (fp32) or 512 B (bf16) transaction). VPT steps per lane
+// are a compile-time count, so all of a row's loads are issued before the first is used and
+// the row is read from HBM exactly once; rows wider than 256 * kMaxVpt take a second pass.
+// Sum of squares and scaling in fp32, one rounding at the store.
+constexpr int kMaxVpt = 8;
 
-template <typename TX, typename TG, typename TY>
+template <int VPT, typename TX, typename TG, typename TY>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX *__restrict__ x,
                                                       const TG *__restrict__ g,
                                                       TY *__restrict__ y, int64_t rows, int d,
@@ -58,28 +59,30 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX *__restrict__ x,
   const TX *xr = x + row * d;
   TY *yr = y + row * d;
   const int ng = d >> 2;
-  f32x4_t c[kCache];
+  f32x4_t c[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int gi = lane + 64 * i;
+    // clamp the index instead of branching so every load issues back to back
+    c[i] = load4(xr + 4 * (gi < ng ? gi : 0));
+    if (gi >= ng) c[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kCache; ++i) {
-    const int gi = lane + 64 * i;
-    if (gi < ng) {
-      c[i] = load4(xr + 4 * gi);
-      ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
-    }
-  }
-  for (int gi = lane + 64 * kCache; gi < ng; gi += 64) {
+  for (int i = 0; i < VPT; ++i)
+    ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
+  for (int gi = lane + 64 * VPT; gi < ng; gi += 64) {
     const f32x4_t v = load4(xr + 4 * gi);
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / (float)d + eps);
 #pragma unroll
-  for (int i = 0; i < kCache; ++i) {
+  for (int i = 0; i < VPT; ++i) {
     const int gi = lane + 64 * i;
     if (gi < ng) store4(yr + 4 * gi, c[i] * inv * load4(g + 4 * gi));
   }
-  for (int gi = lane + 64 * kCache; gi < ng; gi += 64)
+  for (int gi = lane + 64 * VPT; gi < ng; gi += 64)
     store4(yr + 4 * gi, load4(xr + 4 * gi) * inv * load4(g + 4 * gi));
 }
 
@@ -120,12 +123,27 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
 
 inline unsigned blocks_for(int64_t n, int t) { return (unsigned)((n + t - 1) / t); }
 
+template <int VPT, typename TX, typename TG, typename TY>
+hipError_t rms4(const void *x, const void *g, void *y, int64_t rows, int d, float eps,
+                hipStream_t s) {
+  rmsnorm_kernel<VPT, TX, TG, TY><<<blocks_for(rows, 4), 256, 0, s>>>(
+      (const TX *)x, (const TG *)g, (TY *)y, rows, d, eps);
+  return hipGetLastError();
+}
+
 template <typename TX, typename TG, typename TY>
 hipError_t rms3(const void *x, const void *g, void *y, int64_t rows, int d, float eps,
                 hipStream_t s) {
-  rmsnorm_kernel<TX, TG, TY><<<blocks_for(rows, 4), 256, 0, s>>>(
-      (const TX *)x, (const TG *)g, (TY *)y, rows, d, eps);
-  return hipGetLastError();
+  switch ((d + 255) / 256) {   // float4 steps per lane
+    case 1: return rms4<1, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 2: return rms4<2, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 3: return rms4<3, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 4: return rms4<4, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 5: return rms4<5, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 6: return rms4<6, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    case 7: return rms4<7, TX, TG, TY>(x, g, y, rows, d, eps, s);
+    default: return rms4<kMaxVpt, TX, TG, TY>(x, g, y, rows, d, eps, s);
+  }
 }
 
 template <typename TX, typename TG>

@@ -205,11 +205,14 @@ __device__ __forceinline__ int swz_rb(int row) {
 }
 
 // Epilogue staging: output rows of `rb` bytes, 16-byte chunks XOR-swizzled by the row so
-// that the 32 rows written by one store instruction spread over the banks.
+// that the 32 rows written by one store instruction spread over the banks. The XOR stays
+// inside an aligned block of p chunks, p the largest power of two dividing the row's chunk
+// count, so it permutes the chunks of a row even when that count is not a power of two.
 __device__ __forceinline__ int stage_off(int r, int byte, int rb) {
   const int cpr = rb >> 4;
+  const int p = cpr & -cpr;
   const int c = byte >> 4;
-  return r * rb + ((c ^ (r & (cpr - 1) & 31)) << 4) + (byte & 15);
+  return r * rb + ((c ^ (r & (p - 1) & 31)) << 4) + (byte & 15);
 }
 
 template <int BM, int BN, int BK, int NST>
@@ -226,9 +229,9 @@ struct BfTile {
   static_assert(NST >= 2 && (NST - 2) * LOADS <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int BK, int NST, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
-                                                                int tiles_n) {
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
+                                                                  int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = BfTile<BM, BN, BK, NST>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
@@ -237,6 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
   constexpr int NBM = WM / 32, NBN = WN / 32;      // 32x32 blocks per wave
   constexpr int OUT_COLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
   constexpr int LDS = T::RING > BM * OUT_COLS * 2 ? T::RING : BM * OUT_COLS * 2;
+  static_assert(LDS * OCC <= kLdsBytes, "LDS does not allow the requested occupancy");
   static_assert(EPI != EPI_SWIGLU || (NBN % 2) == 0, "SwiGLU needs gate/up block pairs");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
@@ -387,8 +391,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
         const int64_t m = m0 + wm * WM + bm * 32 + l32;
         int pos = 0;
         if constexpr (EPI == EPI_QKV_ROPE) {
-          const int64_t mc = m < g.M ? m : g.M - 1;
-          pos = g.positions ? g.positions[mc] : (int)(mc % g.S);
+          // rows fit in 32 bits here (M * row width < 2^31 elements); no 64-bit division
+          const int mc = (int)(m < g.M ? m : g.M - 1);
+          pos = g.positions ? g.positions[mc] : mc % g.S;
         }
 #pragma unroll
         for (int bn = 0; bn < (EPI == EPI_SWIGLU ? NBN / 2 : NBN); ++bn) {
@@ -411,7 +416,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
                 const int n = n0 + col;
                 if (n < g.n0 + g.n1) {  // q and k columns rotate; v columns pass through
                   if (pos >= 0 && pos < g.max_seq) {
-                    const int i0 = (n % g.d_head) >> 1;
+                    const int dmask = g.d_head - 1;
+                    const int i0 = ((g.d_head & dmask) == 0 ? (n & dmask) : n % g.d_head) >> 1;
                     const f32x4_t cs = *(const f32x4_t *)(g.cos_sin +
                                                           ((int64_t)pos * (g.d_head >> 1) + i0) * 2);
                     const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
@@ -460,10 +466,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
         }
       } else if (out_bf16) {
         bf16_t *y = (bf16_t *)g.y + off;
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
         if (vec_ok && n + 8 <= ncols) {
           *(uint4 *)y = raw;
+        } else if (n + 8 <= ncols && (off & 1) == 0) {
+          // row stride not a multiple of 8 elements: 4-byte stores on an even element
+#pragma unroll
+          for (int x = 0; x < 4; ++x) ((uint32_t *)y)[x] = w4[x];
+        } else if (n + 8 <= ncols) {
+          // odd element offset: one 2-byte store, three 4-byte stores, one 2-byte store
+          y[0] = (bf16_t)(w4[0] & 0xffffu);
+#pragma unroll
+          for (int x = 0; x < 3; ++x)
+            *(uint32_t *)(y + 1 + 2 * x) = (w4[x] >> 16) | (w4[x + 1] << 16);
+          y[7] = (bf16_t)(w4[3] >> 16);
         } else {
-          const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
           for (int x = 0; x < 8 && n + x < ncols; ++x)
             y[x] = (bf16_t)((x & 1) ? (w4[x >> 1] >> 16) : (w4[x >> 1] & 0xffffu));
         }
@@ -605,13 +622,13 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
   tn = EPI == EPI_SWIGLU ? (g.n0 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
 }
 
-template <int BM, int BN, int BK, int NST, int EPI>
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI>), dim3((unsigned)(tm * tn)),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC>), dim3((unsigned)(tm * tn)),
                      dim3(kThreads), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
@@ -629,11 +646,13 @@ hipError_t run_f32(const GemmArgs &g, hipStream_t s) {
 
 hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
   switch (epi) {
-    // tile shapes chosen per epilogue by measurement on the decoder's GEMM shapes
-    case EPI_STORE: return run_bf16<256, 256, 32, 3, EPI_STORE>(g, s);
-    case EPI_RESIDUAL: return run_bf16<256, 128, 32, 4, EPI_RESIDUAL>(g, s);
-    case EPI_QKV_ROPE: return run_bf16<192, 256, 64, 2, EPI_QKV_ROPE>(g, s);
-    case EPI_SWIGLU: return run_bf16<256, 256, 32, 3, EPI_SWIGLU>(g, s);
+    // Tile shapes chosen per epilogue by a sweep on the decoder's GEMM shapes with random
+    // operands. All use <= 80 KB of LDS and <= 256 registers per lane, so two workgroups share
+    // a CU: one multiplies while the other waits on loads or writes its outputs.
+    case EPI_STORE: return run_bf16<256, 128, 32, 3, EPI_STORE, 2>(g, s);
+    case EPI_RESIDUAL: return run_bf16<128, 128, 64, 2, EPI_RESIDUAL, 2>(g, s);
+    case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 2, EPI_QKV_ROPE, 2>(g, s);
+    case EPI_SWIGLU: return run_bf16<128, 256, 32, 3, EPI_SWIGLU, 2>(g, s);
   }
   return hipErrorInvalidValue;
 }

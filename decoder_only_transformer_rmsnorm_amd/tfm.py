@@ -21,7 +21,7 @@ STATUS = {0: "TFM_OK", -1: "TFM_ERR_NULL", -2: "TFM_ERR_SHAPE", -3: "TFM_ERR_DTY
           -7: "TFM_ERR_HIP", -8: "TFM_ERR_TOKEN"}
 
 EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_table_init",
-           "tfm_embed", "tfm_rmsnorm", "tfm_rope", "tfm_linear", "tfm_causal_attention",
+           "tfm_embed", "tfm_rmsnorm", "tfm_rope", "tfm_linear", "tfm_qkv_rope", "tfm_causal_attention",
            "tfm_swiglu_workspace_bytes", "tfm_swiglu_ffn", "tfm_workspace_bytes",
            "tfm_block_forward", "tfm_model_forward", "tfm_check_device_flags"]
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                  c_p]),
             "tfm_linear": (c_int, [c_p, c_p, c_int, c_p, c_p, c_int, c_i64, c_int, c_int, c_i64,
                                    c_p]),
+            "tfm_qkv_rope": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int,
+                                     c_int, c_int, c_p, c_int, c_int, c_p]),
             "tfm_causal_attention": (c_int, [c_p, c_i64, c_p, c_p, c_i64, c_p, c_i64, c_int,
                                              c_int, c_int, c_int, c_int, c_int, c_p]),
             "tfm_swiglu_workspace_bytes": (c_size, [c_i64, c_int, c_int]),
@@ -189,6 +191,20 @@ def tfm_linear(x, w, residual=None, out_dtype=None, y=None, ldy: int | None = No
     _check(lib().tfm_linear(_dev(x), _dev(w), dt_code(x), _dev(residual), _dev(y), dt_code(y), M,
                             N, K, ld, _stream(stream)), "tfm_linear")
     return y
+
+
+def tfm_qkv_rope(xn, wq, wk, wv, n_heads: int, n_kv_heads: int, d_head: int, cos_sin,
+                 max_seq: int, positions=None, qkv=None, stream=None):
+    """xn (B, S, d) -> qkv (B, S, (Hq + 2 Hkv) d_head) with RoPE on the q and k columns."""
+    torch = _torch()
+    B, S, d = xn.shape
+    width = (n_heads + 2 * n_kv_heads) * d_head
+    if qkv is None:
+        qkv = torch.empty((B, S, width), dtype=xn.dtype, device=xn.device)
+    _check(lib().tfm_qkv_rope(_dev(xn), _dev(wq), _dev(wk), _dev(wv), _dev(qkv), _dev(positions), B,
+                              S, d, n_heads, n_kv_heads, d_head, _dev(cos_sin), max_seq,
+                              dt_code(xn), _stream(stream)), "tfm_qkv_rope")
+    return qkv
 
 
 def tfm_causal_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head: int, o=None,

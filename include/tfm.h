@@ -115,6 +115,17 @@ int tfm_rope(void *x, int x_dt, int64_t row_stride, const int32_t *positions, in
 int tfm_linear(const void *x, const void *w, int dt, const float *residual, void *y, int y_dt,
                int64_t M, int N, int K, int64_t ldy, void *stream);
 
+/* Fused QKV projection with RoPE on q and k  [T1 5.4 Q, K, V and 5.5 RoPE; T2 RoPE]:
+ * qkv[r, :] = [xn_r W_Q^T | xn_r W_K^T | xn_r W_V^T], then the q and k heads rotate as in
+ * tfm_rope (adjacent pairs, position positions[r] or r % S); v is not rotated. The rotation
+ * is applied to the fp32 accumulators before the single rounding to dt.
+ * xn: [dev] (B*S, d) of dt; wq: [dev] (Hq*d_head, d); wk, wv: [dev] (Hkv*d_head, d);
+ * qkv: [dev] (B*S, (Hq + 2 Hkv) d_head) of dt; cos_sin: table of max_seq rows.
+ * d % 8 == 0 (bf16) or % 4 (f32); d_head % 4 == 0. */
+int tfm_qkv_rope(const void *xn, const void *wq, const void *wk, const void *wv, void *qkv,
+                 const int32_t *positions, int B, int S, int d, int Hq, int Hkv, int d_head,
+                 const float *cos_sin, int max_seq, int dt, void *stream);
+
 /* Causal multi-head attention  [T1 5.4; T3 8; T2 GQA]:
  * o[b,s,h,:] = sum_{t<=s} softmax_t(q[b,s,h,:] . k[b,t,g,:] / sqrt(d_head)) v[b,t,g,:]
  * with g = h / (Hq/Hkv). Masking follows token order within a sequence (not positions).

@@ -94,6 +94,20 @@ def test_linear_validation(L):
     assert f(None, None, 1, None, None, 1, 0, 8, 16, 8, None) == OK  # M == 0
 
 
+def test_qkv_rope_validation(L):
+    f = L.tfm_qkv_rope
+    ok = dict(xn=P, wq=P, wk=P, wv=P, qkv=P, B=2, S=8, d=64, Hq=4, Hkv=2, dh=16, cs=P, ms=8, dt=0)
+    call = lambda **kw: f(*[dict(ok, **kw)[k] for k in ("xn", "wq", "wk", "wv", "qkv")], None,
+                          *[dict(ok, **kw)[k] for k in ("B", "S", "d", "Hq", "Hkv", "dh", "cs", "ms", "dt")], None)
+    assert call(dt=5) == DTYPE
+    assert call(dh=18) == SHAPE
+    assert call(d=60, dt=1) == SHAPE
+    assert call(S=9) == SHAPE            # S > max_seq with default positions
+    assert call(wk=None) == NULL
+    assert call(qkv=PM) == ALIGN
+    assert call(B=0) == OK
+
+
 def test_attention_validation(L):
     f = L.tfm_causal_attention
     args = lambda **kw: dict(dict(q=P, qs=256, k=P, v=P, kvs=128, o=P, os=256, B=2, S=8, Hq=4,

@@ -133,6 +133,35 @@ def test_linear(dt, M, N, K, ldy_pad, res, out):
         assert np.all(pad == expect), "columns beyond N were written"
 
 
+# ---------------------------------------------------------------- fused QKV + RoPE
+@pytest.mark.parametrize("dt,B,S,d,Hq,Hkv,dh,use_pos", [("bf16", 2, 130, 256, 8, 2, 32, True),
+                                                        ("bf16", 3, 100, 768, 12, 12, 64, False),
+                                                        ("bf16", 1, 70, 512, 4, 1, 128, True),
+                                                        ("f32", 2, 50, 64, 4, 4, 16, True)])
+def test_qkv_rope(dt, B, S, d, Hq, Hkv, dh, use_pos):
+    say(f"qkv_rope dt={dt} B={B} S={S} d={d} Hq={Hq} Hkv={Hkv} dh={dh} pos={use_pos}")
+    tfm = tfm_mod()
+    max_seq = 1024
+    xn = synth.random_array((B, S, d), seed=S, dtype=dt)
+    wq = synth.random_array((Hq * dh, d), seed=1, std=0.05, dtype=dt)
+    wk = synth.random_array((Hkv * dh, d), seed=2, std=0.05, dtype=dt)
+    wv = synth.random_array((Hkv * dh, d), seed=3, std=0.05, dtype=dt)
+    pos = rng(S).integers(0, max_seq, size=(B, S)).astype(np.int32) if use_pos else None
+    cs = tfm.tfm_rope_table_init(max_seq, dh, 10000.0)
+    out = tfm.tfm_qkv_rope(to_dev(xn, dt), to_dev(wq, dt), to_dev(wk, dt), to_dev(wv, dt), Hq, Hkv,
+                           dh, cs, max_seq, positions=None if pos is None else torch.from_numpy(pos).cuda())
+    got = to_np(out)
+    q = oracle.rope(oracle.linear(xn, wq), Hq, 10000.0, pos=pos)
+    k = oracle.rope(oracle.linear(xn, wk), Hkv, 10000.0, pos=pos)
+    v = oracle.linear(xn, wv)
+    ref = np.concatenate([q, k, v], axis=-1)
+    # GEMM bound on |xn||w| (rotation preserves it pairwise) + fp32 rotation + one rounding
+    mag = np.concatenate([np.abs(xn) @ np.abs(w).T.astype(np.float64) for w in (wq, wk, wv)], axis=-1)
+    mag = np.maximum(mag, np.roll(mag, 1, axis=-1)) + np.maximum(mag, np.roll(mag, -1, axis=-1))
+    tol = 2 * d * F32_EPS * mag + (BF16_ULP if dt == "bf16" else 4 * F32_EPS) * np.abs(ref) + 1e-30
+    assert_within(got, ref, tol, "qkv_rope")
+
+
 # ---------------------------------------------------------------- attention
 def _attn_inputs(B, S, Hq, Hkv, dh, dt, seed, qk_scale=1.0):
     """q, k, v packed into one (B, S, Hq*dh + 2*Hkv*dh) buffer as the block lays them out."""
