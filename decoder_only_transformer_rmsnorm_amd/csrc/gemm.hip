@@ -30,6 +30,8 @@
 // row-blocks in its L2.
 // f32 kernel (the small fp32 model): the same tile logic with register-staged loads and
 // v_mfma_f32_32x32x2_f32.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -44,6 +46,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format 
 constexpr uint32_t kOOB = 0x80000000u;        // offset beyond any num_records used here
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -226,10 +229,12 @@ struct BfTile {
   static constexpr int RING = NST * STAGE;
   static_assert(A_INS * 4 * FILL_ROWS == BM && B_INS * 4 * FILL_ROWS == BN, "tile/fill mismatch");
   static_assert(RING <= kLdsBytes, "LDS ring too large");
-  static_assert(NST >= 2 && (NST - 2) * LOADS <= 63, "vmcnt range");
+  static_assert(NST >= 2 && NST <= 6 && (NST - 2) * LOADS <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1>
+// EARLY: issue all fills of the refilled stage right after the barrier (one burst) instead of
+// spreading them between the MFMAs of the step.
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
                                                                   int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -306,7 +311,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
   };
   // Wait until at most `stages` stages of this wave's fills are still in flight.
   auto wait_fills = [&](int stages) {
-    if (NST >= 4 && stages >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+    if (NST >= 6 && stages >= 4) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * LOADS) : "memory");
+    else if (NST >= 5 && stages >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LOADS) : "memory");
+    else if (NST >= 4 && stages >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
     else if (NST >= 3 && stages >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
@@ -319,24 +326,42 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bn][bm][e] = 0.f;
 
-  auto read_frags = [&](const uint8_t *st, int kk, uint4 (&fa)[NBM], uint4 (&fb)[NBN]) {
+  // Fragment reads are issued as inline ds_read_b128: the compiler's wait insertion cannot
+  // tell which LDS bytes an in-flight buffer->LDS fill writes, and would otherwise wait for
+  // every outstanding fill (all prefetched stages) before the first read of a stage. The
+  // fills of the stage being read are already complete (wait_fills + barrier); the reads
+  // are waited for explicitly (wait_frags) before the MFMAs that use them.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t *)lds;
+  auto read_frags = [&](int stage, int kk, u32x4_t (&fa)[NBM], u32x4_t (&fb)[NBN]) {
+    const uint32_t st = lds_base + stage * STAGE;
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
       const int row = wm * WM + bm * 32 + l32;
-      fa[bm] = *(const uint4 *)(st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4));
+      const uint32_t addr = st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(fa[bm]) : "v"(addr) : "memory");
     }
 #pragma unroll
     for (int bn = 0; bn < NBN; ++bn) {
       const int row = BM + wn * WN + bn * 32 + l32;
-      fb[bn] = *(const uint4 *)(st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4));
+      const uint32_t addr = st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(fb[bn]) : "v"(addr) : "memory");
     }
+  };
+  // Wait until at most `pending` fragment reads are in flight; the empty statements tie the
+  // fragments to the wait so no MFMA that reads them is scheduled above it.
+  auto wait_frags = [&](auto pending, u32x4_t (&fa)[NBM], u32x4_t (&fb)[NBN]) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(decltype(pending)::value));
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) asm volatile("" : "+v"(fa[bm]));
+#pragma unroll
+    for (int bn = 0; bn < NBN; ++bn) asm volatile("" : "+v"(fb[bn]));
   };
   // MFMAs of one k step; fills of the refilled stage are slotted in between them (at most
   // one fill per `gap` MFMAs) so the address FIFO drains while the matrix cores work.
   constexpr int MF = NBN * NBM;
   constexpr int PER_STEP = (LOADS + KK - 1) / KK;
   constexpr int GAP = MF / PER_STEP > 0 ? MF / PER_STEP : 1;
-  auto mfma_step = [&](const uint4 (&fa)[NBM], const uint4 (&fb)[NBN], int fill_kt, int fill0) {
+  auto mfma_step = [&](const u32x4_t (&fa)[NBM], const u32x4_t (&fb)[NBN], int fill_kt, int fill0) {
 #pragma unroll
     for (int bn = 0; bn < NBN; ++bn)
 #pragma unroll
@@ -356,17 +381,29 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
   // other waves at the barrier (after which the stage consumed one iteration earlier is
   // free and gets refilled, interleaved with this stage's MFMAs), then multiplies, reading
   // the next k step's fragments while the current step's MFMAs run.
+  static_assert(NBM + NBN <= 15, "fragment reads exceed the lgkmcnt range");
   for (int s = 0; s < NST - 1 && s < nk; ++s) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
     wait_fills(min(NST - 2, nk - 1 - kt));
-    __syncthreads();
-    const int fill_kt = kt + NST - 1 < nk ? kt + NST - 1 : -1;
-    const uint8_t *st = lds + (kt % NST) * STAGE;
-    uint4 fa[2][NBM], fb[2][NBN];
-    read_frags(st, 0, fa[0], fb[0]);
+    // every wave's fills of stage kt are in LDS, and every wave's reads of the stage that
+    // is refilled next have completed
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    int fill_kt = kt + NST - 1 < nk ? kt + NST - 1 : -1;
+    if constexpr (EARLY) {
+      if (fill_kt >= 0) issue(fill_kt);
+      fill_kt = -1;
+    }
+    const int stage = kt % NST;
+    u32x4_t fa[2][NBM], fb[2][NBN];
+    read_frags(stage, 0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) read_frags(st, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk + 1 < KK) {
+        read_frags(stage, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        wait_frags(std::integral_constant<int, NBM + NBN>{}, fa[kk & 1], fb[kk & 1]);
+      } else {
+        wait_frags(std::integral_constant<int, 0>{}, fa[kk & 1], fb[kk & 1]);
+      }
       mfma_step(fa[kk & 1], fb[kk & 1], fill_kt, kk * PER_STEP);
     }
   }
@@ -622,13 +659,13 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
   tn = EPI == EPI_SWIGLU ? (g.n0 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
 }
 
-template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1>
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC>), dim3((unsigned)(tm * tn)),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY>), dim3((unsigned)(tm * tn)),
                      dim3(kThreads), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
@@ -649,8 +686,8 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // Tile shapes chosen per epilogue by a sweep on the decoder's GEMM shapes with random
     // operands. All use <= 80 KB of LDS and <= 256 registers per lane, so two workgroups share
     // a CU: one multiplies while the other waits on loads or writes its outputs.
-    case EPI_STORE: return run_bf16<256, 128, 32, 3, EPI_STORE, 2>(g, s);
-    case EPI_RESIDUAL: return run_bf16<128, 128, 64, 2, EPI_RESIDUAL, 2>(g, s);
+    case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true>(g, s);
+    case EPI_RESIDUAL: return run_bf16<128, 128, 64, 2, EPI_RESIDUAL, 2, true>(g, s);
     case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 2, EPI_QKV_ROPE, 2>(g, s);
     case EPI_SWIGLU: return run_bf16<128, 256, 32, 3, EPI_SWIGLU, 2>(g, s);
   }
