@@ -69,7 +69,9 @@ int check_config(const tfm_config *c, int B, int S) {
   if (c->d_model % kalign != 0 || c->d_ff % kalign != 0 ||
       (c->n_heads * c->d_head) % kalign != 0)
     return TFM_ERR_SHAPE;
-  if (!attention_supported(c->dtype, c->d_head)) return TFM_ERR_UNSUPPORTED;
+  if (!attention_supported(c->dtype, c->d_head) ||
+      !attention_fits(c->dtype, S, (int64_t)(c->n_heads + 2 * c->n_kv_heads) * c->d_head))
+    return TFM_ERR_UNSUPPORTED;
   return TFM_OK;
 }
 
@@ -241,7 +243,8 @@ int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const v
   if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head ||
       kv_stride < (int64_t)Hkv * d_head)
     return TFM_ERR_SHAPE;
-  if (!attention_supported(dt, d_head)) return TFM_ERR_UNSUPPORTED;
+  if (!attention_supported(dt, d_head) || !attention_fits(dt, S, kv_stride))
+    return TFM_ERR_UNSUPPORTED;
   if ((int64_t)B * S == 0) return TFM_OK;
   if (!q || !k || !v || !o) return TFM_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || q_stride % 8 != 0 ||

@@ -7,23 +7,29 @@
 // Keys after s get weight exactly 0 (they are never added); masking is by token order.
 //
 // bf16 kernel (d_head in {32, 64, 128}):
-//  * A workgroup owns 128 queries of one (b, h): 4 waves x 32 queries. K/V tiles of 64
-//    keys are staged in LDS (double-buffered, next tile's global loads in flight during
-//    the current tile's math) and shared by the 4 waves.
+//  * A workgroup owns 128 queries of one (b, h): 4 waves x 32 queries. K and V tiles of 64
+//    keys go from HBM straight into an LDS ring (buffer_load ... lds, no staging registers),
+//    several tiles ahead of the math, and are shared by the 4 waves. Key rows past S read
+//    as zero (buffer bounds) and are masked.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K rows as the
 //    A operand, Q held in registers as the B operand), so each lane holds 16 keys of ONE
 //    query: the running row max needs one cross-lane exchange (lane l <-> l^32) per tile
 //    and the row sum none until the end.
 //  * O^T = V^T P^T: the bf16-rounded probabilities go straight from the score accumulator
-//    into the B operand (no shuffle). V is written into LDS transposed, with the keys of
-//    each 16-key group permuted so that the 8 keys a lane needs are contiguous.
+//    into the B operand (no shuffle). V stays row-major in LDS; its A-operand fragments are
+//    read with the LDS transpose read ds_read_b64_tr_b16, which hands each lane four
+//    consecutive keys of one head dimension. The keys of a 16-key step are taken in the
+//    order the score accumulator holds them ({4h..4h+3, 4h+8..4h+11} for lane half h).
 //  * Softmax state (max, sum, rescale) is fp32; exponentials are base 2 with the
-//    1/sqrt(d_head) * log2(e) factor folded into one multiply.
+//    1/sqrt(d_head) * log2(e) factor folded into one fused multiply-add. The output is only
+//    rescaled when some row maximum of the wave changed.
 //  * Tiles entirely above the diagonal are never loaded; per wave, tiles past its last
 //    query are skipped; only the diagonal tile is masked. Query tiles are issued
 //    longest-first to even out the causal imbalance.
 // f32 kernel (d_head in {16, 32, 64, 128}): one thread per query with the same online
 // softmax in fp32; it exists for the small fp32 model and for tests, not for speed.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -34,219 +40,295 @@ constexpr int kBQ = 128;   // queries per workgroup
 constexpr int kBKV = 64;   // keys per tile
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
-// 16-byte chunk swizzle for an LDS tile whose rows are `RB` bytes: keeps the rows that one
-// 8-lane phase of a 16-byte-per-lane read touches on distinct bank groups.
-template <int RB>
-__device__ __forceinline__ int swz_chunk(int row, int ch) {
-  if constexpr (RB >= 128) {
-    return ch ^ (row & 7);
-  } else {
-    constexpr int rows_per_128 = 128 / RB, cpr = RB / 16;
-    return ch ^ ((row / rows_per_128) & (cpr - 1));
-  }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+template <int DH>
+struct AttnTile {
+  static constexpr int RB = DH * 2;              // bytes of one K or V row
+  static constexpr int CPR = RB / 16;            // 16-byte chunks per row
+  static constexpr int FR = 1024 / RB;           // rows one 64-lane 16-byte fill covers
+  static constexpr int TILE = kBKV * RB;         // bytes of a K (or V) tile
+  static constexpr int INS = TILE / 1024 / 4;    // fills per wave for K (and again for V)
+  static constexpr int LOADS = 2 * INS;
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NST = DH >= 128 ? 2 : 3;  // ring depth
+  static constexpr int OCC = DH >= 128 ? 1 : 2;
+  static_assert(INS >= 1 && INS * 4 * 1024 == TILE, "tile/fill mismatch");
+  // every LDS read offset is a per-lane register plus an immediate below 2^16
+  static_assert((NST - 1) * STAGE + TILE + (kBKV - 4) * RB < 65536, "LDS offset immediate");
+};
+
+// Chunk swizzles. K rows are read 16 bytes per lane (32 consecutive rows, one chunk column);
+// V rows are read with the transpose read (8 rows x 4 chunks per instruction, rows 0..3 in
+// the first half-wave, 4..7 in the second). Both keep one instruction on distinct banks. The
+// V swizzle depends only on row bits that are fixed per lane, so a lane's V addresses differ
+// by constants between key steps.
+template <int DH>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (DH == 32) return ((r >> 1) ^ (r >> 2)) & 3;
+  else if constexpr (DH == 64) return (r ^ (r >> 3)) & 7;
+  else return r & 15;
 }
-
-// Position of key t (0..63 within the tile) in a transposed V row: inside each group of
-// 16 keys, keys {4c+j} for c in 0..3 map so that a lane of half h reads keys
-// {8e'+4h+j : e' in 0..1, j in 0..3} as one contiguous run of 8.
-__device__ __forceinline__ int vt_pos(int t) {
-  const int k16 = t & 15;
-  return (t & ~15) + 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3);
+template <int DH>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (DH == 32) return 0;
+  else if constexpr (DH == 64) return ((r >> 1) & 1) << 2;
+  else return (r & 3) << 2;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 template <int DH>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, int64_t kv_stride, bf16_t *__restrict__ o, int64_t o_stride,
     int B, int S, int Hq, int Hkv, int n_qt, float scale_log2) {
-  constexpr int KRB = DH * 2;                 // K tile row bytes
-  constexpr int KCPR = DH / 8;                // K chunks per row
-  constexpr int K_LD = kBKV * KCPR / kThreads;// K chunks per thread
-  constexpr int VRB = kBKV * 2;               // V^T tile row bytes (128)
-  constexpr int V_UNITS = (kBKV / 2) * (DH / 8);  // (2 keys x 8 dims) units per tile
-  constexpr int K_BYTES = kBKV * KRB, V_BYTES = DH * VRB;
-  constexpr int STAGE = K_BYTES + V_BYTES;
+#if defined(__HIP_DEVICE_COMPILE__)
+  using T = AttnTile<DH>;
+  constexpr int RB = T::RB, CPR = T::CPR, FR = T::FR, TILE = T::TILE, INS = T::INS;
+  constexpr int LOADS = T::LOADS, STAGE = T::STAGE, NST = T::NST;
   constexpr int NKB = kBKV / 32;              // 32-key score blocks per tile
   constexpr int NDB = DH / 32;                // 32-dim output blocks
   constexpr int QK_STEPS = DH / 16;           // k-steps of the score MFMA
   constexpr int PV_STEPS = kBKV / 16;         // k-steps of the PV MFMA
-  constexpr int K_PER_T = K_LD > 0 ? K_LD : 1;
-  constexpr int V_PER_T = (V_UNITS + kThreads - 1) / kThreads;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int bh_count = B * Hq;
   const int qt = n_qt - 1 - (int)(blockIdx.x / bh_count);   // longest first
   const int bh = (int)(blockIdx.x % bh_count);
   const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
   const int q0 = qt * kBQ, qw0 = q0 + wid * 32;
+  const uint32_t kvsb = (uint32_t)(kv_stride * 2);   // bytes between key rows
 
-  const bf16_t *kbase = k + (int64_t)b * S * kv_stride + (int64_t)hkv * DH;
-  const bf16_t *vbase = v + (int64_t)b * S * kv_stride + (int64_t)hkv * DH;
+  // K and V rows 0..S-1 of this (b, kv head); rows at or past S read as zero.
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(k + (int64_t)b * S * kv_stride + (int64_t)hkv * DH), 0,
+      (int)(S * kvsb), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(v + (int64_t)b * S * kv_stride + (int64_t)hkv * DH), 0,
+      (int)(S * kvsb), kRsrcWord3);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query qw0 + l32, dims 16*kk + 8h .. +7
-  uint4 qf[QK_STEPS];
+  // ---- Q fragments (B operand of S^T = K Q^T): query qw0 + l32, dims 16*kk + 8h .. +7.
+  //      The empty statements make the compiler finish these loads here, so it does not wait
+  //      for them (and for every fill issued after them) inside the loop.
+  u32x4_t qf[QK_STEPS];
   {
     const int qi = qw0 + l32;
     const bf16_t *qp = q + ((int64_t)b * S + (qi < S ? qi : 0)) * q_stride + (int64_t)hq * DH;
 #pragma unroll
     for (int kk = 0; kk < QK_STEPS; ++kk)
-      qf[kk] = qi < S ? *(const uint4 *)(qp + 16 * kk + 8 * h) : uint4{0u, 0u, 0u, 0u};
+      qf[kk] = qi < S ? *(const u32x4_t *)(qp + 16 * kk + 8 * h) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) asm volatile("" : "+v"(qf[kk]));
   }
 
   const int kv_end = min(q0 + kBQ, S);
   const int n_tiles = (kv_end + kBKV - 1) / kBKV;
 
-  uint4 rk[K_PER_T];
-  uint4 rv[V_PER_T][2];
-  auto gload = [&](int j) {
-    const int kv0 = j * kBKV;
+  // ---- fills: lane l of a fill lands at base + 16 l, i.e. row frow, chunk slot fchunk; it
+  //      fetches the global chunk that the swizzle places in that slot.
+  const int frow = lane / CPR, fchunk = lane % CPR;
+  uint32_t k_off[INS], v_off[INS];
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / KCPR, ch = c % KCPR;
-      const bool ok = (K_LD > 0 || c < kBKV * KCPR) && kv0 + row < S;
-      rk[i] = ok ? *(const uint4 *)(kbase + (int64_t)(kv0 + row) * kv_stride + ch * 8)
-                 : uint4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < INS; ++i) {
+    const int r = (wid * INS + i) * FR + frow;
+    k_off[i] = (uint32_t)r * kvsb + (uint32_t)((fchunk ^ swz_k<DH>(r)) << 4);
+    v_off[i] = (uint32_t)r * kvsb + (uint32_t)((fchunk ^ swz_v<DH>(r)) << 4);
+  }
+  auto issue = [&](int j, auto slot) {
+    uint8_t *base = lds + decltype(slot)::value * STAGE;
+    const uint32_t t0 = (uint32_t)(j * kBKV) * kvsb;
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + kThreads * i;
-      const int kp = u / (DH / 8), dc = u % (DH / 8);   // key pair, 8-dim column
-      const int t0 = kv0 + 2 * kp;
-      const bool ok = u < V_UNITS;
-      rv[i][0] = (ok && t0 < S) ? *(const uint4 *)(vbase + (int64_t)t0 * kv_stride + dc * 8)
-                                : uint4{0u, 0u, 0u, 0u};
-      rv[i][1] = (ok && t0 + 1 < S)
-                     ? *(const uint4 *)(vbase + (int64_t)(t0 + 1) * kv_stride + dc * 8)
-                     : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < INS; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          k_rsrc, (lds_void_t *)(base + (wid * INS + i) * 1024), 16, t0 + k_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (lds_void_t *)(base + TILE + (wid * INS + i) * 1024), 16, t0 + v_off[i], 0,
+          0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t *Ks = lds + buf * STAGE;
-    uint8_t *Vt = Ks + K_BYTES;
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + kThreads * i;
-      if (K_LD > 0 || c < kBKV * KCPR) {
-        const int row = c / KCPR, ch = c % KCPR;
-        *(uint4 *)(Ks + row * KRB + (swz_chunk<KRB>(row, ch) << 4)) = rk[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + kThreads * i;
-      if (u < V_UNITS) {
-        const int kp = u / (DH / 8), dc = u % (DH / 8);
-        const int col = vt_pos(2 * kp);               // even; key 2kp+1 sits at col + 1
-        const uint32_t *a = (const uint32_t *)&rv[i][0];
-        const uint32_t *bb = (const uint32_t *)&rv[i][1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = dc * 8 + e;
-          const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xffffu);
-          const uint32_t hi = (e & 1) ? (bb[e >> 1] >> 16) : (bb[e >> 1] & 0xffffu);
-          const int off = d * VRB + (swz_chunk<VRB>(d, col >> 3) << 4) + (col & 7) * 2;
-          *(uint32_t *)(Vt + off) = lo | (hi << 16);
-        }
-      }
-    }
+  auto wait_fills = [&](int tiles) {
+    if (NST >= 3 && tiles >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  f32x16_t oacc[NDB];
+  // ---- LDS read addresses: a per-lane register plus an immediate for the slot and step.
+  //      The reads are inline so the compiler does not wait for every in-flight fill before
+  //      them; each is waited for explicitly before its first use.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t *)lds;
+  uint32_t k_rd[NKB][QK_STEPS];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) {
+      const int row = kb * 32 + l32;
+      k_rd[kb][kk] = lds_base + row * RB + (((2 * kk + h) ^ swz_k<DH>(row)) << 4);
+    }
+  // V^T fragment of dims 32 db .. +31, key step ks: lane (group g = lane / 16, i = lane % 16)
+  // addresses row 16 ks + 4 (g / 2) + 8 half + i / 4, dims d0 + 4 (i % 4) with
+  // d0 = 32 db + 16 (g % 2); the transpose read returns to lane i of the group the four keys
+  // of dim d0 + i.
+  const int tg = lane >> 4, ti = lane & 15;
+  uint32_t v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int row = 4 * (tg >> 1) + (ti >> 2);          // row bits the swizzle reads
+    const int chunk = ((db * 32 + 16 * (tg & 1)) >> 3) + ((ti & 3) >> 1);
+    v_rd[db] = lds_base + TILE + row * RB + ((chunk ^ swz_v<DH>(row)) << 4) + 8 * (ti & 1);
+  }
+  auto lgkm_wait0 = [&]() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  auto read_v = [](auto soff, uint32_t addr, u32x2_t (&f)[2 * PV_STEPS]) {
+#pragma unroll
+    for (int ks = 0; ks < PV_STEPS; ++ks)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(f[2 * ks + half])
+                     : "v"(addr), "i"(decltype(soff)::value + (16 * ks + 8 * half) * RB) : "memory");
+  };
+
+  f32x16_t oacc[NDB], lacc;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  float m_run = -__builtin_inff(), l_run = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  // all-ones A operand: the row sums of P come out of the matrix core with the P V product
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  float m_run = -__builtin_inff();
   const int my_q = qw0 + l32;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
+  auto tile = [&](int j, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    constexpr int SOFF = SL * STAGE;
+    wait_fills(min(NST - 2, n_tiles - 1 - j));
+    // every wave's fills of tile j are in LDS; every wave is done reading tile j - 1's slot
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + NST - 1 < n_tiles) issue(j + NST - 1, ic<(SL + NST - 1) % NST>{});
     const int kv0 = j * kBKV;
-    if (kv0 <= qw0 + 31) {
-      const uint8_t *Ks = lds + buf * STAGE;
-      const uint8_t *Vt = Ks + K_BYTES;
-      f32x16_t sacc[NKB];
+    if (kv0 > qw0 + 31) return;   // every key of the tile is after this wave's queries
+
+    // ---- S^T = K Q^T
+    f32x16_t sacc[NKB];
+    {
+      u32x4_t kf[2][QK_STEPS];
+#pragma unroll
+      for (int kk = 0; kk < QK_STEPS; ++kk)
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[0][kk]) : "v"(k_rd[0][kk]), "i"(SOFF) : "memory");
+      lgkm_wait0();
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        if (kb + 1 < NKB) {
+#pragma unroll
+          for (int kk = 0; kk < QK_STEPS; ++kk)
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(kf[(kb + 1) & 1][kk]) : "v"(k_rd[kb + 1][kk]), "i"(SOFF) : "memory");
+        }
+#pragma unroll
+        for (int kk = 0; kk < QK_STEPS; ++kk) asm volatile("" : "+v"(kf[kb & 1][kk]));
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-        const int row = kb * 32 + l32;
 #pragma unroll
-        for (int kk = 0; kk < QK_STEPS; ++kk) {
-          const uint4 a = *(const uint4 *)(Ks + row * KRB + (swz_chunk<KRB>(row, 2 * kk + h) << 4));
+        for (int kk = 0; kk < QK_STEPS; ++kk)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qf[kk]), sacc[kb], 0, 0, 0);
-        }
+              __builtin_bit_cast(bf16x8_t, kf[kb & 1][kk]), __builtin_bit_cast(bf16x8_t, qf[kk]),
+              sacc[kb], 0, 0, 0);
+        lgkm_wait0();
       }
-      // scores in log2 units; mask keys after the query on the diagonal tile
-      const bool diag = kv0 + kBKV - 1 > qw0;
-      float mt = -__builtin_inff();
+    }
+    // V fragments of the first output block load while the softmax runs
+    u32x2_t vf[2][2 * PV_STEPS];
+    read_v(ic<SOFF>{}, v_rd[0], vf[0]);
+
+    // ---- online softmax (scores stay in raw units; the scale is folded into the exponent)
+    if (kv0 + kBKV - 1 > qw0) {   // diagonal tile: keys after the query get no weight
+      const int lim = my_q - kv0 - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float s = sacc[kb][e] * scale_log2;
-          if (diag) {
-            const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (key > my_q) s = -__builtin_inff();
-          }
-          sacc[kb][e] = s;
-          mt = fmaxf(mt, s);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float ls = 0.f;
-      uint4 pf[PV_STEPS];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(sacc[kb][e] - m_new);
-          sacc[kb][e] = p;
-          ls += p;
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t w[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            w[x] = pack_bf16x2(sacc[kb][8 * half + 2 * x], sacc[kb][8 * half + 2 * x + 1]);
-          pf[2 * kb + half] = uint4{w[0], w[1], w[2], w[3]};
-        }
-      }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        oacc[db] *= alpha;
-        const int row = db * 32 + l32;
-#pragma unroll
-        for (int kk = 0; kk < PV_STEPS; ++kk) {
-          const uint4 a = *(const uint4 *)(Vt + row * VRB + (swz_chunk<VRB>(row, 2 * kk + h) << 4));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, pf[kk]), oacc[db], 0, 0, 0);
-        }
-      }
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) sacc[kb][e] = -__builtin_inff();
     }
-    if (j + 1 < n_tiles) sstore(buf ^ 1);
-    __syncthreads();
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+    {   // lanes l and l ^ 32 hold the two key halves of one query
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = fmaxf(m_run, mt);
+    const float mc = m_new * scale_log2;
+    u32x4_t pf[PV_STEPS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4_t w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int e = 8 * half + 2 * x;
+          w[x] = pack_bf16x2(fast_exp2(__builtin_fmaf(sacc[kb][e], scale_log2, -mc)),
+                             fast_exp2(__builtin_fmaf(sacc[kb][e + 1], scale_log2, -mc)));
+        }
+        pf[2 * kb + half] = w;
+      }
+    if (__any(m_new != m_run)) {   // some row maximum moved: rescale the running output
+      const float alpha = fast_exp2(m_run * scale_log2 - mc);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      lacc[0] *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- O^T += V^T P^T, and the row sums (all-ones rows times P^T)
+#pragma unroll
+    for (int ks = 0; ks < PV_STEPS; ++ks)
+      lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ones),
+                                                     __builtin_bit_cast(bf16x8_t, pf[ks]), lacc,
+                                                     0, 0, 0);
+    lgkm_wait0();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (db + 1 < NDB) read_v(ic<SOFF>{}, v_rd[db + 1], vf[(db + 1) & 1]);
+#pragma unroll
+      for (int x = 0; x < 2 * PV_STEPS; ++x) asm volatile("" : "+v"(vf[db & 1][x]));
+#pragma unroll
+      for (int ks = 0; ks < PV_STEPS; ++ks) {
+        const u32x4_t a = {vf[db & 1][2 * ks][0], vf[db & 1][2 * ks][1], vf[db & 1][2 * ks + 1][0],
+                           vf[db & 1][2 * ks + 1][1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, pf[ks]), oacc[db], 0,
+            0, 0);
+      }
+      lgkm_wait0();
+    }
+  };
+
+  issue(0, ic<0>{});
+  if (NST > 2 && n_tiles > 1) issue(1, ic<(NST > 2 ? 1 : 0)>{});
+  for (int j0 = 0; j0 < n_tiles; j0 += NST) {
+    tile(j0, ic<0>{});
+    if (j0 + 1 < n_tiles) tile(j0 + 1, ic<1 % NST>{});
+    if constexpr (NST > 2)
+      if (j0 + 2 < n_tiles) tile(j0 + 2, ic<2 % NST>{});
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (my_q < S) {
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / lacc[0];
     bf16_t *op = o + ((int64_t)b * S + my_q) * o_stride + (int64_t)hq * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -258,6 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         store4(op + 32 * db + 8 * g + 4 * h, r);
       }
   }
+#endif
 }
 
 template <int DH>
@@ -300,7 +383,7 @@ hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int
   const int n_qt = (S + kBQ - 1) / kBQ;
   const int64_t blocks = (int64_t)n_qt * B * Hq;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks > 0x7fffffff || !attention_fits(DT_BF16, S, kvs)) return hipErrorInvalidValue;
   const float sl2 = kLog2e / sqrtf((float)DH);
   attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
       (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S, Hq,
@@ -321,6 +404,10 @@ hipError_t run_f32(const void *q, int64_t qs, const void *k, const void *v, int6
 }
 
 }  // namespace
+
+bool attention_fits(int dt, int S, int64_t kv_stride) {
+  return dt != DT_BF16 || ((int64_t)S + kBKV) * kv_stride * 2 < ((int64_t)1 << 31);
+}
 
 bool attention_supported(int dt, int d_head) {
   if (dt == DT_BF16) return d_head == 32 || d_head == 64 || d_head == 128;

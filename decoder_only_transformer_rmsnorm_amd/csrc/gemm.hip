@@ -218,31 +218,37 @@ __device__ __forceinline__ int stage_off(int r, int byte, int rb) {
   return r * rb + ((c ^ (r & (p - 1) & 31)) << 4) + (byte & 15);
 }
 
-template <int BM, int BN, int BK, int NST>
+template <int BM, int BN, int BK, int NST, int NW>
 struct BfTile {
-  static constexpr int RB = BK * 2;                  // bytes per tile row per stage
-  static constexpr int FILL_ROWS = 1024 / RB;        // rows one 64-lane 16-byte fill covers
-  static constexpr int A_INS = BM / (4 * FILL_ROWS); // fills per wave per stage
-  static constexpr int B_INS = BN / (4 * FILL_ROWS);
+  static constexpr int RB = BK * 2;                   // bytes per tile row per stage
+  static constexpr int FILL_ROWS = 1024 / RB;         // rows one 64-lane 16-byte fill covers
+  static constexpr int A_INS = BM / (NW * FILL_ROWS); // fills per wave per stage
+  static constexpr int B_INS = BN / (NW * FILL_ROWS);
   static constexpr int LOADS = A_INS + B_INS;
   static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int RING = NST * STAGE;
-  static_assert(A_INS * 4 * FILL_ROWS == BM && B_INS * 4 * FILL_ROWS == BN, "tile/fill mismatch");
+  static_assert(A_INS * NW * FILL_ROWS == BM && B_INS * NW * FILL_ROWS == BN,
+                "tile/fill mismatch");
   static_assert(RING <= kLdsBytes, "LDS ring too large");
   static_assert(NST >= 2 && NST <= 6 && (NST - 2) * LOADS <= 63, "vmcnt range");
 };
 
 // EARLY: issue all fills of the refilled stage right after the barrier (one burst) instead of
-// spreading them between the MFMAs of the step.
-template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
-                                                                  int tiles_n) {
+// spreading them between the MFMAs of the step. WGM x WGN waves share the tile (each owns a
+// (BM/WGM) x (BN/WGN) sub-tile); with 8 waves two of them share each SIMD.
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
+          int WGN = 2>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
+                                                                        int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using T = BfTile<BM, BN, BK, NST>;
+  constexpr int NT = 64 * WGM * WGN;
+  using T = BfTile<BM, BN, BK, NST, WGM * WGN>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
   constexpr int LOADS = T::LOADS, STAGE = T::STAGE, KK = BK / 16;
-  constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
+  constexpr int WM = BM / WGM, WN = BN / WGN;      // wave sub-tile
   constexpr int NBM = WM / 32, NBN = WN / 32;      // 32x32 blocks per wave
+  static_assert(NBM * 32 * WGM == BM && NBN * 32 * WGN == BN, "wave grid does not tile");
+  static_assert(WGM % 2 == 0, "the two-pass epilogue splits the waves along M");
   constexpr int OUT_COLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
   constexpr int LDS = T::RING > BM * OUT_COLS * 2 ? T::RING : BM * OUT_COLS * 2;
   static_assert(LDS * OCC <= kLdsBytes, "LDS does not allow the requested occupancy");
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid & 1, wn = wid >> 1;
+  const int wm = wid % WGM, wn = wid / WGM;
   const int h = lane >> 5, l32 = lane & 31;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
   const int nout0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;
   const bool vec_ok = ((g.ldy * ob) & 15) == 0;
   for (int p = 0; p < passes; ++p) {
-    if (passes == 1 || wm == p) {
+    if (passes == 1 || (2 * wm) / WGM == p) {
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
         const int r = wm * WM + bm * 32 + l32 - p * prow;
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_bf16_kernel(GemmArgs g, in
     __syncthreads();
     // coalesced stores: consecutive threads take consecutive 16-byte chunks of a row
     const int cpr = rb >> 4, epc = 16 / ob;
-    for (int idx = tid; idx < prow * cpr; idx += kThreads) {
+    for (int idx = tid; idx < prow * cpr; idx += NT) {
       const int r = idx / cpr, c = idx - r * cpr;
       const int64_t m = m0 + p * prow + r;
       const int n = nout0 + c * epc;
@@ -659,14 +665,15 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
   tn = EPI == EPI_SWIGLU ? (g.n0 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
 }
 
-template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false>
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
+          int WGN = 2>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY>), dim3((unsigned)(tm * tn)),
-                     dim3(kThreads), 0, s, g, (int)tm, (int)tn);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN>),
+                     dim3((unsigned)(tm * tn)), dim3(64 * WGM * WGN), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
 

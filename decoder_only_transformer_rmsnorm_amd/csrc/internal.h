@@ -51,5 +51,7 @@ hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, cons
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                             int Hkv, int d_head, int dt, hipStream_t s);
 bool attention_supported(int dt, int d_head);
+// Whether one sequence's keys fit the bf16 kernel's 32-bit buffer offsets.
+bool attention_fits(int dt, int S, int64_t kv_stride);
 
 }  // namespace tfm

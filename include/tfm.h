@@ -133,7 +133,8 @@ int tfm_qkv_rope(const void *xn, const void *wq, const void *wk, const void *wv,
  * elements with Hkv heads; o: [dev] rows of o_stride elements, Hq heads. All of dtype dt.
  * Softmax state is float32; for bf16 the probabilities are rounded to bf16 before the PV
  * product. bf16 supports d_head in {32, 64, 128}; f32 supports d_head in {16, 32, 64, 128}.
- * Strides % 8 == 0. */
+ * Strides % 8 == 0. bf16 addresses one sequence's keys with 32-bit byte offsets:
+ * (S + 64) * kv_stride * 2 must stay below 2^31, else TFM_ERR_UNSUPPORTED. */
 int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                          int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                          int Hkv, int d_head, int dt, void *stream);

@@ -118,6 +118,9 @@ def test_attention_validation(L):
     assert call(args(qs=128)) == SHAPE
     assert call(args(dh=16)) == UNSUP            # bf16 supports 32/64/128
     assert call(args(dh=48, qs=192, os=192, kvs=96)) == UNSUP
+    # bf16 addresses one sequence's keys with 32-bit byte offsets
+    assert call(args(S=(1 << 20), kvs=1024)) == UNSUP
+    assert call(args(S=(1 << 20), kvs=1024, dt=0, q=None)) == NULL  # f32 has no such limit
     assert call(args(dt=7)) == DTYPE
     assert call(args(q=None)) == NULL
     assert call(args(qs=260)) == ALIGN
