@@ -134,6 +134,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
     ap.add_argument("--logits", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--dense-logits", action="store_true",
+                    help="logits row stride = vocab (default: vocab rounded up to a multiple of "
+                         "8 elements, so every logits row starts 16-byte aligned)")
     ap.add_argument("--counters", action="store_true",
                     help="only a 1 GiB copy and 3 LM-head launches, for rocprofv3 --pmc passes")
     args = ap.parse_args()
@@ -160,10 +163,11 @@ def main() -> int:
     dm = tfm.DeviceModel(inputs)
     stream = torch.cuda.current_stream()
     logits_dtype = torch.float32 if args.logits == "f32" else torch.bfloat16
-    logits = torch.empty((M, cfg.vocab), dtype=logits_dtype, device="cuda")
+    ld_logits = cfg.vocab if args.dense_logits else (cfg.vocab + 7) // 8 * 8
+    logits = torch.empty((M, ld_logits), dtype=logits_dtype, device="cuda")
 
     def step():
-        dm.forward(logits=logits)
+        dm.forward(logits=logits, ld_logits=ld_logits)
 
     if args.counters:
         xn = torch.randn((M, cfg.d_model), device="cuda").to(torch.bfloat16)
@@ -183,7 +187,7 @@ def main() -> int:
         step()
     dm.check_flags()
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(logits[:: max(1, M // 64)]).all())
+    assert bool(torch.isfinite(logits[:: max(1, M // 64), : cfg.vocab]).all())
 
     log(f"timing {args.steps} steps")
     # one event per step boundary on the launch stream: the whole region gives ms_per_step,
@@ -276,7 +280,8 @@ def main() -> int:
         "data": "synthetic (seeded uniform ids, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "batch": B, "seq_len": S, "n_layers": cfg.n_layers,
                    "d_model": cfg.d_model, "n_heads": cfg.n_heads, "d_ff": cfg.d_ff,
-                   "vocab": cfg.vocab, "logits_dtype": args.logits, "parallelism": "single GPU"},
+                   "vocab": cfg.vocab, "logits_dtype": args.logits, "ld_logits": ld_logits,
+                   "parallelism": "single GPU"},
         "end_to_end": {"flops_per_step_causal": int(flops["total"]),
                        "TFLOP/s": round(flops["total"] / (ms / 1e3) / 1e12, 1),
                        "frac_mfma": round(flops["total"] / (ms / 1e3) / PEAK_BF16, 4)},

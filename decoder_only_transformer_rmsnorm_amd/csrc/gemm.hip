@@ -12,7 +12,8 @@
 //  * A K stage is 128 bytes per tile row (64 bf16 or 32 f32), kept in LDS as 16-byte chunks
 //    whose position is XOR-swizzled by the row, so the 32 rows one MFMA fragment reads fall
 //    on distinct banks. Two LDS stages, one barrier per stage.
-//  * Epilogues: plain store (LM head; bf16 or f32, any row stride, odd N), residual add into
+//  * Epilogues: plain store (LM head; bf16 or f32, any row stride, odd N; streaming stores,
+//    since nothing on the path re-reads the logits), residual add into
 //    the fp32 stream (out and down projections), RoPE on the q/k columns of the fused QKV
 //    projection ("Transformer 篇" 5.5; "LLM 2" RoPE) and SiLU(gate) * up for the SwiGLU up
 //    projection ("Transformer 篇" 5.3; "LLM 2" SwiGLU FFN). For SwiGLU the weight tile
@@ -511,11 +512,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
         bf16_t *y = (bf16_t *)g.y + off;
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
         if (vec_ok && n + 8 <= ncols) {
-          *(uint4 *)y = raw;
+          if constexpr (EPI == EPI_STORE)   // logits: streamed out, not re-read here
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, raw), (u32x4_t *)y);
+          else
+            *(uint4 *)y = raw;
         } else if (n + 8 <= ncols && (off & 1) == 0) {
           // row stride not a multiple of 8 elements: 4-byte stores on an even element
 #pragma unroll
-          for (int x = 0; x < 4; ++x) ((uint32_t *)y)[x] = w4[x];
+          for (int x = 0; x < 4; ++x) {
+            if constexpr (EPI == EPI_STORE)
+              __builtin_nontemporal_store(w4[x], (uint32_t *)y + x);
+            else
+              ((uint32_t *)y)[x] = w4[x];
+          }
         } else if (n + 8 <= ncols) {
           // odd element offset: one 2-byte store, three 4-byte stores, one 2-byte store
           y[0] = (bf16_t)(w4[0] & 0xffffu);
@@ -531,7 +540,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
         float *y = (float *)g.y + off;
         f32x4_t v = __builtin_bit_cast(f32x4_t, raw);
         if (vec_ok && n + 4 <= ncols) {
-          *(f32x4_t *)y = v;
+          if constexpr (EPI == EPI_STORE)
+            __builtin_nontemporal_store(v, (f32x4_t *)y);
+          else
+            *(f32x4_t *)y = v;
         } else {
           for (int x = 0; x < 4 && n + x < ncols; ++x) y[x] = v[x];
         }

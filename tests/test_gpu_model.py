@@ -111,11 +111,12 @@ def test_model_small_bf16_full_size(logits):
     assert rel <= BF16_REL
 
 
-def _sampled_model_check(cfg, seq_index, prefix, positions):
+def _sampled_model_check(cfg, seq_index, prefix, positions, ld=None):
     inp = synth.make_inputs(cfg, seed=0)
-    say(f"model {cfg.name}: GPU forward B={cfg.batch} S={cfg.seq}")
-    _, lg = _run_model(cfg, inp)
-    got_all = lg.view(cfg.batch, cfg.seq, cfg.vocab)
+    ld = cfg.vocab if ld is None else ld
+    say(f"model {cfg.name}: GPU forward B={cfg.batch} S={cfg.seq} ld_logits={ld}")
+    _, lg = _run_model(cfg, inp, ld=ld)
+    got_all = lg.view(cfg.batch, cfg.seq, ld)[:, :, :cfg.vocab]
     assert bool(torch.isfinite(got_all).all())
     got = to_np(got_all[seq_index, positions])
     say(f"  oracle on sequence {seq_index}, prefix {prefix}, rows {list(positions)}")
@@ -126,10 +127,14 @@ def _sampled_model_check(cfg, seq_index, prefix, positions):
     return rel
 
 
-def test_model_d768_full_size_sampled():
-    """The d768 / 12-layer / seq-1024 workload at batch 8 (the benchmark's launch), one whole
-    sequence recomputed by the oracle, logits compared at sampled positions."""
-    _sampled_model_check(synth.GPT2S_BF16, 5, 1024, [0, 1, 2, 63, 64, 255, 511, 700, 1022, 1023])
+@pytest.mark.parametrize("ld", ["aligned", "dense"])
+def test_model_d768_full_size_sampled(ld):
+    """The d768 / 12-layer / seq-1024 workload at batch 8, one whole sequence recomputed by the
+    oracle, logits compared at sampled positions; with the benchmark's launch (logits rows
+    padded to a multiple of 8 elements) and with a dense (odd) row stride."""
+    cfg = synth.GPT2S_BF16
+    ldv = (cfg.vocab + 7) // 8 * 8 if ld == "aligned" else cfg.vocab
+    _sampled_model_check(cfg, 5, 1024, [0, 1, 2, 63, 64, 255, 511, 700, 1022, 1023], ld=ldv)
 
 
 def test_model_xl_full_size_sampled():
