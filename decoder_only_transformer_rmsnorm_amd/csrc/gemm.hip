@@ -706,8 +706,8 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // operands. All use <= 80 KB of LDS and <= 256 registers per lane, so two workgroups share
     // a CU: one multiplies while the other waits on loads or writes its outputs.
     case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true>(g, s);
-    case EPI_RESIDUAL: return run_bf16<128, 128, 64, 2, EPI_RESIDUAL, 2, true>(g, s);
-    case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 2, EPI_QKV_ROPE, 2>(g, s);
+    case EPI_RESIDUAL: return run_bf16<128, 192, 64, 4, EPI_RESIDUAL, 1, true, 4, 2>(g, s);
+    case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 4, EPI_QKV_ROPE, 1, true, 4, 2>(g, s);
     case EPI_SWIGLU: return run_bf16<128, 256, 32, 3, EPI_SWIGLU, 2>(g, s);
   }
   return hipErrorInvalidValue;
