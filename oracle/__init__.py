@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_block.argtypes = [ctypes.POINTER(OracleCfg), ctypes.POINTER(OracleLayer), _p,
                                    _p, c_int, c_int]
         L.oracle_model.restype = c_int
+        L.oracle_cross_entropy.argtypes = [_p, c_i64, c_int, _p, _p]
+        L.oracle_cross_entropy.restype = c_double
         L.oracle_model.argtypes = [ctypes.POINTER(OracleCfg), _p, ctypes.POINTER(OracleLayer),
                                    _p, _p, _p, _p, c_int, c_int, _p, _p, c_i64, _p]
         L.oracle_num_threads.restype = c_int
@@ -220,3 +222,26 @@ def model(cfg, inputs, ids=None, pos=None, rows=None, want_hidden: bool = False)
     if rows_a is None:
         logits = logits.reshape(B, S, cfg.vocab)
     return (logits, xf) if want_hidden else logits
+
+
+def cross_entropy(logits, targets):
+    """Per-row next-token cross-entropy (rows with a negative target give 0 and are not
+    counted) and the mean over counted rows; logits (rows, V), targets (rows,) int."""
+    lg = _f64(logits)
+    rows, V = lg.shape
+    t = _i32(targets).reshape(rows)
+    loss = np.zeros(rows, np.float64)
+    mean = lib().oracle_cross_entropy(_ptr(lg), rows, V, _ptr(t), _ptr(loss))
+    if np.isnan(mean):
+        raise ValueError("target outside [0, V)")
+    return loss, float(mean)
+
+
+def next_token_targets(ids):
+    """Targets of next-token prediction for (B, S) ids: row (b, s) predicts ids[b, s + 1];
+    the last position of each sequence has no target (-1)  [T2 Optimize / Loss: inputs and
+    targets are the same sequence shifted by one]."""
+    ids = np.asarray(ids)
+    t = np.full(ids.shape, -1, np.int32)
+    t[:, :-1] = ids[:, 1:]
+    return t

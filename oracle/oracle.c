@@ -241,3 +241,31 @@ int oracle_model(const oracle_cfg *c, const float *embed, const oracle_layer *la
   free(g); free(xf); free(x);
   return 0;
 }
+
+/* [T2 Optimize / Loss; T3 12]: the logsumexp form of -log softmax(logits_r)[t_r]. */
+double oracle_cross_entropy(const double *logits, int64_t rows, int V, const int32_t *targets,
+                            double *loss) {
+  for (int64_t r = 0; r < rows; ++r)
+    if (targets[r] >= V) return NAN;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    if (targets[r] < 0) {
+      loss[r] = 0.0;
+      continue;
+    }
+    const double *a = logits + r * (int64_t)V;
+    double m = a[0];
+    for (int j = 1; j < V; ++j) if (a[j] > m) m = a[j];
+    double sum = 0.0;
+    for (int j = 0; j < V; ++j) sum += exp(a[j] - m);
+    loss[r] = log(sum) + m - a[targets[r]];
+  }
+  double total = 0.0;
+  int64_t counted = 0;
+  for (int64_t r = 0; r < rows; ++r)
+    if (targets[r] >= 0) {
+      total += loss[r];
+      ++counted;
+    }
+  return counted ? total / (double)counted : 0.0;
+}

@@ -18,7 +18,8 @@
  *       SwiGLU, 5.4 Attention, 5.5 RoPE, 5.6 RMSNorm, 5.7 model assembly.
  *  [T2] "LLM 2: Transformer 原理与实现" (juejin.cn): RMSNorm, SwiGLU FFN, RoPE, GQA.
  *  [T3] "从零实现一个完整的LLM（CS336）——Transformer篇" (fengye404.top): 6 RMSNorm,
- *       7 RoPE, 8 Attention, 9 SwiGLU, 10 model assembly, 12 training checks.
+ *       7 RoPE, 8 Attention, 9 SwiGLU, 10 model assembly, 12 training (loss, checks).
+ *  [T2 Optimize / Loss]: next-token cross-entropy in the logsumexp form.
  *
  * Parity pins: every function below is pinned by a CPU test against page values, closed
  * forms, invariants or brute force, except oracle_model at the real workload sizes, whose
@@ -94,6 +95,14 @@ int oracle_model(const oracle_cfg *c, const float *embed, const oracle_layer *la
                  const float *g_final, const float *lm_head, const int32_t *ids,
                  const int32_t *pos, int B, int S, double *x_final, const int64_t *rows,
                  int64_t n_rows, double *logits);
+
+/* Next-token cross-entropy  [T2 Optimize / Loss; T3 12 training]: per row r with target
+ * t = targets[r] in [0, V): loss[r] = log(sum_j exp(logits[r, j] - max_r)) + max_r
+ * - logits[r, t], the max-subtracted logsumexp form. Rows with a negative target are
+ * ignored: loss[r] = 0 and they are left out of the mean. Returns the mean over the counted
+ * rows (0 when none), or NAN if a target is >= V. */
+double oracle_cross_entropy(const double *logits, int64_t rows, int V, const int32_t *targets,
+                            double *loss);
 
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void);

@@ -404,3 +404,67 @@ def test_attention_rows_equal_full_rows():
     full = oracle.attention(q, k, v, 4, 2).reshape(22, 32)
     rows = np.array([0, 5, 10, 11, 21])
     np.testing.assert_array_equal(oracle.attention_rows(q, k, v, 4, 2, rows), full[rows])
+
+
+# ---------------------------------------------------------------- cross-entropy
+def test_cross_entropy_uniform_logits_is_log_vocab():
+    """Equal logits: every target has probability 1/V, so loss = log V and the perplexity
+    exp(mean loss) is V [T2 Optimize / Loss: perplexity is the exponential of the mean]."""
+    V = 50257
+    lg = np.full((3, V), 0.731)
+    loss, mean = oracle.cross_entropy(lg, np.array([0, 12345, V - 1]))
+    assert np.allclose(loss, np.log(V), rtol=0, atol=1e-12)
+    assert abs(np.exp(mean) - V) < 1e-7 * V
+
+
+def test_cross_entropy_two_class_closed_form_and_target_sign():
+    """Two classes: -log softmax([a, b])[0] = log(1 + e^(b - a)); the other target gives
+    log(1 + e^(a - b)). A swapped sign or a missing max term fails one of them."""
+    a, b = 1.7, -0.4
+    loss, _ = oracle.cross_entropy(np.array([[a, b], [a, b]]), np.array([0, 1]))
+    assert abs(loss[0] - np.log1p(np.exp(b - a))) < 1e-14
+    assert abs(loss[1] - np.log1p(np.exp(a - b))) < 1e-14
+
+
+def test_cross_entropy_shift_invariance_and_no_overflow():
+    """Adding a constant to a row leaves the loss unchanged (the max is subtracted), also for
+    logits far beyond exp's range."""
+    g = np.random.Generator(np.random.PCG64(11))
+    lg = g.normal(size=(4, 300))
+    t = g.integers(0, 300, 4)
+    l0, _ = oracle.cross_entropy(lg, t)
+    l1, _ = oracle.cross_entropy(lg + 1000.0, t)
+    assert np.allclose(l0, l1, rtol=0, atol=1e-10)
+    big = np.zeros((2, 5))
+    big[:, 0] = 1000.0
+    lb, _ = oracle.cross_entropy(big, np.array([0, 1]))
+    assert 0.0 <= lb[0] < 1e-300   # log(1 + 4 e^-1000) underflows to 0 but never goes negative
+    assert abs(lb[1] - 1000.0) < 1e-9
+
+
+def test_cross_entropy_matches_naive_log_softmax():
+    """Brute force on small logits: -log(exp(z_t) / sum_j exp(z_j)) computed directly."""
+    g = np.random.Generator(np.random.PCG64(12))
+    lg = g.uniform(-4, 4, size=(16, 37))
+    t = g.integers(0, 37, 16)
+    loss, mean = oracle.cross_entropy(lg, t)
+    e = np.exp(lg)
+    naive = -np.log(e[np.arange(16), t] / e.sum(axis=1))
+    assert np.allclose(loss, naive, rtol=0, atol=1e-12)
+    assert abs(mean - naive.mean()) < 1e-12
+
+
+def test_cross_entropy_ignored_rows_and_bad_target():
+    lg = np.random.Generator(np.random.PCG64(13)).normal(size=(4, 9))
+    t = np.array([3, -1, 0, -1])
+    loss, mean = oracle.cross_entropy(lg, t)
+    assert loss[1] == 0.0 and loss[3] == 0.0
+    assert abs(mean - (loss[0] + loss[2]) / 2) < 1e-15
+    with pytest.raises(ValueError):
+        oracle.cross_entropy(lg, np.array([3, 9, 0, 0]))
+
+
+def test_next_token_targets_shift_by_one():
+    """Targets are the inputs shifted left by one position; the last position has none."""
+    t = oracle.next_token_targets(np.array([[5, 6, 7, 8], [1, 2, 3, 4]]))
+    assert t.tolist() == [[6, 7, 8, -1], [2, 3, 4, -1]]
