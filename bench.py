@@ -77,8 +77,8 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profiles(kernel_key: str):
-    """HBM bytes per launch of the dominant kernel from the committed PMC summary, or None
-    when absent or taken on a different kernel source."""
+    """The committed PMC summary entry of the dominant kernel (HBM bytes per launch, kernel
+    name), or None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         d = json.load(open(path))
@@ -87,7 +87,7 @@ def traffic_from_profiles(kernel_key: str):
     e = d.get(kernel_key)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
-    return e.get("bytes_per_launch")
+    return e
 
 
 def cpu_baseline(cfg, inputs, budget_s: float):
@@ -212,6 +212,8 @@ def main() -> int:
     # ---- per-kernel timing through each entry point, same shapes as inside the step
     kernels = {}
     roofline = None
+    loss_forward = None
+    mfma_util = None
     if not args.no_kernels:
         D, F, V = cfg.d_model, cfg.d_ff, cfg.vocab
         qd = cfg.n_heads * cfg.d_head
@@ -262,10 +264,37 @@ def main() -> int:
         rec("gemm_lm_head", lm_ms, flops_gemm(V, D), "mfma", None)
         lm_flops = flops_gemm(V, D)
         ach = lm_flops / (lm_ms / 1e3) / 1e12
-        roofline = {"bound": "mfma", "kernel": "gemm_bf16_kernel<256,128,32,3,EPI_STORE,2> (LM head, M=8192 N=50257 K=768)",
+        prof = traffic_from_profiles("gemm_lm_head")
+        roofline = {"bound": "mfma",
+                    "kernel": (prof["kernel"] if prof else "gemm_bf16_kernel, plain-store epilogue")
+                              + f" (LM head, M={M} N={V} K={D}, logits row stride {ld_logits})",
                     "achieved": round(ach, 1), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                     "frac": round(ach * 1e12 / PEAK_BF16, 4), "flops_per_launch": int(lm_flops),
-                    "avg_launch_ms": round(lm_ms, 4), "traffic": traffic_from_profiles("gemm_lm_head")}
+                    "avg_launch_ms": round(lm_ms, 4),
+                    "traffic": prof["bytes_per_launch"] if prof else None}
+
+        # fused LM head + next-token cross-entropy (no logits written), and the whole forward
+        # ending in it
+        targets = tfm.next_token_targets(dm.ids)
+        xloss = torch.empty(M, dtype=torch.float32, device="cuda")
+        xmean = torch.empty(1, dtype=torch.float32, device="cuda")
+        rec("lm_head_xent", time_launches(lambda: tfm.tfm_lm_head_xent(
+            xn, dm.lm_head, targets.view(-1), loss=xloss, mean=xmean), n, stream),
+            flops_gemm(V, D), "mfma", None)
+        loss_ms = time_launches(lambda: dm.loss(targets, loss=xloss, mean=xmean), max(2, n // 4),
+                                stream, graph=False)
+        loss_forward = {"ms_per_step": round(loss_ms, 4), "tokens_per_s": round(M / (loss_ms / 1e3), 1),
+                        "mean_loss": round(float(xmean.item()), 4)}
+        log(f"forward with fused loss: {loss_ms:.3f} ms/step, {M / (loss_ms / 1e3) / 1e6:.3f} M tokens/s")
+
+        # MFMA utilisation of the GEMM and attention kernels over one step
+        L_ = cfg.n_layers
+        gemm_f = L_ * (flops_gemm(3 * qd, D) + flops_gemm(D, qd) + flops_gemm(2 * F, D)
+                       + flops_gemm(D, F)) + flops_gemm(V, D)
+        gemm_ms = L_ * (kernels["gemm_qkv_rope"]["ms"] + kernels["gemm_out_residual"]["ms"]
+                        + kernels["swiglu_ffn"]["ms"]) + kernels["gemm_lm_head"]["ms"]
+        mfma_util = {"gemm": round(gemm_f / (gemm_ms / 1e3) / PEAK_BF16, 4),
+                     "attention": kernels["attention"]["frac_mfma"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,7 +315,9 @@ def main() -> int:
                        "TFLOP/s": round(flops["total"] / (ms / 1e3) / 1e12, 1),
                        "frac_mfma": round(flops["total"] / (ms / 1e3) / PEAK_BF16, 4)},
         "roofline": roofline,
+        "mfma_util": mfma_util,
         "kernels": kernels,
+        "loss_forward": loss_forward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -130,6 +130,66 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   return TFM_OK;
 }
 
+// Embedding, every block and the final RMSNorm: leaves RMSNorm(x; g_final) in the xn region
+// of the workspace.
+int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t *ids,
+                  const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *wsb,
+                  const WsPlan &p, hipStream_t s) {
+  const int64_t M = (int64_t)B * S;
+  float *x = (float *)(wsb + p.x);
+  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 1, 0, s));
+  TFM_HIP(launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
+                       (int32_t *)(wsb + p.flag), s));
+  for (int l = 0; l < c->n_layers; ++l)
+    TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p, s));
+  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M, c->d_model,
+                         c->eps, s));
+  return TFM_OK;
+}
+
+// Pointers and alignment every whole-model entry point needs.
+int check_model(const tfm_config *c, const tfm_model_weights *w, const int32_t *ids,
+                const float *cos_sin, const void *ws) {
+  if (!ids || !cos_sin || !ws || !w->embed || !w->g_final || !w->lm_head ||
+      (c->n_layers > 0 && !w->layers))
+    return TFM_ERR_NULL;
+  if (!aligned16(cos_sin) || !aligned16(ws) || !aligned16(w->embed) || !aligned16(w->g_final) ||
+      !aligned16(w->lm_head))
+    return TFM_ERR_ALIGN;
+  for (int l = 0; l < c->n_layers; ++l) TFM_TRY(check_layer(&w->layers[l]));
+  return TFM_OK;
+}
+
+// Workspace of the fused LM-head cross-entropy: per-row partials of every column tile.
+struct XentPlan {
+  size_t x_max, x_sum, x_tgt, total;
+  int parts;
+};
+
+XentPlan plan_xent(int64_t M, int V) {
+  XentPlan p;
+  p.parts = gemm_xent_parts(V);
+  const size_t part_bytes = round256((size_t)M * p.parts * 4);
+  p.x_max = 0;
+  p.x_sum = part_bytes;
+  p.x_tgt = 2 * part_bytes;
+  p.total = 2 * part_bytes + round256((size_t)M * 4);
+  return p;
+}
+
+int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *loss, float *mean,
+                 int64_t M, int V, int K, uint8_t *wsb, const XentPlan &xp, hipStream_t s) {
+  GemmArgs g{};
+  g.a = x; g.lda = K; g.w0 = w; g.M = M; g.N = V; g.K = K;
+  g.targets = targets;
+  g.x_max = (float *)(wsb + xp.x_max);
+  g.x_sum = (float *)(wsb + xp.x_sum);
+  g.x_tgt = (float *)(wsb + xp.x_tgt);
+  TFM_HIP(launch_gemm(EPI_XENT, DT_BF16, g, s));
+  TFM_HIP(launch_xent_reduce(g.x_max, g.x_sum, g.x_tgt, targets, xp.parts, M, V, loss, mean, s));
+  return TFM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,32 +370,65 @@ int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const i
   if (!w) return TFM_ERR_NULL;
   if (ld_logits < cfg->vocab) return TFM_ERR_SHAPE;
   if ((int64_t)B * S == 0) return TFM_OK;
-  if (!ids || !logits || !cos_sin || !ws || !w->embed || !w->g_final || !w->lm_head ||
-      (cfg->n_layers > 0 && !w->layers))
-    return TFM_ERR_NULL;
-  if (!aligned16(logits) || !aligned16(cos_sin) || !aligned16(ws) || !aligned16(w->embed) ||
-      !aligned16(w->g_final) || !aligned16(w->lm_head))
-    return TFM_ERR_ALIGN;
-  for (int l = 0; l < cfg->n_layers; ++l) TFM_TRY(check_layer(&w->layers[l]));
+  if (!logits) return TFM_ERR_NULL;
+  if (!aligned16(logits)) return TFM_ERR_ALIGN;
+  TFM_TRY(check_model(cfg, w, ids, cos_sin, ws));
   const WsPlan p = plan_ws(cfg, B, S);
   if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t *wsb = (uint8_t *)ws;
-  const int64_t M = (int64_t)B * S;
-  float *x = (float *)(wsb + p.x);
-  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 1, 0, s));
-  TFM_HIP(launch_embed(ids, M, w->embed, cfg->dtype, cfg->vocab, cfg->d_model, x,
-                       (int32_t *)(wsb + p.flag), s));
-  for (int l = 0; l < cfg->n_layers; ++l)
-    TFM_TRY(enqueue_block(cfg, &w->layers[l], x, positions, B, S, cos_sin, wsb, p, s));
-  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, cfg->dtype, wsb + p.xn, cfg->dtype, M,
-                         cfg->d_model, cfg->eps, s));
+  TFM_TRY(enqueue_trunk(cfg, w, ids, positions, B, S, cos_sin, wsb, p, s));
   GemmArgs g{};
-  g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = M; g.N = cfg->vocab;
-  g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
+  g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = (int64_t)B * S;
+  g.N = cfg->vocab; g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
   TFM_HIP(launch_gemm(EPI_STORE, cfg->dtype, g, s));
   return TFM_OK;
+}
+
+size_t tfm_xent_workspace_bytes(int64_t M, int V) {
+  if (M < 0 || V <= 0) return 0;
+  return plan_xent(M, V).total;
+}
+
+int tfm_lm_head_xent(const void *x, const void *w, const int32_t *targets, float *loss,
+                     float *mean, int64_t M, int V, int K, void *ws, size_t ws_bytes,
+                     void *stream) {
+  if (M < 0 || V <= 0 || K <= 0) return TFM_ERR_SHAPE;
+  if (K % 8 != 0) return TFM_ERR_SHAPE;
+  if (M == 0) return TFM_OK;
+  if (!x || !w || !targets || !loss || !ws) return TFM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(ws)) return TFM_ERR_ALIGN;
+  const XentPlan xp = plan_xent(M, V);
+  if (ws_bytes < xp.total) return TFM_ERR_WORKSPACE;
+  return enqueue_xent(x, w, targets, loss, mean, M, V, K, (uint8_t *)ws, xp,
+                      (hipStream_t)stream);
+}
+
+size_t tfm_loss_workspace_bytes(const tfm_config *cfg, int B, int S) {
+  if (check_config(cfg, B, S) != TFM_OK) return 0;
+  return plan_ws(cfg, B, S).total + plan_xent((int64_t)B * S, cfg->vocab).total;
+}
+
+int tfm_model_loss(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                   const int32_t *positions, const int32_t *targets, float *loss, float *mean,
+                   int B, int S, const float *cos_sin, void *ws, size_t ws_bytes, void *stream) {
+  TFM_TRY(check_config(cfg, B, S));
+  if (cfg->dtype != TFM_BF16) return TFM_ERR_UNSUPPORTED;
+  if (!w) return TFM_ERR_NULL;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!targets || !loss) return TFM_ERR_NULL;
+  TFM_TRY(check_model(cfg, w, ids, cos_sin, ws));
+  const WsPlan p = plan_ws(cfg, B, S);
+  const int64_t M = (int64_t)B * S;
+  const XentPlan xp = plan_xent(M, cfg->vocab);
+  if (ws_bytes < p.total + xp.total) return TFM_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *wsb = (uint8_t *)ws;
+  TFM_TRY(enqueue_trunk(cfg, w, ids, positions, B, S, cos_sin, wsb, p, s));
+  return enqueue_xent(wsb + p.xn, w->lm_head, targets, loss, mean, M, cfg->vocab,
+                      cfg->d_model, wsb + p.total, xp, s);
 }
 
 int tfm_check_device_flags(const void *ws, void *stream) {

@@ -116,6 +116,61 @@ __global__ void rope_kernel(T *x, int64_t row_stride, const int32_t *pos, int B,
   store4(px, v);
 }
 
+// Next-token cross-entropy ("LLM 2" Optimize / Loss; "Transformer篇" (fengye404.top) 12):
+// combine the LM-head tile partials of one row, max_t and sum_t of exp(logit - max_t), into
+// the row's log-sum-exp (fixed tile order) and subtract the target logit.
+__global__ void xent_reduce_kernel(const float *__restrict__ x_max, const float *__restrict__ x_sum,
+                                   const float *__restrict__ x_tgt, const int32_t *targets, int T,
+                                   int64_t M, int V, float *loss) {
+  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  const int t = targets[m];
+  if (t < 0) {
+    loss[m] = 0.f;
+    return;
+  }
+  if (t >= V) {
+    loss[m] = __builtin_nanf("");
+    return;
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float mx = -__builtin_inff();
+  for (int i = 0; i < T; ++i) mx = fmaxf(mx, x_max[(int64_t)i * M + m]);
+  float se = 0.f;
+  for (int i = 0; i < T; ++i)
+    se += x_sum[(int64_t)i * M + m] * exp2f((x_max[(int64_t)i * M + m] - mx) * kLog2e);
+  loss[m] = mx + logf(se) - x_tgt[m];
+}
+
+// Mean over the rows with a target: one workgroup, strided fp64 partial sums in a fixed order
+// and a fixed tree, so the result does not depend on scheduling.
+constexpr int kMeanThreads = 1024;
+__global__ __launch_bounds__(kMeanThreads) void mean_loss_kernel(const float *loss,
+                                                                 const int32_t *targets,
+                                                                 int64_t M, float *mean) {
+  __shared__ double ps[kMeanThreads];
+  __shared__ int64_t pc[kMeanThreads];
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  int64_t cnt = 0;
+  for (int64_t m = tid; m < M; m += kMeanThreads)
+    if (targets[m] >= 0) {
+      acc += (double)loss[m];
+      ++cnt;
+    }
+  ps[tid] = acc;
+  pc[tid] = cnt;
+  __syncthreads();
+  for (int w = kMeanThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      ps[tid] += ps[tid + w];
+      pc[tid] += pc[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) mean[0] = pc[0] ? (float)(ps[0] / (double)pc[0]) : 0.f;
+}
+
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -202,6 +257,16 @@ hipError_t launch_rope(void *x, int x_dt, int64_t row_stride, const int32_t *pos
   else
     rope_kernel<float><<<blocks_for(total, 256), 256, 0, s>>>(
         (float *)x, row_stride, positions, B, S, H, d_head, cos_sin, max_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_xent_reduce(const float *x_max, const float *x_sum, const float *x_tgt,
+                              const int32_t *targets, int T, int64_t M, int V, float *loss,
+                              float *mean, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  xent_reduce_kernel<<<blocks_for(M, 256), 256, 0, s>>>(x_max, x_sum, x_tgt, targets, T, M, V,
+                                                        loss);
+  if (mean) mean_loss_kernel<<<1, kMeanThreads, 0, s>>>(loss, targets, M, mean);
   return hipGetLastError();
 }
 

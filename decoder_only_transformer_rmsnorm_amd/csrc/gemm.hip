@@ -43,6 +43,7 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;  // bytes of one tile row per K stage
 constexpr int kChunks = 8;      // 16-byte chunks per tile row and stage
 constexpr int kGroupM = 8;      // tile-rows per ordering group
+constexpr int kXentBM = 192, kXentBN = 128;   // tile of the fused LM-head cross-entropy
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr uint32_t kOOB = 0x80000000u;        // offset beyond any num_records used here
 
@@ -250,8 +251,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   constexpr int NBM = WM / 32, NBN = WN / 32;      // 32x32 blocks per wave
   static_assert(NBM * 32 * WGM == BM && NBN * 32 * WGN == BN, "wave grid does not tile");
   static_assert(WGM % 2 == 0, "the two-pass epilogue splits the waves along M");
-  constexpr int OUT_COLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  constexpr int OUT_COLS = EPI == EPI_SWIGLU ? BN / 2 : (EPI == EPI_XENT ? 0 : BN);
   constexpr int LDS = T::RING > BM * OUT_COLS * 2 ? T::RING : BM * OUT_COLS * 2;
+  static_assert(EPI != EPI_XENT || 2 * BM * WGN * 4 <= LDS, "cross-entropy row buffers");
   static_assert(LDS * OCC <= kLdsBytes, "LDS does not allow the requested occupancy");
   static_assert(EPI != EPI_SWIGLU || (NBN % 2) == 0, "SwiGLU needs gate/up block pairs");
 
@@ -415,6 +417,90 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     }
   }
   __syncthreads();  // every wave is done with the ring: reuse it to stage the output
+
+  if constexpr (EPI == EPI_XENT) {
+    // ---- cross-entropy partials ("LLM 2" Optimize / Loss: logsumexp with the max taken
+    //      out). Lane holds row m = m0 + wm*WM + bm*32 + l32 and the columns
+    //      n = n0 + wn*WN + bn*32 + 8q + 4h + r. Per row: max over the lane's columns, over
+    //      the two lane halves (permlane32 swap), then over the WGN waves along N (LDS);
+    //      the same for the sum of exp(logit - max). The logits stay in registers. Column
+    //      bounds are only checked in the last column tile.
+    constexpr float kLog2e = 1.4426950408889634f;
+    float *red = (float *)lds;   // [BM][WGN]
+    const int nw0 = n0 + wn * WN;
+    const bool full = n0 + BN <= g.N;
+    auto col_ok = [&](int bn, int e) {
+      return full || nw0 + bn * 32 + 8 * (e >> 2) + 4 * h + (e & 3) < g.N;
+    };
+    float rmax[NBM];
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      const int rt = wm * WM + bm * 32 + l32;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int bn = 0; bn < NBN; ++bn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (col_ok(bn, e)) mx = fmaxf(mx, acc[bn][bm][e]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      if (h == 0) red[rt * WGN + wn] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      const int rt = wm * WM + bm * 32 + l32;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < WGN; ++w) mx = fmaxf(mx, red[rt * WGN + w]);
+      rmax[bm] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      const int rt = wm * WM + bm * 32 + l32;
+      const int64_t m = m0 + rt;
+      const float mc = rmax[bm] * kLog2e;
+      float se = 0.f;
+#pragma unroll
+      for (int bn = 0; bn < NBN; ++bn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (col_ok(bn, e)) se += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bn][bm][e], kLog2e, -mc));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(se), __float_as_uint(se),
+                                                       false, false);
+      se = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (h == 0) red[rt * WGN + wn] = se;
+      // the row's target logit, if its column is one of this wave's (rare: one column tile)
+      const int tr = (m < g.M ? g.targets[m] : -1) - nw0;
+      const bool mine = tr >= 0 && tr < WN && ((tr >> 2) & 1) == h;
+      if (__any(mine)) {
+        float tv = 0.f;
+#pragma unroll
+        for (int bn = 0; bn < NBN; ++bn)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (tr == bn * 32 + 8 * (e >> 2) + 4 * h + (e & 3)) tv = acc[bn][bm][e];
+        if (mine) g.x_tgt[m] = tv;
+      }
+    }
+    __syncthreads();
+    if (wn == 0 && h == 0) {
+#pragma unroll
+      for (int bm = 0; bm < NBM; ++bm) {
+        const int rt = wm * WM + bm * 32 + l32;
+        const int64_t m = m0 + rt;
+        if (m >= g.M) continue;
+        float se = 0.f;
+#pragma unroll
+        for (int w = 0; w < WGN; ++w) se += red[rt * WGN + w];
+        g.x_max[(int64_t)tn * g.M + m] = rmax[bm];
+        g.x_sum[(int64_t)tn * g.M + m] = se;
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: final values -> LDS (output dtype, row-major tile) -> coalesced rows.
   //      Lane holds acc[bn][bm][4q + r] for n = n0 + wn*WN + bn*32 + 8q + 4h + r and
@@ -709,6 +795,7 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     case EPI_RESIDUAL: return run_bf16<128, 192, 64, 4, EPI_RESIDUAL, 1, true, 4, 2>(g, s);
     case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 4, EPI_QKV_ROPE, 1, true, 4, 2>(g, s);
     case EPI_SWIGLU: return run_bf16<128, 256, 32, 3, EPI_SWIGLU, 2>(g, s);
+    case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -724,6 +811,8 @@ hipError_t dispatch_f32(int epi, const GemmArgs &g, hipStream_t s) {
 }
 
 }  // namespace
+
+int gemm_xent_parts(int N) { return (N + kXentBN - 1) / kXentBN; }
 
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s) {
   if (g.M == 0) return hipSuccess;

@@ -18,13 +18,21 @@ hipError_t launch_rope(void *x, int x_dt, int64_t row_stride, const int32_t *pos
                        int S, int H, int d_head, const float *cos_sin, int max_seq,
                        hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+// Next-token cross-entropy from the LM-head tile partials: loss[m] = max_m + log(sum_m) -
+// tgt[m] with max_m, sum_m combined over the T column tiles in a fixed order; negative
+// targets give 0, targets >= V give NaN. mean (optional) = mean over rows with target >= 0.
+hipError_t launch_xent_reduce(const float *x_max, const float *x_sum, const float *x_tgt,
+                              const int32_t *targets, int T, int64_t M, int V, float *loss,
+                              float *mean, hipStream_t s);
 
 // ---- GEMM family (gemm.hip): y = a w^T with a fused epilogue.
 enum GemmEpi {
   EPI_STORE = 0,     // y = acc (y_dt)
   EPI_RESIDUAL = 1,  // y = residual + acc (float32)
   EPI_QKV_ROPE = 2,  // weight rows from wq | wk | wv; RoPE on the q and k columns
-  EPI_SWIGLU = 3     // gate rows from w1, up rows from w3; y = SiLU(gate) * up
+  EPI_SWIGLU = 3,    // gate rows from w1, up rows from w3; y = SiLU(gate) * up
+  EPI_XENT = 4       // no y: per row and column tile, max and sum of exp of the tile's
+                     // logits, plus the logit of the row's target column (bf16 only)
 };
 
 struct GemmArgs {
@@ -42,7 +50,13 @@ struct GemmArgs {
   const int32_t *positions;// EPI_QKV_ROPE: (M) or NULL -> row % S
   const float *cos_sin;
   int S, d_head, max_seq;
+  // EPI_XENT: targets (M); partials x_max / x_sum laid out [tile_n][M]; x_tgt (M)
+  const int32_t *targets;
+  float *x_max, *x_sum, *x_tgt;
 };
+
+// Column tiles (partials per row) of the EPI_XENT GEMM for N = vocab columns.
+int gemm_xent_parts(int N);
 
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
 

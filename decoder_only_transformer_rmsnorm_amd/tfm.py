@@ -23,7 +23,9 @@ STATUS = {0: "TFM_OK", -1: "TFM_ERR_NULL", -2: "TFM_ERR_SHAPE", -3: "TFM_ERR_DTY
 EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_table_init",
            "tfm_embed", "tfm_rmsnorm", "tfm_rope", "tfm_linear", "tfm_qkv_rope", "tfm_causal_attention",
            "tfm_swiglu_workspace_bytes", "tfm_swiglu_ffn", "tfm_workspace_bytes",
-           "tfm_block_forward", "tfm_model_forward", "tfm_check_device_flags"]
+           "tfm_block_forward", "tfm_model_forward", "tfm_xent_workspace_bytes",
+           "tfm_lm_head_xent", "tfm_loss_workspace_bytes", "tfm_model_loss",
+           "tfm_check_device_flags"]
 
 
 class TfmError(RuntimeError):
@@ -90,6 +92,13 @@ def lib() -> ctypes.CDLL:
             "tfm_model_forward": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
                                           c_p, c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p,
                                           c_size, c_p]),
+            "tfm_xent_workspace_bytes": (c_size, [c_i64, c_int]),
+            "tfm_lm_head_xent": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, c_int, c_int, c_p,
+                                         c_size, c_p]),
+            "tfm_loss_workspace_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
+            "tfm_model_loss": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
+                                       c_p, c_p, c_p, c_p, c_p, c_int, c_int, c_p, c_p, c_size,
+                                       c_p]),
             "tfm_check_device_flags": (c_int, [c_p, c_p]),
         }
         for name, (res, args) in sig.items():
@@ -193,6 +202,31 @@ def tfm_linear(x, w, residual=None, out_dtype=None, y=None, ldy: int | None = No
     return y
 
 
+def next_token_targets(ids):
+    """(B, S) int32 targets for next-token prediction: ids shifted left by one, -1 last."""
+    torch = _torch()
+    t = torch.full_like(ids, -1)
+    t[:, :-1] = ids[:, 1:]
+    return t.contiguous()
+
+
+def tfm_lm_head_xent(x, w, targets, loss=None, mean=None, stream=None):
+    """Fused LM head + cross-entropy: x (M, K) bf16, w (V, K) bf16, targets (M,) int32 ->
+    (loss (M,) float32, mean (1,) float32)."""
+    torch = _torch()
+    V, K = w.shape
+    M = x.numel() // K
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=x.device)
+    if mean is None:
+        mean = torch.empty(1, dtype=torch.float32, device=x.device)
+    n = lib().tfm_xent_workspace_bytes(M, V)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().tfm_lm_head_xent(_dev(x), _dev(w), _dev(targets), _dev(loss), _dev(mean), M, V,
+                                  K, _dev(ws), n, _stream(stream)), "tfm_lm_head_xent")
+    return loss, mean
+
+
 def tfm_qkv_rope(xn, wq, wk, wv, n_heads: int, n_kv_heads: int, d_head: int, cos_sin,
                  max_seq: int, positions=None, qkv=None, stream=None):
     """xn (B, S, d) -> qkv (B, S, (Hq + 2 Hkv) d_head) with RoPE on the q and k columns."""
@@ -281,9 +315,11 @@ class DeviceModel:
         self.device = device
 
     def workspace(self, B: int, S: int):
+        """One workspace per (B, S), large enough for the forward and for the fused loss."""
         torch = _torch()
         if self._ws_shape != (B, S):
-            n = tfm_workspace_bytes(self.ccfg, B, S)
+            n = max(tfm_workspace_bytes(self.ccfg, B, S),
+                    lib().tfm_loss_workspace_bytes(ctypes.byref(self.ccfg), B, S))
             if n == 0:
                 raise TfmError(-2, "tfm_workspace_bytes")
             self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
@@ -308,6 +344,23 @@ class DeviceModel:
                                        ld, B, S, _dev(self.cos_sin), _dev(ws), ws.numel(),
                                        _stream(stream)), "tfm_model_forward")
         return logits
+
+    def loss(self, targets, ids=None, positions=None, loss=None, mean=None, stream=None):
+        """Forward ending in the fused LM-head cross-entropy: per-token loss (B*S,) float32 and
+        the mean over tokens with a target (1,) float32; targets (B, S) int32, -1 = none."""
+        torch = _torch()
+        ids = self.ids if ids is None else ids
+        B, S = ids.shape
+        if loss is None:
+            loss = torch.empty(B * S, dtype=torch.float32, device=self.device)
+        if mean is None:
+            mean = torch.empty(1, dtype=torch.float32, device=self.device)
+        ws = self.workspace(B, S)
+        _check(lib().tfm_model_loss(ctypes.byref(self.ccfg), ctypes.byref(self.weights), _dev(ids),
+                                    _dev(positions), _dev(targets), _dev(loss), _dev(mean), B, S,
+                                    _dev(self.cos_sin), _dev(ws), ws.numel(), _stream(stream)),
+               "tfm_model_loss")
+        return loss, mean
 
     def check_flags(self, stream=None) -> None:
         _check(lib().tfm_check_device_flags(_dev(self._ws), _stream(stream)), "tfm_check_device_flags")

@@ -168,8 +168,32 @@ int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const i
                       int B, int S, const float *cos_sin, void *ws, size_t ws_bytes,
                       void *stream);
 
-/* Waits for `stream`, then returns TFM_ERR_TOKEN if the last tfm_model_forward that used
- * this workspace saw an out-of-range token id, else TFM_OK. */
+/* Fused LM head and next-token cross-entropy  [T2 Optimize / Loss; T3 12 training]:
+ * for each row r, loss[r] = log(sum_j exp(z_rj - max_r)) + max_r - z_r,t with z = x w^T and
+ * t = targets[r]. The logits are formed tile by tile in float32 and reduced in registers to
+ * per-row log-sum-exp partials; they are never written. x: [dev] bf16 (M, K); w: [dev] bf16
+ * (V, K); targets: [dev] int32 (M), a negative target means no prediction for that row
+ * (loss 0, left out of the mean), a target >= V gives loss NaN; loss: [dev] float32 (M);
+ * mean: [dev] one float32 (mean over rows with a target, 0 if none) or NULL.
+ * ws: [dev] workspace of at least tfm_xent_workspace_bytes(M, V) bytes. K % 8 == 0; bf16
+ * only. The result is deterministic (fixed reduction order). */
+size_t tfm_xent_workspace_bytes(int64_t M, int V);
+int tfm_lm_head_xent(const void *x, const void *w, const int32_t *targets, float *loss,
+                     float *mean, int64_t M, int V, int K, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Whole forward ending in the fused cross-entropy instead of logits  [T1 5.7; T2 Optimize /
+ * Loss]: the trunk of tfm_model_forward, then tfm_lm_head_xent on RMSNorm(x; g_final).
+ * For next-token training targets[b, s] = ids[b, s + 1] and -1 at s = S - 1. bf16 models only
+ * (TFM_ERR_UNSUPPORTED otherwise). ws: at least tfm_loss_workspace_bytes(cfg, B, S) bytes;
+ * out-of-range ids are reported by tfm_check_device_flags as for the forward. */
+size_t tfm_loss_workspace_bytes(const tfm_config *cfg, int B, int S);
+int tfm_model_loss(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                   const int32_t *positions, const int32_t *targets, float *loss, float *mean,
+                   int B, int S, const float *cos_sin, void *ws, size_t ws_bytes, void *stream);
+
+/* Waits for `stream`, then returns TFM_ERR_TOKEN if the last tfm_model_forward (or
+ * tfm_model_loss) that used this workspace saw an out-of-range token id, else TFM_OK. */
 int tfm_check_device_flags(const void *ws, void *stream);
 
 #ifdef __cplusplus

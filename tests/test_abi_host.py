@@ -187,6 +187,48 @@ def test_block_and_model_validation(L):
     assert mdl() == NULL
 
 
+def test_xent_validation(L):
+    """Every call here fails validation (or is empty) before any launch."""
+    f = L.tfm_lm_head_xent
+    need = L.tfm_xent_workspace_bytes(16, 100)
+    parts = -(-100 // 128)
+    assert need == 2 * (-(-16 * parts * 4 // 256) * 256) + (-(-16 * 4 // 256) * 256)
+    assert L.tfm_xent_workspace_bytes(-1, 100) == 0 and L.tfm_xent_workspace_bytes(16, 0) == 0
+    call = lambda x=P, w=P, t=P, loss=P, mean=None, M=16, V=100, K=64, ws=P, nb=need: f(
+        x, w, t, loss, mean, M, V, K, ws, nb, None)
+    assert call(M=-1) == SHAPE
+    assert call(V=0) == SHAPE
+    assert call(K=60) == SHAPE
+    assert call(M=0) == OK
+    assert call(x=None) == NULL
+    assert call(t=None) == NULL
+    assert call(loss=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(x=PM) == ALIGN
+    assert call(w=PM) == ALIGN
+    assert call(nb=need - 1) == WS
+
+
+def test_model_loss_validation(L):
+    c = _cfg()
+    layers = (tfm.LayerWeights * 4)(*[_layer() for _ in range(4)])
+    mw = tfm.ModelWeights(P, layers, P, P)
+    need = L.tfm_loss_workspace_bytes(ctypes.byref(c), 2, 16)
+    assert need == L.tfm_workspace_bytes(ctypes.byref(c), 2, 16) + \
+        L.tfm_xent_workspace_bytes(32, c.vocab)
+    loss = lambda cfg=c, w=mw, t=P, out=P, nb=need, B=2: L.tfm_model_loss(
+        ctypes.byref(cfg), ctypes.byref(w) if w is not None else None, P, None, t, out, None, B,
+        16, P, P, nb, None)
+    assert loss(cfg=_cfg(dtype=0)) == UNSUP      # bf16 models only
+    assert loss(t=None) == NULL
+    assert loss(out=None) == NULL
+    assert loss(nb=need - 1) == WS
+    assert loss(w=None) == NULL
+    assert loss(B=0) == OK
+    layers[1].w1 = None
+    assert loss() == NULL
+
+
 def test_swiglu_validation(L):
     f = L.tfm_swiglu_ffn
     need = L.tfm_swiglu_workspace_bytes(64, 704, 1)
