@@ -88,7 +88,7 @@ template <int DH>
 __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, int64_t kv_stride, bf16_t *__restrict__ o, int64_t o_stride,
-    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2) {
+    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = AttnTile<DH>;
   constexpr int RB = T::RB, CPR = T::CPR, FR = T::FR, TILE = T::TILE, INS = T::INS;
@@ -104,8 +104,14 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int bh_count = B * Hq;
-  const int qt = n_qt - 1 - (int)(blockIdx.x / bh_count);   // longest first
-  const int bh = (int)(blockIdx.x % bh_count);
+  // Work items in order of decreasing length (query tile n_qt-1 of every head first). Blocks
+  // take them in a snake over rounds of `cus` blocks (one per CU when the grid is dispatched
+  // in order): a CU's blocks of rounds 0, 1, 2 get long, shorter and short items.
+  const int round = (int)(blockIdx.x / cus), in_round = (int)(blockIdx.x % cus);
+  int item = (round & 1) ? round * cus + (cus - 1 - in_round) : (int)blockIdx.x;
+  if (item >= (int)gridDim.x) item = (int)blockIdx.x;   // partial last round: keep in order
+  const int qt = n_qt - 1 - item / bh_count;
+  const int bh = item % bh_count;
   const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
   const int q0 = qt * kBQ, qw0 = q0 + wid * 32;
   const uint32_t kvsb = (uint32_t)(kv_stride * 2);   // bytes between key rows
@@ -377,6 +383,20 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   for (int e = 0; e < DH; ++e) op[e] = acc[e] * inv;
 }
 
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int DH>
 hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
                     int64_t os, int B, int S, int Hq, int Hkv, hipStream_t st) {
@@ -387,7 +407,7 @@ hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int
   const float sl2 = kLog2e / sqrtf((float)DH);
   attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
       (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S, Hq,
-      Hkv, n_qt, sl2);
+      Hkv, n_qt, sl2, compute_units());
   return hipGetLastError();
 }
 
