@@ -43,6 +43,8 @@ class ModelConfig:
     init_std: float = 0.02
     trunc_sigma: float | None = None   # resample draws with |z| > trunc_sigma
     out_proj_scale: float = 1.0        # multiplies the std of W_O and W2
+    window: int = 0                    # > 0: sliding-window attention of this many keys
+    full_every: int = 0                # > 0: every full_every-th layer keeps full attention
 
     @property
     def q_dim(self) -> int:

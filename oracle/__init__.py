@@ -25,7 +25,7 @@ _p = ctypes.c_void_p
 class OracleCfg(ctypes.Structure):
     _fields_ = [("n_layers", c_int), ("d_model", c_int), ("n_heads", c_int),
                 ("n_kv_heads", c_int), ("d_head", c_int), ("d_ff", c_int), ("vocab", c_int),
-                ("eps", c_double), ("theta", c_double)]
+                ("eps", c_double), ("theta", c_double), ("window", c_int), ("full_every", c_int)]
 
 
 class OracleLayer(ctypes.Structure):
@@ -56,8 +56,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_softmax.argtypes = [_p, c_i64, c_int, _p]
         L.oracle_attention.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int, c_int,
                                        c_int, _p, _p]
+        L.oracle_attention_window.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int,
+                                              c_int, c_int, c_int, _p, _p]
         L.oracle_attention_rows.argtypes = [_p, c_i64, _p, _p, c_i64, c_int, c_int, c_int,
-                                            c_int, c_int, _p, c_i64, _p]
+                                            c_int, c_int, c_int, _p, c_i64, _p]
         L.oracle_silu.restype = c_double
         L.oracle_silu.argtypes = [c_double]
         L.oracle_swiglu.argtypes = [_p, c_i64, c_int, c_int, _p, _p, _p, _p, _p]
@@ -137,28 +139,34 @@ def softmax(s) -> np.ndarray:
     return p
 
 
-def attention(q, k, v, n_heads: int, n_kv_heads: int, want_probs: bool = False):
-    """Causal attention on q (B, S, Hq*dh), k and v (B, S, Hkv*dh)."""
+def attention(q, k, v, n_heads: int, n_kv_heads: int, want_probs: bool = False,
+              window: int = 0):
+    """Causal attention on q (B, S, Hq*dh), k and v (B, S, Hkv*dh); window > 0 limits each
+    query to its `window` most recent keys."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, S, qd = q.shape
     dh = qd // n_heads
     assert k.shape == v.shape == (B, S, n_kv_heads * dh)
     o = np.empty((B, S, qd), dtype=np.float64)
     probs = np.empty((B, n_heads, S, S), dtype=np.float64) if want_probs else None
-    lib().oracle_attention(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
-                           n_kv_heads, dh, _ptr(o), _ptr(probs))
+    if window > 0:
+        lib().oracle_attention_window(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S,
+                                      n_heads, n_kv_heads, dh, window, _ptr(o), _ptr(probs))
+    else:
+        lib().oracle_attention(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
+                               n_kv_heads, dh, _ptr(o), _ptr(probs))
     return (o, probs) if want_probs else o
 
 
-def attention_rows(q, k, v, n_heads: int, n_kv_heads: int, rows):
-    """Causal attention output at the listed rows (b*S + s) only: (len(rows), Hq*dh)."""
+def attention_rows(q, k, v, n_heads: int, n_kv_heads: int, rows, window: int = 0):
+    """Attention output at the listed rows (b*S + s) only: (len(rows), Hq*dh)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, S, qd = q.shape
     dh = qd // n_heads
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     o = np.empty((rows.size, qd), dtype=np.float64)
     lib().oracle_attention_rows(_ptr(q), qd, _ptr(k), _ptr(v), n_kv_heads * dh, B, S, n_heads,
-                                n_kv_heads, dh, _ptr(rows), rows.size, _ptr(o))
+                                n_kv_heads, dh, window, _ptr(rows), rows.size, _ptr(o))
     return o
 
 
@@ -178,7 +186,8 @@ def swiglu(h, w1, w3, w2, want_hidden: bool = False):
 
 def _cfg(cfg) -> OracleCfg:
     return OracleCfg(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
-                     cfg.d_ff, cfg.vocab, cfg.eps, cfg.rope_theta)
+                     cfg.d_ff, cfg.vocab, cfg.eps, cfg.rope_theta,
+                     getattr(cfg, "window", 0), getattr(cfg, "full_every", 0))
 
 
 def _layer(lw, keep: list) -> OracleLayer:
@@ -188,14 +197,16 @@ def _layer(lw, keep: list) -> OracleLayer:
     return OracleLayer(*[a.ctypes.data for a in arrs])
 
 
-def block(cfg, lw, x, pos=None) -> np.ndarray:
-    """One pre-norm block on the residual x of shape (B, S, D); returns a new array."""
+def block(cfg, lw, x, pos=None, window: int = 0) -> np.ndarray:
+    """One pre-norm block on the residual x of shape (B, S, D); returns a new array. window > 0
+    gives the block sliding-window attention."""
     x = _f64(x).copy()
     B, S, _ = x.shape
     keep: list = []
     L = _layer(lw, keep)
     pos = None if pos is None else _i32(np.broadcast_to(pos, (B, S)))
     c = _cfg(cfg)
+    c.window, c.full_every = window, 0
     lib().oracle_block(ctypes.byref(c), ctypes.byref(L), _ptr(x), _ptr(pos), B, S)
     return x
 

@@ -100,12 +100,14 @@ void oracle_softmax(const double *s, int64_t rows, int n, double *p) {
  * heads shares one KV head. One query row of one head; sc is scratch of >= s+1 doubles. */
 static void attend_one(const double *q, int64_t q_stride, const double *k, const double *v,
                        int64_t kv_stride, int S, int Hq, int Hkv, int dh, int b, int h, int s,
-                       double *os, double *prow, double *sc) {
+                       int window, double *os, double *prow, double *sc) {
   const int g = h / (Hq / Hkv);
   const double scale = 1.0 / sqrt((double)dh);
   const double *qs = q + ((int64_t)b * S + s) * q_stride + (int64_t)h * dh;
+  /* [T2 sliding window]: with a window W > 0 the query sees only the W most recent keys */
+  const int t0 = (window > 0 && s - window + 1 > 0) ? s - window + 1 : 0;
   double m = -INFINITY;
-  for (int t = 0; t <= s; ++t) {
+  for (int t = t0; t <= s; ++t) {
     const double *kt = k + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
     double dot = 0.0;
     for (int e = 0; e < dh; ++e) dot += qs[e] * kt[e];
@@ -113,35 +115,43 @@ static void attend_one(const double *q, int64_t q_stride, const double *k, const
     if (sc[t] > m) m = sc[t];
   }
   double sum = 0.0;
-  for (int t = 0; t <= s; ++t) sum += exp(sc[t] - m);
+  for (int t = t0; t <= s; ++t) sum += exp(sc[t] - m);
   for (int e = 0; e < dh; ++e) os[e] = 0.0;
-  for (int t = 0; t <= s; ++t) {
+  for (int t = t0; t <= s; ++t) {
     double pt = exp(sc[t] - m) / sum;
     if (prow) prow[t] = pt;
     const double *vt = v + ((int64_t)b * S + t) * kv_stride + (int64_t)g * dh;
     for (int e = 0; e < dh; ++e) os[e] += pt * vt[e];
   }
-  if (prow)
+  if (prow) {
+    for (int t = 0; t < t0; ++t) prow[t] = 0.0;
     for (int t = s + 1; t < S; ++t) prow[t] = 0.0;
+  }
 }
 
-void oracle_attention(const double *q, int64_t q_stride, const double *k, const double *v,
-                      int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, double *o,
-                      double *probs) {
+void oracle_attention_window(const double *q, int64_t q_stride, const double *k, const double *v,
+                             int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, int window,
+                             double *o, double *probs) {
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < Hq; ++h) {
       double *sc = (double *)malloc(sizeof(double) * (size_t)S);
       for (int s = 0; s < S; ++s)
-        attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s,
+        attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s, window,
                    o + ((int64_t)b * S + s) * ((int64_t)Hq * dh) + (int64_t)h * dh,
                    probs ? probs + (((int64_t)b * Hq + h) * S + s) * S : NULL, sc);
       free(sc);
     }
 }
 
+void oracle_attention(const double *q, int64_t q_stride, const double *k, const double *v,
+                      int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, double *o,
+                      double *probs) {
+  oracle_attention_window(q, q_stride, k, v, kv_stride, B, S, Hq, Hkv, dh, 0, o, probs);
+}
+
 void oracle_attention_rows(const double *q, int64_t q_stride, const double *k, const double *v,
-                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh,
+                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, int window,
                            const int64_t *rows, int64_t n_rows, double *o) {
   (void)B;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -149,7 +159,7 @@ void oracle_attention_rows(const double *q, int64_t q_stride, const double *k, c
     for (int h = 0; h < Hq; ++h) {
       const int b = (int)(rows[i] / S), s = (int)(rows[i] % S);
       double *sc = (double *)malloc(sizeof(double) * (size_t)S);
-      attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s,
+      attend_one(q, q_stride, k, v, kv_stride, S, Hq, Hkv, dh, b, h, s, window,
                  o + i * ((int64_t)Hq * dh) + (int64_t)h * dh, NULL, sc);
       free(sc);
     }
@@ -200,7 +210,8 @@ void oracle_block(const oracle_cfg *c, const oracle_layer *w, double *x, const i
   oracle_linear(h, M, D, w->wv, kvd, v);
   oracle_rope(q, B, S, c->n_heads, c->d_head, qd, pos, c->theta);
   oracle_rope(k, B, S, c->n_kv_heads, c->d_head, kvd, pos, c->theta);
-  oracle_attention(q, qd, k, v, kvd, B, S, c->n_heads, c->n_kv_heads, c->d_head, o, NULL);
+  oracle_attention_window(q, qd, k, v, kvd, B, S, c->n_heads, c->n_kv_heads, c->d_head, c->window,
+                          o, NULL);
   oracle_linear(o, M, qd, w->wo, D, y);
   for (int64_t i = 0; i < M * D; ++i) x[i] += y[i];
 
@@ -221,7 +232,13 @@ int oracle_model(const oracle_cfg *c, const float *embed, const oracle_layer *la
   const int D = c->d_model;
   double *x = (double *)malloc(sizeof(double) * (size_t)(M * D));
   if (oracle_embedding(ids, M, embed, c->vocab, D, x) != 0) { free(x); return -1; }
-  for (int l = 0; l < c->n_layers; ++l) oracle_block(c, &layers[l], x, pos, B, S);
+  for (int l = 0; l < c->n_layers; ++l) {
+    /* [T2 hybrid attention]: windowed layers, except every full_every-th layer */
+    oracle_cfg cl = *c;
+    const int full = c->full_every > 0 && l % c->full_every == c->full_every - 1;
+    cl.window = full ? 0 : c->window;
+    oracle_block(&cl, &layers[l], x, pos, B, S);
+  }
 
   double *g = (double *)malloc(sizeof(double) * (size_t)D);
   double *xf = (double *)malloc(sizeof(double) * (size_t)(M * D));

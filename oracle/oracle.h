@@ -37,6 +37,11 @@ extern "C" {
 typedef struct {
   int n_layers, d_model, n_heads, n_kv_heads, d_head, d_ff, vocab;
   double eps, theta;
+  /* [T2 sliding window and hybrid attention]: window > 0 limits every query to its `window`
+   * most recent keys (itself included); with full_every > 0, layers l with
+   * l % full_every == full_every - 1 keep full causal attention. oracle_block uses `window`
+   * as given. */
+  int window, full_every;
 } oracle_cfg;
 
 typedef struct {
@@ -69,10 +74,17 @@ void oracle_attention(const double *q, int64_t q_stride, const double *k, const 
                       int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, double *o,
                       double *probs);
 
-/* The rows of oracle_attention listed in `rows` (row = b*S + s), every head; o is
+/* Sliding-window causal attention  [T2 sliding window]: as oracle_attention, but query s sees
+ * the keys t with max(0, s - window + 1) <= t <= s; window <= 0 means no limit. probs has zeros
+ * outside the band. */
+void oracle_attention_window(const double *q, int64_t q_stride, const double *k, const double *v,
+                             int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, int window,
+                             double *o, double *probs);
+
+/* The rows of oracle_attention_window listed in `rows` (row = b*S + s), every head; o is
  * (n_rows, Hq*dh). Same definition, for sampled checks at sizes where all rows would be slow. */
 void oracle_attention_rows(const double *q, int64_t q_stride, const double *k, const double *v,
-                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh,
+                           int64_t kv_stride, int B, int S, int Hq, int Hkv, int dh, int window,
                            const int64_t *rows, int64_t n_rows, double *o);
 
 /* SiLU(u) = u * sigmoid(u)  [T1 5.3; T2 SiLU]. */

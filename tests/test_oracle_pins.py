@@ -468,3 +468,76 @@ def test_next_token_targets_shift_by_one():
     """Targets are the inputs shifted left by one position; the last position has none."""
     t = oracle.next_token_targets(np.array([[5, 6, 7, 8], [1, 2, 3, 4]]))
     assert t.tolist() == [[6, 7, 8, -1], [2, 3, 4, -1]]
+
+
+# ---------------------------------------------------------------- sliding-window attention
+def _band_qkv(B, S, H, Hkv, dh, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (g.normal(size=(B, S, H * dh)), g.normal(size=(B, S, Hkv * dh)),
+            g.normal(size=(B, S, Hkv * dh)))
+
+
+def test_window_at_least_seq_is_causal_and_window_one_is_identity():
+    q, k, v = _band_qkv(2, 9, 2, 1, 8, 31)
+    full = oracle.attention(q, k, v, 2, 1)
+    assert np.array_equal(oracle.attention(q, k, v, 2, 1, window=9), full)
+    assert np.array_equal(oracle.attention(q, k, v, 2, 1, window=50), full)
+    # window 1: each query sees only its own key, so the output is its own value row
+    o1 = oracle.attention(q, k, v, 2, 1, window=1)
+    assert np.allclose(o1, np.concatenate([v, v], axis=2), rtol=0, atol=1e-15)
+
+
+def test_window_two_closed_form():
+    """Window 2: o_s = (e^a v_{s-1} + e^b v_s) / (e^a + e^b), a and b the scaled scores of keys
+    s-1 and s; a dropped bound or an off-by-one in the window fails it."""
+    q, k, v = _band_qkv(1, 6, 1, 1, 4, 32)
+    o = oracle.attention(q, k, v, 1, 1, window=2)
+    for s in range(6):
+        if s == 0:
+            ref = v[0, 0]
+        else:
+            a = q[0, s] @ k[0, s - 1] / 2.0
+            b = q[0, s] @ k[0, s] / 2.0
+            ref = (np.exp(a) * v[0, s - 1] + np.exp(b) * v[0, s]) / (np.exp(a) + np.exp(b))
+        assert np.allclose(o[0, s], ref, rtol=0, atol=1e-14)
+
+
+def test_window_brute_force_band_matrix_and_probs():
+    """Explicit S x S scores with the band mask (keys s-W+1 .. s), softmax, P V."""
+    B, S, H, Hkv, dh, W = 2, 13, 4, 2, 8, 5
+    q, k, v = _band_qkv(B, S, H, Hkv, dh, 33)
+    o, probs = oracle.attention(q, k, v, H, Hkv, want_probs=True, window=W)
+    idx = np.arange(S)
+    band = (idx[None, :] <= idx[:, None]) & (idx[None, :] > idx[:, None] - W)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            qs = q[b, :, h * dh:(h + 1) * dh]
+            ks = k[b, :, g * dh:(g + 1) * dh]
+            vs = v[b, :, g * dh:(g + 1) * dh]
+            sc = np.where(band, qs @ ks.T / np.sqrt(dh), -np.inf)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            assert np.allclose(probs[b, h], p, rtol=0, atol=1e-14)
+            assert (probs[b, h][~band] == 0).all()
+            assert np.allclose(o[b, :, h * dh:(h + 1) * dh], p @ vs, rtol=0, atol=1e-13)
+    rows = np.array([0, 4, 5, 12, 13, 25])
+    assert np.allclose(oracle.attention_rows(q, k, v, H, Hkv, rows, window=W),
+                       o.reshape(B * S, -1)[rows], rtol=0, atol=0)
+
+
+def test_hybrid_model_window_rule():
+    """A window covering the whole sequence, or full_every = 1 (every layer full), reproduces
+    the full-attention model exactly; a short window with no full layers changes the logits."""
+    cfg = synth.ModelConfig(name="w", dtype="f32", n_layers=3, d_model=32, n_heads=4,
+                            n_kv_heads=2, d_head=8, d_ff=64, vocab=50, batch=2, seq=24)
+    inp = synth.make_inputs(cfg, seed=5)
+    full = oracle.model(cfg, inp)
+    import dataclasses
+    assert np.array_equal(oracle.model(dataclasses.replace(cfg, window=24), inp), full)
+    assert np.array_equal(oracle.model(dataclasses.replace(cfg, window=4, full_every=1), inp), full)
+    local = oracle.model(dataclasses.replace(cfg, window=4), inp)
+    assert not np.allclose(local, full)
+    # position 3 sees at most 4 keys, so a window of 4 leaves it unchanged in every layer
+    assert np.allclose(local.reshape(2, 24, -1)[:, :4], full.reshape(2, 24, -1)[:, :4],
+                       rtol=0, atol=1e-12)
