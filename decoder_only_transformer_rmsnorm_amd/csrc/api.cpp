@@ -65,6 +65,7 @@ int check_config(const tfm_config *c, int B, int S) {
   if (!(c->eps >= 0.f) || !std::isfinite(c->rope_theta) || !(c->rope_theta > 0.f))
     return TFM_ERR_SHAPE;
   if (B < 0 || S < 0 || S > c->max_seq_len) return TFM_ERR_SHAPE;
+  if (c->attn_window < 0 || c->attn_full_every < 0) return TFM_ERR_SHAPE;
   const int kalign = c->dtype == TFM_BF16 ? 8 : 4;
   if (c->d_model % kalign != 0 || c->d_ff % kalign != 0 ||
       (c->n_heads * c->d_head) % kalign != 0)
@@ -88,7 +89,7 @@ int check_layer(const tfm_layer_weights *w) {
 // Enqueue one block; arguments already validated.
 int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
                   const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *ws,
-                  const WsPlan &p, hipStream_t s) {
+                  const WsPlan &p, int window, hipStream_t s) {
   const int64_t M = (int64_t)B * S;
   const int D = c->d_model, dt = c->dtype;
   const int qd = c->n_heads * c->d_head, kvd = c->n_kv_heads * c->d_head;
@@ -109,7 +110,8 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
 
   TFM_HIP(launch_attention(qkv, qkv_w, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e,
-                           qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt, s));
+                           qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt, window,
+                           s));
 
   g = GemmArgs{};
   g.a = o; g.lda = qd; g.w0 = w->wo; g.M = M; g.N = D; g.K = qd; g.y = x; g.ldy = D;
@@ -130,6 +132,13 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   return TFM_OK;
 }
 
+// Attention window of layer l ("LLM 2" hybrid attention): the configured window, except every
+// attn_full_every-th layer, which keeps full attention.
+int layer_window(const tfm_config *c, int l) {
+  const bool full = c->attn_full_every > 0 && l % c->attn_full_every == c->attn_full_every - 1;
+  return full ? 0 : c->attn_window;
+}
+
 // Embedding, every block and the final RMSNorm: leaves RMSNorm(x; g_final) in the xn region
 // of the workspace.
 int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t *ids,
@@ -141,7 +150,8 @@ int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t
   TFM_HIP(launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
                        (int32_t *)(wsb + p.flag), s));
   for (int l = 0; l < c->n_layers; ++l)
-    TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p, s));
+    TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p,
+                          layer_window(c, l), s));
   TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M, c->d_model,
                          c->eps, s));
   return TFM_OK;
@@ -298,6 +308,14 @@ int tfm_qkv_rope(const void *xn, const void *wq, const void *wk, const void *wv,
 int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                          int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                          int Hkv, int d_head, int dt, void *stream) {
+  return tfm_sliding_window_attention(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv,
+                                      d_head, 0, dt, stream);
+}
+
+int tfm_sliding_window_attention(const void *q, int64_t q_stride, const void *k, const void *v,
+                                 int64_t kv_stride, void *o, int64_t o_stride, int B, int S,
+                                 int Hq, int Hkv, int d_head, int window, int dt, void *stream) {
+  if (window < 0) return TFM_ERR_SHAPE;
   if (!valid_dt(dt)) return TFM_ERR_DTYPE;
   if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || d_head <= 0 || Hq % Hkv != 0) return TFM_ERR_SHAPE;
   if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head ||
@@ -311,7 +329,7 @@ int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const v
       kv_stride % 8 != 0 || o_stride % 8 != 0)
     return TFM_ERR_ALIGN;
   return hip_status(launch_attention(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv,
-                                     d_head, dt, (hipStream_t)stream));
+                                     d_head, dt, window, (hipStream_t)stream));
 }
 
 size_t tfm_swiglu_workspace_bytes(int64_t rows, int d_ff, int dt) {
@@ -358,7 +376,8 @@ int tfm_block_forward(const tfm_config *cfg, const tfm_layer_weights *w, float *
   if (!aligned16(x) || !aligned16(cos_sin) || !aligned16(ws)) return TFM_ERR_ALIGN;
   const WsPlan p = plan_ws(cfg, B, S);
   if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
-  return enqueue_block(cfg, w, x, positions, B, S, cos_sin, (uint8_t *)ws, p, (hipStream_t)stream);
+  return enqueue_block(cfg, w, x, positions, B, S, cos_sin, (uint8_t *)ws, p, cfg->attn_window,
+                       (hipStream_t)stream);
 }
 
 int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,

@@ -26,6 +26,10 @@
 //  * Tiles entirely above the diagonal are never loaded; per wave, tiles past its last
 //    query are skipped; only the diagonal tile is masked. Query tiles are issued
 //    longest-first to even out the causal imbalance.
+//  * Sliding window ("LLM 2" sliding window and hybrid attention): with window W > 0 query s
+//    sees keys s - W + 1 .. s. Tiles older than a workgroup's band are never loaded, a wave
+//    skips tiles outside its queries' band, and tiles on the band's lower edge are masked
+//    like the diagonal tile.
 // f32 kernel (d_head in {16, 32, 64, 128}): one thread per query with the same online
 // softmax in fp32; it exists for the small fp32 model and for tests, not for speed.
 #include <type_traits>
@@ -88,7 +92,7 @@ template <int DH>
 __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, int64_t kv_stride, bf16_t *__restrict__ o, int64_t o_stride,
-    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus) {
+    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus, int window) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = AttnTile<DH>;
   constexpr int RB = T::RB, CPR = T::CPR, FR = T::FR, TILE = T::TILE, INS = T::INS;
@@ -140,6 +144,8 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
 
   const int kv_end = min(q0 + kBQ, S);
   const int n_tiles = (kv_end + kBKV - 1) / kBKV;
+  // sliding window ("LLM 2" sliding window): query s sees keys s - window + 1 .. s
+  const int j_lo = window > 0 ? max(0, q0 - window + 1) / kBKV : 0;
 
   // ---- fills: lane l of a fill lands at base + 16 l, i.e. row frow, chunk slot fchunk; it
   //      fetches the global chunk that the swizzle places in that slot.
@@ -224,6 +230,7 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     if (j + NST - 1 < n_tiles) issue(j + NST - 1, ic<(SL + NST - 1) % NST>{});
     const int kv0 = j * kBKV;
     if (kv0 > qw0 + 31) return;   // every key of the tile is after this wave's queries
+    if (window > 0 && kv0 + kBKV - 1 < qw0 - window + 1) return;   // every key is too old
 
     // ---- S^T = K Q^T
     f32x16_t sacc[NKB];
@@ -266,6 +273,14 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
         for (int e = 0; e < 16; ++e)
           if (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) sacc[kb][e] = -__builtin_inff();
     }
+    if (window > 0 && kv0 < qw0 + 31 - window + 1) {   // band edge: keys older than the window
+      const int lo = my_q - window + 1 - kv0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + (e & 3) < lo) sacc[kb][e] = -__builtin_inff();
+    }
     float mt = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -277,7 +292,8 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const float m_new = fmaxf(m_run, mt);
-    const float mc = m_new * scale_log2;
+    // a lane that has seen no visible key yet (possible at a window's edge) keeps zero weight
+    const float mc = m_new == -__builtin_inff() ? 0.f : m_new * scale_log2;
     u32x4_t pf[PV_STEPS];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -324,9 +340,9 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     }
   };
 
-  issue(0, ic<0>{});
-  if (NST > 2 && n_tiles > 1) issue(1, ic<(NST > 2 ? 1 : 0)>{});
-  for (int j0 = 0; j0 < n_tiles; j0 += NST) {
+  issue(j_lo, ic<0>{});
+  if (NST > 2 && j_lo + 1 < n_tiles) issue(j_lo + 1, ic<(NST > 2 ? 1 : 0)>{});
+  for (int j0 = j_lo; j0 < n_tiles; j0 += NST) {
     tile(j0, ic<0>{});
     if (j0 + 1 < n_tiles) tile(j0 + 1, ic<1 % NST>{});
     if constexpr (NST > 2)
@@ -354,7 +370,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
                                                       const float *__restrict__ k,
                                                       const float *__restrict__ v, int64_t kv_stride,
                                                       float *__restrict__ o, int64_t o_stride, int B,
-                                                      int S, int Hq, int Hkv, float scale) {
+                                                      int S, int Hq, int Hkv, float scale,
+                                                      int window) {
   const int s = blockIdx.x * 64 + threadIdx.x;
   const int hq = blockIdx.y, b = blockIdx.z;
   if (s >= S) return;
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
 #pragma unroll
   for (int e = 0; e < DH; ++e) { qv[e] = qp[e] * scale; acc[e] = 0.f; }
   float m = -__builtin_inff(), l = 0.f;
-  for (int t = 0; t <= s; ++t) {
+  for (int t = window > 0 ? max(0, s - window + 1) : 0; t <= s; ++t) {
     const float *kp = k + ((int64_t)b * S + t) * kv_stride + (int64_t)hkv * DH;
     const float *vp = v + ((int64_t)b * S + t) * kv_stride + (int64_t)hkv * DH;
     float dot = 0.f;
@@ -399,7 +416,7 @@ int compute_units() {
 
 template <int DH>
 hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
-                    int64_t os, int B, int S, int Hq, int Hkv, hipStream_t st) {
+                    int64_t os, int B, int S, int Hq, int Hkv, int window, hipStream_t st) {
   const int n_qt = (S + kBQ - 1) / kBQ;
   const int64_t blocks = (int64_t)n_qt * B * Hq;
   if (blocks == 0) return hipSuccess;
@@ -407,19 +424,19 @@ hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int
   const float sl2 = kLog2e / sqrtf((float)DH);
   attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
       (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S, Hq,
-      Hkv, n_qt, sl2, compute_units());
+      Hkv, n_qt, sl2, compute_units(), window);
   return hipGetLastError();
 }
 
 template <int DH>
 hipError_t run_f32(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
-                   int64_t os, int B, int S, int Hq, int Hkv, hipStream_t st) {
+                   int64_t os, int B, int S, int Hq, int Hkv, int window, hipStream_t st) {
   if ((int64_t)B * S * Hq == 0) return hipSuccess;
   if (B > 65535 || Hq > 65535) return hipErrorInvalidValue;
   dim3 grid((S + 63) / 64, Hq, B);
   attn_f32_kernel<DH><<<grid, dim3(64), 0, st>>>((const float *)q, qs, (const float *)k,
                                                  (const float *)v, kvs, (float *)o, os, B, S, Hq,
-                                                 Hkv, 1.0f / sqrtf((float)DH));
+                                                 Hkv, 1.0f / sqrtf((float)DH), window);
   return hipGetLastError();
 }
 
@@ -436,19 +453,20 @@ bool attention_supported(int dt, int d_head) {
 
 hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
-                            int Hkv, int d_head, int dt, hipStream_t s) {
+                            int Hkv, int d_head, int dt, int window, hipStream_t s) {
+  const int w = window > 0 && window < S ? window : 0;   // a window of S or more is no limit
   if (dt == DT_BF16) {
     switch (d_head) {
-      case 32: return run_bf16<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
-      case 64: return run_bf16<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
-      case 128: return run_bf16<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
+      case 32: return run_bf16<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 64: return run_bf16<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 128: return run_bf16<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
     }
   } else {
     switch (d_head) {
-      case 16: return run_f32<16>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
-      case 32: return run_f32<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
-      case 64: return run_f32<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
-      case 128: return run_f32<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, s);
+      case 16: return run_f32<16>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 32: return run_f32<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 64: return run_f32<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 128: return run_f32<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
     }
   }
   return hipErrorInvalidValue;

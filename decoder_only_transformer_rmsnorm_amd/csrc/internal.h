@@ -61,9 +61,10 @@ int gemm_xent_parts(int N);
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
 
 // ---- attention (attention.hip)
+// window > 0: query s sees keys s - window + 1 .. s only (window >= S or 0: full causal).
 hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
-                            int Hkv, int d_head, int dt, hipStream_t s);
+                            int Hkv, int d_head, int dt, int window, hipStream_t s);
 bool attention_supported(int dt, int d_head);
 // Whether one sequence's keys fit the bf16 kernel's 32-bit buffer offsets.
 bool attention_fits(int dt, int S, int64_t kv_stride);

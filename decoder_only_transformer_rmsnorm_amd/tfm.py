@@ -25,6 +25,7 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_swiglu_workspace_bytes", "tfm_swiglu_ffn", "tfm_workspace_bytes",
            "tfm_block_forward", "tfm_model_forward", "tfm_xent_workspace_bytes",
            "tfm_lm_head_xent", "tfm_loss_workspace_bytes", "tfm_model_loss",
+           "tfm_sliding_window_attention",
            "tfm_check_device_flags"]
 
 
@@ -44,7 +45,7 @@ class Config(ctypes.Structure):
     _fields_ = [("n_layers", c_int), ("d_model", c_int), ("n_heads", c_int),
                 ("n_kv_heads", c_int), ("d_head", c_int), ("d_ff", c_int), ("vocab", c_int),
                 ("max_seq_len", c_int), ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("dtype", c_int)]
+                ("dtype", c_int), ("attn_window", c_int), ("attn_full_every", c_int)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                      c_int, c_int, c_p, c_int, c_int, c_p]),
             "tfm_causal_attention": (c_int, [c_p, c_i64, c_p, c_p, c_i64, c_p, c_i64, c_int,
                                              c_int, c_int, c_int, c_int, c_int, c_p]),
+            "tfm_sliding_window_attention": (c_int, [c_p, c_i64, c_p, c_p, c_i64, c_p, c_i64,
+                                                     c_int, c_int, c_int, c_int, c_int, c_int,
+                                                     c_int, c_p]),
             "tfm_swiglu_workspace_bytes": (c_size, [c_i64, c_int, c_int]),
             "tfm_swiglu_ffn": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_int, c_int, c_int,
                                        c_p, c_size, c_p]),
@@ -257,6 +261,24 @@ def tfm_causal_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head: int, o=
     return o
 
 
+def tfm_sliding_window_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head: int,
+                                 window: int, o=None, q_stride=None, kv_stride=None,
+                                 o_stride=None, stream=None):
+    """Causal attention over the last `window` keys of each query (window >= S is causal)."""
+    torch = _torch()
+    B, S = q.shape[0], q.shape[1]
+    if o is None:
+        o = torch.empty((B, S, n_heads * d_head), dtype=q.dtype, device=q.device)
+    qs = q.stride(1) if q_stride is None else q_stride
+    kvs = k.stride(1) if kv_stride is None else kv_stride
+    os_ = o.stride(1) if o_stride is None else o_stride
+    _check(lib().tfm_sliding_window_attention(_dev(q), qs, _dev(k), _dev(v), kvs, _dev(o), os_,
+                                              B, S, n_heads, n_kv_heads, d_head, window,
+                                              dt_code(q), _stream(stream)),
+           "tfm_sliding_window_attention")
+    return o
+
+
 def tfm_swiglu_ffn(xn, w1, w3, w2, residual=None, out=None, stream=None):
     torch = _torch()
     d_ff, d = w1.shape
@@ -275,7 +297,8 @@ def tfm_swiglu_ffn(xn, w1, w3, w2, residual=None, out=None, stream=None):
 def make_config(cfg, max_seq: int | None = None) -> Config:
     return Config(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.d_head, cfg.d_ff,
                   cfg.vocab, max_seq or cfg.seq, cfg.eps, cfg.rope_theta,
-                  BF16 if cfg.dtype == "bf16" else F32)
+                  BF16 if cfg.dtype == "bf16" else F32, getattr(cfg, "window", 0),
+                  getattr(cfg, "full_every", 0))
 
 
 def tfm_workspace_bytes(ccfg: Config, B: int, S: int) -> int:

@@ -54,6 +54,13 @@ typedef struct {
   float eps;        /* RMSNorm epsilon, inside the square root  [T1 5.6] */
   float rope_theta; /* RoPE base  [T1 5.5] */
   int dtype;        /* tfm_dtype of weights, GEMM operands and activations */
+  /* Sliding-window and hybrid attention  [T2 sliding window and hybrid attention]:
+   * attn_window > 0 limits each query to its attn_window most recent keys (itself
+   * included); 0 = full causal attention. With attn_full_every > 0, layers l with
+   * l % attn_full_every == attn_full_every - 1 keep full attention (tfm_model_forward,
+   * tfm_model_loss); tfm_block_forward applies attn_window as given. Both >= 0. */
+  int attn_window;
+  int attn_full_every;
 } tfm_config;
 
 /* [dev] pointers of one block's weights, all of the model dtype.
@@ -138,6 +145,14 @@ int tfm_qkv_rope(const void *xn, const void *wq, const void *wk, const void *wv,
 int tfm_causal_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                          int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                          int Hkv, int d_head, int dt, void *stream);
+
+/* Sliding-window causal attention  [T2 sliding window and hybrid attention]: as
+ * tfm_causal_attention, but query s attends only to the keys max(0, s - window + 1) .. s.
+ * window >= S (or 0) is plain causal attention; window < 0 is TFM_ERR_SHAPE. Key tiles wholly
+ * outside a query tile's band are never read. */
+int tfm_sliding_window_attention(const void *q, int64_t q_stride, const void *k, const void *v,
+                                 int64_t kv_stride, void *o, int64_t o_stride, int B, int S,
+                                 int Hq, int Hkv, int d_head, int window, int dt, void *stream);
 
 /* SwiGLU FFN  [T1 5.3; T2 SwiGLU FFN]:
  * out = (residual +) W2 ( SiLU(xn W1^T) * (xn W3^T) ), W1 the gate, W3 the up branch.

@@ -128,6 +128,18 @@ def test_attention_validation(L):
     assert call(args(S=0)) == OK
 
 
+def test_sliding_window_attention_validation(L):
+    f = L.tfm_sliding_window_attention
+    call = lambda W, q=P, S=8, dt=1, dh=64: f(q, 256, P, P, 128, P, 256, 2, S, 4, 2, dh, W, dt,
+                                              None)
+    assert call(-1) == SHAPE
+    assert call(-1, S=0) == SHAPE                  # the window is checked before the size
+    assert call(5, dh=16) == UNSUP
+    assert call(5, q=None) == NULL
+    assert call(5, S=0) == OK
+    assert call(0, S=0) == OK
+
+
 def _cfg(**kw):
     c = tfm.make_config(synth.SMALL_BF16)
     for k, v in kw.items():
@@ -166,6 +178,8 @@ def test_block_and_model_validation(L):
     assert blk(cfg=_cfg(dtype=4)) == DTYPE
     assert blk(cfg=_cfg(d_head=16, n_heads=32)) == UNSUP
     assert blk(S=300) == SHAPE
+    assert blk(cfg=_cfg(attn_window=-1)) == SHAPE
+    assert blk(cfg=_cfg(attn_full_every=-2)) == SHAPE
     assert blk(w=None) == NULL
     bad = _layer(); bad.w3 = None
     assert blk(w=bad) == NULL

@@ -149,6 +149,29 @@ def test_model_long_gqa_full_size_sampled():
     _sampled_model_check(synth.LONG_GQA_BF16, 0, 384, [0, 1, 127, 128, 255, 383])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_model_hybrid_sliding_window(dtype):
+    """Layers 0 and 2 attend over a 48-key window, layers 1 and 3 over the whole prefix; all
+    logits against the oracle's model with the same rule, and different from full attention."""
+    cfg = small(dtype, n_layers=4, seq=200, window=48, full_every=2)
+    say(f"model hybrid window {cfg.window} full_every {cfg.full_every} dtype={dtype}")
+    inp = synth.make_inputs(cfg, seed=7)
+    _, lg = _run_model(cfg, inp)
+    got = to_np(lg).reshape(cfg.batch, cfg.seq, cfg.vocab)
+    ref = oracle.model(cfg, inp)
+    if dtype == "f32":
+        err = float(np.abs(got - ref).max())
+        say(f"  max abs err {err:.3e}")
+        assert err <= F32_ABS
+    else:
+        rel = max_rel(got, ref)
+        say(f"  max rel err {rel:.3e}")
+        assert rel <= BF16_REL
+    full = oracle.model(cfg.replace(window=0, full_every=0), inp, ids=inp.ids[:1])
+    assert np.abs(full[0, 60:] - ref[0, 60:]).max() > 10 * np.abs(got[0] - ref[0]).max()
+    assert np.abs(full[0, :48] - ref[0, :48]).max() <= 1e-9 * np.abs(ref).max()
+
+
 # ---------------------------------------------------------------- invariants (bitwise)
 def test_causality_bitwise():
     """Tokens after position t are replaced; logits at positions <= t must not change at all

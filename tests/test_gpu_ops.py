@@ -234,6 +234,66 @@ def test_attention_full_size_sampled(B, S, Hq, Hkv, dh):
     assert_within(got[rows], ref, tol, "attention sampled")
 
 
+@pytest.mark.parametrize("dt,dh", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("B,S,Hq,Hkv,W", [(2, 200, 8, 2, 1), (1, 257, 4, 1, 100), (3, 130, 2, 2, 64),
+                                          (2, 300, 4, 4, 129), (1, 63, 4, 4, 62), (2, 700, 4, 2, 256)])
+def test_sliding_window_attention(dt, dh, B, S, Hq, Hkv, W):
+    """Each query sees its W most recent keys: W = 1 (only itself), W a multiple of the key
+    tile and not, W one short of S, and long sequences where most key tiles are skipped."""
+    say(f"sliding window attention dt={dt} dh={dh} B={B} S={S} Hq={Hq} Hkv={Hkv} W={W}")
+    tfm = tfm_mod()
+    packed, q, k, v = _attn_inputs(B, S, Hq, Hkv, dh, dt, seed=S * dh + W)
+    pd = to_dev(packed, dt)
+    qd, kvd = Hq * dh, Hkv * dh
+    o = tfm.tfm_sliding_window_attention(pd[..., :qd], pd[..., qd:qd + kvd], pd[..., qd + kvd:],
+                                         Hq, Hkv, dh, W)
+    got = to_np(o)
+    ref = oracle.attention(q, k, v, Hq, Hkv, window=W)
+    assert_within(got, ref, _attn_tol(v, ref, Hq, Hkv, dh, dt), "sliding window attention")
+    if W == 1:   # a query that sees only its own key returns its own value row
+        vq = np.repeat(v.reshape(B, S, Hkv, 1, dh), Hq // Hkv, axis=3).reshape(B, S, qd)
+        assert np.array_equal(got.astype(np.float32), vq.astype(np.float32))
+
+
+def test_sliding_window_at_least_s_is_causal_bitwise():
+    tfm = tfm_mod()
+    B, S, H, dh = 2, 333, 4, 64
+    packed, *_ = _attn_inputs(B, S, H, H, dh, "bf16", seed=3)
+    pd = to_dev(packed, "bf16")
+    qd = H * dh
+    args = (pd[..., :qd], pd[..., qd:2 * qd], pd[..., 2 * qd:], H, H, dh)
+    full = tfm.tfm_causal_attention(*args)
+    for W in (0, S, S + 1000):
+        assert torch.equal(tfm.tfm_sliding_window_attention(*args, W), full)
+    assert not torch.equal(tfm.tfm_sliding_window_attention(*args, S - 1), full)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,dh,W", [(8, 1024, 12, 12, 64, 256), (1, 8192, 16, 4, 128, 4096),
+                                             (32, 256, 16, 16, 32, 100)])
+def test_sliding_window_attention_full_size_sampled(B, S, Hq, Hkv, dh, W):
+    """Workload-sized attention with a window, checked at sampled query rows (the band edge
+    and both sides of it)."""
+    say(f"sliding window full size B={B} S={S} Hq={Hq} Hkv={Hkv} dh={dh} W={W}")
+    tfm = tfm_mod()
+    packed, q, k, v = _attn_inputs(B, S, Hq, Hkv, dh, "bf16", seed=6)
+    pd = to_dev(packed, "bf16")
+    qd, kvd = Hq * dh, Hkv * dh
+    o = tfm.tfm_sliding_window_attention(pd[..., :qd], pd[..., qd:qd + kvd], pd[..., qd + kvd:],
+                                         Hq, Hkv, dh, W)
+    got = to_np(o).reshape(B * S, qd)
+    r = rng(S + W)
+    pos = np.unique(np.concatenate([[0, 1, W - 2, W - 1, W, W + 1, W + 64, S // 2, S - 1],
+                                    r.integers(0, S, 8)]))
+    pos = pos[pos < S]
+    bs = r.integers(0, B, size=pos.size)
+    bs[-1] = B - 1
+    rows = bs * S + pos
+    ref = oracle.attention_rows(q, k, v, Hq, Hkv, rows, window=W)
+    tol = _attn_tol(v, np.zeros((B, S, qd)), Hq, Hkv, dh, "bf16").reshape(B * S, qd)[rows]
+    tol = tol + BF16_ULP * np.abs(ref)
+    assert_within(got[rows], ref, tol, "sliding window sampled")
+
+
 # ---------------------------------------------------------------- SwiGLU
 @pytest.mark.parametrize("dt,rows,d,dff,res", [("bf16", 300, 256, 704, False), ("bf16", 129, 512, 352, True),
                                                ("f32", 200, 64, 176, True), ("bf16", 8192, 768, 2048, True)])
