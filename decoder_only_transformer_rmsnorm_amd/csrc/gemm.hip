@@ -3,32 +3,36 @@
 // no bias).
 //
 // Common to both kernels:
-//  * 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BN/2) x (BM/2) sub-tile made
-//    of 32 x 32 MFMA blocks, accumulated in fp32.
+//  * A workgroup computes a BM x BN output tile; its waves split it in a grid, each wave
+//    owning a sub-tile of MS x MS matrix-core blocks accumulated in fp32.
 //  * The WEIGHT rows are the MFMA "A" operand and the activation rows the "B" operand, so
-//    the 32x32 accumulator puts 4 consecutive output columns n (same row m) in each lane.
-//    That makes the RoPE pairs (2i, 2i+1) and the gate/up pairs of SwiGLU lane-local and
-//    lets every lane store 4 contiguous outputs.
-//  * A K stage is 128 bytes per tile row (64 bf16 or 32 f32), kept in LDS as 16-byte chunks
-//    whose position is XOR-swizzled by the row, so the 32 rows one MFMA fragment reads fall
-//    on distinct banks. Two LDS stages, one barrier per stage.
+//    each lane's accumulator holds 4 consecutive output columns n of one row m. That makes
+//    the RoPE pairs (2i, 2i+1) and the gate/up pairs of SwiGLU lane-local and lets every
+//    lane store 4 contiguous outputs.
+//  * K stages are kept in LDS as 16-byte chunks whose position is XOR-swizzled by the row,
+//    so the rows one fragment read touches fall on distinct banks.
 //  * Epilogues: plain store (LM head; bf16 or f32, any row stride, odd N; streaming stores,
 //    since nothing on the path re-reads the logits), residual add into
 //    the fp32 stream (out and down projections), RoPE on the q/k columns of the fused QKV
 //    projection ("Transformer 篇" 5.5; "LLM 2" RoPE) and SiLU(gate) * up for the SwiGLU up
 //    projection ("Transformer 篇" 5.3; "LLM 2" SwiGLU FFN). For SwiGLU the weight tile
-//    interleaves 32 rows of W1 with the matching 32 rows of W3, so the two 32-column
-//    accumulator blocks of a wave hold gate and up of the same hidden units.
+//    interleaves 32 rows of W1 with the matching 32 rows of W3, so a wave's gate and up
+//    accumulator blocks hold the same hidden units.
 //
-// bf16 kernel (the model's GEMMs): tiles up to 256 x 256. Global data goes straight into
-// LDS with buffer_load_dwordx4 ... lds (no staging registers): each wave instruction fills
-// 8 tile rows (64 lanes x 16 B, lane l lands at base + 16 l), and each lane fetches the
-// global chunk that the swizzle assigns to its LDS slot. Buffer resources cover exactly the
-// rows a tile may read, so rows past M or N (and K chunks past K) read as zero without
-// branches. The next stage's loads are issued before the current stage's MFMAs. Tiles are
-// assigned to XCDs in contiguous runs (workgroup b runs on XCD b % 8) and ordered in groups
-// of 8 tile-rows, so the 32 workgroups an XCD runs at once share 8 activation and 4 weight
-// row-blocks in its L2.
+// bf16 kernel (the model's GEMMs): tiles up to 256 x 256, 4 or 8 waves, matrix-core blocks
+// of 32 x 32 x 16 or 16 x 16 x 32 (the latter moves less data through the register file
+// per flop, which is what counts once the chip runs at its power limit). Global data goes
+// straight into LDS with buffer_load_dwordx4 ... lds (no staging registers): each wave
+// instruction fills 1 KB of tile rows (lane l lands at base + 16 l) and each lane fetches
+// the global chunk that the swizzle assigns to its LDS slot; the k offset of a stage rides
+// in the scalar offset, so a fill costs no vector arithmetic. Buffer resources cover
+// exactly the rows a tile may read, so rows past M or N (and K chunks past K) read as zero
+// without branches. A ring of 2-6 stages runs ahead of the MFMAs, refilled between them.
+// The 8-wave ping-pong variant splits the waves into two groups half a step apart, so one
+// group's LDS reads and fills overlap the other's MFMAs on every SIMD. Tiles are assigned
+// to XCDs in contiguous runs (workgroup b runs on XCD b % 8) and ordered in groups of 8
+// tile-rows, so the workgroups an XCD runs at once share activation and weight row-blocks
+// in its L2.
 // f32 kernel (the small fp32 model): the same tile logic with register-staged loads and
 // v_mfma_f32_32x32x2_f32.
 #include <type_traits>
@@ -238,31 +242,48 @@ struct BfTile {
 // EARLY: issue all fills of the refilled stage right after the barrier (one burst) instead of
 // spreading them between the MFMAs of the step. WGM x WGN waves share the tile (each owns a
 // (BM/WGM) x (BN/WGN) sub-tile); with 8 waves two of them share each SIMD.
+// PP (ping-pong, 8 waves): the two waves of a SIMD belong to different wave groups (rows
+// 0..BM/2 and BM/2..BM of the tile) that run half a step apart. While one group multiplies
+// out of registers, the other reads its next fragments from LDS and issues its fills, so
+// the matrix cores of every SIMD alternate between the two waves instead of idling while
+// both wait on memory.
+// MS: matrix-core block, 32 (v_mfma_f32_32x32x16_bf16) or 16 (v_mfma_f32_16x16x32_bf16). The
+// 16x16 form moves less accumulator and operand data through the register file per flop,
+// which pays under the chip's power limit.
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2>
+          int WGN = 2, bool PP = false, int MS = 32>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
                                                                         int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NT = 64 * WGM * WGN;
   using T = BfTile<BM, BN, BK, NST, WGM * WGN>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
-  constexpr int LOADS = T::LOADS, STAGE = T::STAGE, KK = BK / 16;
+  static_assert(MS == 32 || MS == 16, "matrix-core block");
+  constexpr int KM = MS == 32 ? 16 : 32;           // k per MFMA
+  constexpr int LOADS = T::LOADS, STAGE = T::STAGE, KK = BK / KM;
+  constexpr int AE = MS * MS / 64;                 // accumulator elements per lane and block
   constexpr int WM = BM / WGM, WN = BN / WGN;      // wave sub-tile
-  constexpr int NBM = WM / 32, NBN = WN / 32;      // 32x32 blocks per wave
-  static_assert(NBM * 32 * WGM == BM && NBN * 32 * WGN == BN, "wave grid does not tile");
+  constexpr int NBM = WM / MS, NBN = WN / MS;      // MS x MS blocks per wave
+  static_assert(NBM * MS * WGM == BM && NBN * MS * WGN == BN, "wave grid does not tile");
+  static_assert(EPI != EPI_XENT || MS == 32, "the cross-entropy epilogue pairs lanes l, l^32");
+  static_assert(EPI != EPI_SWIGLU || MS == 32 || WN % 64 == 0,
+                "16x16 SwiGLU pairs gate/up blocks inside 64-row groups");
   static_assert(WGM % 2 == 0, "the two-pass epilogue splits the waves along M");
   constexpr int OUT_COLS = EPI == EPI_SWIGLU ? BN / 2 : (EPI == EPI_XENT ? 0 : BN);
   constexpr int LDS = T::RING > BM * OUT_COLS * 2 ? T::RING : BM * OUT_COLS * 2;
   static_assert(EPI != EPI_XENT || 2 * BM * WGN * 4 <= LDS, "cross-entropy row buffers");
   static_assert(LDS * OCC <= kLdsBytes, "LDS does not allow the requested occupancy");
   static_assert(EPI != EPI_SWIGLU || (NBN % 2) == 0, "SwiGLU needs gate/up block pairs");
+  using acc_t = std::conditional_t<MS == 32, f32x16_t, f32x4_t>;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid % WGM, wn = wid / WGM;
-  const int h = lane >> 5, l32 = lane & 31;
+  // ping-pong: waves w and w + 4 share a SIMD and sit in different groups (wm)
+  const int wm = PP ? wid / WGN : wid % WGM, wn = PP ? wid % WGN : wid / WGM;
+  // lane -> (row of the block it reads / m of its outputs, k chunk it reads / n group it holds)
+  const int h = lane / MS, l32 = lane % MS;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
@@ -296,22 +317,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   }
 
   const int nk = (K + BK - 1) / BK;
+  // The k offset of a stage travels in the scalar offset of the load, so a fill costs no
+  // vector arithmetic. Only a ragged last stage (K % BK != 0) switches each lane to its
+  // precomputed tail offset: out of range (reads zero) where its chunk lies past K.
+  const int tail_kt = K % BK != 0 ? nk - 1 : -1;
+  uint32_t a_toff[A_INS], b_toff[B_INS];
+#pragma unroll
+  for (int i = 0; i < A_INS; ++i) a_toff[i] = (nk - 1) * BK + a_k[i] >= K ? kOOB : a_off[i];
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) b_toff[i] = (nk - 1) * BK + b_k[i] >= K ? kOOB : b_off[i];
   // Fill number `idx` (A fills first, then B fills) of stage `kt`.
   auto issue_one = [&](int kt, int idx) {
-    const int kb = kt * BK;
-    const bool tail = kb + BK > K;
+    const int koff = kt * BK * 2;
     uint8_t *base = lds + (kt % NST) * STAGE;
     if (idx < A_INS) {
-      uint32_t off = a_off[idx] + kb * 2;
-      if (tail && kb + a_k[idx] >= K) off = kOOB;
+      const uint32_t off = kt == tail_kt ? a_toff[idx] : a_off[idx];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_void_t *)(base + (wid * A_INS + idx) * FR * RB), 16, off, 0, 0, 0);
+          a_rsrc, (lds_void_t *)(base + (wid * A_INS + idx) * FR * RB), 16, off, koff, 0, 0);
     } else {
       const int i = idx - A_INS;
-      uint32_t off = b_off[i] + kb * 2;
-      if (tail && kb + b_k[i] >= K) off = kOOB;
+      const uint32_t off = kt == tail_kt ? b_toff[i] : b_off[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc[i], (lds_void_t *)(base + (BM + (wid * B_INS + i) * FR) * RB), 16, off, 0, 0, 0);
+          b_rsrc[i], (lds_void_t *)(base + (BM + (wid * B_INS + i) * FR) * RB), 16, off, koff,
+          0, 0);
     }
   };
   auto issue = [&](int kt) {
@@ -327,13 +355,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  f32x16_t acc[NBN][NBM];
+  acc_t acc[NBN][NBM];
 #pragma unroll
   for (int bn = 0; bn < NBN; ++bn)
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[bn][bm][e] = 0.f;
+      for (int e = 0; e < AE; ++e) acc[bn][bm][e] = 0.f;
 
   // Fragment reads are issued as inline ds_read_b128: the compiler's wait insertion cannot
   // tell which LDS bytes an in-flight buffer->LDS fill writes, and would otherwise wait for
@@ -345,14 +373,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     const uint32_t st = lds_base + stage * STAGE;
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
-      const int row = wm * WM + bm * 32 + l32;
-      const uint32_t addr = st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4);
+      const int row = wm * WM + bm * MS + l32;
+      const uint32_t addr = st + row * RB + ((((KM / 8) * kk + h) ^ swz_rb<RB>(row)) << 4);
       asm volatile("ds_read_b128 %0, %1" : "=v"(fa[bm]) : "v"(addr) : "memory");
     }
 #pragma unroll
     for (int bn = 0; bn < NBN; ++bn) {
-      const int row = BM + wn * WN + bn * 32 + l32;
-      const uint32_t addr = st + row * RB + (((2 * kk + h) ^ swz_rb<RB>(row)) << 4);
+      const int row = BM + wn * WN + bn * MS + l32;
+      const uint32_t addr = st + row * RB + ((((KM / 8) * kk + h) ^ swz_rb<RB>(row)) << 4);
       asm volatile("ds_read_b128 %0, %1" : "=v"(fb[bn]) : "v"(addr) : "memory");
     }
   };
@@ -376,9 +404,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
         const int i = bn * NBM + bm;
-        acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, fb[bn]), __builtin_bit_cast(bf16x8_t, fa[bm]),
-            acc[bn][bm], 0, 0, 0);
+        if constexpr (MS == 32)
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, fb[bn]), __builtin_bit_cast(bf16x8_t, fa[bm]),
+              acc[bn][bm], 0, 0, 0);
+        else
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, fb[bn]), __builtin_bit_cast(bf16x8_t, fa[bm]),
+              acc[bn][bm], 0, 0, 0);
         if (fill_kt >= 0 && i % GAP == GAP - 1) {
           const int idx = fill0 + i / GAP;
           if (i / GAP < PER_STEP && idx < LOADS) issue_one(fill_kt, idx);
@@ -391,6 +424,51 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   // free and gets refilled, interleaved with this stage's MFMAs), then multiplies, reading
   // the next k step's fragments while the current step's MFMAs run.
   static_assert(NBM + NBN <= 15, "fragment reads exceed the lgkmcnt range");
+  if constexpr (PP) {
+    // Phases alternate memory / matrix work; group 1 runs one phase behind group 0, and
+    // every phase ends at a barrier of all 8 waves. Fills run D = NST-1 stages ahead: the
+    // memory phase of step kt reads all of stage kt's fragments into registers and issues
+    // this wave's fills of stage kt + D into the slot of stage kt - 1, which both groups
+    // finished reading before the previous barrier. Before the barrier that ends phase
+    // 2kt+1 every wave has its fills of stage kt + 1 complete, so both groups' later reads
+    // of that stage see all of it.
+    static_assert(WGM == 2 && WGM * WGN == 8 && NST >= 3, "ping-pong layout");
+    static_assert(KK * (NBM + NBN) <= 15, "fragment reads exceed the lgkmcnt range");
+    constexpr int D = NST - 1;
+    const int grp = wm;
+    for (int s = 0; s < D && s < nk; ++s) issue(s);
+    wait_fills(min(D - 1, nk - 1));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (grp == 1) asm volatile("s_barrier" ::: "memory");
+    u32x4_t fa[KK][NBM], fb[KK][NBN];
+    for (int kt = 0; kt < nk; ++kt) {
+      // ---- memory phase
+      const int stage = kt % NST;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) read_frags(stage, kk, fa[kk], fb[kk]);
+      if (kt + D < nk) issue(kt + D);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int bm = 0; bm < NBM; ++bm) asm volatile("" : "+v"(fa[kk][bm]));
+#pragma unroll
+        for (int bn = 0; bn < NBN; ++bn) asm volatile("" : "+v"(fb[kk][bn]));
+      }
+      if (grp == 1) wait_fills(min(D - 1, nk - 2 - kt));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- matrix phase
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) mfma_step(fa[kk], fb[kk], -1, 0);
+      if (grp == 0) wait_fills(min(D - 1, nk - 2 - kt));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (grp == 0) asm volatile("s_barrier" ::: "memory");
+  } else {
   for (int s = 0; s < NST - 1 && s < nk; ++s) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
     wait_fills(min(NST - 2, nk - 1 - kt));
@@ -413,8 +491,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
       } else {
         wait_frags(std::integral_constant<int, 0>{}, fa[kk & 1], fb[kk & 1]);
       }
+      // keep each step's MFMAs between its wait and the next step's reads: sunk below the
+      // next wait they would stall on reads they do not need
+      __builtin_amdgcn_sched_barrier(0);
       mfma_step(fa[kk & 1], fb[kk & 1], fill_kt, kk * PER_STEP);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
   }
   __syncthreads();  // every wave is done with the ring: reuse it to stage the output
 
@@ -503,8 +586,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   }
 
   // ---- epilogue: final values -> LDS (output dtype, row-major tile) -> coalesced rows.
-  //      Lane holds acc[bn][bm][4q + r] for n = n0 + wn*WN + bn*32 + 8q + 4h + r and
-  //      m = m0 + wm*WM + bm*32 + l32.
+  //      Lane holds acc[bn][bm][4q + r] for m = m0 + wm*WM + bm*MS + l32 and
+  //      n = n0 + wn*WN + bn*MS + 8q + 4h + r (MS = 32, q < 4) or + 4h + r (MS = 16).
   const bool out_bf16 = EPI == EPI_RESIDUAL ? false : g.y_dt == DT_BF16;
   const int ob = out_bf16 ? 2 : 4;
   const int rb = OUT_COLS * ob;
@@ -517,8 +600,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     if (passes == 1 || (2 * wm) / WGM == p) {
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
-        const int r = wm * WM + bm * 32 + l32 - p * prow;
-        const int64_t m = m0 + wm * WM + bm * 32 + l32;
+        const int r = wm * WM + bm * MS + l32 - p * prow;
+        const int64_t m = m0 + wm * WM + bm * MS + l32;
         int pos = 0;
         if constexpr (EPI == EPI_QKV_ROPE) {
           // rows fit in 32 bits here (M * row width < 2^31 elements); no 64-bit division
@@ -528,18 +611,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
 #pragma unroll
         for (int bn = 0; bn < (EPI == EPI_SWIGLU ? NBN / 2 : NBN); ++bn) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < AE / 4; ++q) {
             f32x4_t v;
             int col;
+            const int nq = MS == 32 ? 8 * q + 4 * h : 4 * h;   // n of the lane's 4 values
             if constexpr (EPI == EPI_SWIGLU) {
-              col = wn * WN / 2 + bn * 32 + 8 * q + 4 * h;
+              // virtual weight rows come in 64-row groups, 32 gate rows then their 32 up
+              // rows; gate block gb pairs with up block ub of the same hidden units
+              const int gb = MS == 32 ? 2 * bn : 4 * (bn >> 1) + (bn & 1);
+              const int ub = MS == 32 ? 2 * bn + 1 : gb + 2;
+              col = wn * WN / 2 + bn * MS + nq;
 #pragma unroll
               for (int x = 0; x < 4; ++x) {
-                const float a = acc[2 * bn][bm][4 * q + x], b = acc[2 * bn + 1][bm][4 * q + x];
+                const float a = acc[gb][bm][4 * q + x], b = acc[ub][bm][4 * q + x];
                 v[x] = a / (1.0f + __expf(-a)) * b;
               }
             } else {
-              col = wn * WN + bn * 32 + 8 * q + 4 * h;
+              col = wn * WN + bn * MS + nq;
 #pragma unroll
               for (int x = 0; x < 4; ++x) v[x] = acc[bn][bm][4 * q + x];
               if constexpr (EPI == EPI_QKV_ROPE) {
@@ -764,13 +852,13 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
 }
 
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2>
+          int WGN = 2, bool PP = false, int MS = 32>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS>),
                      dim3((unsigned)(tm * tn)), dim3(64 * WGM * WGN), 0, s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
@@ -791,10 +879,10 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // Tile shapes chosen per epilogue by a sweep on the decoder's GEMM shapes with random
     // operands. All use <= 80 KB of LDS and <= 256 registers per lane, so two workgroups share
     // a CU: one multiplies while the other waits on loads or writes its outputs.
-    case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true>(g, s);
+    case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
     case EPI_RESIDUAL: return run_bf16<128, 192, 64, 4, EPI_RESIDUAL, 1, true, 4, 2>(g, s);
     case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 4, EPI_QKV_ROPE, 1, true, 4, 2>(g, s);
-    case EPI_SWIGLU: return run_bf16<128, 256, 32, 3, EPI_SWIGLU, 2>(g, s);
+    case EPI_SWIGLU: return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
   }
   return hipErrorInvalidValue;
