@@ -170,6 +170,31 @@ def attention_rows(q, k, v, n_heads: int, n_kv_heads: int, rows, window: int = 0
     return o
 
 
+def decode_attention(q, k_cache, v_cache, n_heads: int, n_kv_heads: int, lens, window: int = 0):
+    """One new query per sequence attending to its cached keys [T4 6.1 KV cache: keys and
+    values of earlier steps are kept and the new token's are appended before attending].
+    q (B, Hq*dh); k_cache, v_cache (B, T, Hkv*dh) token-major, slot t = position t; sequence b
+    sees slots lens[b]-window .. lens[b]-1 (from 0 when window is 0 or larger). Plain fp64:
+    scores, max-subtracted softmax, weighted sum of values."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, qd = q.shape
+    dh = qd // n_heads
+    group = n_heads // n_kv_heads
+    o = np.zeros((B, qd), np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        t0 = max(0, n - window) if window > 0 else 0
+        for h in range(n_heads):
+            g = h // group
+            qh = q[b, h * dh:(h + 1) * dh]
+            kh = kc[b, t0:n, g * dh:(g + 1) * dh]
+            vh = vc[b, t0:n, g * dh:(g + 1) * dh]
+            sc = kh @ qh / np.sqrt(dh)
+            p = np.exp(sc - sc.max())
+            o[b, h * dh:(h + 1) * dh] = (p / p.sum()) @ vh
+    return o
+
+
 def silu(u: float) -> float:
     return lib().oracle_silu(float(u))
 

@@ -541,3 +541,38 @@ def test_hybrid_model_window_rule():
     # position 3 sees at most 4 keys, so a window of 4 leaves it unchanged in every layer
     assert np.allclose(local.reshape(2, 24, -1)[:, :4], full.reshape(2, 24, -1)[:, :4],
                        rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- KV-cache decode attention
+def test_decode_attention_equals_the_causal_row_of_its_position():
+    """[T4 6.1]: the key and value of step t depend only on tokens <= t, so attending from
+    the newest token to the cached keys gives exactly row t of causal attention over the whole
+    prefix; checked at ragged lengths, with grouped heads and with a window."""
+    B, S, H, Hkv, dh = 3, 40, 4, 2, 8
+    q, k, v = _band_qkv(B, S, H, Hkv, dh, 41)
+    pos = np.array([0, 17, 39])
+    rows = np.arange(B) * S + pos
+    for window in (0, 1, 5, 40):
+        got = oracle.decode_attention(q[np.arange(B), pos], k, v, H, Hkv, pos + 1, window=window)
+        ref = oracle.attention_rows(q, k, v, H, Hkv, rows, window=window)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_decode_attention_first_token_returns_its_value_and_zero_query_averages():
+    B, S, H, Hkv, dh = 2, 12, 2, 1, 4
+    q, k, v = _band_qkv(B, S, H, Hkv, dh, 43)
+    one = oracle.decode_attention(q[:, 0], k, v, H, Hkv, np.array([1, 1]))
+    np.testing.assert_allclose(one, np.concatenate([v[:, 0], v[:, 0]], axis=1), atol=1e-15)
+    zero = oracle.decode_attention(np.zeros((B, H * dh)), k, v, H, Hkv, np.array([12, 7]), window=3)
+    np.testing.assert_allclose(zero[0, :dh], v[0, 9:12].mean(axis=0), atol=1e-14)
+    np.testing.assert_allclose(zero[1, dh:], v[1, 4:7].mean(axis=0), atol=1e-14)
+
+
+def test_decode_attention_grouped_heads_equal_replicated_heads():
+    B, S, H, Hkv, dh = 2, 9, 6, 2, 4
+    q, k, v = _band_qkv(B, S, H, Hkv, dh, 47)
+    lens = np.array([9, 4])
+    grouped = oracle.decode_attention(q[:, -1], k, v, H, Hkv, lens)
+    rep = lambda a: np.repeat(a.reshape(B, S, Hkv, 1, dh), H // Hkv, axis=3).reshape(B, S, H * dh)
+    mha = oracle.decode_attention(q[:, -1], rep(k), rep(v), H, H, lens)
+    np.testing.assert_allclose(grouped, mha, atol=1e-15)
