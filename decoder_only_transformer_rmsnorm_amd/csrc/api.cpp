@@ -54,6 +54,36 @@ WsPlan plan_ws(const tfm_config *c, int B, int S) {
   return p;
 }
 
+// Workspace regions of a decode step (B tokens).
+struct DecPlan {
+  size_t flag, x, xn, q, o, u, part, total;
+};
+
+DecPlan plan_decode(const tfm_config *c, int B, int cache_seq) {
+  const size_t qd = (size_t)c->n_heads * c->d_head;
+  DecPlan p;
+  size_t off = 0;
+  p.flag = off; off += 256;
+  p.x = off; off += round256((size_t)B * c->d_model * 4);
+  p.xn = off; off += round256((size_t)B * c->d_model * 2);
+  p.q = off; off += round256((size_t)B * qd * 2);
+  p.o = off; off += round256((size_t)B * qd * 2);
+  p.u = off; off += round256((size_t)B * c->d_ff * 2);
+  p.part = off;
+  off += round256((size_t)B * c->n_heads * decode_chunks(cache_seq) * (2 + c->d_head) * 4);
+  p.total = off;
+  return p;
+}
+
+// What the decode path supports beyond a valid configuration.
+int check_decode_config(const tfm_config *c) {
+  if (c->dtype != TFM_BF16) return TFM_ERR_UNSUPPORTED;
+  if ((c->d_head != 32 && c->d_head != 64 && c->d_head != 128) ||
+      !decode_group_supported(c->n_heads, c->n_kv_heads))
+    return TFM_ERR_UNSUPPORTED;
+  return TFM_OK;
+}
+
 int check_config(const tfm_config *c, int B, int S) {
   if (!c) return TFM_ERR_NULL;
   if (!valid_dt(c->dtype)) return TFM_ERR_DTYPE;
@@ -87,9 +117,25 @@ int check_layer(const tfm_layer_weights *w) {
 }
 
 // Enqueue one block; arguments already validated.
+// KV cache of one layer: its K block and V block (bf16, (B, Hkv, cache_seq, d_head) each).
+struct LayerCache {
+  void *k = nullptr, *v = nullptr;
+  int seq = 0;
+};
+
+LayerCache layer_cache(const tfm_config *c, void *cache, int B, int cache_seq, int l) {
+  LayerCache lc;
+  if (!cache) return lc;
+  const size_t blk = (size_t)B * c->n_kv_heads * cache_seq * c->d_head;
+  lc.k = (uint16_t *)cache + 2 * (size_t)l * blk;
+  lc.v = (uint16_t *)cache + (2 * (size_t)l + 1) * blk;
+  lc.seq = cache_seq;
+  return lc;
+}
+
 int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
                   const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *ws,
-                  const WsPlan &p, int window, hipStream_t s) {
+                  const WsPlan &p, int window, hipStream_t s, const LayerCache &lc = {}) {
   const int64_t M = (int64_t)B * S;
   const int D = c->d_model, dt = c->dtype;
   const int qd = c->n_heads * c->d_head, kvd = c->n_kv_heads * c->d_head;
@@ -108,6 +154,9 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = c->d_head;
   g.max_seq = c->max_seq_len;
   TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
+  if (lc.k)   // prefill: rotated k and v rows into the cache slots of their positions
+    TFM_HIP(launch_kv_store(qkv, qkv_w, qd, kvd, c->d_head, c->n_kv_heads, B, S, positions,
+                            lc.k, lc.v, lc.seq, (int32_t *)(ws + p.flag) + 1, s));
 
   TFM_HIP(launch_attention(qkv, qkv_w, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e,
                            qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt, window,
@@ -143,15 +192,15 @@ int layer_window(const tfm_config *c, int l) {
 // of the workspace.
 int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t *ids,
                   const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *wsb,
-                  const WsPlan &p, hipStream_t s) {
+                  const WsPlan &p, hipStream_t s, void *kv_cache = nullptr, int cache_seq = 0) {
   const int64_t M = (int64_t)B * S;
   float *x = (float *)(wsb + p.x);
-  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 1, 0, s));
+  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 2, 0, s));   // token and position flags
   TFM_HIP(launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
                        (int32_t *)(wsb + p.flag), s));
   for (int l = 0; l < c->n_layers; ++l)
     TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p,
-                          layer_window(c, l), s));
+                          layer_window(c, l), s, layer_cache(c, kv_cache, B, cache_seq, l)));
   TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M, c->d_model,
                          c->eps, s));
   return TFM_OK;
@@ -215,6 +264,7 @@ const char *tfm_status_string(int status) {
     case TFM_ERR_UNSUPPORTED: return "unsupported configuration";
     case TFM_ERR_HIP: return "HIP launch or copy failed";
     case TFM_ERR_TOKEN: return "token id outside the vocabulary";
+    case TFM_ERR_POSITION: return "position outside the KV cache or the RoPE table";
   }
   return "unknown status";
 }
@@ -453,9 +503,140 @@ int tfm_model_loss(const tfm_config *cfg, const tfm_model_weights *w, const int3
 int tfm_check_device_flags(const void *ws, void *stream) {
   if (!ws) return TFM_ERR_NULL;
   TFM_HIP(hipStreamSynchronize((hipStream_t)stream));
-  int32_t flag = 0;
-  TFM_HIP(hipMemcpy(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost));
-  return flag ? TFM_ERR_TOKEN : TFM_OK;
+  int32_t flag[2] = {0, 0};
+  TFM_HIP(hipMemcpy(flag, ws, sizeof(flag), hipMemcpyDeviceToHost));
+  return flag[0] ? TFM_ERR_TOKEN : flag[1] ? TFM_ERR_POSITION : TFM_OK;
+}
+
+// ---- KV-cache incremental decoding
+
+size_t tfm_kv_cache_bytes(const tfm_config *cfg, int B, int cache_seq) {
+  if (!cfg || B < 0 || cache_seq < 0 || cfg->n_layers < 0 || cfg->n_kv_heads <= 0 ||
+      cfg->d_head <= 0)
+    return 0;
+  return 2 * (size_t)cfg->n_layers * B * cfg->n_kv_heads * cache_seq * cfg->d_head * 2;
+}
+
+int tfm_model_prefill(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                      const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                      int B, int S, const float *cos_sin, void *kv_cache, int cache_seq,
+                      void *ws, size_t ws_bytes, void *stream) {
+  TFM_TRY(check_config(cfg, B, S));
+  TFM_TRY(check_decode_config(cfg));
+  if (cache_seq <= 0) return TFM_ERR_SHAPE;
+  if (logits && !valid_dt(logits_dt)) return TFM_ERR_DTYPE;
+  if (!w) return TFM_ERR_NULL;
+  if (logits && ld_logits < cfg->vocab) return TFM_ERR_SHAPE;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!kv_cache) return TFM_ERR_NULL;
+  if (!aligned16(kv_cache) || (logits && !aligned16(logits))) return TFM_ERR_ALIGN;
+  TFM_TRY(check_model(cfg, w, ids, cos_sin, ws));
+  const WsPlan p = plan_ws(cfg, B, S);
+  if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *wsb = (uint8_t *)ws;
+  TFM_TRY(enqueue_trunk(cfg, w, ids, positions, B, S, cos_sin, wsb, p, s, kv_cache, cache_seq));
+  if (!logits) return TFM_OK;
+  GemmArgs g{};
+  g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = (int64_t)B * S;
+  g.N = cfg->vocab; g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
+  TFM_HIP(launch_gemm(EPI_STORE, cfg->dtype, g, s));
+  return TFM_OK;
+}
+
+size_t tfm_decode_workspace_bytes(const tfm_config *cfg, int B, int cache_seq) {
+  if (check_config(cfg, B, 1) != TFM_OK || check_decode_config(cfg) != TFM_OK || cache_seq <= 0)
+    return 0;
+  return plan_decode(cfg, B, cache_seq).total;
+}
+
+int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                     const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                     int B, const float *cos_sin, void *kv_cache, int cache_seq, void *ws,
+                     size_t ws_bytes, void *stream) {
+  TFM_TRY(check_config(cfg, B, 1));
+  TFM_TRY(check_decode_config(cfg));
+  if (cache_seq <= 0) return TFM_ERR_SHAPE;
+  if (!valid_dt(logits_dt)) return TFM_ERR_DTYPE;
+  if (!w) return TFM_ERR_NULL;
+  if (ld_logits < cfg->vocab) return TFM_ERR_SHAPE;
+  if (B == 0) return TFM_OK;
+  if (!positions || !kv_cache || !logits) return TFM_ERR_NULL;
+  if (!aligned16(kv_cache) || !aligned16(logits)) return TFM_ERR_ALIGN;
+  TFM_TRY(check_model(cfg, w, ids, cos_sin, ws));
+  const DecPlan p = plan_decode(cfg, B, cache_seq);
+  if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *wsb = (uint8_t *)ws;
+  const int D = cfg->d_model, F = cfg->d_ff, V = cfg->vocab;
+  const int qd = cfg->n_heads * cfg->d_head, kvd = cfg->n_kv_heads * cfg->d_head;
+  float *x = (float *)(wsb + p.x);
+  void *xn = wsb + p.xn, *q = wsb + p.q, *o = wsb + p.o, *u = wsb + p.u;
+  int32_t *flags = (int32_t *)(wsb + p.flag);
+  TFM_HIP(launch_fill_i32(flags, 2, 0, s));
+  TFM_HIP(launch_embed(ids, B, w->embed, TFM_BF16, V, D, x, flags, s));
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const tfm_layer_weights *lw = &w->layers[l];
+    const LayerCache lc = layer_cache(cfg, kv_cache, B, cache_seq, l);
+    TFM_HIP(launch_rmsnorm(x, DT_F32, lw->g_attn, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
+    DecodeGemmArgs g{};
+    g.x = xn; g.ldx = D; g.w0 = lw->wq; g.w1 = lw->wk; g.w2 = lw->wv; g.n0 = qd; g.n1 = kvd;
+    g.M = B; g.N = qd + 2 * kvd; g.K = D; g.y = q; g.ldy = qd; g.y_dt = DT_BF16;
+    g.positions = positions; g.cos_sin = cos_sin; g.d_head = cfg->d_head;
+    g.max_seq = cfg->max_seq_len; g.k_cache = lc.k; g.v_cache = lc.v; g.cache_seq = cache_seq;
+    g.n_kv_heads = cfg->n_kv_heads; g.pos_flag = flags + 1;
+    TFM_HIP(launch_decode_gemm(EPI_QKV_CACHE, g, s));
+    TFM_HIP(launch_decode_attention(q, qd, lc.k, lc.v, positions, B, cfg->n_heads,
+                                    cfg->n_kv_heads, cfg->d_head, cache_seq,
+                                    layer_window(cfg, l), (float *)(wsb + p.part), o, qd, s));
+    g = DecodeGemmArgs{};
+    g.x = o; g.ldx = qd; g.w0 = lw->wo; g.M = B; g.N = D; g.K = qd; g.y = x; g.ldy = D;
+    g.y_dt = DT_F32;
+    TFM_HIP(launch_decode_gemm(EPI_RESIDUAL, g, s));
+    TFM_HIP(launch_rmsnorm(x, DT_F32, lw->g_ffn, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
+    g = DecodeGemmArgs{};
+    g.x = xn; g.ldx = D; g.w0 = lw->w1; g.w1 = lw->w3; g.n0 = F; g.M = B; g.N = F; g.K = D;
+    g.y = u; g.ldy = F; g.y_dt = DT_BF16;
+    TFM_HIP(launch_decode_gemm(EPI_SWIGLU, g, s));
+    g = DecodeGemmArgs{};
+    g.x = u; g.ldx = F; g.w0 = lw->w2; g.M = B; g.N = D; g.K = F; g.y = x; g.ldy = D;
+    g.y_dt = DT_F32;
+    TFM_HIP(launch_decode_gemm(EPI_RESIDUAL, g, s));
+  }
+  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
+  DecodeGemmArgs g{};
+  g.x = xn; g.ldx = D; g.w0 = w->lm_head; g.M = B; g.N = V; g.K = D; g.y = logits;
+  g.ldy = ld_logits; g.y_dt = logits_dt;
+  TFM_HIP(launch_decode_gemm(EPI_STORE, g, s));
+  return TFM_OK;
+}
+
+size_t tfm_decode_attention_workspace_bytes(int B, int Hq, int d_head, int cache_seq) {
+  if (B < 0 || Hq <= 0 || d_head <= 0 || cache_seq <= 0) return 0;
+  return round256((size_t)B * Hq * decode_chunks(cache_seq) * (2 + d_head) * 4);
+}
+
+int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
+                         const void *v_cache, const int32_t *positions, void *o,
+                         int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
+                         int window, void *ws, size_t ws_bytes, void *stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || cache_seq <= 0 || window < 0)
+    return TFM_ERR_SHAPE;
+  if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head) return TFM_ERR_SHAPE;
+  if ((d_head != 32 && d_head != 64 && d_head != 128) || !decode_group_supported(Hq, Hkv))
+    return TFM_ERR_UNSUPPORTED;
+  if (B == 0) return TFM_OK;
+  if (!q || !k_cache || !v_cache || !positions || !o || !ws) return TFM_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(ws) || q_stride % 8 != 0 || o_stride % 8 != 0)
+    return TFM_ERR_ALIGN;
+  if (ws_bytes < tfm_decode_attention_workspace_bytes(B, Hq, d_head, cache_seq))
+    return TFM_ERR_WORKSPACE;
+  return hip_status(launch_decode_attention(q, q_stride, k_cache, v_cache, positions, B, Hq,
+                                            Hkv, d_head, cache_seq, window, (float *)ws, o,
+                                            o_stride, (hipStream_t)stream));
 }
 
 }  // extern "C"

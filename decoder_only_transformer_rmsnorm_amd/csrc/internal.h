@@ -31,8 +31,9 @@ enum GemmEpi {
   EPI_RESIDUAL = 1,  // y = residual + acc (float32)
   EPI_QKV_ROPE = 2,  // weight rows from wq | wk | wv; RoPE on the q and k columns
   EPI_SWIGLU = 3,    // gate rows from w1, up rows from w3; y = SiLU(gate) * up
-  EPI_XENT = 4       // no y: per row and column tile, max and sum of exp of the tile's
+  EPI_XENT = 4,      // no y: per row and column tile, max and sum of exp of the tile's
                      // logits, plus the logit of the row's target column (bf16 only)
+  EPI_QKV_CACHE = 5  // decode only: q -> y with RoPE; k (RoPE) and v -> KV cache slot
 };
 
 struct GemmArgs {
@@ -66,6 +67,38 @@ hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, cons
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
                             int Hkv, int d_head, int dt, int window, hipStream_t s);
 bool attention_supported(int dt, int d_head);
+// ---- incremental decoding (decode.hip), bf16 only
+struct DecodeGemmArgs {
+  const void *x;            // (M, K) activations, row stride ldx
+  int64_t ldx;
+  const void *w0, *w1, *w2; // weight rows: plain w0; QKV wq | wk | wv; SwiGLU w1 (gate), w3 (up)
+  int n0, n1;               // QKV: rows of wq and of wk; SwiGLU: d_ff
+  int M, N, K;
+  void *y;                  // STORE: (M, ldy) y_dt; RESIDUAL: fp32 in place; SwiGLU: u bf16;
+  int64_t ldy;              // QKV: rotated q (M, ldy) bf16
+  int y_dt;
+  const int32_t *positions; // QKV: position (= cache slot) of row m's token
+  const float *cos_sin;
+  int d_head, max_seq;
+  void *k_cache, *v_cache;  // QKV: this layer's (B, Hkv, cache_seq, d_head) blocks
+  int cache_seq, n_kv_heads;
+  int32_t *pos_flag;        // set to 1 when a position is outside [0, min(cache_seq, max_seq))
+};
+hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s);
+// Partial records per (sequence, query head): decode_chunks(cache_seq), each 2 + d_head floats.
+int decode_chunks(int cache_seq);
+bool decode_group_supported(int Hq, int Hkv);
+// o[b, h] = attention of q[b, h] over cache slots of sequence b up to positions[b] (the last
+// `window` of them when window > 0); part: B * Hq * decode_chunks * (2 + d_head) floats.
+hipError_t launch_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
+                                   const void *v_cache, const int32_t *positions, int B, int Hq,
+                                   int Hkv, int d_head, int cache_seq, int window, float *part,
+                                   void *o, int64_t o_stride, hipStream_t s);
+// Copies the k and v columns of B*S qkv rows into the cache slots positions[r] (or r % S).
+hipError_t launch_kv_store(const void *qkv, int64_t ld, int qd, int kvd, int d_head, int Hkv,
+                           int B, int S, const int32_t *positions, void *k_cache, void *v_cache,
+                           int cache_seq, int32_t *pos_flag, hipStream_t s);
+
 // Whether one sequence's keys fit the bf16 kernel's 32-bit buffer offsets.
 bool attention_fits(int dt, int S, int64_t kv_stride);
 

@@ -18,14 +18,16 @@ LIB_PATH = os.path.join(_HERE, "libtfm.so")
 F32, BF16 = 0, 1
 STATUS = {0: "TFM_OK", -1: "TFM_ERR_NULL", -2: "TFM_ERR_SHAPE", -3: "TFM_ERR_DTYPE",
           -4: "TFM_ERR_WORKSPACE", -5: "TFM_ERR_ALIGN", -6: "TFM_ERR_UNSUPPORTED",
-          -7: "TFM_ERR_HIP", -8: "TFM_ERR_TOKEN"}
+          -7: "TFM_ERR_HIP", -8: "TFM_ERR_TOKEN", -9: "TFM_ERR_POSITION"}
 
 EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_table_init",
            "tfm_embed", "tfm_rmsnorm", "tfm_rope", "tfm_linear", "tfm_qkv_rope", "tfm_causal_attention",
            "tfm_swiglu_workspace_bytes", "tfm_swiglu_ffn", "tfm_workspace_bytes",
            "tfm_block_forward", "tfm_model_forward", "tfm_xent_workspace_bytes",
            "tfm_lm_head_xent", "tfm_loss_workspace_bytes", "tfm_model_loss",
-           "tfm_sliding_window_attention",
+           "tfm_sliding_window_attention", "tfm_kv_cache_bytes", "tfm_model_prefill",
+           "tfm_decode_workspace_bytes", "tfm_model_decode",
+           "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
            "tfm_check_device_flags"]
 
 
@@ -103,6 +105,17 @@ def lib() -> ctypes.CDLL:
             "tfm_model_loss": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
                                        c_p, c_p, c_p, c_p, c_p, c_int, c_int, c_p, c_p, c_size,
                                        c_p]),
+            "tfm_kv_cache_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
+            "tfm_model_prefill": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
+                                          c_p, c_p, c_p, c_int, c_i64, c_int, c_int, c_p, c_p,
+                                          c_int, c_p, c_size, c_p]),
+            "tfm_decode_workspace_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
+            "tfm_model_decode": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
+                                         c_p, c_p, c_p, c_int, c_i64, c_int, c_p, c_p, c_int,
+                                         c_p, c_size, c_p]),
+            "tfm_decode_attention_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
+            "tfm_decode_attention": (c_int, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_int, c_int,
+                                             c_int, c_int, c_int, c_int, c_p, c_size, c_p]),
             "tfm_check_device_flags": (c_int, [c_p, c_p]),
         }
         for name, (res, args) in sig.items():
@@ -387,6 +400,77 @@ class DeviceModel:
 
     def check_flags(self, stream=None) -> None:
         _check(lib().tfm_check_device_flags(_dev(self._ws), _stream(stream)), "tfm_check_device_flags")
+
+    # ---- KV-cache decoding
+    def kv_cache(self, B: int, cache_seq: int):
+        """A zeroed KV cache for B sequences of up to cache_seq positions (all layers)."""
+        torch = _torch()
+        n = lib().tfm_kv_cache_bytes(ctypes.byref(self.ccfg), B, cache_seq)
+        return torch.zeros(n // 2, dtype=torch.bfloat16, device=self.device)
+
+    def prefill(self, cache, cache_seq: int, ids=None, positions=None, logits=True,
+                logits_dtype=None, stream=None):
+        """Forward over ids (B, S) that also fills the cache; returns the logits (or None)."""
+        torch = _torch()
+        ids = self.ids if ids is None else ids
+        B, S = ids.shape
+        V = self.cfg.vocab
+        out = torch.empty((B * S, V), dtype=logits_dtype or self.dtype,
+                          device=self.device) if logits else None
+        ws = self.workspace(B, S)
+        _check(lib().tfm_model_prefill(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                       _dev(ids), _dev(positions), _dev(out),
+                                       dt_code(out) if out is not None else BF16, V, B, S,
+                                       _dev(self.cos_sin), _dev(cache), cache_seq, _dev(ws),
+                                       ws.numel(), _stream(stream)), "tfm_model_prefill")
+        return out
+
+    def decode_workspace(self, B: int, cache_seq: int):
+        torch = _torch()
+        key = ("decode", B, cache_seq)
+        if getattr(self, "_dws_key", None) != key:
+            n = lib().tfm_decode_workspace_bytes(ctypes.byref(self.ccfg), B, cache_seq)
+            if n == 0:
+                raise TfmError(-6, "tfm_decode_workspace_bytes")
+            self._dws = torch.empty(n, dtype=torch.uint8, device=self.device)
+            self._dws_key = key
+        return self._dws
+
+    def decode(self, cache, cache_seq: int, ids, positions, logits=None, logits_dtype=None,
+               stream=None):
+        """One decode step: ids (B,) int32 at positions (B,) int32 -> logits (B, V)."""
+        torch = _torch()
+        B = ids.shape[0]
+        V = self.cfg.vocab
+        if logits is None:
+            logits = torch.empty((B, V), dtype=logits_dtype or self.dtype, device=self.device)
+        ws = self.decode_workspace(B, cache_seq)
+        _check(lib().tfm_model_decode(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                      _dev(ids), _dev(positions), _dev(logits), dt_code(logits),
+                                      logits.shape[-1], B, _dev(self.cos_sin), _dev(cache),
+                                      cache_seq, _dev(ws), ws.numel(), _stream(stream)),
+               "tfm_model_decode")
+        return logits
+
+    def check_decode_flags(self, stream=None) -> None:
+        _check(lib().tfm_check_device_flags(_dev(self._dws), _stream(stream)),
+               "tfm_check_device_flags")
+
+
+def tfm_decode_attention(q, k_cache, v_cache, positions, n_heads: int, n_kv_heads: int,
+                         d_head: int, window: int = 0, o=None, stream=None):
+    """q (B, Hq*dh) bf16; caches (B, Hkv, cache_seq, dh) bf16; positions (B,) int32."""
+    torch = _torch()
+    B, cache_seq = q.shape[0], k_cache.shape[2]
+    if o is None:
+        o = torch.empty((B, n_heads * d_head), dtype=q.dtype, device=q.device)
+    n = lib().tfm_decode_attention_workspace_bytes(B, n_heads, d_head, cache_seq)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().tfm_decode_attention(_dev(q), q.stride(0), _dev(k_cache), _dev(v_cache),
+                                      _dev(positions), _dev(o), o.stride(0), B, n_heads,
+                                      n_kv_heads, d_head, cache_seq, window, _dev(ws), ws.numel(),
+                                      _stream(stream)), "tfm_decode_attention")
+    return o
 
 
 def tfm_block_forward(dm: DeviceModel, layer: int, x, positions=None, stream=None):

@@ -44,7 +44,9 @@ typedef enum {
   TFM_ERR_ALIGN = -5,       /* pointer or stride not aligned as required */
   TFM_ERR_UNSUPPORTED = -6, /* valid request this build does not implement (e.g. d_head) */
   TFM_ERR_HIP = -7,         /* a HIP launch or copy failed */
-  TFM_ERR_TOKEN = -8        /* a token id was outside [0, vocab) (device-side check) */
+  TFM_ERR_TOKEN = -8,       /* a token id was outside [0, vocab) (device-side check) */
+  TFM_ERR_POSITION = -9     /* a decode / prefill position was outside the KV cache or the
+                               RoPE table (device-side check) */
 } tfm_status;
 
 /* Model hyper-parameters. n_heads * d_head need not equal d_model; n_heads % n_kv_heads
@@ -207,8 +209,55 @@ int tfm_model_loss(const tfm_config *cfg, const tfm_model_weights *w, const int3
                    const int32_t *positions, const int32_t *targets, float *loss, float *mean,
                    int B, int S, const float *cos_sin, void *ws, size_t ws_bytes, void *stream);
 
-/* Waits for `stream`, then returns TFM_ERR_TOKEN if the last tfm_model_forward (or
- * tfm_model_loss) that used this workspace saw an out-of-range token id, else TFM_OK. */
+/* ---- KV-cache incremental decoding  [T4 6.1 KV cache: keep every step's keys and values,
+ * compute only the new token's q, k, v, append, then attend; T2 GQA/MQA: generation reads the
+ * cache every step, which grouped heads shrink; T2 RoPE: with a cache, positions are the
+ * tokens' real places in the context]. bf16 models with d_head in {32, 64, 128} and at most 8
+ * query heads per kv head (TFM_ERR_UNSUPPORTED otherwise).
+ *
+ * Cache: a caller-owned device buffer of tfm_kv_cache_bytes(cfg, B, cache_seq) bytes, 16-byte
+ * aligned: per layer l a K block at element 2 l blk and a V block at (2 l + 1) blk,
+ * blk = B * n_kv_heads * cache_seq * d_head, each laid out (B, n_kv_heads, cache_seq, d_head)
+ * bf16. Slot t of sequence b holds the rotated key / the value of its token at position t. */
+size_t tfm_kv_cache_bytes(const tfm_config *cfg, int B, int cache_seq);
+
+/* Prefill: tfm_model_forward over (B, S) tokens that also stores every layer's rotated k and
+ * v in the cache slots of the tokens' positions (positions[b, s], default s). logits may be
+ * NULL (fill the cache only). Workspace as tfm_model_forward. A position outside
+ * [0, cache_seq) stores nothing and makes tfm_check_device_flags return TFM_ERR_POSITION. */
+int tfm_model_prefill(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                      const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                      int B, int S, const float *cos_sin, void *kv_cache, int cache_seq,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Decode step: one new token ids[b] per sequence at position positions[b] ([dev] int32 (B),
+ * required; sequences may sit at different positions). In every layer q and k rotate at that
+ * position, k and v go to cache slot positions[b], and the token attends to slots
+ * 0 .. positions[b] (the last attn_window of them on windowed layers). logits: [dev]
+ * (B, ld_logits) of logits_dt. A position outside [0, min(cache_seq, max_seq_len)) gives a
+ * NaN row, writes no slot and makes tfm_check_device_flags return TFM_ERR_POSITION.
+ * ws: at least tfm_decode_workspace_bytes(cfg, B, cache_seq) bytes. */
+size_t tfm_decode_workspace_bytes(const tfm_config *cfg, int B, int cache_seq);
+int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                     const int32_t *positions, void *logits, int logits_dt, int64_t ld_logits,
+                     int B, const float *cos_sin, void *kv_cache, int cache_seq, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Decode attention alone: o[b, h, :] = softmax over the cache slots t of sequence b,
+ * 0 .. positions[b] (the last `window` of them when window > 0), of q[b, h] . k[b, g, t] /
+ * sqrt(d_head), applied to v[b, g, t], with g = h / (Hq / Hkv). q: [dev] (B, q_stride) bf16;
+ * k_cache, v_cache: [dev] (B, Hkv, cache_seq, d_head) bf16; o: [dev] (B, o_stride) bf16;
+ * positions: [dev] int32 (B); a position outside [0, cache_seq) gives a NaN row. Strides
+ * % 8 == 0. ws: tfm_decode_attention_workspace_bytes(B, Hq, d_head, cache_seq) bytes. */
+size_t tfm_decode_attention_workspace_bytes(int B, int Hq, int d_head, int cache_seq);
+int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
+                         const void *v_cache, const int32_t *positions, void *o,
+                         int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
+                         int window, void *ws, size_t ws_bytes, void *stream);
+
+/* Waits for `stream`, then returns TFM_ERR_TOKEN if the last whole-model call that used this
+ * workspace saw an out-of-range token id, TFM_ERR_POSITION if it saw a position outside the
+ * KV cache or the RoPE table (prefill / decode), else TFM_OK. */
 int tfm_check_device_flags(const void *ws, void *stream);
 
 #ifdef __cplusplus

@@ -260,3 +260,58 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
     for f in os.listdir(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd",
                                                  "csrc", f)).read()
+
+
+def test_kv_cache_and_decode_validation(L):
+    """Every call fails validation (or is empty) before any launch."""
+    c = _cfg()   # d512 bf16: 4 layers, 16/16 heads of 32
+    assert L.tfm_kv_cache_bytes(ctypes.byref(c), 2, 100) == 2 * 4 * 2 * 16 * 100 * 32 * 2
+    assert L.tfm_kv_cache_bytes(ctypes.byref(c), -1, 100) == 0
+    layers = (tfm.LayerWeights * 4)(*[_layer() for _ in range(4)])
+    mw = tfm.ModelWeights(P, layers, P, P)
+    need = L.tfm_decode_workspace_bytes(ctypes.byref(c), 2, 100)
+    assert need > 0
+    assert L.tfm_decode_workspace_bytes(ctypes.byref(_cfg(dtype=0)), 2, 100) == 0
+    dec = lambda cfg=c, w=mw, pos=P, lg=P, ld=c.vocab, B=2, cache=P, cs=100, nb=need, dtl=1: \
+        L.tfm_model_decode(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None, P, pos,
+                           lg, dtl, ld, B, P, cache, cs, P, nb, None)
+    assert dec(cfg=_cfg(dtype=0)) == UNSUP
+    assert dec(cfg=_cfg(n_kv_heads=1)) == UNSUP          # 16 query heads per kv head
+    assert dec(cs=0) == SHAPE
+    assert dec(ld=c.vocab - 1) == SHAPE
+    assert dec(dtl=5) == DTYPE
+    assert dec(B=0) == OK
+    assert dec(pos=None) == NULL
+    assert dec(cache=None) == NULL
+    assert dec(lg=None) == NULL
+    assert dec(w=None) == NULL
+    assert dec(cache=PM) == ALIGN
+    assert dec(nb=need - 1) == WS
+    pre_ws = L.tfm_workspace_bytes(ctypes.byref(c), 2, 16)
+    pre = lambda cfg=c, cache=P, cs=100, lg=P, nb=pre_ws, B=2: L.tfm_model_prefill(
+        ctypes.byref(cfg), ctypes.byref(mw), P, None, lg, 1, cfg.vocab, B, 16, P, cache, cs, P,
+        nb, None)
+    assert pre(cfg=_cfg(dtype=0)) == UNSUP
+    assert pre(cs=0) == SHAPE
+    assert pre(B=0) == OK
+    assert pre(cache=None) == NULL
+    assert pre(nb=pre_ws - 1) == WS
+    assert pre(lg=PM) == ALIGN
+
+
+def test_decode_attention_validation(L):
+    f = L.tfm_decode_attention
+    need = L.tfm_decode_attention_workspace_bytes(2, 8, 64, 300)
+    assert need == -(-2 * 8 * 2 * 66 * 4 // 256) * 256          # 2 chunks of 256 keys
+    call = lambda q=P, qs=512, o=P, os=512, B=2, Hq=8, Hkv=2, dh=64, cs=300, W=0, ws=P, nb=need: f(
+        q, qs, P, P, P, o, os, B, Hq, Hkv, dh, cs, W, ws, nb, None)
+    assert call(Hkv=3) == SHAPE
+    assert call(cs=0) == SHAPE
+    assert call(W=-1) == SHAPE
+    assert call(qs=256) == SHAPE
+    assert call(dh=48, qs=384, os=384) == UNSUP
+    assert call(Hq=16, Hkv=1, qs=1024, os=1024) == UNSUP      # at most 8 query heads per kv head
+    assert call(B=0) == OK
+    assert call(q=None) == NULL
+    assert call(o=PM) == ALIGN
+    assert call(nb=need - 1) == WS

@@ -1,0 +1,195 @@
+"""GPU parity of KV-cache decoding ("LLMs-from-scratch" 6.1 KV cache) against the fp64 oracle.
+
+* tfm_decode_attention against oracle.decode_attention, element by element.
+* Prefill + decode steps of whole models against the oracle's full forward: the logits of a
+  token decoded at position p must equal row p of the forward over the prefix ids[:p+1]
+  (the keys and values of positions <= p depend only on those tokens).
+
+Tolerances: decode attention keeps scores, softmax and the weighted sum in fp32 and rounds the
+output once to bf16: |err| <= 2^-9 |o| + (fp32 error, far below 1e-5 max|v|); tested at
+2^-8 |o| + 1e-5 max|v|. Whole models: the bf16 logits bar max|d| / max|ref| <= 2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from decoder_only_transformer_rmsnorm_amd import synth
+from helpers import BF16_ULP, assert_within, max_rel, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+BF16_REL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decoder_only_transformer_rmsnorm_amd import tfm
+    tfm.lib()
+    yield
+
+
+def tfm_mod():
+    from decoder_only_transformer_rmsnorm_amd import tfm
+    return tfm
+
+
+def head_major(c, Hkv, dh):
+    """(B, T, Hkv*dh) token-major cache -> (B, Hkv, T, dh) as the library stores it."""
+    B, T, _ = c.shape
+    return np.ascontiguousarray(c.reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3))
+
+
+# ---------------------------------------------------------------- decode attention
+@pytest.mark.parametrize("B,Hq,Hkv,dh,T,W", [(3, 4, 4, 64, 300, 0), (2, 8, 2, 32, 257, 0),
+                                            (2, 16, 2, 128, 600, 0), (4, 4, 1, 64, 520, 100),
+                                            (1, 12, 12, 64, 1024, 0), (3, 8, 8, 32, 64, 7)])
+def test_decode_attention_matches_oracle(B, Hq, Hkv, dh, T, W):
+    tfm = tfm_mod()
+    say(f"decode attention B={B} Hq={Hq} Hkv={Hkv} dh={dh} cache={T} window={W}")
+    g = np.random.Generator(np.random.PCG64(B * T + dh))
+    q = synth.round_to_bf16(g.normal(size=(B, Hq * dh)).astype(np.float32))
+    k = synth.round_to_bf16(g.normal(size=(B, T, Hkv * dh)).astype(np.float32))
+    v = synth.round_to_bf16(g.normal(size=(B, T, Hkv * dh)).astype(np.float32))
+    pos = np.array([T - 1, 0, 255, 256, 100, 511][:B]) % T
+    pos = pos.astype(np.int32)
+    kc = to_dev(head_major(k, Hkv, dh), "bf16")
+    vc = to_dev(head_major(v, Hkv, dh), "bf16")
+    o = tfm.tfm_decode_attention(to_dev(q, "bf16"), kc, vc, torch.from_numpy(pos).cuda(), Hq, Hkv,
+                                 dh, window=W)
+    torch.cuda.synchronize()
+    got = to_np(o)
+    ref = oracle.decode_attention(q, k, v, Hq, Hkv, pos + 1, window=W)
+    tol = 2 * BF16_ULP * np.abs(ref) + 1e-5 * float(np.abs(v).max())
+    assert_within(got, ref, tol, "decode attention")
+
+
+def test_decode_attention_bad_position_gives_nan_row_only():
+    tfm = tfm_mod()
+    B, H, dh, T = 3, 4, 64, 40
+    g = np.random.Generator(np.random.PCG64(3))
+    q = synth.round_to_bf16(g.normal(size=(B, H * dh)).astype(np.float32))
+    k = synth.round_to_bf16(g.normal(size=(B, T, H * dh)).astype(np.float32))
+    pos = np.array([5, T, -1], np.int32)
+    kc = to_dev(head_major(k, H, dh), "bf16")
+    o = to_np(tfm.tfm_decode_attention(to_dev(q, "bf16"), kc, kc, torch.from_numpy(pos).cuda(),
+                                       H, H, dh))
+    assert np.isfinite(o[0]).all() and np.isnan(o[1]).all() and np.isnan(o[2]).all()
+
+
+# ---------------------------------------------------------------- prefill + decode
+def small(**kw):
+    base = dict(name="dec", dtype="bf16", n_layers=2, d_model=256, n_heads=8, n_kv_heads=2,
+                d_head=32, d_ff=704, vocab=1000, batch=3, seq=64)
+    base.update(kw)
+    return synth.ModelConfig(**base)
+
+
+def _decode_case(cfg, S0, steps, cache_seq, seqs=None, oracle_prefix=None):
+    """Prefill S0 tokens of every sequence, then decode `steps` tokens one at a time with the
+    inputs' own ids (teacher forcing); compare each step's logits with the oracle."""
+    tfm = tfm_mod()
+    inp = synth.make_inputs(cfg, seed=0)
+    dm = tfm.DeviceModel(inp, max_seq=max(cache_seq, cfg.seq))
+    B = cfg.batch
+    cache = dm.kv_cache(B, cache_seq)
+    ids = dm.ids
+    dm.prefill(cache, cache_seq, ids=ids[:, :S0].contiguous(), logits=False)
+    dm.check_flags()
+    outs = []
+    for i in range(steps):
+        p = S0 + i
+        pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+        lg = dm.decode(cache, cache_seq, ids[:, p].contiguous(), pos)
+        outs.append(to_np(lg))
+    dm.check_decode_flags()
+    seqs = range(B) if seqs is None else seqs
+    worst = 0.0
+    for b in seqs:
+        n = S0 + steps
+        ref = oracle.model(cfg, inp, ids=inp.ids[b:b + 1, :n], rows=np.arange(S0, n))
+        got = np.stack([outs[i][b] for i in range(steps)])
+        rel = max_rel(got, ref)
+        worst = max(worst, rel)
+        say(f"  seq {b}: decode steps {S0}..{n - 1} max rel err {rel:.3e}")
+        assert np.isfinite(got).all()
+        assert rel <= BF16_REL
+    return dm, cache, worst
+
+
+@pytest.mark.parametrize("kv", [2, 8])
+def test_prefill_then_decode_matches_full_forward(kv):
+    say(f"prefill + decode, kv heads {kv}")
+    _decode_case(small(n_kv_heads=kv), S0=37, steps=5, cache_seq=64)
+
+
+def test_decode_hybrid_window_model():
+    """Windowed layers (8 keys) and a full-attention layer every second layer, decoded past
+    the window."""
+    cfg = small(n_layers=4, window=8, full_every=2, n_kv_heads=4)
+    say("decode hybrid window model")
+    _decode_case(cfg, S0=20, steps=4, cache_seq=64)
+
+
+def test_decode_ragged_positions_and_first_token():
+    """Sequences at different positions in one step, including position 0 (the token sees
+    only itself) and a slot rewritten after prefill."""
+    tfm = tfm_mod()
+    cfg = small()
+    inp = synth.make_inputs(cfg, seed=1)
+    dm = tfm.DeviceModel(inp)
+    cache_seq = 64
+    cache = dm.kv_cache(cfg.batch, cache_seq)
+    dm.prefill(cache, cache_seq, ids=dm.ids[:, :12].contiguous(), logits=False)
+    pos_np = np.array([5, 12, 0], np.int32)
+    ids_np = inp.ids[np.arange(3), pos_np].astype(np.int32)
+    lg = to_np(dm.decode(cache, cache_seq, torch.from_numpy(ids_np).cuda(),
+                         torch.from_numpy(pos_np).cuda()))
+    dm.check_decode_flags()
+    for b in range(3):
+        p = int(pos_np[b])
+        ref = oracle.model(cfg, inp, ids=inp.ids[b:b + 1, :p + 1], rows=np.array([p]))
+        rel = max_rel(lg[b:b + 1], ref)
+        say(f"  seq {b} at position {p}: max rel err {rel:.3e}")
+        assert rel <= BF16_REL
+
+
+def test_decode_bad_position_flag_and_determinism():
+    tfm = tfm_mod()
+    cfg = small()
+    inp = synth.make_inputs(cfg, seed=2)
+    dm = tfm.DeviceModel(inp)
+    cache_seq = 32
+    cache = dm.kv_cache(cfg.batch, cache_seq)
+    dm.prefill(cache, cache_seq, ids=dm.ids[:, :10].contiguous(), logits=False)
+    ids = dm.ids[:, 10].contiguous()
+    pos = torch.full((3,), 10, dtype=torch.int32, device="cuda")
+    snapshot = cache.clone()
+    a = dm.decode(cache, cache_seq, ids, pos).clone()
+    cache.copy_(snapshot)
+    b = dm.decode(cache, cache_seq, ids, pos)
+    assert torch.equal(a, b)
+    dm.check_decode_flags()
+    bad = torch.tensor([10, cache_seq, 10], dtype=torch.int32, device="cuda")
+    lg = to_np(dm.decode(cache, cache_seq, ids, bad))
+    with pytest.raises(tfm.TfmError) as e:
+        dm.check_decode_flags()
+    assert e.value.status == -9
+    assert np.isnan(lg[1]).all() and np.isfinite(lg[0]).all() and np.isfinite(lg[2]).all()
+
+
+def test_decode_d768_workload_sampled():
+    """The d768 / 12-layer workload at batch 8 with a 1024-slot cache: prefill 1000 tokens,
+    decode 3; the oracle recomputes sequence 6's 1003-token forward."""
+    say("decode d768 workload")
+    _decode_case(synth.GPT2S_BF16, S0=1000, steps=3, cache_seq=1024, seqs=[6])
+
+
+def test_decode_long_gqa_workload_sampled():
+    """The grouped-query d_head-128 workload with its 8192-slot cache; prefill 380 tokens and
+    decode 4 (the oracle recomputes the 384-token prefix)."""
+    say("decode long GQA workload")
+    _decode_case(synth.LONG_GQA_BF16, S0=380, steps=4, cache_seq=8192)
