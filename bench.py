@@ -214,6 +214,7 @@ def main() -> int:
     roofline = None
     loss_forward = None
     mfma_util = None
+    decode = None
     if not args.no_kernels:
         D, F, V = cfg.d_model, cfg.d_ff, cfg.vocab
         qd = cfg.n_heads * cfg.d_head
@@ -287,6 +288,30 @@ def main() -> int:
                         "mean_loss": round(float(xmean.item()), 4)}
         log(f"forward with fused loss: {loss_ms:.3f} ms/step, {M / (loss_ms / 1e3) / 1e6:.3f} M tokens/s")
 
+        # KV-cache decode: prefill all but the last 24 positions, then time one-token steps at
+        # that context (each step rewrites the same slot, so every step does identical work)
+        cache_seq = S
+        p0 = S - 24
+        cache = dm.kv_cache(B, cache_seq)
+        dm.prefill(cache, cache_seq, ids=dm.ids[:, :p0].contiguous(), logits=False)
+        dec_logits = torch.empty((B, V), dtype=bf, device="cuda")
+        dec_pos = torch.full((B,), p0, dtype=torch.int32, device="cuda")
+        dec_tok = dm.ids[:, p0].contiguous()
+        step_fn = lambda: dm.decode(cache, cache_seq, dec_tok, dec_pos, logits=dec_logits)
+        eager_ms = time_launches(step_fn, 20, stream, graph=False)
+        graph_ms = time_launches(step_fn, 20, stream, graph=True)
+        dm.check_decode_flags()
+        dbytes = accounting.decode_bytes(cfg, B, p0 + 1)
+        decode = {"batch": B, "context": p0 + 1, "cache_seq": cache_seq,
+                  "ms_per_step_graph": round(graph_ms, 4), "ms_per_step_eager": round(eager_ms, 4),
+                  "tokens_per_s": round(B / (graph_ms / 1e3), 1),
+                  "hbm_bytes_per_step": int(dbytes["total"]),
+                  "GB/s": round(dbytes["total"] / (graph_ms / 1e3) / 1e9, 1),
+                  "frac_hbm": round(dbytes["total"] / (graph_ms / 1e3) / PEAK_HBM, 4)}
+        log(f"decode B={B} context {p0 + 1}: {graph_ms * 1e3:.1f} us/step in a graph "
+            f"({eager_ms * 1e3:.1f} eager), {decode['GB/s']} GB/s algorithmic")
+        del cache
+
         # MFMA utilisation of the GEMM and attention kernels over one step
         L_ = cfg.n_layers
         gemm_f = L_ * (flops_gemm(3 * qd, D) + flops_gemm(D, qd) + flops_gemm(2 * F, D)
@@ -318,6 +343,7 @@ def main() -> int:
         "mfma_util": mfma_util,
         "kernels": kernels,
         "loss_forward": loss_forward,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

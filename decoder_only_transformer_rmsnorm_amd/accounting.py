@@ -42,3 +42,18 @@ def rmsnorm_bytes(rows: int, d: int, in_bytes: int = 4, out_bytes: int = 2) -> i
 def model_rmsnorm_bytes(cfg) -> int:
     w = 4 if cfg.dtype == "f32" else 2
     return (2 * cfg.n_layers + 1) * rmsnorm_bytes(cfg.tokens, cfg.d_model, 4, w)
+
+
+def decode_bytes(cfg, batch: int, context: int, elt: int = 2) -> dict:
+    """Algorithmic HBM bytes of one KV-cache decode step (one new token per sequence, each
+    attending to `context` cached positions including its own): every weight matrix read
+    once (the LM head included; B embedding rows), every layer's K and V cache read over the
+    context and one slot of each written. Activations (B rows) are negligible and omitted."""
+    D, F, V, L = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_layers
+    qd, kvd = cfg.n_heads * cfg.d_head, cfg.n_kv_heads * cfg.d_head
+    weights = (L * ((qd + 2 * kvd) * D + qd * D + 3 * F * D + 2 * D) + V * D + D) * elt
+    embed = batch * D * elt
+    cache_read = L * 2 * batch * kvd * context * elt
+    cache_write = L * 2 * batch * kvd * elt
+    total = weights + embed + cache_read + cache_write
+    return {"weights": weights, "kv_cache_read": cache_read, "total": total}

@@ -546,7 +546,8 @@ int tfm_model_prefill(const tfm_config *cfg, const tfm_model_weights *w, const i
 }
 
 size_t tfm_decode_workspace_bytes(const tfm_config *cfg, int B, int cache_seq) {
-  if (check_config(cfg, B, 1) != TFM_OK || check_decode_config(cfg) != TFM_OK || cache_seq <= 0)
+  if (check_config(cfg, B, 1) != TFM_OK || check_decode_config(cfg) != TFM_OK || cache_seq <= 0 ||
+      cache_seq > decode_max_cache())
     return 0;
   return plan_decode(cfg, B, cache_seq).total;
 }
@@ -558,6 +559,7 @@ int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const in
   TFM_TRY(check_config(cfg, B, 1));
   TFM_TRY(check_decode_config(cfg));
   if (cache_seq <= 0) return TFM_ERR_SHAPE;
+  if (cache_seq > decode_max_cache()) return TFM_ERR_UNSUPPORTED;
   if (!valid_dt(logits_dt)) return TFM_ERR_DTYPE;
   if (!w) return TFM_ERR_NULL;
   if (ld_logits < cfg->vocab) return TFM_ERR_SHAPE;
@@ -580,9 +582,8 @@ int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const in
   for (int l = 0; l < cfg->n_layers; ++l) {
     const tfm_layer_weights *lw = &w->layers[l];
     const LayerCache lc = layer_cache(cfg, kv_cache, B, cache_seq, l);
-    TFM_HIP(launch_rmsnorm(x, DT_F32, lw->g_attn, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
-    DecodeGemmArgs g{};
-    g.x = xn; g.ldx = D; g.w0 = lw->wq; g.w1 = lw->wk; g.w2 = lw->wv; g.n0 = qd; g.n1 = kvd;
+    DecodeGemmArgs g{};   // RMSNorm(x; g_attn) fused into the projection
+    g.norm_x = x; g.norm_g = lw->g_attn; g.eps = cfg->eps; g.ldx = D; g.w0 = lw->wq; g.w1 = lw->wk; g.w2 = lw->wv; g.n0 = qd; g.n1 = kvd;
     g.M = B; g.N = qd + 2 * kvd; g.K = D; g.y = q; g.ldy = qd; g.y_dt = DT_BF16;
     g.positions = positions; g.cos_sin = cos_sin; g.d_head = cfg->d_head;
     g.max_seq = cfg->max_seq_len; g.k_cache = lc.k; g.v_cache = lc.v; g.cache_seq = cache_seq;
@@ -595,9 +596,8 @@ int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const in
     g.x = o; g.ldx = qd; g.w0 = lw->wo; g.M = B; g.N = D; g.K = qd; g.y = x; g.ldy = D;
     g.y_dt = DT_F32;
     TFM_HIP(launch_decode_gemm(EPI_RESIDUAL, g, s));
-    TFM_HIP(launch_rmsnorm(x, DT_F32, lw->g_ffn, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
-    g = DecodeGemmArgs{};
-    g.x = xn; g.ldx = D; g.w0 = lw->w1; g.w1 = lw->w3; g.n0 = F; g.M = B; g.N = F; g.K = D;
+    g = DecodeGemmArgs{};   // RMSNorm(x; g_ffn) fused into the up projection
+    g.norm_x = x; g.norm_g = lw->g_ffn; g.eps = cfg->eps; g.ldx = D; g.w0 = lw->w1; g.w1 = lw->w3; g.n0 = F; g.M = B; g.N = F; g.K = D;
     g.y = u; g.ldy = F; g.y_dt = DT_BF16;
     TFM_HIP(launch_decode_gemm(EPI_SWIGLU, g, s));
     g = DecodeGemmArgs{};
@@ -605,9 +605,8 @@ int tfm_model_decode(const tfm_config *cfg, const tfm_model_weights *w, const in
     g.y_dt = DT_F32;
     TFM_HIP(launch_decode_gemm(EPI_RESIDUAL, g, s));
   }
-  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, DT_BF16, xn, DT_BF16, B, D, cfg->eps, s));
-  DecodeGemmArgs g{};
-  g.x = xn; g.ldx = D; g.w0 = w->lm_head; g.M = B; g.N = V; g.K = D; g.y = logits;
+  DecodeGemmArgs g{};   // RMSNorm(x; g_final) fused into the LM head
+  g.norm_x = x; g.norm_g = w->g_final; g.eps = cfg->eps; g.ldx = D; g.w0 = w->lm_head; g.M = B; g.N = V; g.K = D; g.y = logits;
   g.ldy = ld_logits; g.y_dt = logits_dt;
   TFM_HIP(launch_decode_gemm(EPI_STORE, g, s));
   return TFM_OK;
@@ -625,7 +624,8 @@ int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || cache_seq <= 0 || window < 0)
     return TFM_ERR_SHAPE;
   if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head) return TFM_ERR_SHAPE;
-  if ((d_head != 32 && d_head != 64 && d_head != 128) || !decode_group_supported(Hq, Hkv))
+  if ((d_head != 32 && d_head != 64 && d_head != 128) || !decode_group_supported(Hq, Hkv) ||
+      cache_seq > decode_max_cache())
     return TFM_ERR_UNSUPPORTED;
   if (B == 0) return TFM_OK;
   if (!q || !k_cache || !v_cache || !positions || !o || !ws) return TFM_ERR_NULL;

@@ -16,10 +16,10 @@
 //    4 consecutive output columns of one row m = l % 16. The 4 partial sums meet in LDS.
 //    Epilogues: store (logits), residual add, SiLU(gate) * up, and q / k / v with RoPE where
 //    k and v go straight to the cache slot of the token's position.
-//  * dec_attn_kernel: one workgroup per (sequence, kv head, chunk of 256 cached keys); all
+//  * dec_attn_kernel: one workgroup per (sequence, kv head, chunk of 128 cached keys); all
 //    query heads of the group share each K / V row read (grouped-query attention). Scores and
 //    softmax in fp32 (log2 domain); the partial (max, sum, unnormalised output) of each chunk
-//    goes to the workspace and dec_combine_kernel merges the chunks in a fixed order.
+//    goes to the workspace and dec_combine_kernel merges the chunks in chunk order.
 //  * kv_store_kernel: after a prefill block's QKV projection, copies the rotated k and v rows
 //    into the cache slots of their positions.
 #include <cmath>
@@ -30,8 +30,9 @@
 namespace tfm {
 namespace {
 
-constexpr int kDecKeys = 256;   // cached keys per attention workgroup
+constexpr int kDecKeys = 128;   // cached keys (and threads) per attention workgroup
 constexpr int kDecMaxGroup = 8; // query heads per kv head supported by the decode kernel
+constexpr int kMaxChunks = 1024; // chunks per sequence the merge holds (cache_seq <= 131072)
 constexpr float kLog2e = 1.4426950408889634f;
 
 inline unsigned grid1(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -79,6 +80,36 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
   const int mr = m0 + r16;
   const bool xok = mr < g.M;
   const bf16_t *xrow = (const bf16_t *)g.x + (int64_t)(xok ? mr : 0) * g.ldx;
+  // fused RMSNorm ("Transformer 篇" 5.6): 1 / rms of each of the 16 rows, wave w takes rows
+  // 4w .. 4w+3; the operand is then x * inv * g, rounded once to bf16
+  __shared__ float inv_rms[16];
+  const bool fuse = g.norm_x != nullptr;
+  const float *nrow = fuse ? g.norm_x + (int64_t)(xok ? mr : 0) * g.ldx : nullptr;
+  if (fuse) {   // 16 threads per row, each summing every 16th group of 4 columns
+    const int row = threadIdx.x >> 4, part = threadIdx.x & 15;
+    const int m = m0 + row;
+    float ss = 0.f;
+    if (m < g.M) {
+      const float *xr = g.norm_x + (int64_t)m * g.ldx;
+#pragma unroll 4
+      for (int k = 4 * part; k < g.K; k += 64) {
+        const f32x4_t v = load4(xr + k);
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+      }
+    }
+    for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (part == 0) inv_rms[row] = rsqrtf(ss / (float)g.K + g.eps);
+    __syncthreads();
+  }
+  const float rinv = fuse ? inv_rms[r16] : 0.f;
+  auto x_chunk = [&](int k) -> u32x4_t {   // 8 activations of row mr from column k
+    if (!fuse) return ld16(xrow + k);
+    const f32x4_t a = load4(nrow + k), b = load4(nrow + k + 4);
+    const f32x4_t ga = load4((const bf16_t *)g.norm_g + k), gb = load4((const bf16_t *)g.norm_g + k + 4);
+    const f32x4_t ya = a * rinv * ga, yb = b * rinv * gb;
+    return u32x4_t{pack_bf16x2(ya[0], ya[1]), pack_bf16x2(ya[2], ya[3]),
+                   pack_bf16x2(yb[0], yb[1]), pack_bf16x2(yb[2], yb[3])};
+  };
 
   f32x4_t acc[NA];
 #pragma unroll
@@ -92,7 +123,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
     for (int u = 0; u < U; ++u) {
       const int k = (ks0 + 4 * u) * 32 + kc * 8;   // K % 8 == 0: a chunk is all in or out
       const bool kok = ks0 + 4 * u < nks && k < g.K;
-      xa[u] = xok && kok ? ld16(xrow + k) : zero;
+      xa[u] = xok && kok ? x_chunk(k) : zero;
 #pragma unroll
       for (int a = 0; a < NA; ++a) wa[u][a] = wok[a] && kok ? ld16(wrow[a] + k) : zero;
     }
@@ -171,71 +202,85 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
 }
 
 // ---- decode attention
+// One workgroup per (sequence b, kv head grp, chunk c of 128 cached keys). Every thread first
+// loads its key's K and V rows (all loads in flight together); V goes to LDS for the P.V pass.
+// The chunk's partial (max, sum, unnormalised output) per query head goes to `part`;
+// dec_combine_kernel merges the chunks in chunk order.
 template <int DH>
-__global__ __launch_bounds__(256) void dec_attn_kernel(const bf16_t *__restrict__ q,
-                                                       int64_t q_stride,
-                                                       const bf16_t *__restrict__ kc,
-                                                       const bf16_t *__restrict__ vc,
-                                                       const int32_t *__restrict__ positions,
-                                                       int Hq, int Hkv, int cache_seq, int window,
-                                                       float scale_log2, float *__restrict__ part,
-                                                       int n_ch) {
+__global__ __launch_bounds__(kDecKeys) void dec_attn_kernel(
+    const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ kc,
+    const bf16_t *__restrict__ vc, const int32_t *__restrict__ positions, int Hq, int Hkv,
+    int cache_seq, int window, float scale_log2, float *__restrict__ part, int n_ch,
+    bf16_t *__restrict__ o, int64_t o_stride) {
   constexpr int PS = 2 + DH;               // partial record: max, sum, output
+  constexpr int DC = DH / 8;               // 16-byte chunks per K / V row
   constexpr int D4 = DH / 4;               // threads per value row in the P.V pass
-  constexpr int TG = 256 / D4;             // key groups in the P.V pass
+  constexpr int TG = kDecKeys / D4;        // key groups in the P.V pass
+  constexpr int NW = kDecKeys / 64;        // waves (one thread per key of the chunk)
   const int c = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int pos = positions[b];
   const bool valid = pos >= 0 && pos < cache_seq;
-  const int n = pos + 1;
-  const int t0 = window > 0 && n > window ? n - window : 0;
-  const int ks = t0 + c * kDecKeys;
-  const int cnt = valid ? min(kDecKeys, n - ks) : 0;   // keys of this chunk (may be <= 0)
-
-  float *rec0 = part + (((int64_t)b * Hq + grp * G) * n_ch + c) * PS;   // head h: + h n_ch PS
-  if (cnt <= 0) {   // nothing visible here: an empty partial (the merge skips it)
-    for (int i = tid; i < G * PS; i += 256) {
-      const int h = i / PS, e = i % PS;
-      rec0[(int64_t)h * n_ch * PS + e] = e == 0 ? -__builtin_inff() : 0.f;
-    }
+  if (!valid) {   // no cache slot: NaN output for the group's heads
+    if (c == 0)
+      for (int i = tid; i < G * DH; i += kDecKeys)
+        o[(int64_t)b * o_stride + (int64_t)grp * G * DH + i] = f32_to_bf16(__builtin_nanf(""));
     return;
   }
+  const int n = pos + 1;
+  const int t0 = window > 0 && n > window ? n - window : 0;
+  const int used = (n - t0 + kDecKeys - 1) / kDecKeys;
+  if (c >= used) return;
+  const int ks = t0 + c * kDecKeys;
+  const int cnt = min(kDecKeys, n - ks);
 
   __shared__ float qs[kDecMaxGroup][DH];
   __shared__ float sc[kDecMaxGroup][kDecKeys];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[kDecKeys][DH];
   __shared__ __attribute__((aligned(16))) float red[TG][DH];
   __shared__ float stat[kDecMaxGroup][2];
-  __shared__ float wred[4][kDecMaxGroup];
+  __shared__ float wred[NW][kDecMaxGroup];
 
-  for (int i = tid; i < G * DH; i += 256) {
+  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this head
+  u32x4_t kr[DC], vr[DC];
+  if (tid < cnt) {
+    const bf16_t *kp = kc + (head + ks + tid) * DH;
+    const bf16_t *vp = vc + (head + ks + tid) * DH;
+#pragma unroll
+    for (int j = 0; j < DC; ++j) kr[j] = ld16(kp + 8 * j);
+#pragma unroll
+    for (int j = 0; j < DC; ++j) vr[j] = ld16(vp + 8 * j);
+  }
+  for (int i = tid; i < G * DH; i += kDecKeys) {
     const int h = i / DH, d = i % DH;
     qs[h][d] = bf16_to_f32(q[(int64_t)b * q_stride + (int64_t)(grp * G + h) * DH + d]) *
                scale_log2;
   }
+  if (tid < cnt) {
+#pragma unroll
+    for (int j = 0; j < DC; ++j) *(u32x4_t *)&vs[tid][8 * j] = vr[j];
+  }
   __syncthreads();
 
-  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this head
-  // scores: thread t takes key ks + t
+  // scores (log2 units): thread t takes key ks + t
   if (tid < cnt) {
-    const bf16_t *kr = kc + (head + ks + tid) * DH;
     float s[kDecMaxGroup];
 #pragma unroll
     for (int h = 0; h < kDecMaxGroup; ++h) s[h] = 0.f;
 #pragma unroll
-    for (int d0 = 0; d0 < DH; d0 += 8) {
-      const u32x4_t raw = ld16(kr + d0);
+    for (int j = 0; j < DC; ++j) {
       float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(raw[e] << 16);
-        kf[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+        kf[2 * e] = __uint_as_float(kr[j][e] << 16);
+        kf[2 * e + 1] = __uint_as_float(kr[j][e] & 0xffff0000u);
       }
 #pragma unroll
       for (int h = 0; h < kDecMaxGroup; ++h)
         if (h < G) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(qs[h][d0 + e], kf[e], s[h]);
+          for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(qs[h][8 * j + e], kf[e], s[h]);
         }
     }
 #pragma unroll
@@ -247,56 +292,64 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const bf16_t *__restrict_
   for (int h = 0; h < G; ++h) {
     float mx = -__builtin_inff();
     __syncthreads();
-    for (int t = tid; t < cnt; t += 256) mx = fmaxf(mx, sc[h][t]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int t = tid; t < cnt; t += kDecKeys) mx = fmaxf(mx, sc[h][t]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if (lane == 0) wred[wv][h] = mx;
     __syncthreads();
-    mx = fmaxf(fmaxf(wred[0][h], wred[1][h]), fmaxf(wred[2][h], wred[3][h]));
+    mx = wred[0][h];
+    for (int j = 1; j < NW; ++j) mx = fmaxf(mx, wred[j][h]);
     float sum = 0.f;
-    for (int t = tid; t < cnt; t += 256) {
+    for (int t = tid; t < cnt; t += kDecKeys) {
       const float p = exp2f(sc[h][t] - mx);
       sc[h][t] = p;
       sum += p;
     }
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
     __syncthreads();
     if (lane == 0) wred[wv][h] = sum;
     __syncthreads();
     if (tid == 0) {
       stat[h][0] = mx;
-      stat[h][1] = wred[0][h] + wred[1][h] + wred[2][h] + wred[3][h];
+      float tot = 0.f;
+      for (int j = 0; j < NW; ++j) tot += wred[j][h];
+      stat[h][1] = tot;
     }
   }
   __syncthreads();
 
-  // P.V: thread (key group tg, 4 columns d4) sums over keys tg, tg + TG, ...
+  // P.V from LDS: thread (key group tg, 4 columns d4) sums over keys tg, tg + TG, ...
   const int d4 = tid % D4, tg = tid / D4;
   f32x4_t acc[kDecMaxGroup];
 #pragma unroll
   for (int h = 0; h < kDecMaxGroup; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int t = tg; t < cnt; t += TG) {
-    const f32x4_t vv = load4(vc + (head + ks + t) * DH + 4 * d4);
+    const u32x2_t raw = *(const u32x2_t *)&vs[t][4 * d4];
+    const f32x4_t vv = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                        __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
 #pragma unroll
     for (int h = 0; h < kDecMaxGroup; ++h)
       if (h < G) acc[h] += sc[h][t] * vv;
   }
+  float *rec0 = part + (((int64_t)b * Hq + grp * G) * n_ch + c) * PS;   // head h: + h n_ch PS
   for (int h = 0; h < G; ++h) {
     __syncthreads();
     *(f32x4_t *)&red[tg][4 * d4] = acc[h];
     __syncthreads();
-    for (int d = tid; d < DH; d += 256) {
-      float o = 0.f;
-      for (int j = 0; j < TG; ++j) o += red[j][d];
-      rec0[(int64_t)h * n_ch * PS + 2 + d] = o;
+    for (int d = tid; d < DH; d += kDecKeys) {
+      float sum = 0.f;
+      for (int j = 0; j < TG; ++j) sum += red[j][d];
+      rec0[(int64_t)h * n_ch * PS + 2 + d] = sum;
     }
     if (tid == 0) {
       rec0[(int64_t)h * n_ch * PS + 0] = stat[h][0];
       rec0[(int64_t)h * n_ch * PS + 1] = stat[h][1];
     }
   }
+
 }
 
-// Merges the chunk partials of one (sequence, query head) in chunk order.
+// Merges the chunk partials of one (sequence, query head) in chunk order. (A merge by the
+// last chunk workgroup would need device-scope fences, which write back the XCD's L2.)
 template <int DH>
 __global__ __launch_bounds__(128) void dec_combine_kernel(const float *__restrict__ part,
                                                           const int32_t *__restrict__ positions,
@@ -306,26 +359,32 @@ __global__ __launch_bounds__(128) void dec_combine_kernel(const float *__restric
   constexpr int PS = 2 + DH;
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int pos = positions[b];
-  const bool valid = pos >= 0 && pos < cache_seq;
-  bf16_t *out = o + (int64_t)b * o_stride + (int64_t)h * DH;
-  if (!valid) {
-    for (int d = threadIdx.x; d < DH; d += blockDim.x) out[d] = f32_to_bf16(__builtin_nanf(""));
-    return;
-  }
+  if (pos < 0 || pos >= cache_seq) return;   // the attention kernel wrote the NaN row
   const int n = pos + 1;
   const int t0 = window > 0 && n > window ? n - window : 0;
   const int used = (n - t0 + kDecKeys - 1) / kDecKeys;
   const float *rec = part + (int64_t)bh * n_ch * PS;
-  float mx = -__builtin_inff();
-  for (int c = 0; c < used; ++c) mx = fmaxf(mx, rec[c * PS]);
-  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
+  // chunk weights 2^(m_c - max) and the denominator, computed once in LDS
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float den;
+  for (int c = threadIdx.x; c < used; c += blockDim.x) wgt[c] = rec[c * PS];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mx = -__builtin_inff();
+    for (int c = 0; c < used; ++c) mx = fmaxf(mx, wgt[c]);
+    float l = 0.f;
     for (int c = 0; c < used; ++c) {
-      const float f = exp2f(rec[c * PS] - mx);
-      num += f * rec[c * PS + 2 + d];
-      den += f * rec[c * PS + 1];
+      wgt[c] = exp2f(wgt[c] - mx);
+      l += wgt[c] * rec[c * PS + 1];
     }
-    out[d] = f32_to_bf16(num / den);
+    den = l;
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
+    float num = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < used; ++c) num += wgt[c] * rec[c * PS + 2 + d];
+    o[(int64_t)b * o_stride + (int64_t)h * DH + d] = f32_to_bf16(num / den);
   }
 }
 
@@ -355,12 +414,13 @@ __global__ void kv_store_kernel(const bf16_t *__restrict__ qkv, int64_t ld, int 
 template <int DH>
 hipError_t run_dec_attn(const void *q, int64_t q_stride, const void *kc, const void *vc,
                         const int32_t *positions, int B, int Hq, int Hkv, int cache_seq,
-                        int window, float *part, void *o, int64_t o_stride, hipStream_t s) {
+                        int window, float *part, void *o, int64_t o_stride,
+                        hipStream_t s) {
   const int n_ch = decode_chunks(cache_seq);
   const float sl2 = kLog2e / sqrtf((float)DH);
-  dec_attn_kernel<DH><<<dim3(n_ch, Hkv, B), 256, 0, s>>>(
+  dec_attn_kernel<DH><<<dim3(n_ch, Hkv, B), kDecKeys, 0, s>>>(
       (const bf16_t *)q, q_stride, (const bf16_t *)kc, (const bf16_t *)vc, positions, Hq, Hkv,
-      cache_seq, window, sl2, part, n_ch);
+      cache_seq, window, sl2, part, n_ch, (bf16_t *)o, o_stride);
   dec_combine_kernel<DH><<<B * Hq, 128, 0, s>>>(part, positions, Hq, cache_seq, window, n_ch,
                                                 (bf16_t *)o, o_stride);
   return hipGetLastError();
@@ -369,6 +429,7 @@ hipError_t run_dec_attn(const void *q, int64_t q_stride, const void *kc, const v
 }  // namespace
 
 int decode_chunks(int cache_seq) { return (cache_seq + kDecKeys - 1) / kDecKeys; }
+int decode_max_cache() { return kDecKeys * kMaxChunks; }
 bool decode_group_supported(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= kDecMaxGroup; }
 
 hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s) {

@@ -83,10 +83,16 @@ struct DecodeGemmArgs {
   void *k_cache, *v_cache;  // QKV: this layer's (B, Hkv, cache_seq, d_head) blocks
   int cache_seq, n_kv_heads;
   int32_t *pos_flag;        // set to 1 when a position is outside [0, min(cache_seq, max_seq))
+  // Optional fused RMSNorm: when norm_x is set, the activations are RMSNorm(norm_x; norm_g)
+  // (fp32 rows of K elements, row stride ldx; gain bf16), rounded to bf16, and x is unused.
+  const float *norm_x;
+  const void *norm_g;
+  float eps;
 };
 hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s);
 // Partial records per (sequence, query head): decode_chunks(cache_seq), each 2 + d_head floats.
 int decode_chunks(int cache_seq);
+int decode_max_cache();   // largest cache_seq the chunk merge supports
 bool decode_group_supported(int Hq, int Hkv);
 // o[b, h] = attention of q[b, h] over cache slots of sequence b up to positions[b] (the last
 // `window` of them when window > 0); part: B * Hq * decode_chunks * (2 + d_head) floats.

@@ -212,8 +212,9 @@ int tfm_model_loss(const tfm_config *cfg, const tfm_model_weights *w, const int3
 /* ---- KV-cache incremental decoding  [T4 6.1 KV cache: keep every step's keys and values,
  * compute only the new token's q, k, v, append, then attend; T2 GQA/MQA: generation reads the
  * cache every step, which grouped heads shrink; T2 RoPE: with a cache, positions are the
- * tokens' real places in the context]. bf16 models with d_head in {32, 64, 128} and at most 8
- * query heads per kv head (TFM_ERR_UNSUPPORTED otherwise).
+ * tokens' real places in the context]. bf16 models with d_head in {32, 64, 128}, at most 8
+ * query heads per kv head and cache_seq <= 131072 for decoding (TFM_ERR_UNSUPPORTED
+ * otherwise).
  *
  * Cache: a caller-owned device buffer of tfm_kv_cache_bytes(cfg, B, cache_seq) bytes, 16-byte
  * aligned: per layer l a K block at element 2 l blk and a V block at (2 l + 1) blk,

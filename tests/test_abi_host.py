@@ -278,6 +278,7 @@ def test_kv_cache_and_decode_validation(L):
     assert dec(cfg=_cfg(dtype=0)) == UNSUP
     assert dec(cfg=_cfg(n_kv_heads=1)) == UNSUP          # 16 query heads per kv head
     assert dec(cs=0) == SHAPE
+    assert dec(cs=131073) == UNSUP
     assert dec(ld=c.vocab - 1) == SHAPE
     assert dec(dtl=5) == DTYPE
     assert dec(B=0) == OK
@@ -302,11 +303,12 @@ def test_kv_cache_and_decode_validation(L):
 def test_decode_attention_validation(L):
     f = L.tfm_decode_attention
     need = L.tfm_decode_attention_workspace_bytes(2, 8, 64, 300)
-    assert need == -(-2 * 8 * 2 * 66 * 4 // 256) * 256          # 2 chunks of 256 keys
+    assert need == -(-2 * 8 * 3 * 66 * 4 // 256) * 256          # 3 chunks of 128 keys
     call = lambda q=P, qs=512, o=P, os=512, B=2, Hq=8, Hkv=2, dh=64, cs=300, W=0, ws=P, nb=need: f(
         q, qs, P, P, P, o, os, B, Hq, Hkv, dh, cs, W, ws, nb, None)
     assert call(Hkv=3) == SHAPE
     assert call(cs=0) == SHAPE
+    assert call(cs=131073) == UNSUP
     assert call(W=-1) == SHAPE
     assert call(qs=256) == SHAPE
     assert call(dh=48, qs=384, os=384) == UNSUP

@@ -193,3 +193,32 @@ def test_decode_long_gqa_workload_sampled():
     decode 4 (the oracle recomputes the 384-token prefix)."""
     say("decode long GQA workload")
     _decode_case(synth.LONG_GQA_BF16, S0=380, steps=4, cache_seq=8192)
+
+
+def test_decode_step_replayed_from_a_hip_graph_matches_eager():
+    """A captured decode step, replayed several times with eager work in between, gives the
+    eager logits bitwise on every replay."""
+    tfm = tfm_mod()
+    cfg = small()
+    inp = synth.make_inputs(cfg, seed=4)
+    dm = tfm.DeviceModel(inp)
+    cache_seq = 64
+    cache = dm.kv_cache(cfg.batch, cache_seq)
+    dm.prefill(cache, cache_seq, ids=dm.ids[:, :20].contiguous(), logits=False)
+    tok = dm.ids[:, 20].contiguous()
+    pos = torch.full((cfg.batch,), 20, dtype=torch.int32, device="cuda")
+    eager = dm.decode(cache, cache_seq, tok, pos).clone()
+    out = torch.empty_like(eager)
+    side = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dm.decode(cache, cache_seq, tok, pos, logits=out)
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        dm.decode(cache, cache_seq, tok, pos, logits=side)
+        torch.cuda.synchronize()
+        assert torch.equal(side, eager)
+    dm.check_decode_flags()
