@@ -15,6 +15,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRC_TRAIN = os.path.join(_HERE, "oracle_train.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -28,6 +29,15 @@ class OracleCfg(ctypes.Structure):
                 ("eps", c_double), ("theta", c_double), ("window", c_int), ("full_every", c_int)]
 
 
+class OracleLayerD(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")]
+
+
+class OracleParamsD(ctypes.Structure):
+    _fields_ = [("embed", _p), ("layers", ctypes.POINTER(OracleLayerD)), ("g_final", _p),
+                ("lm_head", _p)]
+
+
 class OracleLayer(ctypes.Structure):
     _fields_ = [(n, _p) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")]
 
@@ -36,7 +46,7 @@ def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (plain C, -O2, OpenMP, strict IEEE double)."""
     if force or not os.path.exists(_LIB):
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-ffp-contract=off", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+               "-ffp-contract=off", "-Wall", "-o", _LIB + ".tmp", _SRC, _SRC_TRAIN, "-lm"]
         subprocess.run(cmd, check=True, cwd=_HERE)
         os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -71,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_model.argtypes = [ctypes.POINTER(OracleCfg), _p, ctypes.POINTER(OracleLayer),
                                    _p, _p, _p, _p, c_int, c_int, _p, _p, c_i64, _p]
         L.oracle_num_threads.restype = c_int
+        L.oracle_model_grads.argtypes = [ctypes.POINTER(OracleCfg), ctypes.POINTER(OracleParamsD),
+                                         _p, _p, _p, c_int, c_int, ctypes.POINTER(OracleParamsD)]
+        L.oracle_model_grads.restype = c_double
+        L.oracle_adamw.argtypes = [_p, _p, _p, _p, c_i64, c_double, c_double, c_double, c_double,
+                                   c_double, c_int]
         _lib = L
     return _lib
 
@@ -281,3 +296,84 @@ def next_token_targets(ids):
     t = np.full(ids.shape, -1, np.int32)
     t[:, :-1] = ids[:, 1:]
     return t
+
+
+# ---------------------------------------------------------------- training step
+LAYER_FIELDS = ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")
+
+
+def params_of(inputs) -> dict:
+    """The parameters of a synth.ModelInputs as a dict of float64 arrays (a tied LM head stays
+    the same object as the embedding)."""
+    embed = _f64(inputs.embed).copy()
+    return {"embed": embed,
+            "lm_head": embed if inputs.lm_head is inputs.embed else _f64(inputs.lm_head).copy(),
+            "g_final": _f64(inputs.g_final).copy(),
+            "layers": [{f: _f64(getattr(lw, f)).copy() for f in LAYER_FIELDS}
+                       for lw in inputs.layers]}
+
+
+def _params_struct(params, keep):
+    layers = (OracleLayerD * max(1, len(params["layers"])))(
+        *[OracleLayerD(*[_ptr(L[f]) for f in LAYER_FIELDS]) for L in params["layers"]])
+    keep.append(layers)
+    return OracleParamsD(_ptr(params["embed"]), layers, _ptr(params["g_final"]),
+                         _ptr(params["lm_head"]))
+
+
+def model_grads(cfg, params, ids, targets, pos=None):
+    """Mean next-token cross-entropy and its gradient with respect to every parameter
+    [T2 Optimize / Loss; chain rule through the forward of oracle.model]. params as
+    params_of(); ids, targets (B, S) (targets < 0: no target). Returns (loss, grads) with
+    grads shaped like params (a tied LM head's gradient is part of the embedding's)."""
+    ids = _i32(ids)
+    B, S = ids.shape
+    t = _i32(np.broadcast_to(targets, (B, S)))
+    pos = None if pos is None else _i32(np.broadcast_to(pos, (B, S)))
+    for arr in [params["embed"], params["lm_head"], params["g_final"]] + \
+            [L[f] for L in params["layers"] for f in LAYER_FIELDS]:
+        assert arr.dtype == np.float64 and arr.flags.c_contiguous
+    grads = {"embed": np.zeros_like(params["embed"]), "g_final": np.zeros_like(params["g_final"]),
+             "layers": [{f: np.zeros_like(L[f]) for f in LAYER_FIELDS} for L in params["layers"]]}
+    grads["lm_head"] = grads["embed"] if params["lm_head"] is params["embed"] else \
+        np.zeros_like(params["lm_head"])
+    keep: list = []
+    ps, gs = _params_struct(params, keep), _params_struct(grads, keep)
+    c = _cfg(cfg)
+    loss = lib().oracle_model_grads(ctypes.byref(c), ctypes.byref(ps), _ptr(ids), _ptr(pos),
+                                    _ptr(t), B, S, ctypes.byref(gs))
+    if np.isnan(loss):
+        raise IndexError("token id outside the vocabulary")
+    return float(loss), grads
+
+
+def adamw(theta, grad, m, v, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+          weight_decay: float = 1e-3, t: int = 1):
+    """One AdamW step [T2 Optimizer - AdamW]; returns new (theta, m, v) as float64 copies."""
+    th, mm, vv = _f64(theta).copy(), _f64(m).copy(), _f64(v).copy()
+    g = _f64(grad)
+    lib().oracle_adamw(_ptr(th), _ptr(g), _ptr(mm), _ptr(vv), th.size, lr, betas[0], betas[1],
+                       eps, weight_decay, t)
+    return th, mm, vv
+
+
+def clip_grad_norm(grads, max_norm: float, delta: float = 1e-6):
+    """[T2 Gradient Clip]: the global L2 norm of all gradients (the norm of the per-tensor
+    norms); when it exceeds max_norm every gradient is scaled by max_norm / (norm + delta).
+    Returns (norm, scaled copies)."""
+    gs = [_f64(g) for g in grads]
+    total = float(np.sqrt(sum(float(np.sum(g * g)) for g in gs)))
+    coef = max_norm / (total + delta) if total > max_norm else 1.0
+    return total, [g * coef for g in gs]
+
+
+def cosine_lr(it: int, warmup_iters: int, cos_cycle_iters: int, lr_min: float, lr_max: float):
+    """[T2 Cosine LR Scheduler]: linear warm-up to lr_max, cosine decay to lr_min over
+    (warmup_iters, cos_cycle_iters), lr_min after."""
+    import math
+    if it <= warmup_iters:
+        return lr_max * it / warmup_iters
+    if it < cos_cycle_iters:
+        frac = (it - warmup_iters) / (cos_cycle_iters - warmup_iters)
+        return lr_min + 0.5 * (lr_max - lr_min) * (1 + math.cos(math.pi * frac))
+    return lr_min

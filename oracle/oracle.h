@@ -119,6 +119,30 @@ double oracle_cross_entropy(const double *logits, int64_t rows, int V, const int
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void);
 
+/* ---- training step (oracle_train.c)  [T2 Optimize: Loss, AdamW; T3 12 training]. All
+ * parameters and gradients in double. lm_head may equal embed (tied); then the gradient
+ * buffers must be tied the same way and receive the sum. */
+typedef struct {
+  double *g_attn, *wq, *wk, *wv, *wo, *g_ffn, *w1, *w3, *w2;
+} oracle_layer_d;
+
+typedef struct {
+  double *embed;
+  oracle_layer_d *layers;
+  double *g_final, *lm_head;
+} oracle_params_d;
+
+/* Mean next-token cross-entropy over rows with 0 <= targets[r] < vocab (0 if none) and its
+ * gradient with respect to every parameter, ADDED into the buffers of g (zero them first).
+ * Returns the loss, or NaN if an id is outside the vocabulary. */
+double oracle_model_grads(const oracle_cfg *c, const oracle_params_d *p, const int32_t *ids,
+                          const int32_t *pos, const int32_t *targets, int B, int S,
+                          const oracle_params_d *g);
+
+/* One AdamW step in place on n parameters; t is the 1-based step count. */
+void oracle_adamw(double *theta, const double *grad, double *m, double *v, int64_t n, double lr,
+                  double b1, double b2, double eps, double wd, int t);
+
 #ifdef __cplusplus
 }
 #endif
