@@ -3,6 +3,7 @@
 // pre-norm decoder block ("Transformer 篇" (dujian.net) 5.7; "LLM 2" FFN & PreNorm).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -249,6 +250,92 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
   return TFM_OK;
 }
 
+
+// ---- training step: plan of the workspace and the enqueued forward / backward
+struct TrainPlan {
+  size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxT, dh, hT, du,
+      da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part;
+  size_t layers, layer_bytes;
+  size_t l_x, l_h1, l_qkv, l_o, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
+  int Vp;        // vocabulary padded to a multiple of 8 (K of the head's input-gradient GEMM)
+  int64_t Mp;    // tokens padded to a multiple of 8 (K of the weight-gradient GEMMs)
+  size_t total;
+};
+
+TrainPlan plan_train(const tfm_config *c, int B, int S) {
+  TrainPlan p;
+  const size_t M = (size_t)B * S, e = elt(c->dtype);
+  const size_t D = c->d_model, F = c->d_ff, V = c->vocab;
+  const size_t qd = (size_t)c->n_heads * c->d_head, kvd = (size_t)c->n_kv_heads * c->d_head;
+  const size_t W = qd + 2 * kvd;
+  p.Vp = (int)((V + 7) / 8 * 8);
+  p.Mp = (int64_t)((M + 7) / 8 * 8);
+  const size_t Vp = p.Vp, Mp = p.Mp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += round256(bytes); return o; };
+  p.flag = take(256);
+  p.count = take(4);
+  p.row_loss = take(M * 4);
+  p.xfinal = take(M * D * 4);
+  p.xf = take(M * D * e);
+  p.logits = take(M * Vp * 4);
+  p.dlog = take(M * Vp * e);
+  p.dlogT = take(Vp * Mp * e);
+  p.xfT = take(D * Mp * e);
+  size_t wmax = D * Vp;
+  wmax = std::max(wmax, F * D);
+  wmax = std::max(wmax, D * W);
+  wmax = std::max(wmax, qd * D);
+  p.wT = take(wmax * e);
+  p.dx = take(M * D * 4);
+  p.dxb = take(M * D * e);
+  p.dxT = take(D * Mp * e);
+  p.dh = take(M * D * 4);
+  p.hT = take(D * Mp * e);
+  p.du = take(M * F * 4);
+  p.da = take(M * F * e);
+  p.dc = take(M * F * e);
+  p.daT = take(F * Mp * e);
+  p.dcT = take(F * Mp * e);
+  p.actT = take(std::max(F, qd) * Mp * e);
+  p.dout = take(M * qd * e);
+  p.dqkv = take(M * W * e);
+  p.dqkvT = take(W * Mp * e);
+  p.lse = take(M * c->n_heads * 4);
+  p.dsum = take(M * c->n_heads * 4);
+  p.rms_part = take((size_t)rms_back_parts((int64_t)M) * D * 4);
+  size_t lo = 0;
+  auto ltake = [&](size_t bytes) { const size_t o = lo; lo += round256(bytes); return o; };
+  p.l_x = ltake(M * D * 4);
+  p.l_h1 = ltake(M * D * e);
+  p.l_qkv = ltake(M * W * e);
+  p.l_o = ltake(M * qd * e);
+  p.l_xm = ltake(M * D * 4);
+  p.l_h2 = ltake(M * D * e);
+  p.l_a = ltake(M * F * e);
+  p.l_c = ltake(M * F * e);
+  p.l_u = ltake(M * F * e);
+  p.layer_bytes = lo;
+  p.layers = off;
+  off += lo * (size_t)c->n_layers;
+  p.total = off;
+  return p;
+}
+
+int check_train_config(const tfm_config *c) {
+  if (c->d_model > 2048) return TFM_ERR_UNSUPPORTED;   // RMSNorm backward keeps a row in registers
+  if (!attention_backward_supported(c->d_head)) return TFM_ERR_UNSUPPORTED;
+  return TFM_OK;
+}
+
+// y = a w^T on the forward GEMM kernels; a (M, K) row stride lda, w (N, K) rows of K.
+int gemm(int epi, int dt, const void *a, int64_t lda, const void *w, int64_t M, int N, int K,
+         void *y, int64_t ldy, int y_dt, const float *residual, hipStream_t s) {
+  GemmArgs g{};
+  g.a = a; g.lda = lda; g.w0 = w; g.M = M; g.N = N; g.K = K; g.y = y; g.ldy = ldy; g.y_dt = y_dt;
+  g.residual = residual;
+  return hip_status(launch_gemm(epi, dt, g, s));
+}
 }  // namespace
 
 extern "C" {
@@ -637,6 +724,203 @@ int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
   return hip_status(launch_decode_attention(q, q_stride, k_cache, v_cache, positions, B, Hq,
                                             Hkv, d_head, cache_seq, window, (float *)ws, o,
                                             o_stride, (hipStream_t)stream));
+}
+
+
+// ---- training step
+
+size_t tfm_train_workspace_bytes(const tfm_config *cfg, int B, int S) {
+  if (check_config(cfg, B, S) != TFM_OK || check_train_config(cfg) != TFM_OK) return 0;
+  return plan_train(cfg, B, S).total;
+}
+
+int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                       const int32_t *positions, const int32_t *targets, float *loss_mean,
+                       const tfm_model_grads *gr, int B, int S, const float *cos_sin, void *ws,
+                       size_t ws_bytes, void *stream) {
+  TFM_TRY(check_config(cfg, B, S));
+  TFM_TRY(check_train_config(cfg));
+  if (!w || !gr) return TFM_ERR_NULL;
+  if ((int64_t)B * S == 0) return TFM_OK;
+  if (!targets || !loss_mean) return TFM_ERR_NULL;
+  TFM_TRY(check_model(cfg, w, ids, cos_sin, ws));
+  const bool tied = w->lm_head == w->embed;
+  if (!gr->embed || !gr->g_final || (cfg->n_layers > 0 && !gr->layers)) return TFM_ERR_NULL;
+  if (!tied && !gr->lm_head) return TFM_ERR_NULL;
+  if (tied && gr->lm_head && gr->lm_head != gr->embed) return TFM_ERR_SHAPE;
+  const float *gps[] = {gr->embed, gr->g_final, tied ? gr->embed : gr->lm_head};
+  for (const float *q : gps)
+    if (!aligned16(q)) return TFM_ERR_ALIGN;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const tfm_layer_grads *lg = &gr->layers[l];
+    const float *ps[] = {lg->g_attn, lg->wq, lg->wk, lg->wv, lg->wo, lg->g_ffn, lg->w1, lg->w3, lg->w2};
+    for (const float *q : ps) {
+      if (!q) return TFM_ERR_NULL;
+      if (!aligned16(q)) return TFM_ERR_ALIGN;
+    }
+  }
+  const TrainPlan p = plan_train(cfg, B, S);
+  if (ws_bytes < p.total) return TFM_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *wb = (uint8_t *)ws;
+  const int dt = cfg->dtype;
+  const size_t e = elt(dt);
+  const int64_t M = (int64_t)B * S, Mp = p.Mp;
+  const int D = cfg->d_model, F = cfg->d_ff, V = cfg->vocab, Vp = p.Vp, NL = cfg->n_layers;
+  const int Hq = cfg->n_heads, Hkv = cfg->n_kv_heads, dh = cfg->d_head;
+  const int qd = Hq * dh, kvd = Hkv * dh, W = qd + 2 * kvd;
+  const float eps = cfg->eps;
+  auto LA = [&](int l, size_t off) { return wb + p.layers + (size_t)l * p.layer_bytes + off; };
+  auto X = [&](int l) { return l < NL ? (float *)LA(l, p.l_x) : (float *)(wb + p.xfinal); };
+  int32_t *flags = (int32_t *)(wb + p.flag);
+  void *xf = wb + p.xf, *dlog = wb + p.dlog, *dlogT = wb + p.dlogT, *xfT = wb + p.xfT;
+  void *wT = wb + p.wT, *dxb = wb + p.dxb, *dxT = wb + p.dxT, *hT = wb + p.hT;
+  void *da = wb + p.da, *dc = wb + p.dc, *daT = wb + p.daT, *dcT = wb + p.dcT;
+  void *actT = wb + p.actT, *dout = wb + p.dout, *dqkv = wb + p.dqkv, *dqkvT = wb + p.dqkvT;
+  float *logits = (float *)(wb + p.logits), *dx = (float *)(wb + p.dx);
+  float *dhp = (float *)(wb + p.dh), *du = (float *)(wb + p.du);
+  float *rpart = (float *)(wb + p.rms_part);
+
+  // ---- forward, keeping each layer's activations ("Transformer 篇" 5.7)
+  TFM_HIP(launch_fill_i32(flags, 2, 0, s));
+  TFM_HIP(launch_embed(ids, M, w->embed, dt, V, D, X(0), flags, s));
+  for (int l = 0; l < NL; ++l) {
+    const tfm_layer_weights *lw = &w->layers[l];
+    float *x = X(l), *xm = (float *)LA(l, p.l_xm);
+    uint8_t *qkv = LA(l, p.l_qkv);
+    void *h1 = LA(l, p.l_h1), *o = LA(l, p.l_o), *h2 = LA(l, p.l_h2);
+    void *a = LA(l, p.l_a), *c = LA(l, p.l_c), *u = LA(l, p.l_u);
+    TFM_HIP(launch_rmsnorm(x, DT_F32, lw->g_attn, dt, h1, dt, M, D, eps, s));
+    GemmArgs g{};
+    g.a = h1; g.lda = D; g.w0 = lw->wq; g.w1 = lw->wk; g.w2 = lw->wv; g.n0 = qd; g.n1 = kvd;
+    g.M = M; g.N = W; g.K = D; g.y = qkv; g.ldy = W; g.y_dt = dt;
+    g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = dh;
+    g.max_seq = cfg->max_seq_len;
+    TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
+    TFM_HIP(launch_attention(qkv, W, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e, W, o, qd,
+                             B, S, Hq, Hkv, dh, dt, layer_window(cfg, l), s));
+    TFM_TRY(gemm(EPI_RESIDUAL, dt, o, qd, lw->wo, M, D, qd, xm, D, DT_F32, x, s));
+    TFM_HIP(launch_rmsnorm(xm, DT_F32, lw->g_ffn, dt, h2, dt, M, D, eps, s));
+    TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w1, M, F, D, a, F, dt, nullptr, s));
+    TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w3, M, F, D, c, F, dt, nullptr, s));
+    TFM_HIP(launch_swiglu_fwd(a, c, u, dt, M * F, s));
+    TFM_TRY(gemm(EPI_RESIDUAL, dt, u, F, lw->w2, M, D, F, X(l + 1), D, DT_F32, xm, s));
+  }
+  TFM_HIP(launch_rmsnorm(X(NL), DT_F32, w->g_final, dt, xf, dt, M, D, eps, s));
+  TFM_TRY(gemm(EPI_STORE, dt, xf, D, w->lm_head, M, V, D, logits, Vp, DT_F32, nullptr, s));
+
+  // ---- loss and its gradient with respect to the logits ("LLM 2" Optimize / Loss)
+  TFM_HIP(launch_ce_backward(logits, Vp, targets, M, V, dlog, dt, Vp, (float *)(wb + p.row_loss),
+                             (int32_t *)(wb + p.count), loss_mean, s));
+
+  // ---- LM head and final RMSNorm
+  TFM_HIP(launch_transpose(w->lm_head, dt, D, wT, dt, Vp, Vp, V, D, s));
+  TFM_TRY(gemm(EPI_STORE, dt, dlog, Vp, wT, M, D, Vp, dhp, D, DT_F32, nullptr, s));
+  TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, V, s));
+  TFM_HIP(launch_transpose(xf, dt, D, xfT, dt, Mp, Mp, M, D, s));
+  float *g_lm = tied ? gr->embed : gr->lm_head;
+  TFM_TRY(gemm(EPI_STORE, dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, DT_F32, nullptr, s));
+  TFM_HIP(launch_fill_f32(dx, M * D, 0.f, s));
+  TFM_HIP(launch_rms_backward(X(NL), w->g_final, dt, dhp, dx, gr->g_final, 0, rpart, M, D, eps, s));
+
+  // ---- blocks, last to first; dx holds the gradient of the block's output
+  for (int l = NL - 1; l >= 0; --l) {
+    const tfm_layer_weights *lw = &w->layers[l];
+    const tfm_layer_grads *lg = &gr->layers[l];
+    float *x = X(l), *xm = (float *)LA(l, p.l_xm);
+    uint8_t *qkv = LA(l, p.l_qkv);
+    void *h1 = LA(l, p.l_h1), *o = LA(l, p.l_o), *h2 = LA(l, p.l_h2);
+    void *a = LA(l, p.l_a), *c = LA(l, p.l_c), *u = LA(l, p.l_u);
+    // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
+    TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
+    TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
+    TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
+    TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, DT_F32, nullptr, s));
+    TFM_HIP(launch_swiglu_backward(a, c, du, da, dc, dt, M * F, s));
+    TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, F, F, F, D, s));
+    TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
+    TFM_HIP(launch_transpose(lw->w3, dt, D, wT, dt, F, F, F, D, s));
+    TFM_TRY(gemm(EPI_RESIDUAL, dt, dc, F, wT, M, D, F, dhp, D, DT_F32, dhp, s));
+    TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
+    TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
+    TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
+    TFM_TRY(gemm(EPI_STORE, dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, DT_F32, nullptr, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, DT_F32, nullptr, s));
+    TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, lg->g_ffn, 0, rpart, M, D, eps, s));
+    // attention output projection: xm = x + o Wo^T
+    TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
+    TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
+    TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
+    TFM_HIP(launch_transpose(o, dt, qd, actT, dt, Mp, Mp, M, qd, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, DT_F32, nullptr, s));
+    // attention, then back through the rotations of q and k
+    TFM_HIP(launch_attention_backward(qkv, W, o, qd, dout, qd, dqkv, B, S, Hq, Hkv, dh, dt,
+                                      layer_window(cfg, l), (float *)(wb + p.lse),
+                                      (float *)(wb + p.dsum), s));
+    TFM_HIP(launch_rope_inverse(dqkv, dt, W, positions, M, S, Hq, dh, cos_sin, cfg->max_seq_len, s));
+    TFM_HIP(launch_rope_inverse((uint8_t *)dqkv + (size_t)qd * e, dt, W, positions, M, S, Hkv, dh,
+                                cos_sin, cfg->max_seq_len, s));
+    // q, k, v projections: one GEMM against [Wq; Wk; Wv]^T for the input gradient
+    TFM_HIP(launch_transpose(lw->wq, dt, D, wT, dt, W, qd, qd, D, s));
+    TFM_HIP(launch_transpose(lw->wk, dt, D, (uint8_t *)wT + (size_t)qd * e, dt, W, kvd, kvd, D, s));
+    TFM_HIP(launch_transpose(lw->wv, dt, D, (uint8_t *)wT + (size_t)(qd + kvd) * e, dt, W, kvd, kvd,
+                             D, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wT, M, D, W, dhp, D, DT_F32, nullptr, s));
+    TFM_HIP(launch_transpose(dqkv, dt, W, dqkvT, dt, Mp, Mp, M, W, s));
+    TFM_HIP(launch_transpose(h1, dt, D, hT, dt, Mp, Mp, M, D, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dqkvT, Mp, hT, qd, D, (int)Mp, lg->wq, D, DT_F32, nullptr, s));
+    TFM_TRY(gemm(EPI_STORE, dt, (uint8_t *)dqkvT + (size_t)qd * Mp * e, Mp, hT, kvd, D, (int)Mp,
+                 lg->wk, D, DT_F32, nullptr, s));
+    TFM_TRY(gemm(EPI_STORE, dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
+                 (int)Mp, lg->wv, D, DT_F32, nullptr, s));
+    TFM_HIP(launch_rms_backward(x, lw->g_attn, dt, dhp, dx, lg->g_attn, 0, rpart, M, D, eps, s));
+  }
+  // ---- embedding rows (a tied head's gradient is already in gr->embed)
+  if (!tied) TFM_HIP(launch_fill_f32(gr->embed, (int64_t)V * D, 0.f, s));
+  TFM_HIP(launch_embed_backward(ids, M, V, D, dx, gr->embed, s));
+  return TFM_OK;
+}
+
+size_t tfm_clip_workspace_bytes(int n_tensors) {
+  if (n_tensors < 0) return 0;
+  return round256((size_t)(n_tensors > 0 ? n_tensors : 1) * sumsq_parts() * 8);
+}
+
+int tfm_grad_clip_coef(const float *const *grads, const int64_t *sizes, int n_tensors,
+                       float max_norm, float *coef, float *norm, void *ws, size_t ws_bytes,
+                       void *stream) {
+  if (n_tensors < 0 || !(max_norm > 0.f)) return TFM_ERR_SHAPE;
+  if (!coef || !ws || (n_tensors > 0 && (!grads || !sizes))) return TFM_ERR_NULL;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (sizes[i] < 0) return TFM_ERR_SHAPE;
+    if (sizes[i] > 0 && !grads[i]) return TFM_ERR_NULL;
+  }
+  if (ws_bytes < tfm_clip_workspace_bytes(n_tensors)) return TFM_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  double *part = (double *)ws;
+  const int np = sumsq_parts();
+  for (int i = 0; i < n_tensors; ++i)
+    TFM_HIP(launch_sumsq(sizes[i] > 0 ? grads[i] : nullptr, sizes[i], part + (size_t)i * np, s));
+  TFM_HIP(launch_clip_coef(part, n_tensors * np, max_norm, coef, norm, s));
+  return TFM_OK;
+}
+
+int tfm_adamw_step(float *param, void *param_bf16, const float *grad, float *m, float *v,
+                   int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay,
+                   int step, const float *coef, void *stream) {
+  if (n < 0 || step < 1 || !(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) ||
+      !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) || !(weight_decay >= 0.f))
+    return TFM_ERR_SHAPE;
+  if (n == 0) return TFM_OK;
+  if (!param || !grad || !m || !v) return TFM_ERR_NULL;
+  const float c1 = (float)(1.0 - std::pow((double)beta1, step));
+  const float c2 = (float)(1.0 - std::pow((double)beta2, step));
+  return hip_status(launch_adamw(param, param_bf16, grad, m, v, n, lr, beta1, beta2, eps,
+                                 weight_decay, c1, c2, coef, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -105,6 +105,49 @@ hipError_t launch_kv_store(const void *qkv, int64_t ld, int qd, int kvd, int d_h
                            int B, int S, const int32_t *positions, void *k_cache, void *v_cache,
                            int cache_seq, int32_t *pos_flag, hipStream_t s);
 
+// ---- training step (backward.hip)
+// dst[c, r] = src[r, c] for an R x C source (row strides lds, ldd), converting the dtype;
+// source rows in [R_valid, R) read as zero.
+hipError_t launch_transpose(const void *src, int src_dt, int64_t lds, void *dst, int dst_dt,
+                            int64_t ldd, int64_t R, int64_t R_valid, int C, hipStream_t s);
+hipError_t launch_convert(const void *src, int src_dt, void *dst, int dst_dt, int64_t n,
+                          hipStream_t s);
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
+// dz = d mean-loss / d z for fp32 logits z (M, ldz), written (M, ldd) with zero padding past
+// V; row_loss (M); count = rows with a target in [0, V); mean = mean loss over them.
+hipError_t launch_ce_backward(const float *z, int64_t ldz, const int32_t *targets, int64_t M,
+                              int V, void *dz, int dz_dt, int64_t ldd, float *row_loss,
+                              int32_t *count, float *mean, hipStream_t s);
+// dx += RMSNorm backward of rows x with gain g (d <= 2048); dg = (or +=) gain gradient.
+// dg_part: rms_back_parts(rows) * d floats of scratch.
+int rms_back_parts(int64_t rows);
+hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const float *dy, float *dx,
+                               float *dg, int accumulate_dg, float *dg_part, int64_t rows, int d,
+                               float eps, hipStream_t s);
+hipError_t launch_swiglu_fwd(const void *a, const void *c, void *u, int dt, int64_t n,
+                             hipStream_t s);
+hipError_t launch_swiglu_backward(const void *a, const void *c, const float *du, void *da,
+                                  void *dc, int dt, int64_t n, hipStream_t s);
+hipError_t launch_rope_inverse(void *x, int dt, int64_t row_stride, const int32_t *positions,
+                               int64_t rows, int S, int H, int d_head, const float *cos_sin,
+                               int max_seq, hipStream_t s);
+bool attention_backward_supported(int d_head);
+// dq, dk, dv into the q | k | v columns of dqkv (same layout as qkv); lse, dsum: (B*S, Hq)
+// fp32 scratch (row logsumexp and rowsum(do * o)).
+hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o, int64_t ldo,
+                                     const void *dout, int64_t lddo, void *dqkv, int B, int S,
+                                     int Hq, int Hkv, int d_head, int dt, int window, float *lse,
+                                     float *dsum, hipStream_t s);
+hipError_t launch_embed_backward(const int32_t *ids, int64_t n, int vocab, int d, const float *dx,
+                                 float *dE, hipStream_t s);
+int sumsq_parts();
+hipError_t launch_sumsq(const float *g, int64_t n, double *part, hipStream_t s);
+hipError_t launch_clip_coef(const double *part, int nparts, float max_norm, float *coef,
+                            float *norm, hipStream_t s);
+hipError_t launch_adamw(float *p, void *pb, const float *g, float *m, float *v, int64_t n,
+                        float lr, float b1, float b2, float eps, float wd, float c1, float c2,
+                        const float *coef, hipStream_t s);
+
 // Whether one sequence's keys fit the bf16 kernel's 32-bit buffer offsets.
 bool attention_fits(int dt, int S, int64_t kv_stride);
 

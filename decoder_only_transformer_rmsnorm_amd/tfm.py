@@ -28,7 +28,8 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_sliding_window_attention", "tfm_kv_cache_bytes", "tfm_model_prefill",
            "tfm_decode_workspace_bytes", "tfm_model_decode",
            "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
-           "tfm_check_device_flags"]
+           "tfm_train_workspace_bytes", "tfm_model_backward", "tfm_clip_workspace_bytes",
+           "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_check_device_flags"]
 
 
 class TfmError(RuntimeError):
@@ -56,6 +57,15 @@ class LayerWeights(ctypes.Structure):
 
 class ModelWeights(ctypes.Structure):
     _fields_ = [("embed", c_p), ("layers", ctypes.POINTER(LayerWeights)), ("g_final", c_p),
+                ("lm_head", c_p)]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, c_p) for n in ("g_attn", "wq", "wk", "wv", "wo", "g_ffn", "w1", "w3", "w2")]
+
+
+class ModelGrads(ctypes.Structure):
+    _fields_ = [("embed", c_p), ("layers", ctypes.POINTER(LayerGrads)), ("g_final", c_p),
                 ("lm_head", c_p)]
 
 
@@ -116,6 +126,16 @@ def lib() -> ctypes.CDLL:
             "tfm_decode_attention_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
             "tfm_decode_attention": (c_int, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_int, c_int,
                                              c_int, c_int, c_int, c_int, c_p, c_size, c_p]),
+            "tfm_train_workspace_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
+            "tfm_model_backward": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
+                                           c_p, c_p, c_p, c_p, ctypes.POINTER(ModelGrads), c_int,
+                                           c_int, c_p, c_p, c_size, c_p]),
+            "tfm_clip_workspace_bytes": (c_size, [c_int]),
+            "tfm_grad_clip_coef": (c_int, [ctypes.POINTER(c_p), ctypes.POINTER(c_i64), c_int,
+                                           ctypes.c_float, c_p, c_p, c_p, c_size, c_p]),
+            "tfm_adamw_step": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, c_int, c_p, c_p]),
             "tfm_check_device_flags": (c_int, [c_p, c_p]),
         }
         for name, (res, args) in sig.items():
@@ -485,3 +505,92 @@ def tfm_block_forward(dm: DeviceModel, layer: int, x, positions=None, stream=Non
 
 def tfm_model_forward(dm: DeviceModel, ids=None, positions=None, **kw):
     return dm.forward(ids=ids, positions=positions, **kw)
+
+
+class Trainer:
+    """One training step on the GPU for a DeviceModel [T2 Optimize; T3 12]: forward and
+    backward of the mean next-token cross-entropy (tfm_model_backward), global-norm gradient
+    clipping (tfm_grad_clip_coef) and AdamW (tfm_adamw_step). Keeps fp32 master weights, fp32
+    gradients and the two AdamW moments; for bf16 models the DeviceModel's bf16 weights are
+    rewritten from the masters after every step."""
+
+    def __init__(self, dm: "DeviceModel", lr: float = 1e-3, betas=(0.9, 0.95), eps: float = 1e-8,
+                 weight_decay: float = 0.1, max_norm: float | None = 1.0):
+        torch = _torch()
+        self.dm, self.lr, self.betas, self.eps, self.wd, self.max_norm = dm, lr, betas, eps, \
+            weight_decay, max_norm
+        self.t = 0
+        self.tied = dm.lm_head is dm.embed
+        names = ["embed"] + ([] if self.tied else ["lm_head"]) + ["g_final"]
+        self.params = [(n, getattr(dm, n)) for n in names]
+        for l, L in enumerate(dm.layers):
+            self.params += [(f"layers.{l}.{f}", L[f]) for f in DeviceModel.LAYER_FIELDS]
+        f32 = torch.float32
+        self.master = {n: (w if w.dtype == f32 else w.float()) for n, w in self.params}
+        self.grad = {n: torch.zeros_like(self.master[n], dtype=f32) for n, _ in self.params}
+        self.m = {n: torch.zeros_like(self.grad[n]) for n, _ in self.params}
+        self.v = {n: torch.zeros_like(self.grad[n]) for n, _ in self.params}
+        G = self.grad
+        self._lg = (LayerGrads * max(1, len(dm.layers)))(
+            *[LayerGrads(*[G[f"layers.{l}.{f}"].data_ptr() for f in DeviceModel.LAYER_FIELDS])
+              for l in range(len(dm.layers))])
+        self.cgrads = ModelGrads(G["embed"].data_ptr(), self._lg, G["g_final"].data_ptr(),
+                                 G["embed"].data_ptr() if self.tied else G["lm_head"].data_ptr())
+        self.loss = torch.zeros(1, dtype=f32, device=dm.device)
+        self.coef = torch.ones(1, dtype=f32, device=dm.device)
+        self.norm = torch.zeros(1, dtype=f32, device=dm.device)
+        n = len(self.params)
+        self._gptrs = (c_p * n)(*[G[k].data_ptr() for k, _ in self.params])
+        self._gsizes = (c_i64 * n)(*[G[k].numel() for k, _ in self.params])
+        self._cws = torch.empty(lib().tfm_clip_workspace_bytes(n), dtype=torch.uint8,
+                                device=dm.device)
+        self._ws = None
+        self._ws_shape = None
+
+    def workspace(self, B: int, S: int):
+        torch = _torch()
+        if self._ws_shape != (B, S):
+            nb = lib().tfm_train_workspace_bytes(ctypes.byref(self.dm.ccfg), B, S)
+            if nb == 0:
+                raise TfmError(-6, "tfm_train_workspace_bytes")
+            self._ws = None
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.dm.device)
+            self._ws_shape = (B, S)
+        return self._ws
+
+    def backward(self, ids, targets, positions=None, stream=None):
+        """Fills self.grad; returns the mean loss (device tensor of 1)."""
+        B, S = ids.shape
+        ws = self.workspace(B, S)
+        dm = self.dm
+        _check(lib().tfm_model_backward(ctypes.byref(dm.ccfg), ctypes.byref(dm.weights), _dev(ids),
+                                        _dev(positions), _dev(targets), _dev(self.loss),
+                                        ctypes.byref(self.cgrads), B, S, _dev(dm.cos_sin), _dev(ws),
+                                        ws.numel(), _stream(stream)), "tfm_model_backward")
+        return self.loss
+
+    def clip(self, stream=None):
+        _check(lib().tfm_grad_clip_coef(self._gptrs, self._gsizes, len(self.params),
+                                        self.max_norm, _dev(self.coef), _dev(self.norm),
+                                        _dev(self._cws), self._cws.numel(), _stream(stream)),
+               "tfm_grad_clip_coef")
+
+    def optimizer_step(self, lr: float | None = None, stream=None):
+        self.t += 1
+        lr = self.lr if lr is None else lr
+        coef = self.coef if self.max_norm is not None else None
+        for n, w in self.params:
+            pm = self.master[n]
+            pb = None if w is pm else w
+            _check(lib().tfm_adamw_step(_dev(pm), _dev(pb), _dev(self.grad[n]), _dev(self.m[n]),
+                                        _dev(self.v[n]), pm.numel(), lr, self.betas[0],
+                                        self.betas[1], self.eps, self.wd, self.t, _dev(coef),
+                                        _stream(stream)), "tfm_adamw_step")
+
+    def step(self, ids, targets, positions=None, lr: float | None = None, stream=None):
+        """Forward + backward, clipping (if max_norm) and one AdamW step; returns the loss."""
+        loss = self.backward(ids, targets, positions, stream)
+        if self.max_norm is not None:
+            self.clip(stream)
+        self.optimizer_step(lr, stream)
+        return loss

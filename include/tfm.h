@@ -256,6 +256,54 @@ int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
                          int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
                          int window, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- Training step  [T2 Optimize: Loss, Optimizer - AdamW, Gradient Clip; T3 12 training
+ * loop: loss, backward, clip, step]. fp32 gradients; fp32 master weights and moments. */
+typedef struct {
+  float *g_attn, *wq, *wk, *wv, *wo, *g_ffn, *w1, *w3, *w2;
+} tfm_layer_grads;
+
+typedef struct {
+  float *embed;
+  const tfm_layer_grads *layers; /* host array of n_layers */
+  float *g_final, *lm_head;      /* lm_head: NULL or == embed when the head is tied */
+} tfm_model_grads;
+
+/* Workspace of tfm_model_backward: every layer's forward activations, the logits and their
+ * gradient, transposed operands and activation gradients (0 if the configuration is not
+ * supported for training). */
+size_t tfm_train_workspace_bytes(const tfm_config *cfg, int B, int S);
+
+/* Training forward and backward: loss_mean ([dev] 1 float) = mean next-token cross-entropy over
+ * the rows with 0 <= targets[r] < vocab ([dev] int32 (B, S); others are ignored), and the
+ * gradient of that mean with respect to every parameter written to the fp32 buffers of grads
+ * (shapes of the weights; overwritten). A tied head (w->lm_head == w->embed) adds its gradient
+ * into grads->embed. The forward keeps bf16 (or fp32) activations; the backward's products run
+ * on the forward's GEMM kernels with transposed operands. d_model <= 2048, d_head in
+ * {16 (fp32 only), 32, 64, 128}; TFM_ERR_UNSUPPORTED otherwise. All pointers 16-byte aligned.
+ * The token flag (tfm_check_device_flags) works as for the forward. */
+int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
+                       const int32_t *positions, const int32_t *targets, float *loss_mean,
+                       const tfm_model_grads *grads, int B, int S, const float *cos_sin,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Global-norm clipping coefficient  [T2 Gradient Clip]: norm = sqrt(sum over the n tensors of
+ * sum g^2); coef[0] = max_norm / (norm + 1e-6) when norm > max_norm, else 1; norm[0] (nullable)
+ * = norm. grads, sizes: host arrays of n device pointers (fp32) and element counts; coef, norm:
+ * [dev] 1 float. ws: tfm_clip_workspace_bytes(n) bytes. Sums in fp64 in a fixed order. */
+size_t tfm_clip_workspace_bytes(int n_tensors);
+int tfm_grad_clip_coef(const float *const *grads, const int64_t *sizes, int n_tensors,
+                       float max_norm, float *coef, float *norm, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* One AdamW step  [T2 Optimizer - AdamW] on n parameters, in place: g = grad * coef[0] (coef
+ * nullable: 1); m = b1 m + (1 - b1) g; v = b2 v + (1 - b2) g^2; param = param - lr
+ * (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps) - lr weight_decay param (decay on the
+ * value before the step). param, grad, m, v: [dev] fp32; param_bf16 (nullable): [dev] bf16
+ * copy written with the new value. step >= 1; m, v zero before step 1. */
+int tfm_adamw_step(float *param, void *param_bf16, const float *grad, float *m, float *v,
+                   int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay,
+                   int step, const float *coef, void *stream);
+
 /* Waits for `stream`, then returns TFM_ERR_TOKEN if the last whole-model call that used this
  * workspace saw an out-of-range token id, TFM_ERR_POSITION if it saw a position outside the
  * KV cache or the RoPE table (prefill / decode), else TFM_OK. */

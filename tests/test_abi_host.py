@@ -317,3 +317,48 @@ def test_decode_attention_validation(L):
     assert call(q=None) == NULL
     assert call(o=PM) == ALIGN
     assert call(nb=need - 1) == WS
+
+
+def test_training_entry_points_validation(L):
+    """Every call fails validation (or is empty) before any launch."""
+    c = _cfg()
+    assert L.tfm_train_workspace_bytes(ctypes.byref(c), 2, 16) > 0
+    assert L.tfm_train_workspace_bytes(ctypes.byref(_cfg(d_model=4096, n_heads=128)), 2, 16) == 0
+    layers = (tfm.LayerWeights * 4)(*[_layer() for _ in range(4)])
+    mw = tfm.ModelWeights(P, layers, P, P + 0x100)
+    glayers = (tfm.LayerGrads * 4)(*[tfm.LayerGrads(*([P] * 9)) for _ in range(4)])
+    need = L.tfm_train_workspace_bytes(ctypes.byref(c), 2, 16)
+    def bwd(cfg=c, w=mw, t=P, loss=P, g=None, B=2, nb=need):
+        g = tfm.ModelGrads(P, glayers, P, P + 0x200) if g is None else g
+        return L.tfm_model_backward(ctypes.byref(cfg), ctypes.byref(w), P, None, t, loss,
+                                    ctypes.byref(g), B, 16, P, P, nb, None)
+    assert bwd(B=0) == OK
+    assert bwd(t=None) == NULL
+    assert bwd(loss=None) == NULL
+    assert bwd(nb=need - 1) == WS
+    assert bwd(g=tfm.ModelGrads(P, glayers, P, None)) == NULL          # untied head needs a grad
+    assert bwd(g=tfm.ModelGrads(PM, glayers, P, P)) == ALIGN
+    tied = tfm.ModelWeights(P, layers, P, P)
+    assert bwd(w=tied, g=tfm.ModelGrads(P, glayers, P, P + 0x200)) == SHAPE
+    bad = (tfm.LayerGrads * 4)(*[tfm.LayerGrads(*([P] * 9)) for _ in range(4)])
+    bad[3].w2 = None
+    assert bwd(g=tfm.ModelGrads(P, bad, P, P + 0x200)) == NULL
+
+    clip = L.tfm_grad_clip_coef
+    nb = L.tfm_clip_workspace_bytes(3)
+    ptrs = (ctypes.c_void_p * 3)(P, P, P)
+    sizes = (ctypes.c_int64 * 3)(10, 20, 30)
+    assert clip(ptrs, sizes, 3, 0.0, P, None, P, nb, None) == SHAPE
+    assert clip(ptrs, sizes, -1, 1.0, P, None, P, nb, None) == SHAPE
+    assert clip(ptrs, sizes, 3, 1.0, None, None, P, nb, None) == NULL
+    assert clip(ptrs, sizes, 3, 1.0, P, None, P, nb - 1, None) == WS
+    neg = (ctypes.c_int64 * 3)(10, -1, 30)
+    assert clip(ptrs, neg, 3, 1.0, P, None, P, nb, None) == SHAPE
+
+    adam = lambda n=10, lr=1e-3, b1=0.9, b2=0.999, step=1, p=P: L.tfm_adamw_step(
+        p, None, P, P, P, n, lr, b1, b2, 1e-8, 0.0, step, None, None)
+    assert adam(step=0) == SHAPE
+    assert adam(b1=1.0) == SHAPE
+    assert adam(lr=-1.0) == SHAPE
+    assert adam(n=0) == OK
+    assert adam(p=None) == NULL
