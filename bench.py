@@ -321,6 +321,22 @@ def main() -> int:
         mfma_util = {"gemm": round(gemm_f / (gemm_ms / 1e3) / PEAK_BF16, 4),
                      "attention": kernels["attention"]["frac_mfma"]}
 
+    train = None
+    if not args.no_kernels:
+        # training step on the same batch: forward keeping activations, backward, global-norm
+        # clipping and AdamW (it rewrites the weights, so it runs after every other leg)
+        tr = tfm.Trainer(dm, lr=1e-4, weight_decay=0.1, max_norm=1.0)
+        t_tg = tfm.next_token_targets(dm.ids)
+        loss0 = float(tr.step(dm.ids, t_tg).item())
+        train_ms = time_launches(lambda: tr.step(dm.ids, t_tg), 5, stream, graph=False)
+        fw = accounting.forward_flops(cfg)["total"]
+        train = {"ms_per_step": round(train_ms, 3), "tokens_per_s": round(M / (train_ms / 1e3), 1),
+                 "loss_first_step": round(loss0, 4),
+                 "model_TFLOP/s": round(3 * fw / (train_ms / 1e3) / 1e12, 1),
+                 "flops_note": "3 x forward (causal) per step"}
+        log(f"training step: {train_ms:.2f} ms, {M / (train_ms / 1e3) / 1e3:.1f} k tokens/s")
+        del tr
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle, budget {args.cpu_budget:.0f} s")
@@ -344,6 +360,7 @@ def main() -> int:
         "kernels": kernels,
         "loss_forward": loss_forward,
         "decode": decode,
+        "train_step": train,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

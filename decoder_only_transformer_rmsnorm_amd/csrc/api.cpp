@@ -256,7 +256,7 @@ struct TrainPlan {
   size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxT, dh, hT, du,
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part;
   size_t layers, layer_bytes;
-  size_t l_x, l_h1, l_qkv, l_o, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
+  size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
   int Vp;        // vocabulary padded to a multiple of 8 (K of the head's input-gradient GEMM)
   int64_t Mp;    // tokens padded to a multiple of 8 (K of the weight-gradient GEMMs)
   size_t total;
@@ -310,6 +310,7 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.l_h1 = ltake(M * D * e);
   p.l_qkv = ltake(M * W * e);
   p.l_o = ltake(M * qd * e);
+  p.l_lse = ltake(M * c->n_heads * 4);
   p.l_xm = ltake(M * D * 4);
   p.l_h2 = ltake(M * D * e);
   p.l_a = ltake(M * F * e);
@@ -799,7 +800,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     g.max_seq = cfg->max_seq_len;
     TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
     TFM_HIP(launch_attention(qkv, W, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e, W, o, qd,
-                             B, S, Hq, Hkv, dh, dt, layer_window(cfg, l), s));
+                             B, S, Hq, Hkv, dh, dt, layer_window(cfg, l), s,
+                             (float *)LA(l, p.l_lse)));
     TFM_TRY(gemm(EPI_RESIDUAL, dt, o, qd, lw->wo, M, D, qd, xm, D, DT_F32, x, s));
     TFM_HIP(launch_rmsnorm(xm, DT_F32, lw->g_ffn, dt, h2, dt, M, D, eps, s));
     TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w1, M, F, D, a, F, dt, nullptr, s));
@@ -859,7 +861,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_TRY(gemm(EPI_STORE, dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, DT_F32, nullptr, s));
     // attention, then back through the rotations of q and k
     TFM_HIP(launch_attention_backward(qkv, W, o, qd, dout, qd, dqkv, B, S, Hq, Hkv, dh, dt,
-                                      layer_window(cfg, l), (float *)(wb + p.lse),
+                                      layer_window(cfg, l), (const float *)LA(l, p.l_lse),
                                       (float *)(wb + p.dsum), s));
     TFM_HIP(launch_rope_inverse(dqkv, dt, W, positions, M, S, Hq, dh, cos_sin, cfg->max_seq_len, s));
     TFM_HIP(launch_rope_inverse((uint8_t *)dqkv + (size_t)qd * e, dt, W, positions, M, S, Hkv, dh,

@@ -92,7 +92,8 @@ template <int DH>
 __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
     const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, int64_t kv_stride, bf16_t *__restrict__ o, int64_t o_stride,
-    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus, int window) {
+    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus, int window,
+    float *__restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = AttnTile<DH>;
   constexpr int RB = T::RB, CPR = T::CPR, FR = T::FR, TILE = T::TILE, INS = T::INS;
@@ -350,6 +351,9 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
   }
 
   if (my_q < S) {
+    // row logsumexp of the scaled scores (kept for the backward): max + log(sum)
+    if (lse && h == 0)
+      lse[((int64_t)b * S + my_q) * Hq + hq] = m_run * (scale_log2 / kLog2e) + logf(lacc[0]);
     const float inv = 1.0f / lacc[0];
     bf16_t *op = o + ((int64_t)b * S + my_q) * o_stride + (int64_t)hq * DH;
 #pragma unroll
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
                                                       const float *__restrict__ v, int64_t kv_stride,
                                                       float *__restrict__ o, int64_t o_stride, int B,
                                                       int S, int Hq, int Hkv, float scale,
-                                                      int window) {
+                                                      int window, float *__restrict__ lse) {
   const int s = blockIdx.x * 64 + threadIdx.x;
   const int hq = blockIdx.y, b = blockIdx.z;
   if (s >= S) return;
@@ -395,6 +399,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
     m = m_new;
   }
   float *op = o + ((int64_t)b * S + s) * o_stride + (int64_t)hq * DH;
+  if (lse) lse[((int64_t)b * S + s) * Hq + hq] = m + logf(l);
   const float inv = 1.0f / l;
 #pragma unroll
   for (int e = 0; e < DH; ++e) op[e] = acc[e] * inv;
@@ -416,7 +421,8 @@ int compute_units() {
 
 template <int DH>
 hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
-                    int64_t os, int B, int S, int Hq, int Hkv, int window, hipStream_t st) {
+                    int64_t os, int B, int S, int Hq, int Hkv, int window, float *lse,
+                    hipStream_t st) {
   const int n_qt = (S + kBQ - 1) / kBQ;
   const int64_t blocks = (int64_t)n_qt * B * Hq;
   if (blocks == 0) return hipSuccess;
@@ -424,19 +430,20 @@ hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int
   const float sl2 = kLog2e / sqrtf((float)DH);
   attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
       (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S, Hq,
-      Hkv, n_qt, sl2, compute_units(), window);
+      Hkv, n_qt, sl2, compute_units(), window, lse);
   return hipGetLastError();
 }
 
 template <int DH>
 hipError_t run_f32(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
-                   int64_t os, int B, int S, int Hq, int Hkv, int window, hipStream_t st) {
+                   int64_t os, int B, int S, int Hq, int Hkv, int window, float *lse,
+                   hipStream_t st) {
   if ((int64_t)B * S * Hq == 0) return hipSuccess;
   if (B > 65535 || Hq > 65535) return hipErrorInvalidValue;
   dim3 grid((S + 63) / 64, Hq, B);
   attn_f32_kernel<DH><<<grid, dim3(64), 0, st>>>((const float *)q, qs, (const float *)k,
                                                  (const float *)v, kvs, (float *)o, os, B, S, Hq,
-                                                 Hkv, 1.0f / sqrtf((float)DH), window);
+                                                 Hkv, 1.0f / sqrtf((float)DH), window, lse);
   return hipGetLastError();
 }
 
@@ -453,20 +460,20 @@ bool attention_supported(int dt, int d_head) {
 
 hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
-                            int Hkv, int d_head, int dt, int window, hipStream_t s) {
+                            int Hkv, int d_head, int dt, int window, hipStream_t s, float *lse) {
   const int w = window > 0 && window < S ? window : 0;   // a window of S or more is no limit
   if (dt == DT_BF16) {
     switch (d_head) {
-      case 32: return run_bf16<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
-      case 64: return run_bf16<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
-      case 128: return run_bf16<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 32: return run_bf16<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
+      case 64: return run_bf16<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
+      case 128: return run_bf16<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
     }
   } else {
     switch (d_head) {
-      case 16: return run_f32<16>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
-      case 32: return run_f32<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
-      case 64: return run_f32<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
-      case 128: return run_f32<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, s);
+      case 16: return run_f32<16>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
+      case 32: return run_f32<32>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
+      case 64: return run_f32<64>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
+      case 128: return run_f32<128>(q, q_stride, k, v, kv_stride, o, o_stride, B, S, Hq, Hkv, w, lse, s);
     }
   }
   return hipErrorInvalidValue;

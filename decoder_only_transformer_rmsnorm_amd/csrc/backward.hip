@@ -12,8 +12,8 @@
 //    gradient summed per workgroup and the partials summed in a fixed order;
 //  * swiglu_fwd_kernel / swiglu_back_kernel: u = SiLU(a) c and (da, dc);
 //  * rope_inv_kernel: the backward of a rotation is the rotation by the opposite angle;
-//  * attention backward, flash style in fp32 vector arithmetic: attn_dq_kernel recomputes the
-//    row statistics (logsumexp) of each query and accumulates dq = sum_j P (dP - D) k / sqrt(dh)
+//  * attention backward, flash style in fp32 vector arithmetic: with each query row's
+//    logsumexp kept by the forward, attn_dq_kernel accumulates dq = sum_j P (dP - D) k / sqrt(dh)
 //    with D = rowsum(do * o); attn_dkdv_kernel accumulates dk and dv per key over the queries
 //    (and query heads of a group) that see it. The score matrix is never stored.
 //  * embed_back_kernel: scatter-add of the input gradient into the embedding rows;
@@ -277,12 +277,13 @@ __device__ __forceinline__ float row_dot(float v) {
   return v;
 }
 
-// grid (ceil(S/64), Hq, B); thread (row i of the block, part p)
+// grid (ceil(S/64), Hq, B); thread (row i of the block, part p). lse: each query row's
+// logsumexp, kept by the forward attention.
 template <typename T, int DH>
 __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dq_kernel(
     const T *__restrict__ qkv, int64_t ld, const T *__restrict__ o, int64_t ldo,
     const T *__restrict__ dout, int64_t lddo, T *__restrict__ dqkv, int S, int Hq, int Hkv,
-    int window, float scale, float *__restrict__ lse_out, float *__restrict__ dsum_out) {
+    int window, float scale, const float *__restrict__ lse_in, float *__restrict__ dsum_out) {
   constexpr int DPT = DH < 32 ? DH : 32, TPR = DH / DPT, NT = kAttnRows * TPR;
   const int qd = Hq * DH, kvd = Hkv * DH;
   const int h = blockIdx.y, b = blockIdx.z, g = h / (Hq / Hkv);
@@ -302,35 +303,14 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dq
     dq[e] = 0.f;
   }
   dsum = row_dot<TPR>(dsum);
-  __shared__ float ks[kAttnRows][DH + 1], vs[kAttnRows][DH + 1];
+  const float lse = lse_in[rq * Hq + h];
+  __shared__ __attribute__((aligned(16))) float ks[kAttnRows][DH];
+  __shared__ __attribute__((aligned(16))) float vs[kAttnRows][DH];
   const int i0 = blockIdx.x * kAttnRows;
   const int ilast = min(i0 + kAttnRows, S) - 1;
   const int jlo = window > 0 ? max(0, i0 - window + 1) : 0;
   const int jlo_row = window > 0 ? max(0, i - window + 1) : 0;
-  // pass 1: row max and sum over the visible keys -> logsumexp
-  float mx = -__builtin_inff(), se = 0.f;
-  for (int j0 = jlo - jlo % kAttnRows; j0 <= ilast; j0 += kAttnRows) {
-    __syncthreads();
-    for (int idx = tid; idx < kAttnRows * DH; idx += NT) {
-      const int jj = idx / DH, c = idx % DH, j = j0 + jj;
-      ks[jj][c] = j < S ? ld1(qkv + ((int64_t)b * S + j) * ld + qd + (int64_t)g * DH + c) : 0.f;
-    }
-    __syncthreads();
-    for (int jj = 0; jj < kAttnRows; ++jj) {
-      const int j = j0 + jj;
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) s += qv[e] * ks[jj][part * DPT + e];
-      s = row_dot<TPR>(s) * scale;
-      if (j <= i && j >= jlo_row) {
-        const float mn = fmaxf(mx, s);
-        se = se * expf(mx - mn) + expf(s - mn);
-        mx = mn;
-      }
-    }
-  }
-  const float lse = mx + logf(se);
-  // pass 2: dq = sum_j P_ij (dP_ij - D_i) k_j scale
+  // dq = sum_j P_ij (dP_ij - D_i) k_j scale, P_ij = exp(q_i . k_j scale - lse_i)
   for (int j0 = jlo - jlo % kAttnRows; j0 <= ilast; j0 += kAttnRows) {
     __syncthreads();
     for (int idx = tid; idx < kAttnRows * DH; idx += NT) {
@@ -342,28 +322,35 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dq
     __syncthreads();
     for (int jj = 0; jj < kAttnRows; ++jj) {
       const int j = j0 + jj;
+      const f32x4_t *k4 = (const f32x4_t *)&ks[jj][part * DPT];
+      const f32x4_t *v4 = (const f32x4_t *)&vs[jj][part * DPT];
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) {
-        s += qv[e] * ks[jj][part * DPT + e];
-        dp += dov[e] * vs[jj][part * DPT + e];
+      for (int e4 = 0; e4 < DPT / 4; ++e4) {
+        const f32x4_t kk = k4[e4], vv = v4[e4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          s += qv[4 * e4 + x] * kk[x];
+          dp += dov[4 * e4 + x] * vv[x];
+        }
       }
       s = row_dot<TPR>(s) * scale;
       dp = row_dot<TPR>(dp);
       if (j <= i && j >= jlo_row) {
         const float ds = expf(s - lse) * (dp - dsum) * scale;
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) dq[e] += ds * ks[jj][part * DPT + e];
+        for (int e4 = 0; e4 < DPT / 4; ++e4) {
+          const f32x4_t kk = k4[e4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) dq[4 * e4 + x] += ds * kk[x];
+        }
       }
     }
   }
   if (live) {
 #pragma unroll
     for (int e = 0; e < DPT; ++e) st1(dqkv + rq * ld + (int64_t)h * DH + part * DPT + e, dq[e]);
-    if (part == 0) {
-      lse_out[rq * Hq + h] = lse;
-      dsum_out[rq * Hq + h] = dsum;
-    }
+    if (part == 0) dsum_out[rq * Hq + h] = dsum;
   }
 }
 
@@ -389,7 +376,8 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dk
     vv[e] = ld1(qkv + rk * ld + qd + kvd + (int64_t)g * DH + c);
     dk[e] = dv[e] = 0.f;
   }
-  __shared__ float qs[kAttnRows][DH + 1], ds_[kAttnRows][DH + 1];
+  __shared__ __attribute__((aligned(16))) float qs[kAttnRows][DH];
+  __shared__ __attribute__((aligned(16))) float ds_[kAttnRows][DH];
   __shared__ float ls[kAttnRows], dsm[kAttnRows];
   const int j0b = blockIdx.x * kAttnRows;
   const int jlast = min(j0b + kAttnRows, S) - 1;
@@ -413,11 +401,17 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dk
       __syncthreads();
       for (int ii = 0; ii < kAttnRows; ++ii) {
         const int i = i0 + ii;
+        const f32x4_t *q4 = (const f32x4_t *)&qs[ii][part * DPT];
+        const f32x4_t *d4 = (const f32x4_t *)&ds_[ii][part * DPT];
         float s = 0.f, dp = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) {
-          s += qs[ii][part * DPT + e] * kv[e];
-          dp += ds_[ii][part * DPT + e] * vv[e];
+        for (int e4 = 0; e4 < DPT / 4; ++e4) {
+          const f32x4_t qq = q4[e4], dd = d4[e4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            s += qq[x] * kv[4 * e4 + x];
+            dp += dd[x] * vv[4 * e4 + x];
+          }
         }
         s = row_dot<TPR>(s) * scale;
         dp = row_dot<TPR>(dp);
@@ -426,9 +420,13 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dk
           const float p = expf(s - ls[ii]);
           const float dsv = p * (dp - dsm[ii]) * scale;
 #pragma unroll
-          for (int e = 0; e < DPT; ++e) {
-            dv[e] += p * ds_[ii][part * DPT + e];
-            dk[e] += dsv * qs[ii][part * DPT + e];
+          for (int e4 = 0; e4 < DPT / 4; ++e4) {
+            const f32x4_t qq = q4[e4], dd = d4[e4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              dv[4 * e4 + x] += p * dd[x];
+              dk[4 * e4 + x] += dsv * qq[x];
+            }
           }
         }
       }
@@ -515,7 +513,7 @@ __global__ void adamw_kernel(float *__restrict__ p, bf16_t *__restrict__ pb,
 template <typename T, int DH>
 hipError_t run_attn_back(const void *qkv, int64_t ld, const void *o, int64_t ldo,
                          const void *dout, int64_t lddo, void *dqkv, int B, int S, int Hq,
-                         int Hkv, int window, float *lse, float *dsum, hipStream_t s) {
+                         int Hkv, int window, const float *lse, float *dsum, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)DH);
   const dim3 gq(nblk(S, kAttnRows), Hq, B), gk(nblk(S, kAttnRows), Hkv, B);
   constexpr int NT = kAttnRows * (DH / (DH < 32 ? DH : 32));
@@ -655,8 +653,8 @@ bool attention_backward_supported(int d_head) {
 
 hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o, int64_t ldo,
                                      const void *dout, int64_t lddo, void *dqkv, int B, int S,
-                                     int Hq, int Hkv, int d_head, int dt, int window, float *lse,
-                                     float *dsum, hipStream_t s) {
+                                     int Hq, int Hkv, int d_head, int dt, int window,
+                                     const float *lse, float *dsum, hipStream_t s) {
   if ((int64_t)B * S == 0) return hipSuccess;
   if (B > 65535 || Hq > 65535) return hipErrorInvalidValue;
   const int w = window > 0 && window < S ? window : 0;

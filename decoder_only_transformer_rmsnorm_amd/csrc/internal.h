@@ -63,9 +63,11 @@ hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
 
 // ---- attention (attention.hip)
 // window > 0: query s sees keys s - window + 1 .. s only (window >= S or 0: full causal).
+// lse (nullable): (B*S, Hq) fp32, each query row's logsumexp of its scaled scores.
 hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, const void *v,
                             int64_t kv_stride, void *o, int64_t o_stride, int B, int S, int Hq,
-                            int Hkv, int d_head, int dt, int window, hipStream_t s);
+                            int Hkv, int d_head, int dt, int window, hipStream_t s,
+                            float *lse = nullptr);
 bool attention_supported(int dt, int d_head);
 // ---- incremental decoding (decode.hip), bf16 only
 struct DecodeGemmArgs {
@@ -132,12 +134,12 @@ hipError_t launch_rope_inverse(void *x, int dt, int64_t row_stride, const int32_
                                int64_t rows, int S, int H, int d_head, const float *cos_sin,
                                int max_seq, hipStream_t s);
 bool attention_backward_supported(int d_head);
-// dq, dk, dv into the q | k | v columns of dqkv (same layout as qkv); lse, dsum: (B*S, Hq)
-// fp32 scratch (row logsumexp and rowsum(do * o)).
+// dq, dk, dv into the q | k | v columns of dqkv (same layout as qkv); lse: (B*S, Hq) row
+// logsumexp kept by the forward (launch_attention's lse); dsum: (B*S, Hq) fp32 scratch.
 hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o, int64_t ldo,
                                      const void *dout, int64_t lddo, void *dqkv, int B, int S,
-                                     int Hq, int Hkv, int d_head, int dt, int window, float *lse,
-                                     float *dsum, hipStream_t s);
+                                     int Hq, int Hkv, int d_head, int dt, int window,
+                                     const float *lse, float *dsum, hipStream_t s);
 hipError_t launch_embed_backward(const int32_t *ids, int64_t n, int vocab, int d, const float *dx,
                                  float *dE, hipStream_t s);
 int sumsq_parts();
