@@ -253,6 +253,13 @@ def main() -> int:
             qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),
             cfg.n_heads, cfg.n_kv_heads, cfg.d_head, o=o.view(B, S, qd),
             q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd), n, stream), att_flops, "mfma", None)
+        # sliding-window attention over the same q, k, v (band of 256 keys per query)
+        win = 256
+        rec(f"attention_window{win}", time_launches(lambda: tfm.tfm_sliding_window_attention(
+            qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),
+            cfg.n_heads, cfg.n_kv_heads, cfg.d_head, win, o=o.view(B, S, qd),
+            q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd), n, stream),
+            accounting.attention_flops(B, S, cfg.n_heads, cfg.d_head, win), "mfma", None)
         rec("gemm_out_residual", time_launches(lambda: tfm.tfm_linear(o, L0["wo"], residual=xres, y=xres), n, stream),
             flops_gemm(D, qd), "mfma", None)
         rec("swiglu_ffn", time_launches(lambda: tfm.lib().tfm_swiglu_ffn(

@@ -9,6 +9,19 @@ counts attention as two full T x T products per head; the causal path only needs
 from __future__ import annotations
 
 
+def visible_pairs(seq: int, window: int = 0) -> int:
+    """(query, key) pairs one head of one sequence scores: query s sees keys
+    max(0, s - window + 1) .. s (all s + 1 of them when window is 0 or >= seq)."""
+    if window <= 0 or window >= seq:
+        return seq * (seq + 1) // 2
+    return window * (window + 1) // 2 + (seq - window) * window
+
+
+def attention_flops(batch: int, seq: int, n_heads: int, d_head: int, window: int = 0) -> int:
+    """Two products (Q.K^T and P.V) of 2 * d_head flops per visible pair and head."""
+    return 4 * d_head * n_heads * batch * visible_pairs(seq, window)
+
+
 def forward_flops(cfg, batch: int | None = None, seq: int | None = None,
                   attention: str = "causal") -> dict:
     B = cfg.batch if batch is None else batch
@@ -20,7 +33,7 @@ def forward_flops(cfg, batch: int | None = None, seq: int | None = None,
     out = 2 * M * qd * D
     ffn = 2 * M * D * 2 * F + 2 * M * F * D
     if attention == "causal":
-        att = 4 * cfg.d_head * cfg.n_heads * B * S * (S + 1) // 2
+        att = attention_flops(B, S, cfg.n_heads, cfg.d_head)
     elif attention == "full":
         att = 4 * cfg.d_head * cfg.n_heads * B * S * S
     else:

@@ -16,12 +16,15 @@
 //    4 consecutive output columns of one row m = l % 16. The 4 partial sums meet in LDS.
 //    Epilogues: store (logits), residual add, SiLU(gate) * up, and q / k / v with RoPE where
 //    k and v go straight to the cache slot of the token's position.
-//  * dec_attn_kernel: one workgroup per (sequence, kv head, chunk of 128 cached keys); all
-//    query heads of the group share each K / V row read (grouped-query attention). Scores and
-//    softmax in fp32 (log2 domain); the partial (max, sum, unnormalised output) of each chunk
-//    goes to the workspace and dec_combine_kernel merges the chunks in chunk order.
+//  * dec_attn_kernel: one workgroup per (split of the visible keys, kv head, sequence); its
+//    waves take 64-key chunks with coalesced loads, and all query heads of the group share each
+//    K / V row read (grouped-query attention). Scores and softmax in fp32 (log2 domain), online
+//    over a wave's chunks; the waves merge in LDS. With one split per sequence and head (short
+//    caches, or many sequences) the workgroup writes the output; otherwise each split leaves
+//    a partial (max, sum, unnormalised output) and dec_combine_kernel merges them in order.
 //  * kv_store_kernel: after a prefill block's QKV projection, copies the rotated k and v rows
 //    into the cache slots of their positions.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -30,9 +33,11 @@
 namespace tfm {
 namespace {
 
-constexpr int kDecKeys = 128;   // cached keys (and threads) per attention workgroup
-constexpr int kDecMaxGroup = 8; // query heads per kv head supported by the decode kernel
-constexpr int kMaxChunks = 1024; // chunks per sequence the merge holds (cache_seq <= 131072)
+constexpr int kDecMaxGroup = 8;      // query heads per kv head supported by the decode kernel
+constexpr int kDecMaxCache = 131072; // largest cache (slots per sequence) decoding supports
+constexpr int kDecTargetGroups = 256;  // attention workgroups when chunks are scarce
+constexpr int kDecBusyWaves = 1024;    // chunk waves that keep HBM busy without more splits
+constexpr int kMaxSplits = 1024;   // split records per (sequence, head) the merge holds
 constexpr float kLog2e = 1.4426950408889634f;
 
 inline unsigned grid1(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -49,9 +54,12 @@ __device__ __forceinline__ f32x4_t rope4(f32x4_t v, const float *cos_sin, int po
                  x2 * cs[3] + x3 * cs[2]};
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
+// NWV waves share the workgroup's 16 columns and split K; each wave keeps the loads of U
+// 32-wide k steps in flight together
+template <int EPI, int NWV, int U>
+__global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
   constexpr int NA = EPI == EPI_SWIGLU ? 2 : 1;   // weight row sets (gate, up)
+  constexpr int NT = 64 * NWV;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, kc = lane >> 4;
   const int nb0 = blockIdx.x * 16;     // first output column (SwiGLU: hidden unit)
@@ -80,26 +88,43 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
   const int mr = m0 + r16;
   const bool xok = mr < g.M;
   const bf16_t *xrow = (const bf16_t *)g.x + (int64_t)(xok ? mr : 0) * g.ldx;
-  // fused RMSNorm ("Transformer 篇" 5.6): 1 / rms of each of the 16 rows, wave w takes rows
-  // 4w .. 4w+3; the operand is then x * inv * g, rounded once to bf16
+  const int nks = (g.K + 31) / 32;   // 32-wide k steps; wave w takes steps w, w + NWV, ...
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  u32x4_t wa[U][NA];
+  auto load_w = [&](int ks0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (ks0 + NWV * u) * 32 + kc * 8;   // K % 8 == 0: a chunk is all in or out
+      const bool kok = ks0 + NWV * u < nks && k < g.K;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) wa[u][a] = wok[a] && kok ? ld16(wrow[a] + k) : zero;
+    }
+  };
+  load_w(w);   // the first weights are in flight while the norm is computed
+
+  // fused RMSNorm ("Transformer 篇" 5.6): 1 / rms of each of the 16 rows (NT / 16 threads
+  // per row); the operand is then x * inv * g, rounded once to bf16
   __shared__ float inv_rms[16];
   const bool fuse = g.norm_x != nullptr;
   const float *nrow = fuse ? g.norm_x + (int64_t)(xok ? mr : 0) * g.ldx : nullptr;
-  if (fuse) {   // 16 threads per row, each summing every 16th group of 4 columns
-    const int row = threadIdx.x >> 4, part = threadIdx.x & 15;
+  if (fuse) {
+    constexpr int TPR = NT / 16;
+    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
     const int m = m0 + row;
     float ss = 0.f;
     if (m < g.M) {
       const float *xr = g.norm_x + (int64_t)m * g.ldx;
-#pragma unroll 4
-      for (int k = 4 * part; k < g.K; k += 64) {
+#pragma unroll 2
+      for (int k = 4 * part; k < g.K; k += 4 * TPR) {
         const f32x4_t v = load4(xr + k);
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
       }
     }
-    for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if (part == 0) inv_rms[row] = rsqrtf(ss / (float)g.K + g.eps);
-    __syncthreads();
+    // LDS only: the weight loads above stay in flight across this barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   const float rinv = fuse ? inv_rms[r16] : 0.f;
   auto x_chunk = [&](int k) -> u32x4_t {   // 8 activations of row mr from column k
@@ -114,18 +139,13 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
   f32x4_t acc[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) acc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  const int nks = (g.K + 31) / 32;   // 32-wide k steps; wave w takes steps w, w + 4, ...
-  constexpr int U = 4;               // steps whose loads are in flight together
-  for (int ks0 = w; ks0 < nks; ks0 += 4 * U) {
-    u32x4_t xa[U], wa[U][NA];
+  for (int ks0 = w; ks0 < nks; ks0 += NWV * U) {
+    u32x4_t xa[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (ks0 + 4 * u) * 32 + kc * 8;   // K % 8 == 0: a chunk is all in or out
-      const bool kok = ks0 + 4 * u < nks && k < g.K;
+      const int k = (ks0 + NWV * u) * 32 + kc * 8;
+      const bool kok = ks0 + NWV * u < nks && k < g.K;
       xa[u] = xok && kok ? x_chunk(k) : zero;
-#pragma unroll
-      for (int a = 0; a < NA; ++a) wa[u][a] = wok[a] && kok ? ld16(wrow[a] + k) : zero;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -134,20 +154,23 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
         acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u][a]),
                                                         __builtin_bit_cast(bf16x8_t, xa[u]),
                                                         acc[a], 0, 0, 0);
+    if (ks0 + NWV * U < nks) load_w(ks0 + NWV * U);
   }
 
-  // the four waves' partial sums meet in LDS; wave 0 finishes
-  __shared__ __attribute__((aligned(16))) f32x4_t red[3][NA][64];
-  if (w > 0) {
+  // the waves' partial sums meet in LDS; wave 0 finishes
+  if constexpr (NWV > 1) {
+    __shared__ __attribute__((aligned(16))) f32x4_t red[NWV - 1][NA][64];
+    if (w > 0) {
 #pragma unroll
-    for (int a = 0; a < NA; ++a) red[w - 1][a][lane] = acc[a];
+      for (int a = 0; a < NA; ++a) red[w - 1][a][lane] = acc[a];
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int j = 0; j < NWV - 1; ++j) acc[a] += red[j][a][lane];
   }
-  __syncthreads();
-  if (w > 0) return;
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) acc[a] += red[j][a][lane];
 
   // lane holds columns n .. n+3 of row m
   const int m = m0 + r16;
@@ -202,74 +225,92 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DecodeGemmArgs g) {
 }
 
 // ---- decode attention
-// One workgroup per (sequence b, kv head grp, chunk c of 128 cached keys). Every thread first
-// loads its key's K and V rows (all loads in flight together); V goes to LDS for the P.V pass.
-// The chunk's partial (max, sum, unnormalised output) per query head goes to `part`;
-// dec_combine_kernel merges the chunks in chunk order.
-template <int DH>
-__global__ __launch_bounds__(kDecKeys) void dec_attn_kernel(
+// Workgroup = (split s, kv head grp, sequence b) with NWV waves; a wave takes 64-key chunks of
+// the visible keys (chunk c covers keys t0 + 64 c ..), chunks s*cps .. (s+1)*cps - 1 of the
+// split in steps of NWV. Loads are coalesced: with PPR = d_head / 8 pieces of 8 elements per
+// row and RPI = 64 / PPR rows per 1 KB, load j of a chunk gives lane l piece l % PPR of key
+// row RPI j + l / PPR. The lane's q piece (8 elements per head) sits in registers; the dot
+// products are summed over the PPR lanes of a row, the chunk maximum over the row groups.
+// Softmax is online over the wave's chunks (fp32, log2 domain); p . v accumulates per lane
+// and is summed over the row groups once at the end. The waves' (max, sum, output) meet in
+// LDS: with one split the workgroup writes the normalised output, otherwise a partial record
+// per query head that dec_combine_kernel merges in split order.
+constexpr int dec_regs(int dh, int g) { return 8 * g + dh + (dh / 8) * g + 8 * g + 24; }
+constexpr int dec_waves(int dh, int g) {
+  return dec_regs(dh, g) <= 128 ? 16 : dec_regs(dh, g) <= 256 ? 8 : 4;
+}
+
+template <int DH, int GM, int NWV>
+__global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
     const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ kc,
     const bf16_t *__restrict__ vc, const int32_t *__restrict__ positions, int Hq, int Hkv,
-    int cache_seq, int window, float scale_log2, float *__restrict__ part, int n_ch,
+    int cache_seq, int window, int cps, float scale_log2, float *__restrict__ part, int n_split,
     bf16_t *__restrict__ o, int64_t o_stride) {
-  constexpr int PS = 2 + DH;               // partial record: max, sum, output
-  constexpr int DC = DH / 8;               // 16-byte chunks per K / V row
-  constexpr int D4 = DH / 4;               // threads per value row in the P.V pass
-  constexpr int TG = kDecKeys / D4;        // key groups in the P.V pass
-  constexpr int NW = kDecKeys / 64;        // waves (one thread per key of the chunk)
-  const int c = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  constexpr int PPR = DH / 8, RPI = 64 / PPR, NJ = PPR, PS = 2 + DH;
+  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int nwv = blockDim.x >> 6;   // waves of this launch, <= NWV
+  const int pc = lane % PPR, rg = lane / PPR;
   const int pos = positions[b];
-  const bool valid = pos >= 0 && pos < cache_seq;
-  if (!valid) {   // no cache slot: NaN output for the group's heads
-    if (c == 0)
-      for (int i = tid; i < G * DH; i += kDecKeys)
+  if (pos < 0 || pos >= cache_seq) {   // no cache slot: NaN output for the group's heads
+    if (split == 0)
+      for (int i = tid; i < G * DH; i += 64 * nwv)
         o[(int64_t)b * o_stride + (int64_t)grp * G * DH + i] = f32_to_bf16(__builtin_nanf(""));
     return;
   }
   const int n = pos + 1;
   const int t0 = window > 0 && n > window ? n - window : 0;
-  const int used = (n - t0 + kDecKeys - 1) / kDecKeys;
-  if (c >= used) return;
-  const int ks = t0 + c * kDecKeys;
-  const int cnt = min(kDecKeys, n - ks);
+  const int nch = (n - t0 + 63) / 64;
+  const int c_end = min((split + 1) * cps, nch);
 
-  __shared__ float qs[kDecMaxGroup][DH];
-  __shared__ float sc[kDecMaxGroup][kDecKeys];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[kDecKeys][DH];
-  __shared__ __attribute__((aligned(16))) float red[TG][DH];
-  __shared__ float stat[kDecMaxGroup][2];
-  __shared__ float wred[NW][kDecMaxGroup];
-
-  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this head
-  u32x4_t kr[DC], vr[DC];
-  if (tid < cnt) {
-    const bf16_t *kp = kc + (head + ks + tid) * DH;
-    const bf16_t *vp = vc + (head + ks + tid) * DH;
+  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this kv head
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  // this lane's q pieces (raw bf16); converted inside the loop, so the first chunk's K / V
+  // loads are issued before anything waits on q
+  u32x4_t qraw[GM];
 #pragma unroll
-    for (int j = 0; j < DC; ++j) kr[j] = ld16(kp + 8 * j);
+  for (int h = 0; h < GM; ++h)
+    qraw[h] = h < G ? ld16(q + (int64_t)b * q_stride + (int64_t)(grp * G + h) * DH + 8 * pc) : zero;
+  float m[GM], l[GM], acc[GM][8];
 #pragma unroll
-    for (int j = 0; j < DC; ++j) vr[j] = ld16(vp + 8 * j);
+  for (int h = 0; h < GM; ++h) {
+    m[h] = -__builtin_inff();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  for (int i = tid; i < G * DH; i += kDecKeys) {
-    const int h = i / DH, d = i % DH;
-    qs[h][d] = bf16_to_f32(q[(int64_t)b * q_stride + (int64_t)(grp * G + h) * DH + d]) *
-               scale_log2;
-  }
-  if (tid < cnt) {
+  for (int c = split * cps + w; c < c_end; c += nwv) {
+    const int k0 = t0 + 64 * c;
+    // rows past the last visible key load that key again (no branch around the loads) and
+    // are zeroed afterwards
+    u32x4_t kr[NJ], vr[NJ];
 #pragma unroll
-    for (int j = 0; j < DC; ++j) *(u32x4_t *)&vs[tid][8 * j] = vr[j];
-  }
-  __syncthreads();
-
-  // scores (log2 units): thread t takes key ks + t
-  if (tid < cnt) {
-    float s[kDecMaxGroup];
+    for (int j = 0; j < NJ; ++j)
+      kr[j] = ld16(kc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
 #pragma unroll
-    for (int h = 0; h < kDecMaxGroup; ++h) s[h] = 0.f;
+    for (int j = 0; j < NJ; ++j)
+      vr[j] = ld16(vc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
 #pragma unroll
-    for (int j = 0; j < DC; ++j) {
+    for (int j = 0; j < NJ; ++j)
+      if (k0 + RPI * j + rg >= n) vr[j] = zero;
+    // q is used after this chunk's loads are issued: the empty statement keeps its conversion
+    // (and the wait for it) in the loop, below the loads
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < GM; ++h) asm volatile("" : "+v"(qraw[h]));
+    float qf[GM][8];   // q pieces in log2 units
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[h][2 * e] = __uint_as_float(qraw[h][e] << 16) * scale_log2;
+        qf[h][2 * e + 1] = __uint_as_float(qraw[h][e] & 0xffff0000u) * scale_log2;
+      }
+    // scores of the lane's rows, summed over the PPR lanes of each row
+    float sc[NJ][GM];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
       float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -277,103 +318,117 @@ __global__ __launch_bounds__(kDecKeys) void dec_attn_kernel(
         kf[2 * e + 1] = __uint_as_float(kr[j][e] & 0xffff0000u);
       }
 #pragma unroll
-      for (int h = 0; h < kDecMaxGroup; ++h)
-        if (h < G) {
+      for (int h = 0; h < GM; ++h) {
+        float d = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(qs[h][8 * j + e], kf[e], s[h]);
+        for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
+#pragma unroll
+        for (int x = 1; x < PPR; x <<= 1) d += __shfl_xor(d, x);
+        sc[j][h] = k0 + RPI * j + rg < n ? d : -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      float mx = sc[0][h];
+#pragma unroll
+      for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, sc[j][h]);
+#pragma unroll
+      for (int x = PPR; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+      const float mn = fmaxf(m[h], mx);        // finite: the chunk has a visible key
+      const float alpha = exp2f(m[h] - mn);    // 0 for the first chunk
+      m[h] = mn;
+      float ls = 0.f;
+      float a8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a8[e] = acc[h][e] * alpha;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float p = exp2f(sc[j][h] - mn);
+        ls += p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a8[2 * e] = __builtin_fmaf(p, __uint_as_float(vr[j][e] << 16), a8[2 * e]);
+          a8[2 * e + 1] = __builtin_fmaf(p, __uint_as_float(vr[j][e] & 0xffff0000u), a8[2 * e + 1]);
         }
-    }
+      }
+      l[h] = l[h] * alpha + ls;
 #pragma unroll
-    for (int h = 0; h < kDecMaxGroup; ++h)
-      if (h < G) sc[h][tid] = s[h];
-  }
-  // per head: max over the chunk, then p = 2^(s - max) and its sum
-  const int wv = tid >> 6, lane = tid & 63;
-  for (int h = 0; h < G; ++h) {
-    float mx = -__builtin_inff();
-    __syncthreads();
-    for (int t = tid; t < cnt; t += kDecKeys) mx = fmaxf(mx, sc[h][t]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) wred[wv][h] = mx;
-    __syncthreads();
-    mx = wred[0][h];
-    for (int j = 1; j < NW; ++j) mx = fmaxf(mx, wred[j][h]);
-    float sum = 0.f;
-    for (int t = tid; t < cnt; t += kDecKeys) {
-      const float p = exp2f(sc[h][t] - mx);
-      sc[h][t] = p;
-      sum += p;
+      for (int e = 0; e < 8; ++e) acc[h][e] = a8[e];
     }
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    __syncthreads();
-    if (lane == 0) wred[wv][h] = sum;
-    __syncthreads();
-    if (tid == 0) {
-      stat[h][0] = mx;
-      float tot = 0.f;
-      for (int j = 0; j < NW; ++j) tot += wred[j][h];
-      stat[h][1] = tot;
+  }
+  // sums over the row groups (lanes with the same piece)
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int x = PPR; x < 64; x <<= 1) {
+      l[h] += __shfl_xor(l[h], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], x);
+    }
+
+  __shared__ float wm[NWV][GM], wl[NWV][GM];
+  __shared__ __attribute__((aligned(16))) float wo[NWV][GM][DH];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (lane == 0) {
+      wm[w][h] = m[h];
+      wl[w][h] = l[h];
+    }
+    if (rg == 0) {
+      *(f32x4_t *)&wo[w][h][8 * pc] = f32x4_t{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *(f32x4_t *)&wo[w][h][8 * pc + 4] = f32x4_t{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
     }
   }
   __syncthreads();
-
-  // P.V from LDS: thread (key group tg, 4 columns d4) sums over keys tg, tg + TG, ...
-  const int d4 = tid % D4, tg = tid / D4;
-  f32x4_t acc[kDecMaxGroup];
-#pragma unroll
-  for (int h = 0; h < kDecMaxGroup; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int t = tg; t < cnt; t += TG) {
-    const u32x2_t raw = *(const u32x2_t *)&vs[t][4 * d4];
-    const f32x4_t vv = {__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
-                        __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
-#pragma unroll
-    for (int h = 0; h < kDecMaxGroup; ++h)
-      if (h < G) acc[h] += sc[h][t] * vv;
-  }
-  float *rec0 = part + (((int64_t)b * Hq + grp * G) * n_ch + c) * PS;   // head h: + h n_ch PS
-  for (int h = 0; h < G; ++h) {
-    __syncthreads();
-    *(f32x4_t *)&red[tg][4 * d4] = acc[h];
-    __syncthreads();
-    for (int d = tid; d < DH; d += kDecKeys) {
-      float sum = 0.f;
-      for (int j = 0; j < TG; ++j) sum += red[j][d];
-      rec0[(int64_t)h * n_ch * PS + 2 + d] = sum;
+  for (int i = tid; i < G * DH; i += 64 * nwv) {
+    const int h = i / DH, d = i % DH;
+    float M = -__builtin_inff();
+    for (int v = 0; v < nwv; ++v) M = fmaxf(M, wm[v][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int v = 0; v < nwv; ++v) {
+        const float f = exp2f(wm[v][h] - M);   // 0 for a wave without keys
+        L += f * wl[v][h];
+        O += f * wo[v][h][d];
+      }
     }
-    if (tid == 0) {
-      rec0[(int64_t)h * n_ch * PS + 0] = stat[h][0];
-      rec0[(int64_t)h * n_ch * PS + 1] = stat[h][1];
+    if (n_split == 1) {
+      o[(int64_t)b * o_stride + (int64_t)(grp * G + h) * DH + d] = f32_to_bf16(O / L);
+    } else {
+      float *rec = part + (((int64_t)b * Hq + grp * G + h) * n_split + split) * PS;
+      rec[2 + d] = O;
+      if (d == 0) {
+        rec[0] = M;
+        rec[1] = L;
+      }
     }
   }
-
 }
 
-// Merges the chunk partials of one (sequence, query head) in chunk order. (A merge by the
-// last chunk workgroup would need device-scope fences, which write back the XCD's L2.)
+// Merges the split records of one (sequence, query head) in split order; a split without
+// visible keys holds (-inf, 0, 0). (A merge by the last workgroup would need device-scope
+// fences, which write back the XCD's L2.)
 template <int DH>
 __global__ __launch_bounds__(128) void dec_combine_kernel(const float *__restrict__ part,
                                                           const int32_t *__restrict__ positions,
-                                                          int Hq, int cache_seq, int window,
-                                                          int n_ch, bf16_t *__restrict__ o,
+                                                          int Hq, int cache_seq, int n_split,
+                                                          bf16_t *__restrict__ o,
                                                           int64_t o_stride) {
   constexpr int PS = 2 + DH;
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int pos = positions[b];
   if (pos < 0 || pos >= cache_seq) return;   // the attention kernel wrote the NaN row
-  const int n = pos + 1;
-  const int t0 = window > 0 && n > window ? n - window : 0;
-  const int used = (n - t0 + kDecKeys - 1) / kDecKeys;
-  const float *rec = part + (int64_t)bh * n_ch * PS;
-  // chunk weights 2^(m_c - max) and the denominator, computed once in LDS
-  __shared__ float wgt[kMaxChunks];
+  const float *rec = part + (int64_t)bh * n_split * PS;
+  // split weights 2^(m_s - max) and the denominator, computed once in LDS
+  __shared__ float wgt[kMaxSplits];
   __shared__ float den;
-  for (int c = threadIdx.x; c < used; c += blockDim.x) wgt[c] = rec[c * PS];
+  for (int c = threadIdx.x; c < n_split; c += blockDim.x) wgt[c] = rec[c * PS];
   __syncthreads();
   if (threadIdx.x == 0) {
     float mx = -__builtin_inff();
-    for (int c = 0; c < used; ++c) mx = fmaxf(mx, wgt[c]);
+    for (int c = 0; c < n_split; ++c) mx = fmaxf(mx, wgt[c]);
     float l = 0.f;
-    for (int c = 0; c < used; ++c) {
+    for (int c = 0; c < n_split; ++c) {
       wgt[c] = exp2f(wgt[c] - mx);
       l += wgt[c] * rec[c * PS + 1];
     }
@@ -383,7 +438,7 @@ __global__ __launch_bounds__(128) void dec_combine_kernel(const float *__restric
   for (int d = threadIdx.x; d < DH; d += blockDim.x) {
     float num = 0.f;
 #pragma unroll 4
-    for (int c = 0; c < used; ++c) num += wgt[c] * rec[c * PS + 2 + d];
+    for (int c = 0; c < n_split; ++c) num += wgt[c] * rec[c * PS + 2 + d];
     o[(int64_t)b * o_stride + (int64_t)h * DH + d] = f32_to_bf16(num / den);
   }
 }
@@ -411,40 +466,84 @@ __global__ void kv_store_kernel(const bf16_t *__restrict__ qkv, int64_t ld, int 
   *(u32x4_t *)dst = ld16(qkv + r * ld + qd + c);
 }
 
-template <int DH>
+// Splits per (sequence, kv head) and waves per split: a split's waves take its 64-key chunks
+// (at most NWV waves, each looping when a split has more chunks than waves).
+template <int DH, int GM>
 hipError_t run_dec_attn(const void *q, int64_t q_stride, const void *kc, const void *vc,
                         const int32_t *positions, int B, int Hq, int Hkv, int cache_seq,
-                        int window, float *part, void *o, int64_t o_stride,
-                        hipStream_t s) {
-  const int n_ch = decode_chunks(cache_seq);
+                        int window, float *part, void *o, int64_t o_stride, hipStream_t s) {
+  constexpr int NWV = dec_waves(DH, GM);
+  const int span = window > 0 ? std::min(window, cache_seq) : cache_seq;
+  const int chunks = (span + 63) / 64;
+  const int64_t groups = (int64_t)B * Hkv;
+  // Fewest splits that give every chunk a wave: a split costs the merge launch, which at the
+  // d768 workload's 1001-key context outweighs what spreading the cache over more CUs gains
+  // (measured: 96 workgroups 10.8 us; 768 workgroups 8.4 us + 3.7 us merge). More splits only
+  // while the chunk waves are too few to keep the memory system busy.
+  int n_split = (chunks + NWV - 1) / NWV;
+  if (groups * chunks < kDecBusyWaves)
+    n_split = (int)std::max<int64_t>(n_split, std::min<int64_t>(chunks, (kDecTargetGroups + groups - 1) / groups));
+  n_split = std::min(n_split, decode_chunks(cache_seq));
+  const int cps = (chunks + n_split - 1) / n_split;
+  n_split = (chunks + cps - 1) / cps;
+  const int waves = std::min(NWV, cps);
   const float sl2 = kLog2e / sqrtf((float)DH);
-  dec_attn_kernel<DH><<<dim3(n_ch, Hkv, B), kDecKeys, 0, s>>>(
+  dec_attn_kernel<DH, GM, NWV><<<dim3(n_split, Hkv, B), 64 * waves, 0, s>>>(
       (const bf16_t *)q, q_stride, (const bf16_t *)kc, (const bf16_t *)vc, positions, Hq, Hkv,
-      cache_seq, window, sl2, part, n_ch, (bf16_t *)o, o_stride);
-  dec_combine_kernel<DH><<<B * Hq, 128, 0, s>>>(part, positions, Hq, cache_seq, window, n_ch,
-                                                (bf16_t *)o, o_stride);
+      cache_seq, window, cps, sl2, part, n_split, (bf16_t *)o, o_stride);
+  if (n_split > 1)
+    dec_combine_kernel<DH><<<B * Hq, 128, 0, s>>>(part, positions, Hq, cache_seq, n_split,
+                                                  (bf16_t *)o, o_stride);
   return hipGetLastError();
+}
+
+template <int DH>
+hipError_t run_dec_attn_g(const void *q, int64_t q_stride, const void *kc, const void *vc,
+                          const int32_t *positions, int B, int Hq, int Hkv, int cache_seq,
+                          int window, float *part, void *o, int64_t o_stride, hipStream_t s) {
+  const int G = Hq / Hkv;
+  if (G == 1)
+    return run_dec_attn<DH, 1>(q, q_stride, kc, vc, positions, B, Hq, Hkv, cache_seq, window,
+                               part, o, o_stride, s);
+  if (G == 2)
+    return run_dec_attn<DH, 2>(q, q_stride, kc, vc, positions, B, Hq, Hkv, cache_seq, window,
+                               part, o, o_stride, s);
+  if (G <= 4)
+    return run_dec_attn<DH, 4>(q, q_stride, kc, vc, positions, B, Hq, Hkv, cache_seq, window,
+                               part, o, o_stride, s);
+  return run_dec_attn<DH, 8>(q, q_stride, kc, vc, positions, B, Hq, Hkv, cache_seq, window,
+                             part, o, o_stride, s);
 }
 
 }  // namespace
 
-int decode_chunks(int cache_seq) { return (cache_seq + kDecKeys - 1) / kDecKeys; }
-int decode_max_cache() { return kDecKeys * kMaxChunks; }
+int decode_chunks(int cache_seq) { return std::min(kMaxSplits, (cache_seq + 63) / 64); }
+int decode_max_cache() { return kDecMaxCache; }
 bool decode_group_supported(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= kDecMaxGroup; }
+
+template <int NWV, int U>
+hipError_t run_dgemm(int epi, const DecodeGemmArgs &g, dim3 grid, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: dgemm_kernel<EPI_STORE, NWV, U><<<grid, 64 * NWV, 0, s>>>(g); break;
+    case EPI_RESIDUAL: dgemm_kernel<EPI_RESIDUAL, NWV, U><<<grid, 64 * NWV, 0, s>>>(g); break;
+    case EPI_SWIGLU: dgemm_kernel<EPI_SWIGLU, NWV, U><<<grid, 64 * NWV, 0, s>>>(g); break;
+    case EPI_QKV_CACHE: dgemm_kernel<EPI_QKV_CACHE, NWV, U><<<grid, 64 * NWV, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
   const int cols = epi == EPI_SWIGLU ? g.n0 : g.N;
   const dim3 grid(grid1(cols, 16), grid1(g.M, 16));
   if (grid.y > 65535) return hipErrorInvalidValue;
-  switch (epi) {
-    case EPI_STORE: dgemm_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g); break;
-    case EPI_RESIDUAL: dgemm_kernel<EPI_RESIDUAL><<<grid, 256, 0, s>>>(g); break;
-    case EPI_SWIGLU: dgemm_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(g); break;
-    case EPI_QKV_CACHE: dgemm_kernel<EPI_QKV_CACHE><<<grid, 256, 0, s>>>(g); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // Few column blocks (the layers' projections): 8 waves split K with 8 steps each in flight,
+  // so one round of loads covers K <= 2048 on the few CUs that have work. Many blocks (the LM
+  // head) fill the chip anyway: 4 waves with 4 steps each keep the registers, and so the
+  // occupancy, of a streaming kernel.
+  if ((int64_t)grid.x * grid.y >= 1024) return run_dgemm<4, 4>(epi, g, grid, s);
+  return run_dgemm<8, 8>(epi, g, grid, s);
 }
 
 hipError_t launch_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
@@ -454,11 +553,11 @@ hipError_t launch_decode_attention(const void *q, int64_t q_stride, const void *
   if (B == 0) return hipSuccess;
   if (B > 65535 || Hkv > 65535) return hipErrorInvalidValue;
   switch (d_head) {
-    case 32: return run_dec_attn<32>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
+    case 32: return run_dec_attn_g<32>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
                                      cache_seq, window, part, o, o_stride, s);
-    case 64: return run_dec_attn<64>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
+    case 64: return run_dec_attn_g<64>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
                                      cache_seq, window, part, o, o_stride, s);
-    case 128: return run_dec_attn<128>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
+    case 128: return run_dec_attn_g<128>(q, q_stride, k_cache, v_cache, positions, B, Hq, Hkv,
                                        cache_seq, window, part, o, o_stride, s);
   }
   return hipErrorInvalidValue;

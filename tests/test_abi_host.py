@@ -303,7 +303,7 @@ def test_kv_cache_and_decode_validation(L):
 def test_decode_attention_validation(L):
     f = L.tfm_decode_attention
     need = L.tfm_decode_attention_workspace_bytes(2, 8, 64, 300)
-    assert need == -(-2 * 8 * 3 * 66 * 4 // 256) * 256          # 3 chunks of 128 keys
+    assert need == -(-2 * 8 * 5 * 66 * 4 // 256) * 256          # at most one split per 64 keys
     call = lambda q=P, qs=512, o=P, os=512, B=2, Hq=8, Hkv=2, dh=64, cs=300, W=0, ws=P, nb=need: f(
         q, qs, P, P, P, o, os, B, Hq, Hkv, dh, cs, W, ws, nb, None)
     assert call(Hkv=3) == SHAPE

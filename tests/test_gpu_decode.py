@@ -46,7 +46,9 @@ def head_major(c, Hkv, dh):
 # ---------------------------------------------------------------- decode attention
 @pytest.mark.parametrize("B,Hq,Hkv,dh,T,W", [(3, 4, 4, 64, 300, 0), (2, 8, 2, 32, 257, 0),
                                             (2, 16, 2, 128, 600, 0), (4, 4, 1, 64, 520, 100),
-                                            (1, 12, 12, 64, 1024, 0), (3, 8, 8, 32, 64, 7)])
+                                            (1, 12, 12, 64, 1024, 0), (3, 8, 8, 32, 64, 7),
+                                            (2, 6, 3, 64, 200, 0), (2, 12, 4, 32, 130, 50),
+                                            (8, 12, 12, 64, 1024, 0)])
 def test_decode_attention_matches_oracle(B, Hq, Hkv, dh, T, W):
     tfm = tfm_mod()
     say(f"decode attention B={B} Hq={Hq} Hkv={Hkv} dh={dh} cache={T} window={W}")
@@ -54,7 +56,7 @@ def test_decode_attention_matches_oracle(B, Hq, Hkv, dh, T, W):
     q = synth.round_to_bf16(g.normal(size=(B, Hq * dh)).astype(np.float32))
     k = synth.round_to_bf16(g.normal(size=(B, T, Hkv * dh)).astype(np.float32))
     v = synth.round_to_bf16(g.normal(size=(B, T, Hkv * dh)).astype(np.float32))
-    pos = np.array([T - 1, 0, 255, 256, 100, 511][:B]) % T
+    pos = np.array([T - 1, 0, 255, 256, 100, 511, 1000, 63][:B]) % T
     pos = pos.astype(np.int32)
     kc = to_dev(head_major(k, Hkv, dh), "bf16")
     vc = to_dev(head_major(v, Hkv, dh), "bf16")
