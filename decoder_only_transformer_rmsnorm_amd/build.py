@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtfm.so")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "decode.hip", "backward.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "decode.hip", "backward.hip",
+               "attn_back.hip"]
 HOST_SOURCES = ["api.cpp"]
 ARCH = os.environ.get("TFM_OFFLOAD_ARCH", "gfx950")
 

@@ -254,13 +254,30 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
 // ---- training step: plan of the workspace and the enqueued forward / backward
 struct TrainPlan {
   size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxT, dh, hT, du,
-      da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part;
+      da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
   int Vp;        // vocabulary padded to a multiple of 8 (K of the head's input-gradient GEMM)
   int64_t Mp;    // tokens padded to a multiple of 8 (K of the weight-gradient GEMMs)
   size_t total;
 };
+
+// Weight-gradient products contract over the tokens (K = B S) into small outputs, so they
+// launch few tiles; they are split along K into `parts` contiguous ranges (each a multiple of
+// 64, at least 512 long) so about kSplitTarget workgroups run, and the fp32 partials are
+// summed in part order (deterministic).
+constexpr int64_t kSplitTarget = 512;
+constexpr int kSplitMax = 16;
+int splitk_parts(int dt, int64_t M, int N, int64_t K) {
+  const int64_t tiles = gemm_store_tiles(dt, M, N);
+  int64_t parts = (kSplitTarget + tiles - 1) / tiles;
+  parts = std::min<int64_t>(parts, std::max<int64_t>(1, K / 512));
+  return (int)std::min<int64_t>(parts, kSplitMax);
+}
+size_t splitk_bytes(int dt, int64_t M, int N, int64_t K) {
+  const int parts = splitk_parts(dt, M, N, K);
+  return parts > 1 ? (size_t)parts * M * N * 4 : 0;
+}
 
 TrainPlan plan_train(const tfm_config *c, int B, int S) {
   TrainPlan p;
@@ -304,6 +321,17 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.lse = take(M * c->n_heads * 4);
   p.dsum = take(M * c->n_heads * 4);
   p.rms_part = take((size_t)rms_back_parts((int64_t)M) * D * 4);
+  {   // split-K partials of the largest weight-gradient product
+    const int dt = c->dtype == TFM_BF16 ? DT_BF16 : DT_F32;
+    const int64_t K = (int64_t)Mp;
+    size_t sk = splitk_bytes(dt, (int64_t)V, (int)D, K);
+    sk = std::max(sk, splitk_bytes(dt, (int64_t)D, (int)F, K));
+    sk = std::max(sk, splitk_bytes(dt, (int64_t)F, (int)D, K));
+    sk = std::max(sk, splitk_bytes(dt, (int64_t)D, (int)qd, K));
+    sk = std::max(sk, splitk_bytes(dt, (int64_t)qd, (int)D, K));
+    sk = std::max(sk, splitk_bytes(dt, (int64_t)kvd, (int)D, K));
+    p.splitk = take(std::max<size_t>(sk, 4));
+  }
   size_t lo = 0;
   auto ltake = [&](size_t bytes) { const size_t o = lo; lo += round256(bytes); return o; };
   p.l_x = ltake(M * D * 4);
@@ -336,6 +364,21 @@ int gemm(int epi, int dt, const void *a, int64_t lda, const void *w, int64_t M, 
   g.a = a; g.lda = lda; g.w0 = w; g.M = M; g.N = N; g.K = K; g.y = y; g.ldy = ldy; g.y_dt = y_dt;
   g.residual = residual;
   return hip_status(launch_gemm(epi, dt, g, s));
+}
+
+// Weight gradient y (M, N) fp32 = a w^T over K = tokens, split along K (splitk_parts).
+int gemm_wgrad(int dt, const void *a, int64_t lda, const void *w, int64_t M, int N, int K,
+               float *y, int64_t ldy, float *part, hipStream_t s) {
+  const int parts = splitk_parts(dt, M, N, K);
+  if (parts <= 1) return gemm(EPI_STORE, dt, a, lda, w, M, N, K, y, ldy, DT_F32, nullptr, s);
+  const int ks = ((K + parts - 1) / parts + 63) / 64 * 64;
+  const int n = (K + ks - 1) / ks;
+  GemmArgs g{};
+  g.a = a; g.lda = lda; g.w0 = w; g.M = M; g.N = N; g.K = K;
+  g.y = part; g.ldy = N; g.y_dt = DT_F32;
+  g.kparts = n; g.kpart = ks; g.ypart = M * N;
+  TFM_HIP(launch_gemm(EPI_STORE, dt, g, s));
+  return hip_status(launch_sum_parts(part, n, M, N, y, ldy, s));
 }
 }  // namespace
 
@@ -782,6 +825,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   float *logits = (float *)(wb + p.logits), *dx = (float *)(wb + p.dx);
   float *dhp = (float *)(wb + p.dh), *du = (float *)(wb + p.du);
   float *rpart = (float *)(wb + p.rms_part);
+  float *skp = (float *)(wb + p.splitk);
 
   // ---- forward, keeping each layer's activations ("Transformer 篇" 5.7)
   TFM_HIP(launch_fill_i32(flags, 2, 0, s));
@@ -822,7 +866,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, V, s));
   TFM_HIP(launch_transpose(xf, dt, D, xfT, dt, Mp, Mp, M, D, s));
   float *g_lm = tied ? gr->embed : gr->lm_head;
-  TFM_TRY(gemm(EPI_STORE, dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, DT_F32, nullptr, s));
+  TFM_TRY(gemm_wgrad(dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, skp, s));
   TFM_HIP(launch_fill_f32(dx, M * D, 0.f, s));
   TFM_HIP(launch_rms_backward(X(NL), w->g_final, dt, dhp, dx, gr->g_final, 0, rpart, M, D, eps, s));
 
@@ -840,7 +884,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
     TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, DT_F32, nullptr, s));
+    TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, skp, s));
     TFM_HIP(launch_swiglu_backward(a, c, du, da, dc, dt, M * F, s));
     TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, F, F, F, D, s));
     TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
@@ -849,8 +893,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
     TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
     TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
-    TFM_TRY(gemm(EPI_STORE, dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, DT_F32, nullptr, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, DT_F32, nullptr, s));
+    TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
+    TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
     TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, lg->g_ffn, 0, rpart, M, D, eps, s));
     // attention output projection: xm = x + o Wo^T
     TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
@@ -858,7 +902,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
     TFM_HIP(launch_transpose(o, dt, qd, actT, dt, Mp, Mp, M, qd, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, DT_F32, nullptr, s));
+    TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, skp, s));
     // attention, then back through the rotations of q and k
     TFM_HIP(launch_attention_backward(qkv, W, o, qd, dout, qd, dqkv, B, S, Hq, Hkv, dh, dt,
                                       layer_window(cfg, l), (const float *)LA(l, p.l_lse),
@@ -874,11 +918,11 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wT, M, D, W, dhp, D, DT_F32, nullptr, s));
     TFM_HIP(launch_transpose(dqkv, dt, W, dqkvT, dt, Mp, Mp, M, W, s));
     TFM_HIP(launch_transpose(h1, dt, D, hT, dt, Mp, Mp, M, D, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dqkvT, Mp, hT, qd, D, (int)Mp, lg->wq, D, DT_F32, nullptr, s));
-    TFM_TRY(gemm(EPI_STORE, dt, (uint8_t *)dqkvT + (size_t)qd * Mp * e, Mp, hT, kvd, D, (int)Mp,
-                 lg->wk, D, DT_F32, nullptr, s));
-    TFM_TRY(gemm(EPI_STORE, dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
-                 (int)Mp, lg->wv, D, DT_F32, nullptr, s));
+    TFM_TRY(gemm_wgrad(dt, dqkvT, Mp, hT, qd, D, (int)Mp, lg->wq, D, skp, s));
+    TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)qd * Mp * e, Mp, hT, kvd, D, (int)Mp,
+                       lg->wk, D, skp, s));
+    TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
+                       (int)Mp, lg->wv, D, skp, s));
     TFM_HIP(launch_rms_backward(x, lw->g_attn, dt, dhp, dx, lg->g_attn, 0, rpart, M, D, eps, s));
   }
   // ---- embedding rows (a tied head's gradient is already in gr->embed)
@@ -905,8 +949,7 @@ int tfm_grad_clip_coef(const float *const *grads, const int64_t *sizes, int n_te
   hipStream_t s = (hipStream_t)stream;
   double *part = (double *)ws;
   const int np = sumsq_parts();
-  for (int i = 0; i < n_tensors; ++i)
-    TFM_HIP(launch_sumsq(sizes[i] > 0 ? grads[i] : nullptr, sizes[i], part + (size_t)i * np, s));
+  TFM_HIP(launch_sumsq_multi(grads, sizes, n_tensors, part, s));
   TFM_HIP(launch_clip_coef(part, n_tensors * np, max_norm, coef, norm, s));
   return TFM_OK;
 }
@@ -923,6 +966,27 @@ int tfm_adamw_step(float *param, void *param_bf16, const float *grad, float *m, 
   const float c2 = (float)(1.0 - std::pow((double)beta2, step));
   return hip_status(launch_adamw(param, param_bf16, grad, m, v, n, lr, beta1, beta2, eps,
                                  weight_decay, c1, c2, coef, (hipStream_t)stream));
+}
+
+int tfm_adamw_step_multi(float *const *params, void *const *params_bf16,
+                         const float *const *grads, float *const *m, float *const *v,
+                         const int64_t *sizes, int n_tensors, float lr, float beta1, float beta2,
+                         float eps, float weight_decay, int step, const float *coef,
+                         void *stream) {
+  if (n_tensors < 0 || step < 1 || !(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) ||
+      !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) || !(weight_decay >= 0.f))
+    return TFM_ERR_SHAPE;
+  if (n_tensors == 0) return TFM_OK;
+  if (!params || !grads || !m || !v || !sizes) return TFM_ERR_NULL;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (sizes[i] < 0) return TFM_ERR_SHAPE;
+    if (sizes[i] > 0 && (!params[i] || !grads[i] || !m[i] || !v[i])) return TFM_ERR_NULL;
+  }
+  const float c1 = (float)(1.0 - std::pow((double)beta1, step));
+  const float c2 = (float)(1.0 - std::pow((double)beta2, step));
+  return hip_status(launch_adamw_multi(params, params_bf16, grads, m, v, sizes, n_tensors, lr,
+                                       beta1, beta2, eps, weight_decay, c1, c2, coef,
+                                       (hipStream_t)stream));
 }
 
 }  // extern "C"

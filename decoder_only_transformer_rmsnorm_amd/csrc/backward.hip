@@ -12,10 +12,11 @@
 //    gradient summed per workgroup and the partials summed in a fixed order;
 //  * swiglu_fwd_kernel / swiglu_back_kernel: u = SiLU(a) c and (da, dc);
 //  * rope_inv_kernel: the backward of a rotation is the rotation by the opposite angle;
-//  * attention backward, flash style in fp32 vector arithmetic: with each query row's
-//    logsumexp kept by the forward, attn_dq_kernel accumulates dq = sum_j P (dP - D) k / sqrt(dh)
-//    with D = rowsum(do * o); attn_dkdv_kernel accumulates dk and dv per key over the queries
-//    (and query heads of a group) that see it. The score matrix is never stored.
+//  * attention backward of fp32 models, flash style in fp32 vector arithmetic: with each query
+//    row's logsumexp kept by the forward, attn_dq_kernel accumulates
+//    dq = sum_j P (dP - D) k / sqrt(dh) with D = rowsum(do * o); attn_dkdv_kernel accumulates
+//    dk and dv per key over the queries (and query heads of a group) that see it. The score
+//    matrix is never stored. bf16 models use the matrix-core kernels of attn_back.hip.
 //  * embed_back_kernel: scatter-add of the input gradient into the embedding rows;
 //  * sumsq / clip_coef / adamw: the global-norm clipping coefficient and the AdamW update.
 #include <cmath>
@@ -442,6 +443,29 @@ __global__ __launch_bounds__(kAttnRows *(DH / (DH < 32 ? DH : 32))) void attn_dk
   }
 }
 
+// ---- split-K partial sums in a fixed order (4 outputs per thread; N % 4 == 0 or scalar tail)
+__global__ void sum_parts_kernel(const float *__restrict__ part, int parts, int64_t M, int N,
+                                 float *__restrict__ y, int64_t ldy) {
+  const int64_t n4 = (N + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * n4) return;
+  const int64_t m = idx / n4;
+  const int n = (int)(idx % n4) * 4;
+  const int64_t stride = M * N;
+  const float *p = part + m * N + n;
+  if (n + 4 <= N && (N & 3) == 0 && (ldy & 3) == 0 && ((uintptr_t)y & 15) == 0) {
+    f32x4_t acc = *(const f32x4_t *)p;
+    for (int q = 1; q < parts; ++q) acc += *(const f32x4_t *)(p + q * stride);
+    *(f32x4_t *)(y + m * ldy + n) = acc;
+  } else {
+    for (int x = 0; x < 4 && n + x < N; ++x) {
+      float acc = p[x];
+      for (int q = 1; q < parts; ++q) acc += p[q * stride + x];
+      y[m * ldy + n + x] = acc;
+    }
+  }
+}
+
 // ---- embedding backward: dE[ids[r]] += dx[r] (fp32 atomics: rows with the same id add in
 // an unspecified order)
 __global__ void embed_back_kernel(const int32_t *__restrict__ ids, int64_t n, int vocab, int d,
@@ -492,14 +516,46 @@ __global__ __launch_bounds__(256) void clip_coef_kernel(const double *__restrict
   }
 }
 
-__global__ void adamw_kernel(float *__restrict__ p, bf16_t *__restrict__ pb,
-                             const float *__restrict__ g, float *__restrict__ m,
-                             float *__restrict__ v, int64_t n, float lr, float b1, float b2,
-                             float eps, float wd, float c1, float c2,
-                             const float *__restrict__ coef) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float gg = g[i] * (coef ? coef[0] : 1.0f);
+// Tensors of one batched launch (kernel arguments, so no table in device memory).
+constexpr int kBatch = 32;
+struct SumsqBatch {
+  const float *g[kBatch];
+  int64_t n[kBatch];
+};
+struct AdamwBatch {
+  float *p[kBatch];
+  bf16_t *pb[kBatch];
+  const float *g[kBatch];
+  float *m[kBatch], *v[kBatch];
+  int64_t n[kBatch];
+  int64_t blk0[kBatch + 1];   // first block of each tensor; blk0[count] = total blocks
+  int count;
+};
+
+// sumsq_kernel for tensor blockIdx.y of a batch, partials at part + blockIdx.y * kSumsqBlocks
+__global__ __launch_bounds__(256) void sumsq_multi_kernel(SumsqBatch bt, double *__restrict__ part) {
+  const int t = blockIdx.y;
+  const float *g = bt.g[t];
+  const int64_t n = bt.n[t];
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)kSumsqBlocks * 256)
+    s += (double)g[i] * (double)g[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(int64_t)t * kSumsqBlocks + blockIdx.x] = red[0];
+}
+
+__device__ __forceinline__ void adamw_elem(float *__restrict__ p, bf16_t *__restrict__ pb,
+                                           const float *__restrict__ g, float *__restrict__ m,
+                                           float *__restrict__ v, int64_t i, float lr, float b1,
+                                           float b2, float eps, float wd, float c1, float c2,
+                                           float cf) {
+  const float gg = g[i] * cf;
   const float mi = b1 * m[i] + (1.0f - b1) * gg;
   const float vi = b2 * v[i] + (1.0f - b2) * gg * gg;
   m[i] = mi;
@@ -508,6 +564,31 @@ __global__ void adamw_kernel(float *__restrict__ p, bf16_t *__restrict__ pb,
   const float nw = th - lr * (mi / c1) / (sqrtf(vi / c2) + eps) - lr * wd * th;
   p[i] = nw;
   if (pb) pb[i] = f32_to_bf16(nw);
+}
+
+__global__ void adamw_kernel(float *__restrict__ p, bf16_t *__restrict__ pb,
+                             const float *__restrict__ g, float *__restrict__ m,
+                             float *__restrict__ v, int64_t n, float lr, float b1, float b2,
+                             float eps, float wd, float c1, float c2,
+                             const float *__restrict__ coef) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  adamw_elem(p, pb, g, m, v, i, lr, b1, b2, eps, wd, c1, c2, coef ? coef[0] : 1.0f);
+}
+
+// one launch over a batch of tensors: block b belongs to the tensor t with
+// blk0[t] <= b < blk0[t + 1]
+__global__ __launch_bounds__(256) void adamw_multi_kernel(AdamwBatch bt, float lr, float b1,
+                                                          float b2, float eps, float wd,
+                                                          float c1, float c2,
+                                                          const float *__restrict__ coef) {
+  const int64_t b = blockIdx.x;
+  int t = 0;
+  while (t + 1 < bt.count && bt.blk0[t + 1] <= b) ++t;
+  const int64_t i = (b - bt.blk0[t]) * 256 + threadIdx.x;
+  if (i >= bt.n[t]) return;
+  adamw_elem(bt.p[t], bt.pb[t], bt.g[t], bt.m[t], bt.v[t], i, lr, b1, b2, eps, wd, c1, c2,
+             coef ? coef[0] : 1.0f);
 }
 
 template <typename T, int DH>
@@ -661,11 +742,8 @@ hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o,
 #define TFM_AB(T, D)                                                                          \
   return run_attn_back<T, D>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s);
   if (dt == DT_BF16) {
-    switch (d_head) {
-      case 32: TFM_AB(bf16_t, 32)
-      case 64: TFM_AB(bf16_t, 64)
-      case 128: TFM_AB(bf16_t, 128)
-    }
+    return launch_attention_backward_bf16(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv,
+                                          d_head, w, lse, dsum, s);
   } else {
     switch (d_head) {
       case 16: TFM_AB(float, 16)
@@ -676,6 +754,61 @@ hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o,
   }
 #undef TFM_AB
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_sumsq_multi(const float *const *g, const int64_t *n, int count, double *part,
+                              hipStream_t s) {
+  for (int t0 = 0; t0 < count; t0 += kBatch) {
+    SumsqBatch bt{};
+    const int c = count - t0 < kBatch ? count - t0 : kBatch;
+    for (int t = 0; t < c; ++t) {
+      bt.g[t] = n[t0 + t] > 0 ? g[t0 + t] : nullptr;
+      bt.n[t] = n[t0 + t];
+    }
+    sumsq_multi_kernel<<<dim3(kSumsqBlocks, c), 256, 0, s>>>(bt, part + (size_t)t0 * kSumsqBlocks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_adamw_multi(float *const *p, void *const *pb, const float *const *g,
+                              float *const *m, float *const *v, const int64_t *n, int count,
+                              float lr, float b1, float b2, float eps, float wd, float c1,
+                              float c2, const float *coef, hipStream_t s) {
+  int t = 0;
+  while (t < count) {
+    AdamwBatch bt{};
+    int c = 0;
+    int64_t blocks = 0;
+    for (; t < count && c < kBatch; ++t) {   // empty tensors take no slot
+      if (n[t] == 0) continue;
+      bt.p[c] = p[t];
+      bt.pb[c] = pb ? (bf16_t *)pb[t] : nullptr;
+      bt.g[c] = g[t];
+      bt.m[c] = m[t];
+      bt.v[c] = v[t];
+      bt.n[c] = n[t];
+      bt.blk0[c] = blocks;
+      blocks += nblk(n[t], 256);
+      ++c;
+    }
+    if (c == 0) break;
+    bt.blk0[c] = blocks;
+    bt.count = c;
+    adamw_multi_kernel<<<(unsigned)blocks, 256, 0, s>>>(bt, lr, b1, b2, eps, wd, c1, c2, coef);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sum_parts(const float *part, int parts, int64_t M, int N, float *y,
+                            int64_t ldy, hipStream_t s) {
+  const int64_t total = M * ((N + 3) / 4);
+  if (total == 0) return hipSuccess;
+  sum_parts_kernel<<<nblk(total, 256), 256, 0, s>>>(part, parts, M, N, y, ldy);
+  return hipGetLastError();
 }
 
 hipError_t launch_embed_backward(const int32_t *ids, int64_t n, int vocab, int d, const float *dx,

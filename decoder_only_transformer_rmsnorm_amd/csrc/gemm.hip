@@ -80,6 +80,25 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // Weight rows: pointer to virtual row n and the number of rows of that source from n on.
+// Row stride of the weight rows (a weight-gradient product over part of K keeps the full rows).
+__device__ __forceinline__ int64_t wstride(const GemmArgs &g) { return g.ldw > 0 ? g.ldw : g.K; }
+
+// The arguments of K part blockIdx.y of a split product: operands advanced to the part's first
+// k (the weight rows keep their full stride), K cut to the part, output advanced to its slab.
+template <typename T>
+__device__ __forceinline__ GemmArgs k_part(const GemmArgs &g0) {
+  GemmArgs g = g0;
+  if (g0.kparts > 1) {
+    const int64_t k0 = (int64_t)blockIdx.y * g0.kpart;
+    g.ldw = wstride(g0);
+    g.a = (const T *)g0.a + k0;
+    g.w0 = (const T *)g0.w0 + k0;
+    g.K = (int)min((int64_t)g0.kpart, (int64_t)g0.K - k0);
+    g.y = (uint8_t *)g0.y + (size_t)blockIdx.y * g0.ypart * (g0.y_dt == DT_F32 ? 4 : 2);
+  }
+  return g;
+}
+
 template <int EPI, typename T>
 __device__ __forceinline__ const T *weight_rows(const GemmArgs &g, int n, int &rows_left) {
   if constexpr (EPI == EPI_SWIGLU) {
@@ -87,21 +106,21 @@ __device__ __forceinline__ const T *weight_rows(const GemmArgs &g, int n, int &r
     const int j = ((n >> 6) << 5) | (n & 31);
     rows_left = min(g.n0 - j, 32 - (n & 31));
     const T *base = (const T *)(((n >> 5) & 1) ? g.w1 : g.w0);
-    return base + (int64_t)(rows_left > 0 ? j : 0) * g.K;
+    return base + (int64_t)(rows_left > 0 ? j : 0) * wstride(g);
   } else if constexpr (EPI == EPI_QKV_ROPE) {
     if (n < g.n0) {
       rows_left = g.n0 - n;
-      return (const T *)g.w0 + (int64_t)n * g.K;
+      return (const T *)g.w0 + (int64_t)n * wstride(g);
     }
     if (n < g.n0 + g.n1) {
       rows_left = g.n0 + g.n1 - n;
-      return (const T *)g.w1 + (int64_t)(n - g.n0) * g.K;
+      return (const T *)g.w1 + (int64_t)(n - g.n0) * wstride(g);
     }
     rows_left = g.N - n;
-    return (const T *)g.w2 + (int64_t)(rows_left > 0 ? n - g.n0 - g.n1 : 0) * g.K;
+    return (const T *)g.w2 + (int64_t)(rows_left > 0 ? n - g.n0 - g.n1 : 0) * wstride(g);
   } else {
     rows_left = g.N - n;
-    return (const T *)g.w0 + (int64_t)(rows_left > 0 ? n : 0) * g.K;
+    return (const T *)g.w0 + (int64_t)(rows_left > 0 ? n : 0) * wstride(g);
   }
 }
 
@@ -252,9 +271,10 @@ struct BfTile {
 // which pays under the chip's power limit.
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
           int WGN = 2, bool PP = false, int MS = 32>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g, int tiles_m,
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g0, int tiles_m,
                                                                         int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  const GemmArgs g = k_part<bf16_t>(g0);
   constexpr int NT = 64 * WGM * WGN;
   using T = BfTile<BM, BN, BK, NST, WGM * WGN>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
@@ -311,9 +331,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     const int r0 = (wid * B_INS + i) * FR;
     int rows_left;
     const bf16_t *src = weight_rows<EPI, bf16_t>(g, n0 + r0, rows_left);
-    b_rsrc[i] = make_rsrc(src, (int64_t)min(rows_left, FR) * K * 2);
+    b_rsrc[i] = make_rsrc(src, (int64_t)min(rows_left, FR) * wstride(g) * 2);
     b_k[i] = (fchunk ^ swz_rb<RB>(r0 + frow)) * 8;
-    b_off[i] = (uint32_t)(frow * K * 2 + b_k[i] * 2);
+    b_off[i] = (uint32_t)(frow * wstride(g) * 2 + b_k[i] * 2);
   }
 
   const int nk = (K + BK - 1) / BK;
@@ -730,8 +750,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
 
 // ------------------------------------------------------------------ f32 kernel
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmArgs g, int tiles_m,
+__global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmArgs g0, int tiles_m,
                                                                int tiles_n) {
+  const GemmArgs g = k_part<float>(g0);
   constexpr int CE = 4;                              // floats per 16-byte chunk
   constexpr int BKE = kRowBytes / 4;                 // K elements per stage
   constexpr int A_LD = BM * kChunks / kThreads;
@@ -859,7 +880,8 @@ hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS>),
-                     dim3((unsigned)(tm * tn)), dim3(64 * WGM * WGN), 0, s, g, (int)tm, (int)tn);
+                     dim3((unsigned)(tm * tn), g.kparts > 1 ? g.kparts : 1), dim3(64 * WGM * WGN), 0,
+                     s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
 
@@ -869,7 +891,7 @@ hipError_t run_f32(const GemmArgs &g, hipStream_t s) {
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, EPI>), dim3((unsigned)(tm * tn)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, EPI>), dim3((unsigned)(tm * tn), g.kparts > 1 ? g.kparts : 1), dim3(kThreads), 0,
                      s, g, (int)tm, (int)tn);
   return hipGetLastError();
 }
@@ -901,6 +923,12 @@ hipError_t dispatch_f32(int epi, const GemmArgs &g, hipStream_t s) {
 }  // namespace
 
 int gemm_xent_parts(int N) { return (N + kXentBN - 1) / kXentBN; }
+
+int64_t gemm_store_tiles(int dt, int64_t M, int N) {
+  // the plain-store tile shapes of dispatch_bf16 / dispatch_f32
+  const int64_t bm = dt == DT_BF16 ? 192 : 128, bn = 128;
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
 
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s) {
   if (g.M == 0) return hipSuccess;

@@ -44,6 +44,11 @@ struct GemmArgs {
   int64_t M;
   int N;                   // output columns (QKV: n0 + 2 n1; SwiGLU: d_ff)
   int K;
+  int64_t ldw;             // row stride of the weight rows in elements (0: K)
+  // split K (EPI_STORE): part q = blockIdx.y of kparts > 1 multiplies k in
+  // [q kpart, (q + 1) kpart) and stores at y + q ypart elements
+  int kparts, kpart;
+  int64_t ypart;
   void *y;
   int64_t ldy;
   int y_dt;
@@ -60,6 +65,8 @@ struct GemmArgs {
 int gemm_xent_parts(int N);
 
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
+// Workgroups of a plain-store GEMM of M x N outputs.
+int64_t gemm_store_tiles(int dt, int64_t M, int N);
 
 // ---- attention (attention.hip)
 // window > 0: query s sees keys s - window + 1 .. s only (window >= S or 0: full causal).
@@ -140,6 +147,24 @@ hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o,
                                      const void *dout, int64_t lddo, void *dqkv, int B, int S,
                                      int Hq, int Hkv, int d_head, int dt, int window,
                                      const float *lse, float *dsum, hipStream_t s);
+// The bf16 path of launch_attention_backward (attn_back.hip): d_head 32, 64 or 128.
+hipError_t launch_attention_backward_bf16(const void *qkv, int64_t ld, const void *o,
+                                          int64_t ldo, const void *dout, int64_t lddo,
+                                          void *dqkv, int B, int S, int Hq, int Hkv, int d_head,
+                                          int window, const float *lse, float *dsum,
+                                          hipStream_t s);
+// The sum-of-squares partials of `count` tensors (host arrays of device pointers and sizes),
+// tensor t at part + t * sumsq_parts(), in launches of up to 32 tensors.
+hipError_t launch_sumsq_multi(const float *const *g, const int64_t *n, int count, double *part,
+                              hipStream_t s);
+// AdamW over `count` tensors (host arrays; pb nullable, or entries nullable), batched.
+hipError_t launch_adamw_multi(float *const *p, void *const *pb, const float *const *g,
+                              float *const *m, float *const *v, const int64_t *n, int count,
+                              float lr, float b1, float b2, float eps, float wd, float c1,
+                              float c2, const float *coef, hipStream_t s);
+// y[m, n] = sum over p < parts of part[p][m, n] (part: parts x M x N fp32, summed in order p).
+hipError_t launch_sum_parts(const float *part, int parts, int64_t M, int N, float *y,
+                            int64_t ldy, hipStream_t s);
 hipError_t launch_embed_backward(const int32_t *ids, int64_t n, int vocab, int d, const float *dx,
                                  float *dE, hipStream_t s);
 int sumsq_parts();

@@ -29,7 +29,8 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_decode_workspace_bytes", "tfm_model_decode",
            "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
            "tfm_train_workspace_bytes", "tfm_model_backward", "tfm_clip_workspace_bytes",
-           "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_check_device_flags"]
+           "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_adamw_step_multi",
+           "tfm_check_device_flags"]
 
 
 class TfmError(RuntimeError):
@@ -136,6 +137,11 @@ def lib() -> ctypes.CDLL:
             "tfm_adamw_step": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_float, c_int, c_p, c_p]),
+            "tfm_adamw_step_multi": (c_int, [ctypes.POINTER(c_p), ctypes.POINTER(c_p),
+                                             ctypes.POINTER(c_p), ctypes.POINTER(c_p),
+                                             ctypes.POINTER(c_p), ctypes.POINTER(c_i64), c_int,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                             ctypes.c_float, ctypes.c_float, c_int, c_p, c_p]),
             "tfm_check_device_flags": (c_int, [c_p, c_p]),
         }
         for name, (res, args) in sig.items():
@@ -510,7 +516,7 @@ def tfm_model_forward(dm: DeviceModel, ids=None, positions=None, **kw):
 class Trainer:
     """One training step on the GPU for a DeviceModel [T2 Optimize; T3 12]: forward and
     backward of the mean next-token cross-entropy (tfm_model_backward), global-norm gradient
-    clipping (tfm_grad_clip_coef) and AdamW (tfm_adamw_step). Keeps fp32 master weights, fp32
+    clipping (tfm_grad_clip_coef) and AdamW (tfm_adamw_step_multi). Keeps fp32 master weights, fp32
     gradients and the two AdamW moments; for bf16 models the DeviceModel's bf16 weights are
     rewritten from the masters after every step."""
 
@@ -544,6 +550,13 @@ class Trainer:
         self._gsizes = (c_i64 * n)(*[G[k].numel() for k, _ in self.params])
         self._cws = torch.empty(lib().tfm_clip_workspace_bytes(n), dtype=torch.uint8,
                                 device=dm.device)
+        # pointer tables of the batched AdamW step
+        pm = [self.master[k] for k, _ in self.params]
+        self._pptrs = (c_p * n)(*[t.data_ptr() for t in pm])
+        self._pbptrs = (c_p * n)(*[None if w is self.master[k] else w.data_ptr()
+                                   for k, w in self.params])
+        self._mptrs = (c_p * n)(*[self.m[k].data_ptr() for k, _ in self.params])
+        self._vptrs = (c_p * n)(*[self.v[k].data_ptr() for k, _ in self.params])
         self._ws = None
         self._ws_shape = None
 
@@ -579,13 +592,10 @@ class Trainer:
         self.t += 1
         lr = self.lr if lr is None else lr
         coef = self.coef if self.max_norm is not None else None
-        for n, w in self.params:
-            pm = self.master[n]
-            pb = None if w is pm else w
-            _check(lib().tfm_adamw_step(_dev(pm), _dev(pb), _dev(self.grad[n]), _dev(self.m[n]),
-                                        _dev(self.v[n]), pm.numel(), lr, self.betas[0],
-                                        self.betas[1], self.eps, self.wd, self.t, _dev(coef),
-                                        _stream(stream)), "tfm_adamw_step")
+        _check(lib().tfm_adamw_step_multi(self._pptrs, self._pbptrs, self._gptrs, self._mptrs,
+                                          self._vptrs, self._gsizes, len(self.params), lr,
+                                          self.betas[0], self.betas[1], self.eps, self.wd, self.t,
+                                          _dev(coef), _stream(stream)), "tfm_adamw_step_multi")
 
     def step(self, ids, targets, positions=None, lr: float | None = None, stream=None):
         """Forward + backward, clipping (if max_norm) and one AdamW step; returns the loss."""

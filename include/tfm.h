@@ -304,6 +304,17 @@ int tfm_adamw_step(float *param, void *param_bf16, const float *grad, float *m, 
                    int64_t n, float lr, float beta1, float beta2, float eps, float weight_decay,
                    int step, const float *coef, void *stream);
 
+/* tfm_adamw_step on n_tensors tensors in a few launches (up to 32 tensors each), with the
+ * same per-element arithmetic, so the results equal n_tensors single calls bit for bit.
+ * params, grads, m, v, sizes: host arrays of n_tensors entries (device pointers, element
+ * counts); params_bf16: host array (nullable; entries nullable) of bf16 copies. A tensor of
+ * size 0 is skipped (its pointers may be NULL). */
+int tfm_adamw_step_multi(float *const *params, void *const *params_bf16,
+                         const float *const *grads, float *const *m, float *const *v,
+                         const int64_t *sizes, int n_tensors, float lr, float beta1, float beta2,
+                         float eps, float weight_decay, int step, const float *coef,
+                         void *stream);
+
 /* Waits for `stream`, then returns TFM_ERR_TOKEN if the last whole-model call that used this
  * workspace saw an out-of-range token id, TFM_ERR_POSITION if it saw a position outside the
  * KV cache or the RoPE table (prefill / decode), else TFM_OK. */

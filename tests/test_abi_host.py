@@ -362,3 +362,16 @@ def test_training_entry_points_validation(L):
     assert adam(lr=-1.0) == SHAPE
     assert adam(n=0) == OK
     assert adam(p=None) == NULL
+
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    sz = (ctypes.c_int64 * 2)(10, 0)
+    multi = lambda ps=arr(P, None), gs=arr(P, None), n=2, sizes=sz, step=1, b2=0.999: \
+        L.tfm_adamw_step_multi(ps, None, gs, arr(P, None), arr(P, None), sizes, n, 1e-3, 0.9, b2,
+                               1e-8, 0.0, step, None, None)
+    assert multi(n=0) == OK
+    assert multi(n=-1) == SHAPE
+    assert multi(step=0) == SHAPE
+    assert multi(b2=1.0) == SHAPE
+    assert multi(ps=None) == NULL
+    assert multi(gs=arr(None, None)) == NULL                 # tensor 0 has elements
+    assert multi(sizes=(ctypes.c_int64 * 2)(10, -3)) == SHAPE

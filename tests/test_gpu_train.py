@@ -104,6 +104,15 @@ def test_gradients_bf16(kv, dh):
     _grad_case(cfg, 2, 2.5e-2, cos_bar=0.9995)
 
 
+def test_gradients_bf16_split_k_weight_products():
+    """2048 tokens: the weight-gradient products contract over K = 2048 in 4 parts of 512
+    (summed in order), and the attention backward runs over 1024-long sequences (8 key
+    tiles per query block, GQA 4:2)."""
+    cfg = synth.ModelConfig("train_bf16_long", "bf16", 2, 256, 4, 2, 64, 704, 1000, 2, 1024)
+    say("gradients bf16 split-K, 2 x 1024 tokens")
+    _grad_case(cfg, 4, 2.5e-2, cos_bar=0.9995)
+
+
 def test_gradients_bf16_d768_two_layers():
     """The benchmark model's widths (d768, 12 heads of 64, d_ff 2048, the 50257 vocabulary)
     with two layers, one sequence of 64 tokens."""
@@ -150,6 +159,40 @@ def test_adamw_and_clip_match_oracle():
     assert (err <= 1e-6 * np.abs(ref_th) + 1e-6).all()
     assert np.array_equal(to_np(pb).astype(np.float32),
                           synth.round_to_bf16(to_np(p).astype(np.float32)))
+
+
+def test_adamw_multi_equals_single_calls():
+    """The batched AdamW step (35 tensors, so two launches, one of them empty and several with
+    bf16 copies) gives the single-tensor entry point's results bit for bit."""
+    tfm = tfm_mod()
+    import ctypes
+    g = np.random.Generator(np.random.PCG64(9))
+    sizes = [int(g.integers(1, 3000)) if i != 4 else 0 for i in range(35)]
+    mk = lambda n: torch.from_numpy(g.normal(size=n).astype(np.float32)).cuda()
+    P = [mk(n) for n in sizes]
+    G = [mk(n) for n in sizes]
+    M = [mk(n).abs() * 0.1 for n in sizes]
+    V = [mk(n).abs() * 0.01 for n in sizes]
+    PB = [torch.empty(n, dtype=torch.bfloat16, device="cuda") if i % 3 == 0 else None
+          for i, n in enumerate(sizes)]
+    coef = torch.full((1,), 0.7, device="cuda")
+    clone = lambda L: [t.clone() for t in L]
+    P1, M1, V1 = clone(P), clone(M), clone(V)
+    PB1 = [None if t is None else t.clone() for t in PB]
+    hp = (1e-2, 0.9, 0.95, 1e-8, 0.1, 3)
+    for i in range(len(sizes)):
+        assert tfm.lib().tfm_adamw_step(P1[i].data_ptr(), None if PB1[i] is None else PB1[i].data_ptr(),
+                                        G[i].data_ptr(), M1[i].data_ptr(), V1[i].data_ptr(),
+                                        sizes[i], *hp, coef.data_ptr(), None) == 0
+    ptr = lambda L: (ctypes.c_void_p * len(L))(*[None if t is None else t.data_ptr() for t in L])
+    assert tfm.lib().tfm_adamw_step_multi(ptr(P), ptr(PB), ptr(G), ptr(M), ptr(V),
+                                          (ctypes.c_int64 * len(sizes))(*sizes), len(sizes), *hp,
+                                          coef.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        assert torch.equal(P[i], P1[i]) and torch.equal(M[i], M1[i]) and torch.equal(V[i], V1[i])
+        if PB[i] is not None:
+            assert torch.equal(PB[i], PB1[i])
 
 
 def test_training_steps_reduce_the_loss():
