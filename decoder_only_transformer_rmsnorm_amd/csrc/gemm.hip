@@ -224,12 +224,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, f32x16_t (&acc)[NBN]
 // ------------------------------------------------------------------ bf16 kernel
 constexpr int kLdsBytes = 160 * 1024;   // gfx950 LDS per workgroup
 
-// Chunk swizzle of a tile row of RB bytes (RB/16 chunks): the rows that one 8- or 16-lane
-// phase of a 16-byte fragment read touches land on distinct bank groups (32 or 64 banks).
+// Chunk swizzle of a tile row of RB bytes (RB/16 chunks), chosen by measuring ds_read_b128
+// throughput for the fragment reads of both matrix-core blocks (16 rows x 4 chunks and
+// 32 rows x 2 chunks per instruction): this mask keeps both at the LDS port's full rate
+// (~200 B/clk per CU) for 64- and 128-byte rows, where e.g. row ^ (row >> 3) halves it for
+// 16-row reads of 128-byte rows (2-way bank conflicts). The fills swizzle a weight row by its
+// row within the weight part of the tile and the reads by its row within the whole tile (BM
+// further on), so the mask must repeat with a period that divides BM: it repeats every 32.
 template <int RB>
 __device__ __forceinline__ int swz_rb(int row) {
-  if constexpr (RB == 128) return (row ^ (row >> 3)) & 7;
-  else return ((row >> 1) ^ (row >> 2)) & 3;
+  return ((row >> 1) ^ (row >> 2)) & (RB / 16 - 1);
 }
 
 // Epilogue staging: output rows of `rb` bytes, 16-byte chunks XOR-swizzled by the row so
