@@ -340,6 +340,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     b_off[i] = (uint32_t)(frow * wstride(g) * 2 + b_k[i] * 2);
   }
 
+  // Residual epilogue: the fp32 residual tile is read into registers before the main loop,
+  // in the chunk order of the coalesced output stores, so its HBM latency hides behind the
+  // matrix work instead of stalling each store of the epilogue. These loads are older than
+  // every fill, so the first stage's wait also covers them. Chunks a vector load cannot take
+  // (ragged tile edge, row stride not a multiple of 4) are read again in the epilogue.
+  constexpr bool kRes = EPI == EPI_RESIDUAL;
+  constexpr int RES_CPR = BN * 4 / 16;                    // 16-byte chunks per fp32 tile row
+  constexpr int RES_LDS = T::RING > BM * BN * 2 ? T::RING : BM * BN * 2;
+  constexpr int RES_PASSES = BM * BN * 4 > RES_LDS ? 2 : 1;
+  constexpr int RES_IT = (BM / RES_PASSES) * RES_CPR / NT; // chunks per thread and pass
+  static_assert(!kRes || RES_IT * NT == (BM / RES_PASSES) * RES_CPR, "residual chunk split");
+  f32x4_t resv[kRes ? RES_PASSES * RES_IT : 1];
+  if constexpr (kRes) {
+    const bool rvec = (g.ldy & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < RES_PASSES * RES_IT; ++j) {
+      const int idx = tid + (j % RES_IT) * NT;
+      const int64_t m = m0 + (j / RES_IT) * (BM / RES_PASSES) + idx / RES_CPR;
+      const int n = n0 + (idx % RES_CPR) * 4;
+      resv[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (rvec && m < g.M && n + 4 <= g.N) resv[j] = *(const f32x4_t *)(g.residual + m * g.ldy + n);
+    }
+  }
+
   const int nk = (K + BK - 1) / BK;
   // The k offset of a stage travels in the scalar offset of the load, so a fill costs no
   // vector arithmetic. Only a ragged last stage (K % BK != 0) switches each lane to its
@@ -615,23 +639,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   const bool out_bf16 = EPI == EPI_RESIDUAL ? false : g.y_dt == DT_BF16;
   const int ob = out_bf16 ? 2 : 4;
   const int rb = OUT_COLS * ob;
-  const int passes = BM * rb > LDS ? 2 : 1;
+  const int passes = kRes ? RES_PASSES : (BM * rb > LDS ? 2 : 1);
+  static_assert(!kRes || RES_LDS == LDS, "residual pass split");
   const int prow = BM / passes;
   const int ncols = EPI == EPI_SWIGLU ? g.n0 : g.N;
   const int nout0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;
   const bool vec_ok = ((g.ldy * ob) & 15) == 0;
+#pragma unroll
   for (int p = 0; p < passes; ++p) {
     if (passes == 1 || (2 * wm) / WGM == p) {
+      // RoPE: the (cos, sin) pairs of a row block are all loaded before any is used, and the
+      // next block's while this one is rotated, so the table reads cost one latency instead
+      // of one per output group. Indices are clamped into the table; a position outside it
+      // turns the rotated values into NaN below.
+      constexpr int NQ = EPI == EPI_QKV_ROPE ? NBN * (AE / 4) : 1;
+      f32x4_t csr[2][NQ];
+      bool pok[2] = {true, true};
+      auto load_cs = [&](int bm, f32x4_t (&c)[NQ], bool &ok) {
+        // rows fit in 32 bits here (M * row width < 2^31 elements); no 64-bit division
+        const int64_t m = m0 + wm * WM + bm * MS + l32;
+        const int mc = (int)(m < g.M ? m : g.M - 1);
+        int pos = g.positions ? g.positions[mc] : mc % g.S;
+        ok = pos >= 0 && pos < g.max_seq;
+        pos = ok ? pos : 0;
+        const int dmask = g.d_head - 1;
+        const bool pow2 = (g.d_head & dmask) == 0;
+#pragma unroll
+        for (int bn = 0; bn < NBN; ++bn)
+#pragma unroll
+          for (int q = 0; q < AE / 4; ++q) {
+            const int n = n0 + wn * WN + bn * MS + (MS == 32 ? 8 * q + 4 * h : 4 * h);
+            const int i0 = (pow2 ? (n & dmask) : n % g.d_head) >> 1;
+            c[bn * (AE / 4) + q] =
+                *(const f32x4_t *)(g.cos_sin + ((int64_t)pos * (g.d_head >> 1) + i0) * 2);
+          }
+      };
+      if constexpr (EPI == EPI_QKV_ROPE) load_cs(0, csr[0], pok[0]);
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
         const int r = wm * WM + bm * MS + l32 - p * prow;
-        const int64_t m = m0 + wm * WM + bm * MS + l32;
-        int pos = 0;
-        if constexpr (EPI == EPI_QKV_ROPE) {
-          // rows fit in 32 bits here (M * row width < 2^31 elements); no 64-bit division
-          const int mc = (int)(m < g.M ? m : g.M - 1);
-          pos = g.positions ? g.positions[mc] : mc % g.S;
-        }
+        if constexpr (EPI == EPI_QKV_ROPE)
+          if (bm + 1 < NBM) load_cs(bm + 1, csr[(bm + 1) & 1], pok[(bm + 1) & 1]);
 #pragma unroll
         for (int bn = 0; bn < (EPI == EPI_SWIGLU ? NBN / 2 : NBN); ++bn) {
 #pragma unroll
@@ -657,11 +705,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
               if constexpr (EPI == EPI_QKV_ROPE) {
                 const int n = n0 + col;
                 if (n < g.n0 + g.n1) {  // q and k columns rotate; v columns pass through
-                  if (pos >= 0 && pos < g.max_seq) {
-                    const int dmask = g.d_head - 1;
-                    const int i0 = ((g.d_head & dmask) == 0 ? (n & dmask) : n % g.d_head) >> 1;
-                    const f32x4_t cs = *(const f32x4_t *)(g.cos_sin +
-                                                          ((int64_t)pos * (g.d_head >> 1) + i0) * 2);
+                  if (pok[bm & 1]) {
+                    const f32x4_t cs = csr[bm & 1][bn * (AE / 4) + q];
                     const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
                     v[0] = x0 * cs[0] - x1 * cs[1];
                     v[1] = x0 * cs[1] + x1 * cs[0];
@@ -690,6 +735,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     __syncthreads();
     // coalesced stores: consecutive threads take consecutive 16-byte chunks of a row
     const int cpr = rb >> 4, epc = 16 / ob;
+    if constexpr (kRes) {
+      // a fresh copy of the thread id: without it the compiler keeps every chunk's address
+      // from the prefetch alive through the main loop (and spills)
+      int tid_e = tid;
+      asm volatile("" : "+v"(tid_e));
+#pragma unroll
+      for (int i = 0; i < RES_IT; ++i) {
+        const int idx = tid_e + i * NT;
+        const int r = idx / RES_CPR, c = idx % RES_CPR;
+        const int64_t m = m0 + p * prow + r;
+        const int n = n0 + c * 4;
+        if (m >= g.M || n >= g.N) continue;
+        const f32x4_t v = *(const f32x4_t *)(lds + stage_off(r, c * 16, rb));
+        const int64_t off = m * g.ldy + n;
+        float *y = (float *)g.y + off;
+        if (vec_ok && n + 4 <= g.N) {
+          *(f32x4_t *)y = v + resv[p * RES_IT + i];
+        } else {
+          const float *res = g.residual + off;
+          for (int x = 0; x < 4 && n + x < g.N; ++x) y[x] = v[x] + res[x];
+        }
+      }
+    } else {
     for (int idx = tid; idx < prow * cpr; idx += NT) {
       const int r = idx / cpr, c = idx - r * cpr;
       const int64_t m = m0 + p * prow + r;
@@ -697,16 +765,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
       if (m >= g.M || n >= ncols) continue;
       const uint4 raw = *(const uint4 *)(lds + stage_off(r, c * 16, rb));
       const int64_t off = m * g.ldy + n;
-      if constexpr (EPI == EPI_RESIDUAL) {
-        f32x4_t v = __builtin_bit_cast(f32x4_t, raw);
-        const float *res = g.residual + off;
-        float *y = (float *)g.y + off;
-        if (vec_ok && n + 4 <= ncols) {
-          *(f32x4_t *)y = v + *(const f32x4_t *)res;
-        } else {
-          for (int x = 0; x < 4 && n + x < ncols; ++x) y[x] = v[x] + res[x];
-        }
-      } else if (out_bf16) {
+      if (out_bf16) {
         bf16_t *y = (bf16_t *)g.y + off;
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
         if (vec_ok && n + 8 <= ncols) {
@@ -746,6 +805,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
           for (int x = 0; x < 4 && n + x < ncols; ++x) y[x] = v[x];
         }
       }
+    }
     }
     if (p + 1 < passes) __syncthreads();
   }
@@ -908,10 +968,12 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // runs the step at its power limit, so a kernel that is faster alone can make the step
     // slower (the LM head on the 256 x 256 ping-pong kernel: 650 against 693 us alone, but
     // 3.39 against 3.28 ms per forward step; 128 x 96 residual and 128 x 192 QKV tiles of 4
-    // waves: 6-12 % faster alone, 3.452 against 3.435 ms per step).
+    // waves: 6-12 % faster alone, 3.452 against 3.435 ms per step). QKV + RoPE on the
+    // 192 x 128 16x16 tiles of the plain store: 3.24 against 3.38 ms per step (QKV 47 against
+    // 54 us); residual products on those tiles: 3.62 ms, SwiGLU on them: no gain.
     case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
     case EPI_RESIDUAL: return run_bf16<128, 192, 64, 4, EPI_RESIDUAL, 1, true, 4, 2>(g, s);
-    case EPI_QKV_ROPE: return run_bf16<128, 192, 64, 4, EPI_QKV_ROPE, 1, true, 4, 2>(g, s);
+    case EPI_QKV_ROPE: return run_bf16<192, 128, 64, 2, EPI_QKV_ROPE, 2, true, 2, 2, false, 16>(g, s);
     case EPI_SWIGLU: return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
   }
