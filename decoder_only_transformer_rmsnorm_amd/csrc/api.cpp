@@ -37,8 +37,15 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace regions of the block and model forward.
 struct WsPlan {
-  size_t flag, x, xn, qkv, o, u, total;
+  size_t flag, x, xn, qkv, o, u, nrm, total;
 };
+
+// The RMSNorm before the QKV and SwiGLU products is split across the product that writes the
+// residual and the product that reads the norm (bf16 models with d_model within the width
+// whose row partials one nrm row holds); the others run the standalone RMSNorm kernel.
+bool norm_split(const tfm_config *c) {
+  return c->dtype == TFM_BF16 && c->d_model <= gemm_norm_max_cols();
+}
 
 WsPlan plan_ws(const tfm_config *c, int B, int S) {
   const size_t M = (size_t)B * S, e = elt(c->dtype);
@@ -51,6 +58,8 @@ WsPlan plan_ws(const tfm_config *c, int B, int S) {
   p.qkv = off; off += round256(M * (qd + 2 * kvd) * e);
   p.o = off; off += round256(M * qd * e);
   p.u = off; off += round256(M * c->d_ff * e);
+  p.nrm = off;
+  if (norm_split(c)) off += round256(M * kNormParts * 4);
   p.total = off;
   return p;
 }
@@ -134,9 +143,13 @@ LayerCache layer_cache(const tfm_config *c, void *cache, int B, int cache_seq, i
   return lc;
 }
 
+// norm_in: the previous block's down projection already left bf16(x * g_attn) in xn and
+// its row partials in nrm (split RMSNorm). g_next: the gain of the next block's first
+// RMSNorm, split into this block's down projection the same way (nullptr: not split).
 int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
                   const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *ws,
-                  const WsPlan &p, int window, hipStream_t s, const LayerCache &lc = {}) {
+                  const WsPlan &p, int window, hipStream_t s, const LayerCache &lc = {},
+                  bool norm_in = false, const void *g_next = nullptr) {
   const int64_t M = (int64_t)B * S;
   const int D = c->d_model, dt = c->dtype;
   const int qd = c->n_heads * c->d_head, kvd = c->n_kv_heads * c->d_head;
@@ -146,14 +159,25 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   uint8_t *qkv = ws + p.qkv;
   void *o = ws + p.o;
   void *u = ws + p.u;
+  const bool split = norm_split(c);
+  float *nrm = split ? (float *)(ws + p.nrm) : nullptr;
+  // the reading product's side of a split RMSNorm: 1 / rms(x) per row from the partials
+  auto scale_rows = [&](GemmArgs &g) {
+    g.rs_part = nrm; g.rs_parts = gemm_residual_col_tiles(D); g.rs_d = D; g.rs_eps = c->eps;
+  };
+  // the writing product's side: bf16(x * gain) into xn and the row partials into nrm
+  auto emit_norm = [&](GemmArgs &g, const void *gain) {
+    g.nrm_g = gain; g.nrm_y = xn; g.nrm_part = nrm;
+  };
 
-  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
+  if (!norm_in) TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
 
   GemmArgs g{};
   g.a = xn; g.lda = D; g.w0 = w->wq; g.w1 = w->wk; g.w2 = w->wv; g.n0 = qd; g.n1 = kvd;
   g.M = M; g.N = qkv_w; g.K = D; g.y = qkv; g.ldy = qkv_w; g.y_dt = dt;
   g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = c->d_head;
   g.max_seq = c->max_seq_len;
+  if (norm_in) scale_rows(g);
   TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
   if (lc.k)   // prefill: rotated k and v rows into the cache slots of their positions
     TFM_HIP(launch_kv_store(qkv, qkv_w, qd, kvd, c->d_head, c->n_kv_heads, B, S, positions,
@@ -166,18 +190,21 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   g = GemmArgs{};
   g.a = o; g.lda = qd; g.w0 = w->wo; g.M = M; g.N = D; g.K = qd; g.y = x; g.ldy = D;
   g.y_dt = DT_F32; g.residual = x;
+  if (split) emit_norm(g, w->g_ffn);
   TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
 
-  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_ffn, dt, xn, dt, M, D, c->eps, s));
+  if (!split) TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_ffn, dt, xn, dt, M, D, c->eps, s));
 
   g = GemmArgs{};
   g.a = xn; g.lda = D; g.w0 = w->w1; g.w1 = w->w3; g.n0 = c->d_ff; g.M = M; g.N = c->d_ff;
   g.K = D; g.y = u; g.ldy = c->d_ff; g.y_dt = dt;
+  if (split) scale_rows(g);
   TFM_HIP(launch_gemm(EPI_SWIGLU, dt, g, s));
 
   g = GemmArgs{};
   g.a = u; g.lda = c->d_ff; g.w0 = w->w2; g.M = M; g.N = D; g.K = c->d_ff; g.y = x; g.ldy = D;
   g.y_dt = DT_F32; g.residual = x;
+  if (split && g_next) emit_norm(g, g_next);
   TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
   return TFM_OK;
 }
@@ -199,9 +226,13 @@ int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t
   TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 2, 0, s));   // token and position flags
   TFM_HIP(launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
                        (int32_t *)(wsb + p.flag), s));
-  for (int l = 0; l < c->n_layers; ++l)
+  const bool split = norm_split(c);
+  for (int l = 0; l < c->n_layers; ++l) {
+    const void *g_next = split && l + 1 < c->n_layers ? w->layers[l + 1].g_attn : nullptr;
     TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p,
-                          layer_window(c, l), s, layer_cache(c, kv_cache, B, cache_seq, l)));
+                          layer_window(c, l), s, layer_cache(c, kv_cache, B, cache_seq, l),
+                          split && l > 0, g_next));
+  }
   TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M, c->d_model,
                          c->eps, s));
   return TFM_OK;

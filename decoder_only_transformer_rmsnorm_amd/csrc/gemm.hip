@@ -48,6 +48,7 @@ constexpr int kRowBytes = 128;  // bytes of one tile row per K stage
 constexpr int kChunks = 8;      // 16-byte chunks per tile row and stage
 constexpr int kGroupM = 8;      // tile-rows per ordering group
 constexpr int kXentBM = 192, kXentBN = 128;   // tile of the fused LM-head cross-entropy
+constexpr int kResidualBN = 192;              // BN of the bf16 residual product
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr uint32_t kOOB = 0x80000000u;        // offset beyond any num_records used here
 
@@ -352,15 +353,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   constexpr int RES_IT = (BM / RES_PASSES) * RES_CPR / NT; // chunks per thread and pass
   static_assert(!kRes || RES_IT * NT == (BM / RES_PASSES) * RES_CPR, "residual chunk split");
   f32x4_t resv[kRes ? RES_PASSES * RES_IT : 1];
+  // fused RMSNorm: the gain of each chunk's 4 columns (bf16), read with the residual
+  uint2 gnv[kRes ? RES_PASSES * RES_IT : 1];
   if constexpr (kRes) {
     const bool rvec = (g.ldy & 3) == 0;
+    const bool fuse = g.nrm_y != nullptr;
 #pragma unroll
     for (int j = 0; j < RES_PASSES * RES_IT; ++j) {
       const int idx = tid + (j % RES_IT) * NT;
       const int64_t m = m0 + (j / RES_IT) * (BM / RES_PASSES) + idx / RES_CPR;
       const int n = n0 + (idx % RES_CPR) * 4;
       resv[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      gnv[j] = uint2{0u, 0u};
       if (rvec && m < g.M && n + 4 <= g.N) resv[j] = *(const f32x4_t *)(g.residual + m * g.ldy + n);
+      if (fuse && n + 4 <= g.N) gnv[j] = *(const uint2 *)((const bf16_t *)g.nrm_g + n);
     }
   }
 
@@ -675,6 +681,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
           }
       };
       if constexpr (EPI == EPI_QKV_ROPE) load_cs(0, csr[0], pok[0]);
+      // RMSNorm split across the products: each of the lane's rows gets 1 / rms(x) from the
+      // producer's per-tile sums of squares (summed in tile order), all read up front
+      float rsv[NBM];
+#pragma unroll
+      for (int bm = 0; bm < NBM; ++bm) rsv[bm] = 1.f;
+      if constexpr (EPI == EPI_QKV_ROPE || EPI == EPI_SWIGLU) {
+        if (g.rs_part) {
+          f32x4_t pr[NBM];
+#pragma unroll
+          for (int bm = 0; bm < NBM; ++bm) {
+            const int64_t m = m0 + wm * WM + bm * MS + l32;
+            pr[bm] = *(const f32x4_t *)(g.rs_part + (m < g.M ? m : g.M - 1) * kNormParts);
+          }
+#pragma unroll
+          for (int bm = 0; bm < NBM; ++bm) {
+            float ss = 0.f;
+#pragma unroll
+            for (int t = 0; t < kNormParts; ++t) ss += t < g.rs_parts ? pr[bm][t] : 0.f;
+            rsv[bm] = rsqrtf(ss / (float)g.rs_d + g.rs_eps);
+          }
+        }
+      }
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
         const int r = wm * WM + bm * MS + l32 - p * prow;
@@ -695,13 +723,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
               col = wn * WN / 2 + bn * MS + nq;
 #pragma unroll
               for (int x = 0; x < 4; ++x) {
-                const float a = acc[gb][bm][4 * q + x], b = acc[ub][bm][4 * q + x];
+                const float a = acc[gb][bm][4 * q + x] * rsv[bm], b = acc[ub][bm][4 * q + x] * rsv[bm];
                 v[x] = a / (1.0f + __expf(-a)) * b;
               }
             } else {
               col = wn * WN + bn * MS + nq;
 #pragma unroll
-              for (int x = 0; x < 4; ++x) v[x] = acc[bn][bm][4 * q + x];
+              for (int x = 0; x < 4; ++x) v[x] = acc[bn][bm][4 * q + x] * rsv[bm];
               if constexpr (EPI == EPI_QKV_ROPE) {
                 const int n = n0 + col;
                 if (n < g.n0 + g.n1) {  // q and k columns rotate; v columns pass through
@@ -740,21 +768,59 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
       // from the prefetch alive through the main loop (and spills)
       int tid_e = tid;
       asm volatile("" : "+v"(tid_e));
+      const bool fuse = g.nrm_y != nullptr;
+      // fused RMSNorm: each chunk's sum of squares, [row][chunk] after this pass's staged rows
+      constexpr int PSQ_LD = RES_CPR + 1;
+      static_assert(!kRes || (BM / RES_PASSES) * (BN * 4 + PSQ_LD * 4) <= LDS,
+                    "fused RMSNorm partials do not fit");
+      float *psq = (float *)(lds + prow * rb);
 #pragma unroll
       for (int i = 0; i < RES_IT; ++i) {
         const int idx = tid_e + i * NT;
         const int r = idx / RES_CPR, c = idx % RES_CPR;
         const int64_t m = m0 + p * prow + r;
         const int n = n0 + c * 4;
-        if (m >= g.M || n >= g.N) continue;
-        const f32x4_t v = *(const f32x4_t *)(lds + stage_off(r, c * 16, rb));
-        const int64_t off = m * g.ldy + n;
-        float *y = (float *)g.y + off;
-        if (vec_ok && n + 4 <= g.N) {
-          *(f32x4_t *)y = v + resv[p * RES_IT + i];
-        } else {
-          const float *res = g.residual + off;
-          for (int x = 0; x < 4 && n + x < g.N; ++x) y[x] = v[x] + res[x];
+        float sq = 0.f;
+        if (m < g.M && n < g.N) {
+          const f32x4_t v = *(const f32x4_t *)(lds + stage_off(r, c * 16, rb));
+          const int64_t off = m * g.ldy + n;
+          float *y = (float *)g.y + off;
+          if (vec_ok && n + 4 <= g.N) {
+            const f32x4_t xv = v + resv[p * RES_IT + i];
+            *(f32x4_t *)y = xv;
+            if (fuse) {
+              const uint2 gg = gnv[p * RES_IT + i];
+              sq = xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
+              uint2 hv;
+              hv.x = pack_bf16x2(xv[0] * __uint_as_float(gg.x << 16),
+                                 xv[1] * __uint_as_float(gg.x & 0xffff0000u));
+              hv.y = pack_bf16x2(xv[2] * __uint_as_float(gg.y << 16),
+                                 xv[3] * __uint_as_float(gg.y & 0xffff0000u));
+              *(uint2 *)((bf16_t *)g.nrm_y + off) = hv;
+            }
+          } else {
+            const float *res = g.residual + off;
+            for (int x = 0; x < 4 && n + x < g.N; ++x) {
+              const float xv = v[x] + res[x];
+              y[x] = xv;
+              if (fuse) {
+                sq += xv * xv;
+                ((bf16_t *)g.nrm_y)[off + x] =
+                    f32_to_bf16(xv * bf16_to_f32(((const bf16_t *)g.nrm_g)[n + x]));
+              }
+            }
+          }
+        }
+        if (fuse) psq[r * PSQ_LD + c] = sq;
+      }
+      if (fuse) {
+        // each row's sum over the tile's columns, chunks in order
+        __syncthreads();
+        if (tid < prow) {
+          const int64_t m = m0 + p * prow + tid;
+          float ss = 0.f;
+          for (int c = 0; c < RES_CPR; ++c) ss += psq[tid * PSQ_LD + c];
+          if (m < g.M) g.nrm_part[m * kNormParts + tn] = ss;
         }
       }
     } else {
@@ -970,9 +1036,11 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // 3.39 against 3.28 ms per forward step; 128 x 96 residual and 128 x 192 QKV tiles of 4
     // waves: 6-12 % faster alone, 3.452 against 3.435 ms per step). QKV + RoPE on the
     // 192 x 128 16x16 tiles of the plain store: 3.24 against 3.38 ms per step (QKV 47 against
-    // 54 us); residual products on those tiles: 3.62 ms, SwiGLU on them: no gain.
+    // 54 us); residual products on those tiles: 3.62 ms, SwiGLU on them: no gain. Residual
+    // products on 16x16 blocks of the same 128 x 192 tiles: 3.179 against 3.197 ms.
     case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
-    case EPI_RESIDUAL: return run_bf16<128, 192, 64, 4, EPI_RESIDUAL, 1, true, 4, 2>(g, s);
+    case EPI_RESIDUAL:
+      return run_bf16<128, kResidualBN, 64, 4, EPI_RESIDUAL, 1, true, 4, 2, false, 16>(g, s);
     case EPI_QKV_ROPE: return run_bf16<192, 128, 64, 2, EPI_QKV_ROPE, 2, true, 2, 2, false, 16>(g, s);
     case EPI_SWIGLU: return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
@@ -993,6 +1061,9 @@ hipError_t dispatch_f32(int epi, const GemmArgs &g, hipStream_t s) {
 }  // namespace
 
 int gemm_xent_parts(int N) { return (N + kXentBN - 1) / kXentBN; }
+
+int gemm_residual_col_tiles(int N) { return (N + kResidualBN - 1) / kResidualBN; }
+int gemm_norm_max_cols() { return kNormParts * kResidualBN; }
 
 int64_t gemm_store_tiles(int dt, int64_t M, int N) {
   // the plain-store tile shapes of dispatch_bf16 / dispatch_f32

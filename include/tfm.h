@@ -171,13 +171,22 @@ size_t tfm_workspace_bytes(const tfm_config *cfg, int B, int S);
 
 /* One pre-norm block  [T1 5.7; T2 FFN & PreNorm] on the float32 residual x (B*S, d_model),
  * in place:  x <- x + W_O attn(RoPE(RMSNorm(x) W_{Q,K,V}^T));  x <- x + SwiGLU(RMSNorm(x)).
- * positions: [dev] int32 (B, S) or NULL; cos_sin: table of cfg->max_seq_len rows. */
+ * positions: [dev] int32 (B, S) or NULL; cos_sin: table of cfg->max_seq_len rows.
+ * bf16 models with d_model <= 768 split the RMSNorm [T1 5.6] between two products, since its
+ * per-row factor commutes with a linear map: RMSNorm(x) W^T = (1/rms(x)) ((x * g) W^T). The
+ * product that writes x also writes bf16(x * g) and each row's partial sums of squares; the
+ * product that reads it scales its fp32 output rows by 1/rms(x). The bf16 rounding then falls
+ * on x * g instead of on x * g / rms(x) (the same relative size). The block's first RMSNorm,
+ * and every RMSNorm of the other models, run as the standalone kernel. */
 int tfm_block_forward(const tfm_config *cfg, const tfm_layer_weights *w, float *x,
                       const int32_t *positions, int B, int S, const float *cos_sin, void *ws,
                       size_t ws_bytes, void *stream);
 
 /* Whole forward  [T1 5.7]: x = embed[ids]; n_layers blocks; RMSNorm(g_final); logits =
- * x_f lm_head^T for every position, no softmax. ids: [dev] int32 (B, S); logits: [dev]
+ * x_f lm_head^T for every position, no softmax. bf16 models with d_model <= 768 split each
+ * block's RMSNorms as tfm_block_forward does, the first one of block l > 0 into block l-1's
+ * down projection; the first block's and the final RMSNorm run standalone.
+ * ids: [dev] int32 (B, S); logits: [dev]
  * (B*S, ld_logits) of logits_dt, ld_logits >= vocab (any value; odd is allowed).
  * An out-of-range id is reported by tfm_check_device_flags (NaN logits for that row). */
 int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const int32_t *ids,
