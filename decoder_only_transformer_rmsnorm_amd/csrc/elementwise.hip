@@ -118,28 +118,44 @@ __global__ void rope_kernel(T *x, int64_t row_stride, const int32_t *pos, int B,
 
 // Next-token cross-entropy ("LLM 2" Optimize / Loss; "Transformer篇" (fengye404.top) 12):
 // combine the LM-head tile partials of one row, max_t and sum_t of exp(logit - max_t), into
-// the row's log-sum-exp (fixed tile order) and subtract the target logit.
-__global__ void xent_reduce_kernel(const float *__restrict__ x_max, const float *__restrict__ x_sum,
-                                   const float *__restrict__ x_tgt, const int32_t *targets, int T,
-                                   int64_t M, int V, float *loss) {
-  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  const int t = targets[m];
-  if (t < 0) {
-    loss[m] = 0.f;
-    return;
-  }
-  if (t >= V) {
-    loss[m] = __builtin_nanf("");
-    return;
-  }
+// the row's log-sum-exp in a fixed order and subtract the target logit.
+// A workgroup takes 64 consecutive rows (lane = row, so every load of a wave reads 256
+// consecutive bytes of one partial column) and its 8 waves split the column tiles t = w, w + 8,
+// ...; the waves' maxima, then their sums of exp, are combined through LDS in wave order, so
+// the result is deterministic.
+constexpr int kXentWaves = 8;
+__global__ __launch_bounds__(64 * kXentWaves) void xent_reduce_kernel(
+    const float *__restrict__ x_max, const float *__restrict__ x_sum,
+    const float *__restrict__ x_tgt, const int32_t *targets, int T, int64_t M, int V,
+    float *loss) {
+  __shared__ float red[kXentWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t m = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t mc = m < M ? m : M - 1;
   constexpr float kLog2e = 1.4426950408889634f;
   float mx = -__builtin_inff();
-  for (int i = 0; i < T; ++i) mx = fmaxf(mx, x_max[(int64_t)i * M + m]);
+#pragma unroll 4
+  for (int i = w; i < T; i += kXentWaves) mx = fmaxf(mx, x_max[(int64_t)i * M + mc]);
+  red[w][lane] = mx;
+  __syncthreads();
+  mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kXentWaves; ++i) mx = fmaxf(mx, red[i][lane]);
+  __syncthreads();
   float se = 0.f;
-  for (int i = 0; i < T; ++i)
-    se += x_sum[(int64_t)i * M + m] * exp2f((x_max[(int64_t)i * M + m] - mx) * kLog2e);
-  loss[m] = mx + logf(se) - x_tgt[m];
+#pragma unroll 4
+  for (int i = w; i < T; i += kXentWaves)
+    se += x_sum[(int64_t)i * M + mc] * exp2f((x_max[(int64_t)i * M + mc] - mx) * kLog2e);
+  red[w][lane] = se;
+  __syncthreads();
+  if (w != 0 || m >= M) return;
+  se = 0.f;
+#pragma unroll
+  for (int i = 0; i < kXentWaves; ++i) se += red[i][lane];
+  const int t = targets[m];
+  if (t < 0) loss[m] = 0.f;
+  else if (t >= V) loss[m] = __builtin_nanf("");
+  else loss[m] = mx + logf(se) - x_tgt[m];
 }
 
 // Mean over the rows with a target: one workgroup, strided fp64 partial sums in a fixed order
@@ -264,8 +280,8 @@ hipError_t launch_xent_reduce(const float *x_max, const float *x_sum, const floa
                               const int32_t *targets, int T, int64_t M, int V, float *loss,
                               float *mean, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  xent_reduce_kernel<<<blocks_for(M, 256), 256, 0, s>>>(x_max, x_sum, x_tgt, targets, T, M, V,
-                                                        loss);
+  xent_reduce_kernel<<<blocks_for(M, 64), 64 * kXentWaves, 0, s>>>(x_max, x_sum, x_tgt, targets,
+                                                                   T, M, V, loss);
   if (mean) mean_loss_kernel<<<1, kMeanThreads, 0, s>>>(loss, targets, M, mean);
   return hipGetLastError();
 }
