@@ -21,8 +21,9 @@
 //    consecutive keys of one head dimension. The keys of a 16-key step are taken in the
 //    order the score accumulator holds them ({4h..4h+3, 4h+8..4h+11} for lane half h).
 //  * Softmax state (max, sum, rescale) is fp32; exponentials are base 2 with the
-//    1/sqrt(d_head) * log2(e) factor folded into one fused multiply-add. The output is only
-//    rescaled when some row maximum of the wave changed.
+//    1/sqrt(d_head) * log2(e) factor folded into one fused multiply-add. A row's reference
+//    maximum only moves when a tile's scores exceed it by more than 8 in log2 units, so the
+//    output is rescaled rarely (softmax does not depend on the shift).
 //  * Tiles entirely above the diagonal are never loaded; per wave, tiles past its last
 //    query are skipped; only the diagonal tile is masked. Query tiles are issued
 //    longest-first to even out the causal imbalance.
@@ -44,6 +45,7 @@ constexpr int kBQ = 128;   // queries per workgroup
 constexpr int kBKV = 64;   // keys per tile
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.f;   // headroom of the softmax reference maximum (log2 units)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -292,7 +294,12 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
                                                        false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float m_new = fmaxf(m_run, mt);
+    // The reference maximum only moves when the tile's maximum exceeds it by more than 2^8 in
+    // probability (log2 units): exp2(s - ref) then stays below 256, and the result does not
+    // depend on which reference is used (the same one scales the row sum), so the running
+    // output is rescaled rarely instead of on almost every tile.
+    const bool move = (mt - m_run) * scale_log2 > kLazyLog2;
+    const float m_new = move ? fmaxf(m_run, mt) : m_run;
     // a lane that has seen no visible key yet (possible at a window's edge) keeps zero weight
     const float mc = m_new == -__builtin_inff() ? 0.f : m_new * scale_log2;
     u32x4_t pf[PV_STEPS];
@@ -309,8 +316,8 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
         }
         pf[2 * kb + half] = w;
       }
-    if (__any(m_new != m_run)) {   // some row maximum moved: rescale the running output
-      const float alpha = fast_exp2(m_run * scale_log2 - mc);
+    if (__any(move)) {   // some row's reference moved: rescale the running output
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run * scale_log2 - mc);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       lacc[0] *= alpha;
