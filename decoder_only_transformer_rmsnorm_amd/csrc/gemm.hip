@@ -721,10 +721,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
               const int gb = MS == 32 ? 2 * bn : 4 * (bn >> 1) + (bn & 1);
               const int ub = MS == 32 ? 2 * bn + 1 : gb + 2;
               col = wn * WN / 2 + bn * MS + nq;
+              // SiLU(a) b = a b / (1 + 2^(-a log2 e)) with the hardware exp2 and reciprocal
+              // (about 1 ulp each, far inside the bf16 rounding that follows); a very negative
+              // a gives 2^(+big) = inf, a reciprocal of 0 and SiLU = -0
 #pragma unroll
               for (int x = 0; x < 4; ++x) {
                 const float a = acc[gb][bm][4 * q + x] * rsv[bm], b = acc[ub][bm][4 * q + x] * rsv[bm];
-                v[x] = a / (1.0f + __expf(-a)) * b;
+                v[x] = a * b *
+                       __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
               }
             } else {
               col = wn * WN + bn * MS + nq;
