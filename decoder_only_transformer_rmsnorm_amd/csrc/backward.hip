@@ -106,7 +106,10 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return r;
 }
 
-// one workgroup per row: dz[j] = (exp(z_j - lse) - [j == t]) / N for j < V, 0 in [V, ldd)
+// one workgroup per row: dz[j] = (exp(z_j - lse) - [j == t]) / N for j < V, 0 in [V, ldd).
+// Rows are read 16 bytes per lane when the row stride allows it (three passes: max, sum of
+// exp, gradient; the later ones mostly hit L2); exponentials use the hardware exp2 (about
+// 1 ulp, far below the bf16 rounding of the stored gradient), the loss itself logf.
 template <typename TO>
 __global__ __launch_bounds__(256) void ce_back_kernel(const float *__restrict__ z, int64_t ldz,
                                                       const int32_t *__restrict__ targets, int V,
@@ -114,29 +117,58 @@ __global__ __launch_bounds__(256) void ce_back_kernel(const float *__restrict__ 
                                                       TO *__restrict__ dz, int64_t ldd,
                                                       float *__restrict__ row_loss) {
   __shared__ float red[4];
+  constexpr float kLog2e = 1.4426950408889634f;
   const int64_t m = blockIdx.x;
   const float *zr = z + m * ldz;
   TO *dr = dz + m * ldd;
   const int t = targets[m];
+  const int tid = threadIdx.x;
   if (t < 0 || t >= V) {
-    for (int64_t j = threadIdx.x; j < ldd; j += 256) st1(dr + j, 0.f);
-    if (threadIdx.x == 0) row_loss[m] = 0.f;
+    for (int64_t j = tid; j < ldd; j += 256) st1(dr + j, 0.f);
+    if (tid == 0) row_loss[m] = 0.f;
     return;
   }
+  // 16-byte groups [0, nv) when rows start 16-byte aligned, scalar columns [4 nv, V) after
+  const int nv = (ldz & 3) == 0 ? V >> 2 : 0;
   float mx = -__builtin_inff();
-  for (int j = threadIdx.x; j < V; j += 256) mx = fmaxf(mx, zr[j]);
+  for (int j = tid; j < nv; j += 256) {
+    const f32x4_t v = *(const f32x4_t *)(zr + 4 * j);
+    mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  }
+  for (int j = 4 * nv + tid; j < V; j += 256) mx = fmaxf(mx, zr[j]);
   mx = block_max(mx, red);
+  const float mc = mx * kLog2e;
   float se = 0.f;
-  for (int j = threadIdx.x; j < V; j += 256) se += expf(zr[j] - mx);
+  for (int j = tid; j < nv; j += 256) {
+    const f32x4_t v = *(const f32x4_t *)(zr + 4 * j);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) se += __builtin_amdgcn_exp2f(__builtin_fmaf(v[x], kLog2e, -mc));
+  }
+  for (int j = 4 * nv + tid; j < V; j += 256)
+    se += __builtin_amdgcn_exp2f(__builtin_fmaf(zr[j], kLog2e, -mc));
   se = block_sum(se, red);
   const float lse = mx + logf(se);
+  const float lc = lse * kLog2e;
   const float inv_n = 1.0f / (float)n_valid[0];
-  for (int64_t j = threadIdx.x; j < ldd; j += 256) {
+  // vector stores need 4 consecutive outputs 4-aligned in the output row as well
+  const int nvo = ((ldd & 3) == 0) ? nv : 0;
+  for (int j = tid; j < nvo; j += 256) {
+    const f32x4_t v = *(const f32x4_t *)(zr + 4 * j);
+    f32x4_t d;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      d[x] = (__builtin_amdgcn_exp2f(__builtin_fmaf(v[x], kLog2e, -lc)) -
+              (4 * j + x == t ? 1.f : 0.f)) * inv_n;
+    store4(dr + 4 * j, d);
+  }
+  for (int64_t j = 4 * (int64_t)nvo + tid; j < ldd; j += 256) {
     float d = 0.f;
-    if (j < V) d = (expf(zr[j] - lse) - (j == t ? 1.f : 0.f)) * inv_n;
+    if (j < V)
+      d = (__builtin_amdgcn_exp2f(__builtin_fmaf(zr[j], kLog2e, -lc)) - (j == t ? 1.f : 0.f)) *
+          inv_n;
     st1(dr + j, d);
   }
-  if (threadIdx.x == 0) row_loss[m] = lse - zr[t];
+  if (tid == 0) row_loss[m] = lse - zr[t];
 }
 
 // mean of the row losses over the counted rows (fp64, fixed order)
@@ -156,7 +188,7 @@ __global__ __launch_bounds__(1024) void mean_rows_kernel(const float *row_loss, 
 
 // ---- RMSNorm backward ("Transformer 篇" 5.6): one wave per row, 4 waves x kRows rows per
 // workgroup; lane holds the 4-column groups lane + 64 i.
-constexpr int kRmsRows = 16;   // rows per wave
+constexpr int kRmsRows = 4;   // rows per wave
 template <int VPT, typename TG>
 __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__ x,
                                                        const TG *__restrict__ g,
@@ -176,17 +208,21 @@ __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__
   for (int k = 0; k < kRmsRows; ++k) {
     const int64_t r = ((int64_t)blockIdx.x * 4 + w) * kRmsRows + k;
     if (r >= rows) break;
-    f32x4_t xv[VPT], dv[VPT];
+    f32x4_t xv[VPT], dv[VPT], ov[VPT];
     float ss = 0.f, dot = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
+    for (int i = 0; i < VPT; ++i) {   // x, dy and the dx being accumulated, all issued first
       const int gi = lane + 64 * i;
       if (gi < ng) {
         xv[i] = load4(x + r * d + 4 * gi);
         dv[i] = load4(dy + r * d + 4 * gi);
+        ov[i] = load4(dx + r * d + 4 * gi);
       } else {
-        xv[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        xv[i] = dv[i] = ov[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
       const f32x4_t t = dv[i] * gv[i] * xv[i];
       ss += xv[i][0] * xv[i][0] + xv[i][1] * xv[i][1] + xv[i][2] * xv[i][2] + xv[i][3] * xv[i][3];
       dot += t[0] + t[1] + t[2] + t[3];
@@ -199,8 +235,7 @@ __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__
     for (int i = 0; i < VPT; ++i) {
       const int gi = lane + 64 * i;
       if (gi < ng) {
-        float *p = dx + r * d + 4 * gi;
-        store4(p, load4(p) + ri * gv[i] * dv[i] - xv[i] * c3);
+        store4(dx + r * d + 4 * gi, ov[i] + ri * gv[i] * dv[i] - xv[i] * c3);
         gacc[i] += dv[i] * xv[i] * ri;
       }
     }
@@ -217,13 +252,27 @@ __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__
     dg_part[(int64_t)blockIdx.x * d + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
 }
 
-// out[c] (=|+=) sum over parts in order
-__global__ void colsum_kernel(const float *__restrict__ part, int nparts, int d,
-                              float *__restrict__ out, int accumulate) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= d) return;
+// out[c] (=|+=) sum over parts: a workgroup takes 64 columns (lane = column, so each load is
+// 256 contiguous bytes); its 16 waves take parts w, w + 16, ... in order and their sums meet
+// in LDS in wave order, so the result does not depend on scheduling.
+constexpr int kColsumWaves = 16;
+__global__ __launch_bounds__(64 * kColsumWaves) void colsum_kernel(const float *__restrict__ part,
+                                                                   int nparts, int d,
+                                                                   float *__restrict__ out,
+                                                                   int accumulate) {
+  __shared__ float red[kColsumWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int cc = c < d ? c : d - 1;
   float s = 0.f;
-  for (int i = 0; i < nparts; ++i) s += part[(int64_t)i * d + c];
+#pragma unroll 4
+  for (int i = w; i < nparts; i += kColsumWaves) s += part[(int64_t)i * d + cc];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w != 0 || c >= d) return;
+  s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kColsumWaves; ++i) s += red[i][lane];
   out[c] = accumulate ? out[c] + s : s;
 }
 
@@ -686,7 +735,7 @@ hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const fl
     default: return hipErrorInvalidValue;
   }
 #undef TFM_RMSB
-  colsum_kernel<<<nblk(d, 256), 256, 0, s>>>(dg_part, (int)nb, d, dg, accumulate_dg);
+  colsum_kernel<<<nblk(d, 64), 64 * kColsumWaves, 0, s>>>(dg_part, (int)nb, d, dg, accumulate_dg);
   return hipGetLastError();
 }
 
