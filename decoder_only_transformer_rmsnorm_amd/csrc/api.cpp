@@ -894,7 +894,9 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   // ---- LM head and final RMSNorm
   TFM_HIP(launch_transpose(w->lm_head, dt, D, wT, dt, Vp, Vp, V, D, s));
   TFM_TRY(gemm(EPI_STORE, dt, dlog, Vp, wT, M, D, Vp, dhp, D, DT_F32, nullptr, s));
-  TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, V, s));
+  // all Vp columns (the cross-entropy backward zeroes [V, Vp)), so the transpose takes the
+  // 16-byte path; rows [V, Vp) of dlogT are zeros the weight-gradient product never reads
+  TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, Vp, s));
   TFM_HIP(launch_transpose(xf, dt, D, xfT, dt, Mp, Mp, M, D, s));
   float *g_lm = tied ? gr->embed : gr->lm_head;
   TFM_TRY(gemm_wgrad(dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, skp, s));

@@ -58,6 +58,45 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI *__restrict__ s
   }
 }
 
+// bf16 -> bf16 transpose with 16-byte global accesses (every dimension and stride a multiple
+// of 8 elements): a 64 x 64 tile, each thread reads 8 consecutive elements of a source row
+// (two rows per thread) into LDS (pitch 66 elements, so the 8 threads that later read one
+// column segment hit distinct banks) and writes 8 consecutive elements of a destination row.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
+                                                             int64_t lds,
+                                                             uint16_t *__restrict__ dst,
+                                                             int64_t ldd, int64_t R,
+                                                             int64_t R_valid, int C) {
+  constexpr int P = 66;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, g8 = tid & 7, row = tid >> 3;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    const int i = row + 32 * ps;
+    const int64_t r = r0 + i;
+    const int c = c0 + 8 * g8;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < R_valid && c < C) v = *(const uint4 *)(src + r * lds + c);
+    uint32_t *t = (uint32_t *)(tile + i * P + 8 * g8);
+    t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    const int oc = row + 32 * ps;
+    const int c = c0 + oc;
+    const int64_t r = r0 + 8 * g8;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)tile[(8 * g8 + 2 * k) * P + oc] |
+             ((uint32_t)tile[(8 * g8 + 2 * k + 1) * P + oc] << 16);
+    if (c < C && r < R) *(uint4 *)(dst + (int64_t)c * ldd + r) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 template <typename TI, typename TO>
 __global__ void convert_kernel(const TI *__restrict__ src, TO *__restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -662,7 +701,11 @@ hipError_t launch_transpose(const void *src, int src_dt, int64_t lds, void *dst,
   if (R == 0 || C == 0) return hipSuccess;
   const dim3 grid(nblk(C, 64), nblk(R, 64));
   if (grid.y > 65535) return hipErrorInvalidValue;
-  if (src_dt == DT_BF16 && dst_dt == DT_BF16)
+  const bool vec = ((lds | ldd | R | C) & 7) == 0 && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0;
+  if (src_dt == DT_BF16 && dst_dt == DT_BF16 && vec)
+    transpose_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t *)src, lds, (uint16_t *)dst, ldd,
+                                               R, R_valid, C);
+  else if (src_dt == DT_BF16 && dst_dt == DT_BF16)
     transpose_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>((const bf16_t *)src, lds, (bf16_t *)dst, ldd, R, R_valid, C);
   else if (src_dt == DT_F32 && dst_dt == DT_BF16)
     transpose_kernel<float, bf16_t><<<grid, 256, 0, s>>>((const float *)src, lds, (bf16_t *)dst, ldd, R, R_valid, C);
