@@ -20,6 +20,7 @@
 //  * embed_back_kernel: scatter-add of the input gradient into the embedding rows;
 //  * sumsq / clip_coef / adamw: the global-norm clipping coefficient and the AdamW update.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -317,23 +318,44 @@ __global__ __launch_bounds__(64 * kColsumWaves) void colsum_kernel(const float *
 
 // ---- SwiGLU ("Transformer 篇" 5.3): u = SiLU(a) c; da = du c SiLU'(a), dc = du SiLU(a),
 // SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))).
+// sigma(a) = 1 / (1 + e^-a): for bf16 data with the hardware exp2 and reciprocal (about 1 ulp
+// each, far below the bf16 rounding of the results), for fp32 data with the library forms.
+template <typename T>
+__device__ __forceinline__ float sigmoid_of(float a) {
+  if constexpr (std::is_same<T, bf16_t>::value)
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+  else
+    return 1.0f / (1.0f + __expf(-a));
+}
+
+// 4 consecutive elements per thread (n % 4 == 0 and 4-element aligned buffers, which the
+// callers' shapes give: d_ff is a multiple of 4)
 template <typename T>
 __global__ void swiglu_fwd_kernel(const T *a, const T *c, T *u, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
-  const float av = ld1(a + i);
-  st1(u + i, av / (1.0f + __expf(-av)) * ld1(c + i));
+  const f32x4_t av = load4(a + i), cv = load4(c + i);
+  f32x4_t r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) r[x] = av[x] * sigmoid_of<T>(av[x]) * cv[x];
+  store4(u + i, r);
 }
 
 template <typename T>
 __global__ void swiglu_back_kernel(const T *a, const T *c, const float *du, T *da, T *dc,
                                    int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
-  const float av = ld1(a + i), cv = ld1(c + i), g = du[i];
-  const float sg = 1.0f / (1.0f + __expf(-av));
-  st1(da + i, g * cv * sg * (1.0f + av * (1.0f - sg)));
-  st1(dc + i, g * av * sg);
+  const f32x4_t av = load4(a + i), cv = load4(c + i), g = load4(du + i);
+  f32x4_t ra, rc;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const float sg = sigmoid_of<T>(av[x]);
+    ra[x] = g[x] * cv[x] * sg * (1.0f + av[x] * (1.0f - sg));
+    rc[x] = g[x] * av[x] * sg;
+  }
+  store4(da + i, ra);
+  store4(dc + i, rc);
 }
 
 // ---- inverse RoPE in place on H heads of rows (row stride), position p (or row % S)
@@ -785,11 +807,12 @@ hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const fl
 hipError_t launch_swiglu_fwd(const void *a, const void *c, void *u, int dt, int64_t n,
                              hipStream_t s) {
   if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;   // the kernel takes 4 elements per thread
   if (dt == DT_BF16)
-    swiglu_fwd_kernel<bf16_t><<<nblk(n, 256), 256, 0, s>>>((const bf16_t *)a, (const bf16_t *)c,
+    swiglu_fwd_kernel<bf16_t><<<nblk(n / 4, 256), 256, 0, s>>>((const bf16_t *)a, (const bf16_t *)c,
                                                            (bf16_t *)u, n);
   else
-    swiglu_fwd_kernel<float><<<nblk(n, 256), 256, 0, s>>>((const float *)a, (const float *)c,
+    swiglu_fwd_kernel<float><<<nblk(n / 4, 256), 256, 0, s>>>((const float *)a, (const float *)c,
                                                           (float *)u, n);
   return hipGetLastError();
 }
@@ -797,11 +820,12 @@ hipError_t launch_swiglu_fwd(const void *a, const void *c, void *u, int dt, int6
 hipError_t launch_swiglu_backward(const void *a, const void *c, const float *du, void *da,
                                   void *dc, int dt, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;   // the kernel takes 4 elements per thread
   if (dt == DT_BF16)
-    swiglu_back_kernel<bf16_t><<<nblk(n, 256), 256, 0, s>>>(
+    swiglu_back_kernel<bf16_t><<<nblk(n / 4, 256), 256, 0, s>>>(
         (const bf16_t *)a, (const bf16_t *)c, du, (bf16_t *)da, (bf16_t *)dc, n);
   else
-    swiglu_back_kernel<float><<<nblk(n, 256), 256, 0, s>>>(
+    swiglu_back_kernel<float><<<nblk(n / 4, 256), 256, 0, s>>>(
         (const float *)a, (const float *)c, du, (float *)da, (float *)dc, n);
   return hipGetLastError();
 }
