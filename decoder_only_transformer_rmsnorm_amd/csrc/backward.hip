@@ -147,9 +147,12 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 }
 
 // one workgroup per row: dz[j] = (exp(z_j - lse) - [j == t]) / N for j < V, 0 in [V, ldd).
-// Rows are read 16 bytes per lane when the row stride allows it (three passes: max, sum of
-// exp, gradient; the later ones mostly hit L2); exponentials use the hardware exp2 (about
-// 1 ulp, far below the bf16 rounding of the stored gradient), the loss itself logf.
+// Rows are read 16 bytes per lane when the row stride allows it, in two passes: the first
+// forms each thread's sum of exp against its own reference maximum (moved only when a value
+// exceeds it by more than 8 in log2 units, so the sum is rescaled rarely and stays below 2^8
+// per term), the threads' (reference, sum) pairs are combined against the row maximum, and
+// the second pass writes the gradient. Exponentials use the hardware exp2 (about 1 ulp, far
+// below the bf16 rounding of the stored gradient), the loss itself logf.
 template <typename TO>
 __global__ __launch_bounds__(256) void ce_back_kernel(const float *__restrict__ z, int64_t ldz,
                                                       const int32_t *__restrict__ targets, int V,
@@ -170,25 +173,25 @@ __global__ __launch_bounds__(256) void ce_back_kernel(const float *__restrict__ 
   }
   // 16-byte groups [0, nv) when rows start 16-byte aligned, scalar columns [4 nv, V) after
   const int nv = (ldz & 3) == 0 ? V >> 2 : 0;
-  float mx = -__builtin_inff();
+  float ref = -__builtin_inff(), sum = 0.f;   // this thread's reference (log2 units) and sum
+  auto add = [&](float zv) {
+    const float y = zv * kLog2e;
+    if (y > ref + 8.f) {   // rare after the first values: move the reference up to y
+      sum *= __builtin_amdgcn_exp2f(ref - y);   // 0 while ref is still -inf
+      ref = y;
+    }
+    sum += __builtin_amdgcn_exp2f(y - ref);
+  };
   for (int j = tid; j < nv; j += 256) {
     const f32x4_t v = *(const f32x4_t *)(zr + 4 * j);
-    mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    add(v[0]); add(v[1]); add(v[2]); add(v[3]);
   }
-  for (int j = 4 * nv + tid; j < V; j += 256) mx = fmaxf(mx, zr[j]);
-  mx = block_max(mx, red);
-  const float mc = mx * kLog2e;
-  float se = 0.f;
-  for (int j = tid; j < nv; j += 256) {
-    const f32x4_t v = *(const f32x4_t *)(zr + 4 * j);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) se += __builtin_amdgcn_exp2f(__builtin_fmaf(v[x], kLog2e, -mc));
-  }
-  for (int j = 4 * nv + tid; j < V; j += 256)
-    se += __builtin_amdgcn_exp2f(__builtin_fmaf(zr[j], kLog2e, -mc));
+  for (int j = 4 * nv + tid; j < V; j += 256) add(zr[j]);
+  const float mref = block_max(ref, red);   // the row maximum is within 8 of it
+  float se = ref == -__builtin_inff() ? 0.f : sum * __builtin_amdgcn_exp2f(ref - mref);
   se = block_sum(se, red);
-  const float lse = mx + logf(se);
-  const float lc = lse * kLog2e;
+  const float lc = mref + log2f(se);        // log-sum-exp in log2 units
+  const float lse = lc * 0.6931471805599453f;
   const float inv_n = 1.0f / (float)n_valid[0];
   // vector stores need 4 consecutive outputs 4-aligned in the output row as well
   const int nvo = ((ldd & 3) == 0) ? nv : 0;
