@@ -412,20 +412,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   for (int e = 0; e < DH; ++e) op[e] = acc[e] * inv;
 }
 
-// Compute units of the current device (cached per device).
-int compute_units() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int DH>
 hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int64_t kvs, void *o,
                     int64_t os, int B, int S, int Hq, int Hkv, int window, float *lse,
@@ -455,6 +441,20 @@ hipError_t run_f32(const void *q, int64_t qs, const void *k, const void *v, int6
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 bool attention_fits(int dt, int S, int64_t kv_stride) {
   return dt != DT_BF16 || ((int64_t)S + kBKV) * kv_stride * 2 < ((int64_t)1 << 31);

@@ -109,23 +109,34 @@ struct TileLoader {
   }
 };
 
+// Work item of block `bid` in a grid of `n` blocks: rounds of `cus` blocks (one per CU when
+// the grid is dispatched in order) alternate direction, so a CU's blocks of successive rounds
+// take items from the long and the short end of the longest-first order.
+__device__ __forceinline__ int snake_item(int bid, int n, int cus) {
+  const int round = bid / cus, in_round = bid % cus;
+  const int item = (round & 1) ? round * cus + (cus - 1 - in_round) : bid;
+  return item < n ? item : bid;   // partial last round: keep in order
+}
+
 // ---------------------------------------------------------------- dQ (and D)
-// grid (ceil(S / 128), Hq, B)
+// grid ceil(S / 128) * Hq * B, query tiles longest first (the last tile sees every key)
 template <int DH>
 __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dq_mfma_kernel(
     const bf16_t *__restrict__ qkv, int64_t ld, const bf16_t *__restrict__ o, int64_t ldo,
     const bf16_t *__restrict__ dout, int64_t lddo, bf16_t *__restrict__ dqkv, int S, int Hq,
     int Hkv, int window, float scale, const float *__restrict__ lse_in,
-    float *__restrict__ dsum_out) {
+    float *__restrict__ dsum_out, int B, int cus) {
   constexpr int KS = DH / 16, NDB = DH / 32;
   using TL = BTile<DH>;
   __shared__ __attribute__((aligned(16))) uint8_t kt[TL::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vt[TL::BYTES];
   const int qd = Hq * DH, kvd = Hkv * DH;
-  const int hq = blockIdx.y, b = blockIdx.z, g = hq / (Hq / Hkv);
+  const int nqt = (S + kRows - 1) / kRows;
+  const int item = snake_item((int)blockIdx.x, (int)gridDim.x, cus);
+  const int hq = (item % (Hq * B)) % Hq, b = (item % (Hq * B)) / Hq, g = hq / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int q0 = blockIdx.x * kRows, qw0 = q0 + 32 * w;
+  const int q0 = (nqt - 1 - item / (Hq * B)) * kRows, qw0 = q0 + 32 * w;
   const int my_q = qw0 + l32;
   const bool live = my_q < S;
   const int64_t rq = (int64_t)b * S + (live ? my_q : S - 1);
@@ -234,22 +245,24 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dq_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- dK, dV
-// grid (ceil(S / 128), Hkv, B); loops over the query heads of the group
+// grid ceil(S / 128) * Hkv * B, key tiles longest first (the first tile is seen by every
+// query); loops over the query heads of the group
 template <int DH>
 __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
     const bf16_t *__restrict__ qkv, int64_t ld, const bf16_t *__restrict__ dout, int64_t lddo,
     bf16_t *__restrict__ dqkv, int S, int Hq, int Hkv, int window, float scale,
-    const float *__restrict__ lse_in, const float *__restrict__ dsum_in) {
+    const float *__restrict__ lse_in, const float *__restrict__ dsum_in, int B, int cus) {
   constexpr int KS = DH / 16, NDB = DH / 32;
   using TL = BTile<DH>;
   __shared__ __attribute__((aligned(16))) uint8_t qt[TL::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t ot[TL::BYTES];
   __shared__ __attribute__((aligned(16))) float ls[kTile], dsm[kTile];
   const int qd = Hq * DH, kvd = Hkv * DH, G = Hq / Hkv;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int item = snake_item((int)blockIdx.x, (int)gridDim.x, cus);
+  const int g = (item % (Hkv * B)) % Hkv, b = (item % (Hkv * B)) / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int k0 = blockIdx.x * kRows, kw0 = k0 + 32 * w;
+  const int k0 = (item / (Hkv * B)) * kRows, kw0 = k0 + 32 * w;
   const int my_k = kw0 + l32;
   const bool live = my_k < S;
   const int64_t rk = (int64_t)b * S + (live ? my_k : S - 1);
@@ -380,13 +393,15 @@ hipError_t run(const void *qkv, int64_t ld, const void *o, int64_t ldo, const vo
                int64_t lddo, void *dqkv, int B, int S, int Hq, int Hkv, int window,
                const float *lse, float *dsum, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)DH);
-  const unsigned nb = (unsigned)((S + kRows - 1) / kRows);
-  attn_dq_mfma_kernel<DH><<<dim3(nb, Hq, B), 256, 0, s>>>(
+  const int64_t nb = (S + kRows - 1) / kRows;
+  if (nb * Hq * B > 0x7fffffff) return hipErrorInvalidValue;
+  const int cus = compute_units();
+  attn_dq_mfma_kernel<DH><<<dim3((unsigned)(nb * Hq * B)), 256, 0, s>>>(
       (const bf16_t *)qkv, ld, (const bf16_t *)o, ldo, (const bf16_t *)dout, lddo,
-      (bf16_t *)dqkv, S, Hq, Hkv, window, scale, lse, dsum);
-  attn_dkdv_mfma_kernel<DH><<<dim3(nb, Hkv, B), 256, 0, s>>>(
+      (bf16_t *)dqkv, S, Hq, Hkv, window, scale, lse, dsum, B, cus);
+  attn_dkdv_mfma_kernel<DH><<<dim3((unsigned)(nb * Hkv * B)), 256, 0, s>>>(
       (const bf16_t *)qkv, ld, (const bf16_t *)dout, lddo, (bf16_t *)dqkv, S, Hq, Hkv, window,
-      scale, lse, dsum);
+      scale, lse, dsum, B, cus);
   return hipGetLastError();
 }
 

@@ -96,6 +96,9 @@ hipError_t launch_attention(const void *q, int64_t q_stride, const void *k, cons
                             int Hkv, int d_head, int dt, int window, hipStream_t s,
                             float *lse = nullptr);
 bool attention_supported(int dt, int d_head);
+// Compute units of the current device (cached per device), for work orders over rounds of
+// one workgroup per CU.
+int compute_units();
 // ---- incremental decoding (decode.hip), bf16 only
 struct DecodeGemmArgs {
   const void *x;            // (M, K) activations, row stride ldx
