@@ -136,7 +136,8 @@ def main() -> int:
     ap.add_argument("--logits", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--dense-logits", action="store_true",
                     help="logits row stride = vocab (default: vocab rounded up to a multiple of "
-                         "8 elements, so every logits row starts 16-byte aligned)")
+                         "64 elements, so every logits row starts on a 128-byte line and no line "
+                         "is shared by two output tiles)")
     ap.add_argument("--counters", action="store_true",
                     help="only a 1 GiB copy and 3 LM-head launches, for rocprofv3 --pmc passes")
     args = ap.parse_args()
@@ -163,7 +164,7 @@ def main() -> int:
     dm = tfm.DeviceModel(inputs)
     stream = torch.cuda.current_stream()
     logits_dtype = torch.float32 if args.logits == "f32" else torch.bfloat16
-    ld_logits = cfg.vocab if args.dense_logits else (cfg.vocab + 7) // 8 * 8
+    ld_logits = cfg.vocab if args.dense_logits else (cfg.vocab + 63) // 64 * 64
     logits = torch.empty((M, ld_logits), dtype=logits_dtype, device="cuda")
 
     def step():

@@ -133,7 +133,8 @@ def test_model_d768_full_size_sampled(ld):
     oracle, logits compared at sampled positions; with the benchmark's launch (logits rows
     padded to a multiple of 8 elements) and with a dense (odd) row stride."""
     cfg = synth.GPT2S_BF16
-    ldv = (cfg.vocab + 7) // 8 * 8 if ld == "aligned" else cfg.vocab
+    # "aligned": the benchmark's stride (rows start on 128-byte lines); "dense": odd stride
+    ldv = (cfg.vocab + 63) // 64 * 64 if ld == "aligned" else cfg.vocab
     _sampled_model_check(cfg, 5, 1024, [0, 1, 2, 63, 64, 255, 511, 700, 1022, 1023], ld=ldv)
 
 
