@@ -818,9 +818,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
         if (fuse) psq[r * PSQ_LD + c] = sq;
       }
       if (fuse) {
-        // each row's sum over the tile's columns, chunks in order
+        // each row's sum over the tile's columns: TPR consecutive lanes per row each sum a
+        // run of chunks in order, then the runs are added pairwise across the lanes (a fixed
+        // order, so the partial is deterministic)
         __syncthreads();
-        if (tid < prow) {
+        constexpr int PROW = BM / RES_PASSES, TPR = NT / PROW;
+        if constexpr (TPR >= 1 && TPR <= 4 && (TPR & (TPR - 1)) == 0 && TPR * PROW == NT &&
+                      RES_CPR % TPR == 0) {
+          constexpr int RUN = RES_CPR / TPR;
+          const int r = tid / TPR, part = tid % TPR;
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < RUN; ++c) ss += psq[r * PSQ_LD + part * RUN + c];
+#pragma unroll
+          for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o);
+          const int64_t m = m0 + p * prow + r;
+          if (part == 0 && m < g.M) g.nrm_part[m * kNormParts + tn] = ss;
+        } else if (tid < prow) {
           const int64_t m = m0 + p * prow + tid;
           float ss = 0.f;
           for (int c = 0; c < RES_CPR; ++c) ss += psq[tid * PSQ_LD + c];
