@@ -435,6 +435,12 @@ int tfm_last_hip_error(void) { return g_last_hip; }
 
 const char *tfm_version(void) { return "tfm 0.1 gfx950"; }
 
+int tfm_mfma_rate(int64_t iters, int blocks, float *sink, void *stream) {
+  if (!sink) return TFM_ERR_NULL;
+  if (iters <= 0 || blocks <= 0) return TFM_ERR_SHAPE;
+  return hip_status(launch_mfma_rate(iters, blocks, sink, (hipStream_t)stream));
+}
+
 int tfm_rope_table_init(float *cos_sin, int max_seq, int d_head, double theta, void *stream) {
   if (!cos_sin) return TFM_ERR_NULL;
   if (!aligned16(cos_sin)) return TFM_ERR_ALIGN;

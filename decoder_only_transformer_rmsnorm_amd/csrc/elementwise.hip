@@ -231,7 +231,52 @@ hipError_t rms1(const void *x, const void *g, int g_dt, void *y, int y_dt, int64
                          : rms2<TX, float>(x, g, y, y_dt, rows, d, eps, s);
 }
 
+// Matrix-core rate probe (a measurement of the sustained bf16 MFMA rate, the second
+// denominator beside the published peak): each wave runs `iters` rounds of 8 independent
+// v_mfma_f32_16x16x32_bf16 on operands held in registers, filled with pseudo-random bf16
+// values in +-[1, 2) (the chip sustains less with random than with constant operands), and
+// writes a checksum so that no product can be dropped.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int64_t iters, float *sink) {
+  uint32_t x = 0x9e3779b9u * (uint32_t)(blockIdx.x * 256 + threadIdx.x + 1);
+  u32x4_t a[2], b[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+      a[i][j] = (x & 0x807f807fu) | 0x3f803f80u;
+      x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+      b[i][j] = (x & 0x807f807fu) | 0x3f803f80u;
+    }
+  // 8 independent accumulators, written out one by one so that each stays in its registers
+  const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, a[0]), a1 = __builtin_bit_cast(bf16x8_t, a[1]);
+  const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, b[0]), b1 = __builtin_bit_cast(bf16x8_t, b[1]);
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t c0 = z, c1 = z, c2 = z, c3 = z, c4 = z, c5 = z, c6 = z, c7 = z;
+  // the products are written as instructions with each accumulator read and written in place
+  // (left to itself the compiler moves the accumulators between registers every round, and
+  // those moves, not the products, then set the rate)
+#define TFM_MFMA(C, A, B) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(C) : "v"(A), "v"(B))
+  for (int64_t it = 0; it < iters; ++it) {
+    TFM_MFMA(c0, a0, b0); TFM_MFMA(c1, a1, b0); TFM_MFMA(c2, a0, b1); TFM_MFMA(c3, a1, b1);
+    TFM_MFMA(c4, a0, b0); TFM_MFMA(c5, a1, b0); TFM_MFMA(c6, a0, b1); TFM_MFMA(c7, a1, b1);
+  }
+#undef TFM_MFMA
+  // the vector ALU reads the last products only after they have left the matrix core
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  const f32x4_t t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+  float s = t[0] + t[1] + t[2] + t[3];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_rate(int64_t iters, int blocks, float *sink, hipStream_t s) {
+  if (blocks <= 0 || iters <= 0) return hipSuccess;
+  mfma_rate_kernel<<<blocks, 256, 0, s>>>(iters, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_table(float *cos_sin, int max_seq, int d_head, double theta,
                              hipStream_t s) {

@@ -30,7 +30,7 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
            "tfm_train_workspace_bytes", "tfm_model_backward", "tfm_clip_workspace_bytes",
            "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_adamw_step_multi",
-           "tfm_check_device_flags"]
+           "tfm_check_device_flags", "tfm_mfma_rate"]
 
 
 class TfmError(RuntimeError):
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "tfm_status_string": (ctypes.c_char_p, [c_int]),
             "tfm_last_hip_error": (c_int, []),
             "tfm_version": (ctypes.c_char_p, []),
+            "tfm_mfma_rate": (c_int, [c_i64, c_int, c_p, c_p]),
             "tfm_rope_table_init": (c_int, [c_p, c_int, c_int, ctypes.c_double, c_p]),
             "tfm_embed": (c_int, [c_p, c_i64, c_p, c_int, c_int, c_int, c_p, c_p, c_p]),
             "tfm_rmsnorm": (c_int, [c_p, c_int, c_p, c_int, c_p, c_int, c_i64, c_int,

@@ -87,6 +87,15 @@ int tfm_last_hip_error(void);
 /* Library version string. */
 const char *tfm_version(void);
 
+/* Matrix-core rate probe, a measurement helper beside the decoder path: `blocks` workgroups of
+ * 4 waves each run `iters` rounds of 8 independent bf16 16x16x32 matrix-core products
+ * (2 * 16 * 16 * 32 flops each) on pseudo-random operands held in registers, so
+ * flops = blocks * 4 * iters * 8 * 16384; timing the launch gives the rate the chip sustains
+ * under random bf16 data (below the published dense peak, which assumes the top clock).
+ * sink: [dev] float32, blocks * 4 checksums (caller-owned). Errors: TFM_ERR_NULL, TFM_ERR_SHAPE
+ * (iters or blocks <= 0), TFM_ERR_HIP. Asynchronous on `stream`. */
+int tfm_mfma_rate(int64_t iters, int blocks, float *sink, void *stream);
+
 /* RoPE table  [T1 5.5; T2 RoPE]: for p in [0, max_seq) and pair i in [0, d_head/2),
  * angle = p * theta^(-2i/d_head) formed in double precision;
  * cos_sin[(p*(d_head/2) + i)*2 + 0] = cos(angle), [... + 1] = sin(angle), stored as float.

@@ -377,3 +377,11 @@ def test_training_entry_points_validation(L):
     assert multi(ps=None) == NULL
     assert multi(gs=arr(None, None)) == NULL                 # tensor 0 has elements
     assert multi(sizes=(ctypes.c_int64 * 2)(10, -3)) == SHAPE
+
+
+def test_mfma_rate_validation(L):
+    L.tfm_mfma_rate.restype = ctypes.c_int
+    L.tfm_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.tfm_mfma_rate(10, 4, None, None) == NULL        # no checksum buffer
+    assert L.tfm_mfma_rate(0, 4, P, None) == SHAPE           # no iterations
+    assert L.tfm_mfma_rate(10, 0, P, None) == SHAPE          # no workgroups
