@@ -15,7 +15,8 @@ Besides the step time it reports:
 
 With --counters it runs only what the hardware-counter passes need: one plain device copy of
 a known size (the scale reference for the HBM byte counters) and a few launches of the
-LM-head GEMM, then exits without a JSON line.
+LM-head GEMM, then exits without a JSON line; --attention-counters likewise runs only ten
+launches of the step's attention.
 """
 from __future__ import annotations
 
@@ -140,6 +141,9 @@ def main() -> int:
                          "is shared by two output tiles)")
     ap.add_argument("--counters", action="store_true",
                     help="only a 1 GiB copy and 3 LM-head launches, for rocprofv3 --pmc passes")
+    ap.add_argument("--attention-counters", action="store_true",
+                    help="only 10 launches of the step's causal attention (random q, k, v of "
+                         "the workload's shape), for rocprofv3 --pmc passes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -169,6 +173,19 @@ def main() -> int:
 
     def step():
         dm.forward(logits=logits, ld_logits=ld_logits)
+
+    if args.attention_counters:
+        qd = cfg.n_heads * cfg.d_head
+        qkv = torch.randn((M, 3 * qd), device="cuda").to(torch.bfloat16)
+        o = torch.empty((M, qd), dtype=torch.bfloat16, device="cuda")
+        for _ in range(10):
+            tfm.tfm_causal_attention(
+                qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd),
+                qkv[:, 2 * qd:].view(B, S, qd), cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
+                o=o.view(B, S, qd), q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd)
+        torch.cuda.synchronize()
+        log("attention counters run done: 10 launches")
+        return 0
 
     if args.counters:
         xn = torch.randn((M, cfg.d_model), device="cuda").to(torch.bfloat16)
