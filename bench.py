@@ -148,7 +148,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward shards by sequence with no exchange, "
-              "so a multi-GPU figure is not produced by this build (run with --gpus 1).",
+              "and this benchmark reports the one-GPU rate only (run with --gpus 1).",
               file=sys.stderr)
         return 2
 

@@ -42,7 +42,7 @@ typedef enum {
   TFM_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
   TFM_ERR_WORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes() figure */
   TFM_ERR_ALIGN = -5,       /* pointer or stride not aligned as required */
-  TFM_ERR_UNSUPPORTED = -6, /* valid request this build does not implement (e.g. d_head) */
+  TFM_ERR_UNSUPPORTED = -6, /* valid request the library does not implement (e.g. d_head) */
   TFM_ERR_HIP = -7,         /* a HIP launch or copy failed */
   TFM_ERR_TOKEN = -8,       /* a token id was outside [0, vocab) (device-side check) */
   TFM_ERR_POSITION = -9     /* a decode / prefill position was outside the KV cache or the
