@@ -264,6 +264,23 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                                                  "csrc", f)).read()
 
 
+
+def test_missing_library_raises(monkeypatch):
+    """Without libtfm.so the binding raises instead of computing anything another way."""
+    monkeypatch.setattr(tfm, "_lib", None)
+    monkeypatch.setattr(tfm, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libtfm.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        tfm.lib()
+
+
+def test_host_tensors_are_refused():
+    """A host (CPU) tensor is refused before any call reaches the library."""
+    import torch
+    x = torch.zeros((4, 64))
+    g = torch.ones(64)
+    with pytest.raises(ValueError, match="GPU"):
+        tfm.tfm_rmsnorm(x, g, y=torch.empty_like(x))
+
 def test_kv_cache_and_decode_validation(L):
     """Every call fails validation (or is empty) before any launch."""
     c = _cfg()   # d512 bf16: 4 layers, 16/16 heads of 32
