@@ -99,15 +99,18 @@ def test_rope_table_values():
 
 
 # ---------------------------------------------------------------- Linear
-@pytest.mark.parametrize("dt,M,N,K,ldy_pad,res", [
+_LINEAR_SHAPES = [
     ("bf16", 1000, 333, 768, 0, False), ("bf16", 257, 1001, 64, 3, False),
     ("bf16", 130, 768, 2048, 0, True), ("bf16", 5, 50257, 128, 0, False),
     ("f32", 300, 200, 64, 0, False), ("f32", 77, 65, 176, 1, True), ("bf16", 128, 128, 8, 0, False),
-    ("f32", 1, 1, 4, 0, False)])
-@pytest.mark.parametrize("out", ["bf16", "f32"])
+    ("f32", 1, 1, 4, 0, False)]
+
+
+# the residual accumulates into fp32, so a residual product has only the fp32 output (the
+# library refuses the bf16 one with a dtype status, checked on the host)
+@pytest.mark.parametrize("dt,M,N,K,ldy_pad,res,out", [
+    (*c, out) for c in _LINEAR_SHAPES for out in ("bf16", "f32") if not (c[5] and out == "bf16")])
 def test_linear(dt, M, N, K, ldy_pad, res, out):
-    if res and out == "bf16":
-        pytest.skip("residual accumulates into fp32")
     say(f"linear dt={dt} M={M} N={N} K={K} ldy=N+{ldy_pad} res={res} out={out}")
     tfm = tfm_mod()
     a = synth.random_array((M, K), seed=M + K, dtype=dt)
