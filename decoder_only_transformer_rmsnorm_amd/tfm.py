@@ -170,7 +170,7 @@ def dt_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TfmError(-3, f"tensor has dtype {t.dtype}, expected torch.float32 or torch.bfloat16")
 
 
 def torch_dtype(code: int):
@@ -178,19 +178,98 @@ def torch_dtype(code: int):
     return torch.bfloat16 if code == BF16 else torch.float32
 
 
-def _dev(t):
-    """Device pointer of a contiguous GPU tensor, or None."""
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError("tensor must live on the GPU")
-    return t.data_ptr()
+class _Arg:
+    """A tensor argument of a library call with the checks it needs. The library receives bare
+    pointers and cannot check anything, so `_call` checks every argument's dtype, layout and
+    the element count the call touches on the host, then that each lives on the GPU, and only
+    then passes the pointers."""
+
+    __slots__ = ("t", "what", "dtype", "numel", "exact", "rows")
+
+    def __init__(self, t, what, dtype=None, numel=None, exact=False, rows=None):
+        self.t, self.what, self.dtype, self.numel, self.exact, self.rows = \
+            t, what, dtype, numel, exact, rows
+
+    def host_check(self) -> None:
+        t, what = self.t, self.what
+        if self.dtype is not None:
+            allowed = self.dtype if isinstance(self.dtype, tuple) else (self.dtype,)
+            if t.dtype not in allowed:
+                raise TfmError(-3, f"{what} has dtype {t.dtype}, expected "
+                                   f"{' or '.join(map(str, allowed))}")
+        if self.rows is not None:
+            rows, width, stride = self.rows
+            if t.dim() == 0 or t.stride(-1) != 1:
+                raise TfmError(-2, f"{what} must have unit stride along its last dimension")
+            if stride < width:
+                raise TfmError(-2, f"{what}: row stride {stride} below the row width {width}")
+            need = (rows - 1) * stride + width if rows > 0 else 0
+            avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+            if need > avail:
+                raise TfmError(-2, f"{what}: {rows} rows of {width} (stride {stride}) exceed "
+                                   "its storage")
+            return
+        if not t.is_contiguous():
+            raise TfmError(-2, f"{what} is not contiguous")
+        n = self.numel
+        if n is not None and (t.numel() != n if self.exact else t.numel() < n):
+            raise TfmError(-2, f"{what} has {t.numel()} elements, the call uses "
+                               f"{'' if self.exact else 'at least '}{n}")
+
+    def pointer(self) -> int:
+        if not self.t.is_cuda:
+            raise ValueError(f"{self.what} must live on the GPU")
+        return self.t.data_ptr()
+
+
+def _dev(t, what: str = "tensor", dtype=None, numel: int | None = None, exact: bool = False):
+    """A contiguous device tensor argument (None passes through as a null pointer); `numel` is
+    the element count the call touches (at least, or exactly)."""
+    return None if t is None else _Arg(t, what, dtype, numel, exact)
+
+
+def _dev_rows(t, what: str, dtype, rows: int, width: int, stride: int):
+    """A row-view argument: `rows` rows of `width` elements, `stride` elements apart, which must
+    lie inside the tensor's storage."""
+    return None if t is None else _Arg(t, what, dtype, rows=(rows, width, stride))
+
+
+def _call(name: str, *args) -> None:
+    """Call library function `name` after checking every tensor argument on the host, then on
+    the device; raise TfmError on a non-zero status."""
+    tensors = [a for a in args if isinstance(a, _Arg)]
+    for a in tensors:
+        a.host_check()
+    ptrs = [a.pointer() if isinstance(a, (_Arg, _StreamArg)) else a for a in args]
+    _check(getattr(lib(), name)(*ptrs), name)
+
+
+def _int32():
+    return _torch().int32
+
+
+def _float_types():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+class _StreamArg:
+    """The HIP stream argument of a library call (torch's current stream by default), looked up
+    after the tensor arguments have passed their checks."""
+
+    __slots__ = ("stream",)
+
+    def __init__(self, stream):
+        self.stream = stream
+
+    def pointer(self):
+        torch = _torch()
+        s = torch.cuda.current_stream() if self.stream is None else self.stream
+        return ctypes.c_void_p(s.cuda_stream)
 
 
 def _stream(stream=None):
-    torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return _StreamArg(stream)
 
 
 # ------------------------------------------------------------------ entry points
@@ -198,8 +277,8 @@ def tfm_rope_table_init(max_seq: int, d_head: int, theta: float = 10000.0, devic
                         stream=None):
     torch = _torch()
     t = torch.empty(max_seq * d_head, dtype=torch.float32, device=device)
-    _check(lib().tfm_rope_table_init(_dev(t), max_seq, d_head, float(theta), _stream(stream)),
-           "tfm_rope_table_init")
+    _call("tfm_rope_table_init", _dev(t, "cos_sin"), max_seq, d_head, float(theta),
+                                     _stream(stream))
     return t
 
 
@@ -209,8 +288,9 @@ def tfm_embed(ids, table, x=None, err_flag=None, stream=None):
     vocab, d = table.shape
     if x is None:
         x = torch.empty(ids.shape + (d,), dtype=torch.float32, device=table.device)
-    _check(lib().tfm_embed(_dev(ids), n, _dev(table), dt_code(table), vocab, d, _dev(x),
-                           _dev(err_flag), _stream(stream)), "tfm_embed")
+    _call("tfm_embed", _dev(ids, "ids", _int32()), n, _dev(table, "table", _float_types()),
+                           dt_code(table), vocab, d, _dev(x, "x", torch.float32, n * d),
+                           _dev(err_flag, "err_flag", _int32(), 1), _stream(stream))
     return x
 
 
@@ -219,8 +299,10 @@ def tfm_rmsnorm(x, g, eps: float = 1e-5, out_dtype=None, y=None, stream=None):
     d = x.shape[-1]
     if y is None:
         y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _check(lib().tfm_rmsnorm(_dev(x), dt_code(x), _dev(g), dt_code(g), _dev(y), dt_code(y),
-                             x.numel() // d, d, float(eps), _stream(stream)), "tfm_rmsnorm")
+    ft = _float_types()
+    _call("tfm_rmsnorm", _dev(x, "x", ft), dt_code(x), _dev(g, "g", ft, d, exact=True),
+                             dt_code(g), _dev(y, "y", ft, x.numel()), dt_code(y), x.numel() // d,
+                             d, float(eps), _stream(stream))
     return y
 
 
@@ -229,8 +311,11 @@ def tfm_rope(x, n_heads: int, d_head: int, cos_sin, max_seq: int, positions=None
     """In-place RoPE on x of shape (B, S, row) (heads at offsets h*d_head)."""
     B, S = x.shape[0], x.shape[1]
     rs = x.stride(1) if row_stride is None else row_stride
-    _check(lib().tfm_rope(_dev(x), dt_code(x), rs, _dev(positions), B, S, n_heads, d_head,
-                          _dev(cos_sin), max_seq, _stream(stream)), "tfm_rope")
+    _call("tfm_rope", _dev_rows(x, "x", _float_types(), B * S, n_heads * d_head, rs),
+                          dt_code(x), rs, _dev(positions, "positions", _int32(), B * S, exact=True),
+                          B, S, n_heads, d_head,
+                          _dev(cos_sin, "cos_sin", _torch().float32, max_seq * d_head),
+                          max_seq, _stream(stream))
     return x
 
 
@@ -241,8 +326,11 @@ def tfm_linear(x, w, residual=None, out_dtype=None, y=None, ldy: int | None = No
     if y is None:
         y = torch.empty((M, N if ldy is None else ldy), dtype=out_dtype or x.dtype, device=x.device)
     ld = y.shape[-1] if ldy is None else ldy
-    _check(lib().tfm_linear(_dev(x), _dev(w), dt_code(x), _dev(residual), _dev(y), dt_code(y), M,
-                            N, K, ld, _stream(stream)), "tfm_linear")
+    ft = _float_types()
+    _call("tfm_linear", _dev(x, "x", ft, M * K, exact=True), _dev(w, "w", x.dtype), dt_code(x),
+                            _dev(residual, "residual", torch.float32, M * ld),
+                            _dev_rows(y, "y", ft, M, N, ld), dt_code(y), M, N, K, ld,
+                            _stream(stream))
     return y
 
 
@@ -266,8 +354,11 @@ def tfm_lm_head_xent(x, w, targets, loss=None, mean=None, stream=None):
         mean = torch.empty(1, dtype=torch.float32, device=x.device)
     n = lib().tfm_xent_workspace_bytes(M, V)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
-    _check(lib().tfm_lm_head_xent(_dev(x), _dev(w), _dev(targets), _dev(loss), _dev(mean), M, V,
-                                  K, _dev(ws), n, _stream(stream)), "tfm_lm_head_xent")
+    _call("tfm_lm_head_xent", _dev(x, "x", torch.bfloat16), _dev(w, "w", torch.bfloat16),
+                                  _dev(targets, "targets", _int32(), M, exact=True),
+                                  _dev(loss, "loss", torch.float32, M),
+                                  _dev(mean, "mean", torch.float32, 1), M, V, K, _dev(ws), n,
+                                  _stream(stream))
     return loss, mean
 
 
@@ -279,9 +370,16 @@ def tfm_qkv_rope(xn, wq, wk, wv, n_heads: int, n_kv_heads: int, d_head: int, cos
     width = (n_heads + 2 * n_kv_heads) * d_head
     if qkv is None:
         qkv = torch.empty((B, S, width), dtype=xn.dtype, device=xn.device)
-    _check(lib().tfm_qkv_rope(_dev(xn), _dev(wq), _dev(wk), _dev(wv), _dev(qkv), _dev(positions), B,
-                              S, d, n_heads, n_kv_heads, d_head, _dev(cos_sin), max_seq,
-                              dt_code(xn), _stream(stream)), "tfm_qkv_rope")
+    dt = xn.dtype
+    _call("tfm_qkv_rope", _dev(xn, "xn", _float_types()),
+                              _dev(wq, "wq", dt, n_heads * d_head * d, exact=True),
+                              _dev(wk, "wk", dt, n_kv_heads * d_head * d, exact=True),
+                              _dev(wv, "wv", dt, n_kv_heads * d_head * d, exact=True),
+                              _dev(qkv, "qkv", dt, B * S * width),
+                              _dev(positions, "positions", _int32(), B * S, exact=True), B,
+                              S, d, n_heads, n_kv_heads, d_head,
+                              _dev(cos_sin, "cos_sin", torch.float32, max_seq * d_head), max_seq,
+                              dt_code(xn), _stream(stream))
     return qkv
 
 
@@ -295,9 +393,12 @@ def tfm_causal_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head: int, o=
     qs = q.stride(1) if q_stride is None else q_stride
     kvs = k.stride(1) if kv_stride is None else kv_stride
     os_ = o.stride(1) if o_stride is None else o_stride
-    _check(lib().tfm_causal_attention(_dev(q), qs, _dev(k), _dev(v), kvs, _dev(o), os_, B, S,
-                                      n_heads, n_kv_heads, d_head, dt_code(q), _stream(stream)),
-           "tfm_causal_attention")
+    ft, n = _float_types(), B * S
+    _call("tfm_causal_attention", _dev_rows(q, "q", ft, n, n_heads * d_head, qs), qs,
+                                      _dev_rows(k, "k", q.dtype, n, n_kv_heads * d_head, kvs),
+                                      _dev_rows(v, "v", q.dtype, n, n_kv_heads * d_head, kvs), kvs,
+                                      _dev_rows(o, "o", q.dtype, n, n_heads * d_head, os_), os_, B,
+                                      S, n_heads, n_kv_heads, d_head, dt_code(q), _stream(stream))
     return o
 
 
@@ -312,10 +413,13 @@ def tfm_sliding_window_attention(q, k, v, n_heads: int, n_kv_heads: int, d_head:
     qs = q.stride(1) if q_stride is None else q_stride
     kvs = k.stride(1) if kv_stride is None else kv_stride
     os_ = o.stride(1) if o_stride is None else o_stride
-    _check(lib().tfm_sliding_window_attention(_dev(q), qs, _dev(k), _dev(v), kvs, _dev(o), os_,
-                                              B, S, n_heads, n_kv_heads, d_head, window,
-                                              dt_code(q), _stream(stream)),
-           "tfm_sliding_window_attention")
+    ft, n = _float_types(), B * S
+    _call("tfm_sliding_window_attention", _dev_rows(q, "q", ft, n, n_heads * d_head, qs), qs,
+                                              _dev_rows(k, "k", q.dtype, n, n_kv_heads * d_head, kvs),
+                                              _dev_rows(v, "v", q.dtype, n, n_kv_heads * d_head, kvs),
+                                              kvs, _dev_rows(o, "o", q.dtype, n, n_heads * d_head, os_),
+                                              os_, B, S, n_heads, n_kv_heads, d_head, window,
+                                              dt_code(q), _stream(stream))
     return o
 
 
@@ -328,9 +432,13 @@ def tfm_swiglu_ffn(xn, w1, w3, w2, residual=None, out=None, stream=None):
         out = torch.empty((rows, d), dtype=torch.float32, device=xn.device)
     nbytes = lib().tfm_swiglu_workspace_bytes(rows, d_ff, dt)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=xn.device)
-    _check(lib().tfm_swiglu_ffn(_dev(xn), _dev(w1), _dev(w3), _dev(w2), _dev(residual), _dev(out),
-                                rows, d, d_ff, dt, _dev(ws), nbytes, _stream(stream)),
-           "tfm_swiglu_ffn")
+    wt = xn.dtype
+    _call("tfm_swiglu_ffn", _dev(xn, "xn", _float_types()), _dev(w1, "w1", wt, d_ff * d, exact=True),
+                                _dev(w3, "w3", wt, d_ff * d, exact=True),
+                                _dev(w2, "w2", wt, d * d_ff, exact=True),
+                                _dev(residual, "residual", torch.float32, rows * d),
+                                _dev(out, "out", torch.float32, rows * d),
+                                rows, d, d_ff, dt, _dev(ws), nbytes, _stream(stream))
     return out
 
 
@@ -402,10 +510,12 @@ class DeviceModel:
         if logits is None:
             logits = torch.empty((B * S, ld), dtype=logits_dtype or self.dtype, device=self.device)
         ws = self.workspace(B, S)
-        _check(lib().tfm_model_forward(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
-                                       _dev(ids), _dev(positions), _dev(logits), dt_code(logits),
-                                       ld, B, S, _dev(self.cos_sin), _dev(ws), ws.numel(),
-                                       _stream(stream)), "tfm_model_forward")
+        _call("tfm_model_forward", ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                       _dev(ids, "ids", _int32(), B * S, exact=True),
+                                       _dev(positions, "positions", _int32(), B * S, exact=True),
+                                       _dev_rows(logits, "logits", _float_types(), B * S, V, ld),
+                                       dt_code(logits), ld, B, S, _dev(self.cos_sin), _dev(ws),
+                                       ws.numel(), _stream(stream))
         return logits
 
     def loss(self, targets, ids=None, positions=None, loss=None, mean=None, stream=None):
@@ -419,14 +529,17 @@ class DeviceModel:
         if mean is None:
             mean = torch.empty(1, dtype=torch.float32, device=self.device)
         ws = self.workspace(B, S)
-        _check(lib().tfm_model_loss(ctypes.byref(self.ccfg), ctypes.byref(self.weights), _dev(ids),
-                                    _dev(positions), _dev(targets), _dev(loss), _dev(mean), B, S,
-                                    _dev(self.cos_sin), _dev(ws), ws.numel(), _stream(stream)),
-               "tfm_model_loss")
+        i32, f32, n = _int32(), torch.float32, B * S
+        _call("tfm_model_loss", ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                    _dev(ids, "ids", i32, n, exact=True),
+                                    _dev(positions, "positions", i32, n, exact=True),
+                                    _dev(targets, "targets", i32, n, exact=True),
+                                    _dev(loss, "loss", f32, n), _dev(mean, "mean", f32, 1), B, S,
+                                    _dev(self.cos_sin), _dev(ws), ws.numel(), _stream(stream))
         return loss, mean
 
     def check_flags(self, stream=None) -> None:
-        _check(lib().tfm_check_device_flags(_dev(self._ws), _stream(stream)), "tfm_check_device_flags")
+        _call("tfm_check_device_flags", _dev(self._ws), _stream(stream))
 
     # ---- KV-cache decoding
     def kv_cache(self, B: int, cache_seq: int):
@@ -445,11 +558,15 @@ class DeviceModel:
         out = torch.empty((B * S, V), dtype=logits_dtype or self.dtype,
                           device=self.device) if logits else None
         ws = self.workspace(B, S)
-        _check(lib().tfm_model_prefill(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
-                                       _dev(ids), _dev(positions), _dev(out),
+        need = lib().tfm_kv_cache_bytes(ctypes.byref(self.ccfg), B, cache_seq)
+        _call("tfm_model_prefill", ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                       _dev(ids, "ids", _int32(), B * S, exact=True),
+                                       _dev(positions, "positions", _int32(), B * S, exact=True),
+                                       _dev(out, "logits"),
                                        dt_code(out) if out is not None else BF16, V, B, S,
-                                       _dev(self.cos_sin), _dev(cache), cache_seq, _dev(ws),
-                                       ws.numel(), _stream(stream)), "tfm_model_prefill")
+                                       _dev(self.cos_sin),
+                                       _dev(cache, "kv_cache", torch.bfloat16, need // 2),
+                                       cache_seq, _dev(ws), ws.numel(), _stream(stream))
         return out
 
     def decode_workspace(self, B: int, cache_seq: int):
@@ -472,16 +589,19 @@ class DeviceModel:
         if logits is None:
             logits = torch.empty((B, V), dtype=logits_dtype or self.dtype, device=self.device)
         ws = self.decode_workspace(B, cache_seq)
-        _check(lib().tfm_model_decode(ctypes.byref(self.ccfg), ctypes.byref(self.weights),
-                                      _dev(ids), _dev(positions), _dev(logits), dt_code(logits),
-                                      logits.shape[-1], B, _dev(self.cos_sin), _dev(cache),
-                                      cache_seq, _dev(ws), ws.numel(), _stream(stream)),
-               "tfm_model_decode")
+        need = lib().tfm_kv_cache_bytes(ctypes.byref(self.ccfg), B, cache_seq)
+        ld = logits.shape[-1]
+        _call("tfm_model_decode", ctypes.byref(self.ccfg), ctypes.byref(self.weights),
+                                      _dev(ids, "ids", _int32(), B, exact=True),
+                                      _dev(positions, "positions", _int32(), B, exact=True),
+                                      _dev_rows(logits, "logits", _float_types(), B, V, ld),
+                                      dt_code(logits), ld, B, _dev(self.cos_sin),
+                                      _dev(cache, "kv_cache", torch.bfloat16, need // 2),
+                                      cache_seq, _dev(ws), ws.numel(), _stream(stream))
         return logits
 
     def check_decode_flags(self, stream=None) -> None:
-        _check(lib().tfm_check_device_flags(_dev(self._dws), _stream(stream)),
-               "tfm_check_device_flags")
+        _call("tfm_check_device_flags", _dev(self._dws), _stream(stream))
 
 
 def tfm_decode_attention(q, k_cache, v_cache, positions, n_heads: int, n_kv_heads: int,
@@ -493,10 +613,15 @@ def tfm_decode_attention(q, k_cache, v_cache, positions, n_heads: int, n_kv_head
         o = torch.empty((B, n_heads * d_head), dtype=q.dtype, device=q.device)
     n = lib().tfm_decode_attention_workspace_bytes(B, n_heads, d_head, cache_seq)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().tfm_decode_attention(_dev(q), q.stride(0), _dev(k_cache), _dev(v_cache),
-                                      _dev(positions), _dev(o), o.stride(0), B, n_heads,
+    bf, cache_n = torch.bfloat16, B * n_kv_heads * cache_seq * d_head
+    _call("tfm_decode_attention", _dev_rows(q, "q", bf, B, n_heads * d_head, q.stride(0)),
+                                      q.stride(0), _dev(k_cache, "k_cache", bf, cache_n, exact=True),
+                                      _dev(v_cache, "v_cache", bf, cache_n, exact=True),
+                                      _dev(positions, "positions", _int32(), B, exact=True),
+                                      _dev_rows(o, "o", bf, B, n_heads * d_head, o.stride(0)),
+                                      o.stride(0), B, n_heads,
                                       n_kv_heads, d_head, cache_seq, window, _dev(ws), ws.numel(),
-                                      _stream(stream)), "tfm_decode_attention")
+                                      _stream(stream))
     return o
 
 
@@ -504,9 +629,12 @@ def tfm_block_forward(dm: DeviceModel, layer: int, x, positions=None, stream=Non
     """One block of ``dm`` on the fp32 residual x (B, S, D), in place."""
     B, S = x.shape[0], x.shape[1]
     ws = dm.workspace(B, S)
-    _check(lib().tfm_block_forward(ctypes.byref(dm.ccfg), ctypes.byref(dm.layer_struct(layer)),
-                                   _dev(x), _dev(positions), B, S, _dev(dm.cos_sin), _dev(ws),
-                                   ws.numel(), _stream(stream)), "tfm_block_forward")
+    n = B * S
+    _call("tfm_block_forward", ctypes.byref(dm.ccfg), ctypes.byref(dm.layer_struct(layer)),
+                                   _dev(x, "x", _torch().float32, n * dm.cfg.d_model, exact=True),
+                                   _dev(positions, "positions", _int32(), n, exact=True), B, S,
+                                   _dev(dm.cos_sin), _dev(ws),
+                                   ws.numel(), _stream(stream))
     return x
 
 
@@ -577,26 +705,29 @@ class Trainer:
         B, S = ids.shape
         ws = self.workspace(B, S)
         dm = self.dm
-        _check(lib().tfm_model_backward(ctypes.byref(dm.ccfg), ctypes.byref(dm.weights), _dev(ids),
-                                        _dev(positions), _dev(targets), _dev(self.loss),
+        i32 = _int32()
+        _call("tfm_model_backward", ctypes.byref(dm.ccfg), ctypes.byref(dm.weights),
+                                        _dev(ids, "ids", i32, B * S, exact=True),
+                                        _dev(positions, "positions", i32, B * S, exact=True),
+                                        _dev(targets, "targets", i32, B * S, exact=True),
+                                        _dev(self.loss),
                                         ctypes.byref(self.cgrads), B, S, _dev(dm.cos_sin), _dev(ws),
-                                        ws.numel(), _stream(stream)), "tfm_model_backward")
+                                        ws.numel(), _stream(stream))
         return self.loss
 
     def clip(self, stream=None):
-        _check(lib().tfm_grad_clip_coef(self._gptrs, self._gsizes, len(self.params),
+        _call("tfm_grad_clip_coef", self._gptrs, self._gsizes, len(self.params),
                                         self.max_norm, _dev(self.coef), _dev(self.norm),
-                                        _dev(self._cws), self._cws.numel(), _stream(stream)),
-               "tfm_grad_clip_coef")
+                                        _dev(self._cws), self._cws.numel(), _stream(stream))
 
     def optimizer_step(self, lr: float | None = None, stream=None):
         self.t += 1
         lr = self.lr if lr is None else lr
         coef = self.coef if self.max_norm is not None else None
-        _check(lib().tfm_adamw_step_multi(self._pptrs, self._pbptrs, self._gptrs, self._mptrs,
+        _call("tfm_adamw_step_multi", self._pptrs, self._pbptrs, self._gptrs, self._mptrs,
                                           self._vptrs, self._gsizes, len(self.params), lr,
                                           self.betas[0], self.betas[1], self.eps, self.wd, self.t,
-                                          _dev(coef), _stream(stream)), "tfm_adamw_step_multi")
+                                          _dev(coef), _stream(stream))
 
     def step(self, ids, targets, positions=None, lr: float | None = None, stream=None):
         """Forward + backward, clipping (if max_norm) and one AdamW step; returns the loss."""

@@ -281,6 +281,62 @@ def test_host_tensors_are_refused():
     with pytest.raises(ValueError, match="GPU"):
         tfm.tfm_rmsnorm(x, g, y=torch.empty_like(x))
 
+def _host_model():
+    """A DeviceModel shell on the CPU (no weights uploaded): enough to reach the binding's
+    argument checks, which run before anything touches the device or the library."""
+    import torch
+    cfg = synth.ModelConfig(name="h", dtype="bf16", n_layers=1, d_model=64, n_heads=2,
+                            n_kv_heads=2, d_head=32, d_ff=128, vocab=100, batch=2, seq=8)
+    dm = object.__new__(tfm.DeviceModel)
+    dm.cfg, dm.dtype, dm.device, dm.max_seq = cfg, torch.bfloat16, "cpu", 8
+    dm.ccfg = tfm.make_config(cfg, 8)
+    dm._ws, dm._ws_shape = None, None
+    dm.cos_sin = torch.zeros(8 * 32)
+    dm._layer_structs = (tfm.LayerWeights * 1)()
+    dm.weights = tfm.ModelWeights(None, dm._layer_structs, None, None)
+    return dm
+
+
+def test_binding_checks_dtype_layout_and_size():
+    """The library receives bare pointers, so the binding checks dtype, contiguity and the
+    element count a call will touch before the call (int64 ids read as int32, a logits buffer
+    smaller than B*S rows of the vocabulary, a non-contiguous tensor or a row view running past
+    its storage would otherwise be read or written out of bounds on the GPU)."""
+    import torch
+    dm = _host_model()
+    ids32 = torch.zeros((2, 8), dtype=torch.int32)
+    cases = [
+        (lambda: dm.forward(ids=ids32.long()), -3, "ids"),                              # int64 ids
+        (lambda: dm.forward(ids=ids32, positions=torch.arange(16).view(2, 8)), -3, "positions"),
+        (lambda: dm.forward(ids=ids32.t()), -2, "contiguous"),                          # transposed
+        (lambda: dm.forward(ids=ids32, logits=torch.empty((15, 100), dtype=torch.bfloat16)), -2, "logits"),
+        (lambda: dm.forward(ids=ids32, logits=torch.empty((16, 100), dtype=torch.int32)), -3, "dtype"),
+        (lambda: dm.forward(ids=ids32, ld_logits=99), -2, "logits"),                    # ld < V
+        (lambda: dm.loss(torch.zeros((2, 8), dtype=torch.int64), ids=ids32), -3, "targets"),
+        (lambda: dm.loss(torch.zeros((2, 7), dtype=torch.int32), ids=ids32), -2, "targets"),
+        (lambda: dm.decode(torch.zeros(16, dtype=torch.bfloat16), 8, ids32[:, 0].contiguous(),
+                           torch.zeros(3, dtype=torch.int32)), -2, "positions"),
+        (lambda: tfm.tfm_embed(ids32.long(), torch.zeros((100, 64))), -3, "ids"),
+        (lambda: tfm.tfm_lm_head_xent(torch.zeros((4, 64), dtype=torch.bfloat16),
+                                      torch.zeros((100, 64), dtype=torch.bfloat16),
+                                      torch.zeros(4, dtype=torch.int64)), -3, "targets"),
+        (lambda: tfm.tfm_linear(torch.zeros((4, 64)), torch.zeros((100, 64)),
+                                y=torch.empty((3, 100))), -2, "y"),
+        (lambda: tfm.tfm_causal_attention(torch.zeros((1, 8, 64)), torch.zeros((1, 8, 80))[..., :64],
+                                          torch.zeros((1, 8, 80))[..., 32:], 2, 2, 32,
+                                          kv_stride=80), -2, "v"),         # last row past the end
+        (lambda: tfm.tfm_rmsnorm(torch.zeros((4, 64)), torch.ones(63)), -2, "g"),
+    ]
+    for fn, status, what in cases:
+        with pytest.raises(tfm.TfmError) as e:
+            fn()
+        assert e.value.status == status, (what, e.value)
+        assert what in str(e.value), (what, str(e.value))
+    # well-formed host tensors pass the checks and are then refused for living on the host
+    with pytest.raises(ValueError, match="GPU"):
+        dm.forward(ids=ids32)
+
+
 def test_kv_cache_and_decode_validation(L):
     """Every call fails validation (or is empty) before any launch."""
     c = _cfg()   # d512 bf16: 4 layers, 16/16 heads of 32

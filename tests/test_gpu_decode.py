@@ -90,11 +90,11 @@ def small(**kw):
     return synth.ModelConfig(**base)
 
 
-def _decode_case(cfg, S0, steps, cache_seq, seqs=None, oracle_prefix=None):
+def _decode_case(cfg, S0, steps, cache_seq, seqs=None, gamma_std=None):
     """Prefill S0 tokens of every sequence, then decode `steps` tokens one at a time with the
     inputs' own ids (teacher forcing); compare each step's logits with the oracle."""
     tfm = tfm_mod()
-    inp = synth.make_inputs(cfg, seed=0)
+    inp = synth.make_inputs(cfg, seed=0, gamma_std=gamma_std)
     dm = tfm.DeviceModel(inp, max_seq=max(cache_seq, cfg.seq))
     B = cfg.batch
     cache = dm.kv_cache(B, cache_seq)
@@ -122,10 +122,14 @@ def _decode_case(cfg, S0, steps, cache_seq, seqs=None, oracle_prefix=None):
     return dm, cache, worst
 
 
-@pytest.mark.parametrize("kv", [2, 8])
-def test_prefill_then_decode_matches_full_forward(kv):
-    say(f"prefill + decode, kv heads {kv}")
-    _decode_case(small(n_kv_heads=kv), S0=37, steps=5, cache_seq=64)
+@pytest.mark.parametrize("kv,gamma_std", [(2, None), (8, None), (2, 0.1)])
+def test_prefill_then_decode_matches_full_forward(kv, gamma_std):
+    """Prefill runs the forward's trunk (RMSNorm split across products in these bf16 d256
+    models), decode fuses each RMSNorm into the projection after it; with gains
+    1 + N(0, 0.1) both have to apply every block's own gains."""
+    say(f"prefill + decode, kv heads {kv}, gamma_std {gamma_std}")
+    _decode_case(small(n_kv_heads=kv, n_layers=3), S0=37, steps=5, cache_seq=64,
+                 gamma_std=gamma_std)
 
 
 def test_decode_hybrid_window_model():

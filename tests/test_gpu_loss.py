@@ -129,9 +129,9 @@ def test_lm_head_xent_full_size_sampled():
     assert np.isfinite(to_np(loss)).all()
 
 
-def _model_case(cfg, seqs, prefix=None):
+def _model_case(cfg, seqs, prefix=None, gamma_std=None):
     tfm = tfm_mod()
-    inp = synth.make_inputs(cfg, seed=0)
+    inp = synth.make_inputs(cfg, seed=0, gamma_std=gamma_std)
     dm = tfm.DeviceModel(inp)
     ids = dm.ids
     targets = tfm.next_token_targets(ids)
@@ -166,6 +166,16 @@ def test_model_loss_small_full_size():
     tfm = tfm_mod()
     again, _ = dm.loss(tfm.next_token_targets(dm.ids))
     assert torch.equal(loss, again)
+
+
+def test_model_loss_split_norm_nonunit_gains():
+    """A 3-layer d256 bf16 model with RMSNorm gains 1 + N(0, 0.1): the fused loss runs the same
+    trunk as the forward, with each block's RMSNorms split across the products that write and
+    read the residual ("Transformer 篇" (dujian.net) 5.6), so every row's loss is compared with
+    the oracle's."""
+    cfg = synth.ModelConfig(name="loss_gain", dtype="bf16", n_layers=3, d_model=256, n_heads=8,
+                            n_kv_heads=2, d_head=32, d_ff=704, vocab=1000, batch=3, seq=96)
+    _model_case(cfg, [0, 1, 2], gamma_std=0.1)
 
 
 def test_model_loss_d768_full_size_sampled():

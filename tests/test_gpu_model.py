@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 
 F32_ABS = 1e-4
 BF16_REL = 2e-2
+GAIN_STD = 0.1   # RMSNorm gains 1 + N(0, GAIN_STD) where a test exercises the gain indexing
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -93,13 +94,13 @@ def test_model_tiny_fp32_full():
     assert err <= F32_ABS
 
 
-@pytest.mark.parametrize("logits", ["bf16", "f32"])
-def test_model_small_bf16_full_size(logits):
+@pytest.mark.parametrize("logits,gamma_std", [("bf16", None), ("f32", None), ("bf16", GAIN_STD)])
+def test_model_small_bf16_full_size(logits, gamma_std):
     """The d512 / 4-layer / seq-256 workload at its full batch of 32; 4 sequences checked
-    row by row against the oracle."""
+    row by row against the oracle (also with gains 1 + N(0, 0.1) on the split RMSNorm)."""
     cfg = synth.SMALL_BF16
-    say(f"model {cfg.name} logits={logits}")
-    inp = synth.make_inputs(cfg, seed=0)
+    say(f"model {cfg.name} logits={logits} gamma_std={gamma_std}")
+    inp = synth.make_inputs(cfg, seed=0, gamma_std=gamma_std)
     _, lg = _run_model(cfg, inp, logits_dtype=torch.float32 if logits == "f32" else None,
                        ld=cfg.vocab + 3)
     got = to_np(lg[:, :cfg.vocab]).reshape(cfg.batch, cfg.seq, cfg.vocab)  # padding unwritten
@@ -111,8 +112,8 @@ def test_model_small_bf16_full_size(logits):
     assert rel <= BF16_REL
 
 
-def _sampled_model_check(cfg, seq_index, prefix, positions, ld=None):
-    inp = synth.make_inputs(cfg, seed=0)
+def _sampled_model_check(cfg, seq_index, prefix, positions, ld=None, gamma_std=None):
+    inp = synth.make_inputs(cfg, seed=0, gamma_std=gamma_std)
     ld = cfg.vocab if ld is None else ld
     say(f"model {cfg.name}: GPU forward B={cfg.batch} S={cfg.seq} ld_logits={ld}")
     _, lg = _run_model(cfg, inp, ld=ld)
@@ -139,15 +140,57 @@ def test_model_d768_full_size_sampled(ld):
 
 
 def test_model_xl_full_size_sampled():
-    """The d1600 / 48-layer workload at batch 4 x 1024; the oracle recomputes a 48-token
-    prefix of sequence 2."""
-    _sampled_model_check(synth.XL_BF16, 2, 48, [0, 1, 17, 46, 47])
+    """The d1600 / 48-layer workload at batch 4 x 1024; the oracle recomputes a 512-token
+    prefix of sequence 2 and rows in all four 128-query attention tiles are compared."""
+    _sampled_model_check(synth.XL_BF16, 2, 512, [0, 1, 47, 127, 128, 255, 300, 384, 511])
 
 
 def test_model_long_gqa_full_size_sampled():
-    """The GQA 16/4, d_head 128, seq 8192 workload; the oracle recomputes a 384-token prefix
-    (full-length attention is checked separately at sampled rows)."""
-    _sampled_model_check(synth.LONG_GQA_BF16, 0, 384, [0, 1, 127, 128, 255, 383])
+    """The GQA 16/4, d_head 128, seq 8192 workload; the oracle recomputes a 1024-token prefix
+    and rows in eight different 128-query tiles are compared (full-length attention is checked
+    separately at sampled rows up to 8191)."""
+    _sampled_model_check(synth.LONG_GQA_BF16, 0, 1024,
+                         [0, 1, 127, 128, 255, 383, 500, 640, 777, 895, 1000, 1023])
+
+
+def _swap_gain(inp, layer: int, field: str, src_layer: int, src_field: str):
+    """A copy of the inputs whose block `layer` uses block src_layer's src_field gain as its
+    `field` gain: a planted mistake in the oracle's inputs, not in either implementation."""
+    import copy
+    bad = copy.copy(inp)
+    bad.layers = [copy.copy(lw) for lw in inp.layers]
+    setattr(bad.layers[layer], field, getattr(inp.layers[src_layer], src_field))
+    return bad
+
+
+@pytest.mark.parametrize("case", ["d256_gqa", "d768_mha"])
+def test_model_split_norm_nonunit_gains(case):
+    """bf16 models with d <= 768 split each block's RMSNorms across two products ("Transformer
+    篇" (dujian.net) 5.6, the per-dimension gain g): block l's down projection writes
+    bf16(x * g_attn of block l + 1) and the row sums of squares, and block l + 1's QKV product
+    rescales its rows by 1 / rms(x). With gains 1 + N(0, 0.1) every logit is compared with the
+    oracle. The same oracle run with one gain taken from the wrong place (block 1's FFN gain,
+    block 0's attention gain, or block 1's attention gain as block 0's FFN gain) differs from
+    the reference by more than the bar, so none of those choices on the GPU could pass."""
+    if case == "d256_gqa":
+        cfg = small("bf16", n_layers=3, seq=160, batch=3)
+    else:
+        cfg = synth.GPT2S_BF16.replace(name="d768_L2", n_layers=2, batch=2, seq=256)
+    say(f"model split RMSNorm gains {case}: L={cfg.n_layers} d={cfg.d_model} B={cfg.batch} S={cfg.seq}")
+    inp = synth.make_inputs(cfg, seed=11, gamma_std=GAIN_STD)
+    assert np.abs(inp.layers[1].g_attn - 1).max() > 0.1
+    _, lg = _run_model(cfg, inp, ld=(cfg.vocab + 63) // 64 * 64)
+    got = to_np(lg[:, :cfg.vocab]).reshape(cfg.batch, cfg.seq, cfg.vocab)
+    ref = oracle.model(cfg, inp)
+    rel = max_rel(got, ref)
+    say(f"  max rel err {rel:.3e}")
+    assert np.isfinite(got).all()
+    assert rel <= BF16_REL
+    for wrong in [_swap_gain(inp, 1, "g_attn", 1, "g_ffn"), _swap_gain(inp, 1, "g_attn", 0, "g_attn"),
+                  _swap_gain(inp, 0, "g_ffn", 1, "g_attn")]:
+        d = max_rel(oracle.model(cfg, wrong, ids=inp.ids[:1]), ref[:1])
+        say(f"  oracle with a misplaced gain differs by {d:.3e}")
+        assert d > BF16_REL and d > 3 * rel
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -216,7 +216,8 @@ def test_attention_peaked_softmax(dh):
     assert_within(to_np(o), ref, _attn_tol(v, ref, H, H, dh, "bf16"), "attention peaked")
 
 
-@pytest.mark.parametrize("B,S,Hq,Hkv,dh", [(8, 1024, 12, 12, 64), (1, 8192, 16, 4, 128), (32, 256, 16, 16, 32)])
+@pytest.mark.parametrize("B,S,Hq,Hkv,dh", [(8, 1024, 12, 12, 64), (1, 8192, 16, 4, 128), (32, 256, 16, 16, 32),
+                                            (4, 1024, 25, 25, 64)])
 def test_attention_full_size_sampled(B, S, Hq, Hkv, dh):
     """The attention shapes of the real workloads, checked at sampled query rows."""
     say(f"attention full size B={B} S={S} Hq={Hq} Hkv={Hkv} dh={dh}")
