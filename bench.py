@@ -1,22 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the decoder forward on one MI355X.
 
-A step is one tfm_model_forward over a batch of synthetic token ids: embedding, 12 pre-norm
-blocks (RMSNorm, QKV GEMM + RoPE, causal flash attention, out projection + residual,
-RMSNorm, SwiGLU up GEMM, down projection + residual), final RMSNorm and the LM-head GEMM,
-with weights, ids and the RoPE table already resident in HBM. Prints one JSON line.
+A step is one tfm_model_forward over a batch of synthetic token ids: embedding, the pre-norm
+blocks (RMSNorm, QKV GEMM + RoPE, causal flash attention, out projection + residual, RMSNorm,
+SwiGLU up GEMM, down projection + residual), final RMSNorm and the LM-head GEMM, with weights,
+ids and the RoPE table already resident in HBM. Prints one JSON line.
+
+Default workload: d_model 768, 12 layers, 12 heads of 64, d_ff 2048, vocabulary 50257, batch
+8 x 1024 tokens, bf16 (--workload names the others).
 
 Besides the step time it reports:
-  roofline      the dominant kernel (the LM-head GEMM) timed alone through its entry point
-                on the same stream with HIP events: algorithmic FLOPs per launch divided by
-                the average launch duration, against the bf16 dense MFMA peak.
-  kernels       the same measurement for each kernel family of the step.
-  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload.
+  step_kernels  every kernel family of the step timed INSIDE real steps: a second pass of the
+                same number of steps runs with the library's launch trace on, so each launch is
+                bracketed by HIP events on the launch stream. Per family: launches per step,
+                average launch duration, time per step, algorithmic FLOPs and bytes per launch,
+                and the fraction of its binding roofline (HBM when the algorithmic intensity is
+                below the bf16 ridge of 312.5 flop/B, MFMA otherwise).
+  roofline      that entry for the family with the most time per step (the dominant kernel),
+                with its HBM traffic from the committed counter passes; roofline_lm_head the
+                same for the LM head.
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload, with all
+                host threads and with one.
 
-With --counters it runs only what the hardware-counter passes need: one plain device copy of
-a known size (the scale reference for the HBM byte counters) and a few launches of the
-LM-head GEMM, then exits without a JSON line; --attention-counters likewise runs only ten
-launches of the step's attention.
+With --counters it runs only what the hardware-counter passes need: a plain device copy of a
+known size (the scale reference for the HBM byte counters), then two traced forward steps
+(no warm-up) whose dispatches a counter summary attributes to kernel families by launch order;
+it prints the launch labels of one step and exits without a JSON line.
 """
 from __future__ import annotations
 
@@ -31,9 +40,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15       # dense bf16 MFMA FLOP/s (MI355X published)
+PEAK_F32 = 157.3e12      # dense fp32 MFMA FLOP/s (MI355X published)
 PEAK_HBM = 8.0e12        # HBM3E bytes/s (MI355X published)
 COPY_BYTES = 1 << 30     # plain copy used to scale the HBM byte counters
 METRIC = "decoder forward tokens/sec + attention/GEMM MFMA util, d768 L12 seq1024"
+
+WORKLOADS = {"tiny": "TINY_F32", "small": "SMALL_BF16", "gpt2s": "GPT2S_BF16", "xl": "XL_BF16",
+             "long_gqa": "LONG_GQA_BF16"}
 
 
 def log(msg: str) -> None:
@@ -41,10 +54,8 @@ def log(msg: str) -> None:
 
 
 def time_launches(fn, n: int, stream, graph: bool = True) -> float:
-    """Average duration (ms) of fn() over n back-to-back launches on `stream`.
-
-    With `graph`, the n launches are captured once in a HIP graph and the replay is timed,
-    so host-side launch overhead (Python, ctypes) does not inflate short kernels."""
+    """Average duration (ms) of fn() over n back-to-back launches on `stream` (captured once in
+    a HIP graph and replayed when `graph`, so host launch overhead does not count)."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
@@ -72,46 +83,69 @@ def time_launches(fn, n: int, stream, graph: bool = True) -> float:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in ("gemm.hip", "attention.hip", "elementwise.hip", "common.h", "api.cpp"):
         h.update(open(os.path.join(ROOT, "decoder_only_transformer_rmsnorm_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key: str):
-    """The committed PMC summary entry of the dominant kernel (HBM bytes per launch, kernel
-    name), or None when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_from_profiles(workload: str, label: str):
+    """The committed counter summary of one kernel family (HBM bytes per launch from FETCH_SIZE
+    and WRITE_SIZE), or None when absent or taken on different kernel sources."""
     try:
-        d = json.load(open(path))
+        d = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     except (OSError, ValueError):
         return None
-    e = d.get(kernel_key)
+    e = d.get(workload, {}).get(label)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
     return e
 
 
-def cpu_baseline(cfg, inputs, budget_s: float):
-    """The fp64 oracle on a bounded sample of the workload: whole sequences (every position,
-    every logit), one after another, until about `budget_s` seconds of CPU work have been
-    spent; tokens/s = tokens / wall time. Sequences are independent, so this is a fair rate.
-    If one sequence alone would exceed the budget, a prefix of sequence 0 is timed instead."""
+def host_cpu() -> dict:
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(cfg, inputs, budget_s: float, threads: int):
+    """The fp64 oracle on a bounded sample of the workload with `threads` OpenMP threads: whole
+    sequences (every position, every logit) until about `budget_s` seconds have been spent, or
+    a prefix of sequence 0 when one sequence alone would exceed it; tokens/s = tokens / wall
+    time. Sequences are independent, so whole sequences give a fair rate; a prefix slightly
+    overstates it (attention per token grows with the position)."""
     import numpy as np
     import oracle
-    threads = oracle.num_threads()
+    oracle.set_num_threads(threads)
+    p0 = min(64, cfg.seq)
     t0 = time.perf_counter()
-    oracle.model(cfg, inputs, ids=inputs.ids[:1, :64])
+    logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :p0])
     t64 = time.perf_counter() - t0
-    if t64 * (cfg.seq / 64) * 1.15 > budget_s:
+    if t64 > 0.4 * budget_s:      # the probe alone is a long enough sample
+        assert np.isfinite(logits).all()
+        sample = (f"sequence 0 of {cfg.batch}, positions 0..{p0 - 1} ({p0} tokens), all "
+                  f"{cfg.vocab} logits per token")
+        return {"value": round(p0 / t64, 2), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle", "sample": sample, "seconds": round(t64, 2)}
+    if t64 * (cfg.seq / p0) * 1.15 > budget_s:
         prefix = max(64, int(64 * budget_s / max(t64, 1e-9) / 1.15) // 64 * 64)
         t0 = time.perf_counter()
         logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :prefix])
         dt = time.perf_counter() - t0
         assert np.isfinite(logits).all()
         sample = (f"sequence 0 of {cfg.batch}, positions 0..{prefix - 1} ({prefix} tokens), all "
-                  f"{cfg.vocab} logits per token, fp64 oracle with {threads} OpenMP threads")
-        return {"value": prefix / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": sample, "seconds": round(dt, 2)}
+                  f"{cfg.vocab} logits per token")
+        return {"value": round(prefix / dt, 2), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
     done, dt = 0, 0.0
     while done < cfg.batch and dt < budget_s * 0.6:
         t0 = time.perf_counter()
@@ -119,10 +153,36 @@ def cpu_baseline(cfg, inputs, budget_s: float):
         dt += time.perf_counter() - t0
         assert np.isfinite(logits).all()
         done += 1
-    sample = (f"sequences 0..{done - 1} of {cfg.batch} ({done} x {cfg.seq} tokens), every position "
-              f"and all {cfg.vocab} logits, fp64 oracle with {threads} OpenMP threads")
-    return {"value": done * cfg.seq / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+    sample = (f"sequences 0..{done - 1} of {cfg.batch} ({done} x {cfg.seq} tokens), every "
+              f"position and all {cfg.vocab} logits")
+    return {"value": round(done * cfg.seq / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
+
+
+def rate_entry(label: str, w: dict, avg_ms: float, peak_mfma: float) -> dict:
+    """A kernel family against its binding roofline; both fractions are given."""
+    s = avg_ms / 1e3
+    e = {"kernel": label, "bound": w["bound"], "avg_launch_us": round(avg_ms * 1e3, 2),
+         "flops_per_launch": int(w["flops"]), "bytes_per_launch": int(w["bytes"]),
+         "TFLOP/s": round(w["flops"] / s / 1e12, 1), "GB/s": round(w["bytes"] / s / 1e9, 1),
+         "frac_mfma": round(w["flops"] / s / peak_mfma, 4),
+         "frac_hbm": round(w["bytes"] / s / PEAK_HBM, 4)}
+    e["frac"] = e["frac_mfma"] if w["bound"] == "mfma" else e["frac_hbm"]
+    return e
+
+
+def roofline_of(entry: dict, peak_mfma: float, traffic) -> dict:
+    mfma = entry["bound"] == "mfma"
+    return {"bound": entry["bound"], "kernel": entry["kernel"],
+            "achieved": entry["TFLOP/s"] if mfma else entry["GB/s"],
+            "peak": round(peak_mfma / 1e12, 1) if mfma else PEAK_HBM / 1e9,
+            "unit": "TFLOP/s" if mfma else "GB/s", "frac": entry["frac"],
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
+            "per_launch": "algorithmic FLOPs" if mfma else "algorithmic HBM bytes",
+            "flops_per_launch": entry["flops_per_launch"],
+            "bytes_per_launch": entry["bytes_per_launch"],
+            "avg_launch_us": entry["avg_launch_us"],
+            "timing": "HIP events around every launch inside the traced steps, launch stream"}
 
 
 def main() -> int:
@@ -130,20 +190,19 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2s")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work per thread count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the sustained-rate probe, fused-loss, decode and training legs")
     ap.add_argument("--logits", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--dense-logits", action="store_true",
                     help="logits row stride = vocab (default: vocab rounded up to a multiple of "
                          "64 elements, so every logits row starts on a 128-byte line and no line "
                          "is shared by two output tiles)")
     ap.add_argument("--counters", action="store_true",
-                    help="only a 1 GiB copy and 3 LM-head launches, for rocprofv3 --pmc passes")
-    ap.add_argument("--attention-counters", action="store_true",
-                    help="only 10 launches of the step's causal attention (random q, k, v of "
-                         "the workload's shape), for rocprofv3 --pmc passes")
+                    help="only a 1 GiB copy and 2 forward steps, for rocprofv3 --pmc passes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,43 +220,40 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    cfg = synth.GPT2S_BF16
+    cfg = getattr(synth, WORKLOADS[args.workload])
     B, S, M = cfg.batch, cfg.seq, cfg.tokens
-    log(f"workload {cfg.name}: B={B} S={S} L={cfg.n_layers} d={cfg.d_model} V={cfg.vocab}")
+    bf16_model = cfg.dtype == "bf16"
+    peak_mfma = PEAK_BF16 if bf16_model else PEAK_F32
+    log(f"workload {cfg.name}: B={B} S={S} L={cfg.n_layers} d={cfg.d_model} "
+        f"H={cfg.n_heads}/{cfg.n_kv_heads} dh={cfg.d_head} F={cfg.d_ff} V={cfg.vocab} {cfg.dtype}")
+    t0 = time.perf_counter()
     inputs = synth.make_inputs(cfg, seed=0)
     dm = tfm.DeviceModel(inputs)
+    log(f"inputs drawn and uploaded in {time.perf_counter() - t0:.1f} s")
     stream = torch.cuda.current_stream()
-    logits_dtype = torch.float32 if args.logits == "f32" else torch.bfloat16
+    logits_dtype = torch.float32 if (args.logits == "f32" or not bf16_model) else torch.bfloat16
     ld_logits = cfg.vocab if args.dense_logits else (cfg.vocab + 63) // 64 * 64
     logits = torch.empty((M, ld_logits), dtype=logits_dtype, device="cuda")
+    lbytes = 4 if logits_dtype == torch.float32 else 2
 
     def step():
         dm.forward(logits=logits, ld_logits=ld_logits)
 
-    if args.attention_counters:
-        qd = cfg.n_heads * cfg.d_head
-        qkv = torch.randn((M, 3 * qd), device="cuda").to(torch.bfloat16)
-        o = torch.empty((M, qd), dtype=torch.bfloat16, device="cuda")
-        for _ in range(10):
-            tfm.tfm_causal_attention(
-                qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd),
-                qkv[:, 2 * qd:].view(B, S, qd), cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
-                o=o.view(B, S, qd), q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd)
-        torch.cuda.synchronize()
-        log("attention counters run done: 10 launches")
-        return 0
-
     if args.counters:
-        xn = torch.randn((M, cfg.d_model), device="cuda").to(torch.bfloat16)
         src = torch.randn(COPY_BYTES // 4, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)              # reference: reads and writes exactly COPY_BYTES each
         torch.cuda.synchronize()
-        for _ in range(3):
-            tfm.tfm_linear(xn, dm.lm_head, y=logits)
-        torch.cuda.synchronize()
-        log(f"counters run done: copy {COPY_BYTES} B, 3 LM-head launches")
+        with tfm.LaunchTrace(4096) as tr:
+            step()
+            step()
+        labels = [l for l, _ in tr.records]
+        per = len(labels) // 2
+        assert labels[:per] == labels[per:]
+        log(f"counters run done: copy {COPY_BYTES} B, 2 forward steps of {per} launches")
+        print(json.dumps({"counters_run": cfg.name, "copy_bytes": COPY_BYTES,
+                          "launch_labels_per_step": labels[:per]}), flush=True)
         return 0
 
     log(f"warmup {args.warmup}")
@@ -227,190 +283,162 @@ def main() -> int:
     log(f"{ms:.3f} ms/step, {tok_s / 1e6:.3f} M tokens/s, "
         f"{flops['total'] / (ms / 1e3) / 1e12:.1f} TFLOP/s end to end (wall {wall:.2f} s)")
 
-    # ---- the sustained matrix-core rate: a register-only loop of bf16 16x16x32 products on
-    #      pseudo-random operands (tfm_mfma_rate), the second denominator beside the published
-    #      dense peak, which assumes the top clock the chip does not hold under random data
-    mfma_sustained = None
-    if not args.no_kernels:
+    # ---- the same number of steps again with every launch bracketed by HIP events
+    work = accounting.step_kernels(cfg, logits_bytes=lbytes)
+    with tfm.LaunchTrace(args.steps * 80 * max(1, cfg.n_layers) + 16, stream) as tr:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    traced_ms = sum(t for _, t in tr.records) / args.steps
+    agg = {}
+    for label, t in tr.records:
+        a = agg.setdefault(label, [0, 0.0])
+        a[0] += 1
+        a[1] += t
+    step_kernels = {}
+    for label, (n, tot) in agg.items():
+        w = work.get(label)
+        avg = tot / n
+        e = rate_entry(label, w, avg, peak_mfma) if w else {"kernel": label,
+                                                            "avg_launch_us": round(avg * 1e3, 2)}
+        e["launches_per_step"] = n // args.steps
+        e["us_per_step"] = round(tot / args.steps * 1e3, 1)
+        e["share_of_step"] = round(tot / args.steps / traced_ms, 4)
+        step_kernels[label] = e
+    order = sorted(step_kernels, key=lambda k: -step_kernels[k]["us_per_step"])
+    for k in order:
+        e = step_kernels[k]
+        log(f"in-step {k}: {e['launches_per_step']} x {e['avg_launch_us']} us = {e['us_per_step']} "
+            f"us/step ({e['share_of_step']:.1%})" + (f", {e['bound']} frac {e['frac']}" if "frac" in e else ""))
+    log(f"traced steps: {traced_ms:.3f} ms/step (untraced {ms:.3f})")
+    dominant = next(k for k in order if k in work)
+    roofline = roofline_of(step_kernels[dominant], peak_mfma,
+                           traffic_from_profiles(cfg.name, dominant))
+    roofline_lm = (roofline_of(step_kernels["gemm_lm_head"], peak_mfma,
+                               traffic_from_profiles(cfg.name, "gemm_lm_head"))
+                   if "gemm_lm_head" in step_kernels else None)
+    gemm_labels = [k for k in step_kernels if k.startswith("gemm_")]
+    att_labels = [k for k in step_kernels if k.startswith("attention")]
+    def family(labels):
+        f = sum(work[k]["flops"] * work[k]["launches"] for k in labels)
+        t = sum(step_kernels[k]["us_per_step"] for k in labels) / 1e6
+        return {"TFLOP/s": round(f / t / 1e12, 1), "frac_mfma": round(f / t / peak_mfma, 4),
+                "us_per_step": round(t * 1e6, 1)} if t > 0 else None
+    mfma_util = {"gemm": family(gemm_labels), "attention": family(att_labels)}
+    rms = step_kernels.get("rmsnorm")
+    rmsnorm_hbm = ({"GB/s": rms["GB/s"], "frac_hbm": rms["frac_hbm"],
+                    "bytes_per_launch": rms["bytes_per_launch"],
+                    "avg_launch_us": rms["avg_launch_us"]} if rms else None)
+
+    extras = {}
+    if not args.no_extras and bf16_model:
+        # sustained matrix-core rate: a register-only loop of bf16 16x16x32 products on
+        # pseudo-random operands, the second denominator beside the published dense peak
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         blocks, iters = 8 * cus, 20000
         sink = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
         L = tfm.lib()
-        rate_ms = time_launches(lambda: L.tfm_mfma_rate(iters, blocks, sink.data_ptr(), tfm._stream()),
-                                3, stream)
+        rate_ms = time_launches(lambda: L.tfm_mfma_rate(iters, blocks, sink.data_ptr(),
+                                                        tfm._stream().pointer()), 3, stream)
         rate = blocks * 4 * iters * 8 * 2 * 16 * 16 * 32 / (rate_ms / 1e3)
-        mfma_sustained = {"TFLOP/s": round(rate / 1e12, 1), "frac_of_published": round(rate / PEAK_BF16, 4),
-                          "ms": round(rate_ms, 3), "workgroups": blocks, "iterations": iters,
-                          "kernel": "register-only loop of 8 independent v_mfma_f32_16x16x32_bf16 "
-                                    "per wave, pseudo-random bf16 operands"}
+        extras["mfma_sustained"] = {
+            "TFLOP/s": round(rate / 1e12, 1), "frac_of_published": round(rate / PEAK_BF16, 4),
+            "kernel": "register-only loop of 8 independent v_mfma_f32_16x16x32_bf16 per wave, "
+                      "pseudo-random bf16 operands, 8 workgroups of 4 waves per CU"}
         log(f"sustained bf16 MFMA rate: {rate / 1e12:.1f} TFLOP/s ({rate / PEAK_BF16:.3f} of published)")
+        roofline["frac_sustained"] = round(roofline["achieved"] / (rate / 1e12), 4) \
+            if roofline["bound"] == "mfma" else None
 
-    # ---- per-kernel timing through each entry point, same shapes as inside the step
-    kernels = {}
-    roofline = None
-    loss_forward = None
-    mfma_util = None
-    decode = None
-    if not args.no_kernels:
-        D, F, V = cfg.d_model, cfg.d_ff, cfg.vocab
-        qd = cfg.n_heads * cfg.d_head
-        bf = torch.bfloat16
-        gen = torch.Generator(device="cuda").manual_seed(0)
-        xres = torch.randn((M, D), device="cuda", generator=gen)
-        xn = torch.randn((M, D), device="cuda", generator=gen).to(bf)
-        L0 = dm.layers[0]
-        qkv = torch.randn((M, qd * 3), device="cuda", generator=gen).to(bf)
-        o = torch.empty((M, qd), dtype=bf, device="cuda")
-        u = torch.randn((M, F), device="cuda", generator=gen).to(bf)
-        ws_ffn = torch.empty(tfm.lib().tfm_swiglu_workspace_bytes(M, F, 1), dtype=torch.uint8, device="cuda")
-        xout = torch.empty((M, D), device="cuda")
-        n = args.kernel_reps
-        flops_gemm = lambda N, K: 2.0 * M * N * K
-
-        def rec(name, ms_k, work, bound, unit_work):
-            if bound == "hbm":
-                ach = work / (ms_k / 1e3)
-                kernels[name] = {"ms": round(ms_k, 4), "GB/s": round(ach / 1e9, 1),
-                                 "frac_hbm": round(ach / PEAK_HBM, 4), "bytes": int(work)}
-            else:
-                ach = work / (ms_k / 1e3)
-                kernels[name] = {"ms": round(ms_k, 4), "TFLOP/s": round(ach / 1e12, 1),
-                                 "frac_mfma": round(ach / PEAK_BF16, 4), "flops": int(work)}
-            log(f"kernel {name}: {ms_k * 1e3:.1f} us, {kernels[name]}")
-
-        rec("rmsnorm", time_launches(lambda: tfm.tfm_rmsnorm(xres, L0["g_attn"], cfg.eps, y=xn), n, stream),
-            accounting.rmsnorm_bytes(M, D, 4, 2), "hbm", None)
-        qkv_out = torch.empty((B, S, 3 * qd), dtype=bf, device="cuda")
-        rec("gemm_qkv_rope", time_launches(lambda: tfm.tfm_qkv_rope(
-            xn.view(B, S, D), L0["wq"], L0["wk"], L0["wv"], cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
-            dm.cos_sin, dm.max_seq, qkv=qkv_out), n, stream), flops_gemm(3 * qd, D), "mfma", None)
-        att_flops = accounting.forward_flops(cfg)["attn"] / cfg.n_layers
-        rec("attention", time_launches(lambda: tfm.tfm_causal_attention(
-            qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),
-            cfg.n_heads, cfg.n_kv_heads, cfg.d_head, o=o.view(B, S, qd),
-            q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd), n, stream), att_flops, "mfma", None)
-        # sliding-window attention over the same q, k, v (band of 256 keys per query)
-        win = 256
-        rec(f"attention_window{win}", time_launches(lambda: tfm.tfm_sliding_window_attention(
-            qkv[:, :qd].view(B, S, qd), qkv[:, qd:2 * qd].view(B, S, qd), qkv[:, 2 * qd:].view(B, S, qd),
-            cfg.n_heads, cfg.n_kv_heads, cfg.d_head, win, o=o.view(B, S, qd),
-            q_stride=3 * qd, kv_stride=3 * qd, o_stride=qd), n, stream),
-            accounting.attention_flops(B, S, cfg.n_heads, cfg.d_head, win), "mfma", None)
-        rec("gemm_out_residual", time_launches(lambda: tfm.tfm_linear(o, L0["wo"], residual=xres, y=xres), n, stream),
-            flops_gemm(D, qd), "mfma", None)
-        rec("swiglu_ffn", time_launches(lambda: tfm.lib().tfm_swiglu_ffn(
-            xn.data_ptr(), L0["w1"].data_ptr(), L0["w3"].data_ptr(), L0["w2"].data_ptr(), xres.data_ptr(),
-            xout.data_ptr(), M, D, F, 1, ws_ffn.data_ptr(), ws_ffn.numel(), tfm._stream()), n, stream),
-            flops_gemm(2 * F, D) + flops_gemm(D, F), "mfma", None)
-        rec("gemm_down_residual", time_launches(lambda: tfm.tfm_linear(u, L0["w2"], residual=xres, y=xres), n, stream),
-            flops_gemm(D, F), "mfma", None)
-        lm_ms = time_launches(lambda: tfm.tfm_linear(xn, dm.lm_head, y=logits), n, stream)
-        rec("gemm_lm_head", lm_ms, flops_gemm(V, D), "mfma", None)
-        lm_flops = flops_gemm(V, D)
-        ach = lm_flops / (lm_ms / 1e3) / 1e12
-        prof = traffic_from_profiles("gemm_lm_head")
-        roofline = {"bound": "mfma",
-                    "kernel": (prof["kernel"] if prof else "gemm_bf16_kernel, plain-store epilogue")
-                              + f" (LM head, M={M} N={V} K={D}, logits row stride {ld_logits})",
-                    "achieved": round(ach, 1), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                    "frac": round(ach * 1e12 / PEAK_BF16, 4), "flops_per_launch": int(lm_flops),
-                    "avg_launch_ms": round(lm_ms, 4),
-                    "traffic": prof["bytes_per_launch"] if prof else None}
-        if mfma_sustained:
-            roofline["peak_sustained"] = mfma_sustained["TFLOP/s"]
-            roofline["frac_sustained"] = round(ach / mfma_sustained["TFLOP/s"], 4)
-
-        # fused LM head + next-token cross-entropy (no logits written), and the whole forward
-        # ending in it
+        # forward ending in the fused LM head + next-token cross-entropy (no logits written)
         targets = tfm.next_token_targets(dm.ids)
         xloss = torch.empty(M, dtype=torch.float32, device="cuda")
         xmean = torch.empty(1, dtype=torch.float32, device="cuda")
-        rec("lm_head_xent", time_launches(lambda: tfm.tfm_lm_head_xent(
-            xn, dm.lm_head, targets.view(-1), loss=xloss, mean=xmean), n, stream),
-            flops_gemm(V, D), "mfma", None)
-        loss_ms = time_launches(lambda: dm.loss(targets, loss=xloss, mean=xmean), max(2, n // 4),
-                                stream, graph=False)
-        loss_forward = {"ms_per_step": round(loss_ms, 4), "tokens_per_s": round(M / (loss_ms / 1e3), 1),
-                        "mean_loss": round(float(xmean.item()), 4)}
+        loss_ms = time_launches(lambda: dm.loss(targets, loss=xloss, mean=xmean), 10, stream,
+                                graph=False)
+        extras["loss_forward"] = {"ms_per_step": round(loss_ms, 4),
+                                  "tokens_per_s": round(M / (loss_ms / 1e3), 1),
+                                  "mean_loss": round(float(xmean.item()), 4)}
         log(f"forward with fused loss: {loss_ms:.3f} ms/step, {M / (loss_ms / 1e3) / 1e6:.3f} M tokens/s")
 
-        # KV-cache decode: prefill all but the last 24 positions, then time one-token steps at
-        # that context (each step rewrites the same slot, so every step does identical work)
-        cache_seq = S
-        p0 = S - 24
-        cache = dm.kv_cache(B, cache_seq)
-        dm.prefill(cache, cache_seq, ids=dm.ids[:, :p0].contiguous(), logits=False)
-        dec_logits = torch.empty((B, V), dtype=bf, device="cuda")
-        dec_pos = torch.full((B,), p0, dtype=torch.int32, device="cuda")
-        dec_tok = dm.ids[:, p0].contiguous()
-        step_fn = lambda: dm.decode(cache, cache_seq, dec_tok, dec_pos, logits=dec_logits)
-        eager_ms = time_launches(step_fn, 20, stream, graph=False)
-        graph_ms = time_launches(step_fn, 20, stream, graph=True)
-        dm.check_decode_flags()
-        dbytes = accounting.decode_bytes(cfg, B, p0 + 1)
-        decode = {"batch": B, "context": p0 + 1, "cache_seq": cache_seq,
-                  "ms_per_step_graph": round(graph_ms, 4), "ms_per_step_eager": round(eager_ms, 4),
-                  "tokens_per_s": round(B / (graph_ms / 1e3), 1),
-                  "hbm_bytes_per_step": int(dbytes["total"]),
-                  "GB/s": round(dbytes["total"] / (graph_ms / 1e3) / 1e9, 1),
-                  "frac_hbm": round(dbytes["total"] / (graph_ms / 1e3) / PEAK_HBM, 4)}
-        log(f"decode B={B} context {p0 + 1}: {graph_ms * 1e3:.1f} us/step in a graph "
-            f"({eager_ms * 1e3:.1f} eager), {decode['GB/s']} GB/s algorithmic")
-        del cache
+        if cfg.name == synth.GPT2S_BF16.name:
+            # KV-cache decode: prefill all but the last 24 positions, then time one-token steps
+            # at that context (each step rewrites the same slot: identical work every step)
+            cache_seq = S
+            p0 = S - 24
+            cache = dm.kv_cache(B, cache_seq)
+            dm.prefill(cache, cache_seq, ids=dm.ids[:, :p0].contiguous(), logits=False)
+            dec_logits = torch.empty((B, cfg.vocab), dtype=torch.bfloat16, device="cuda")
+            dec_pos = torch.full((B,), p0, dtype=torch.int32, device="cuda")
+            dec_tok = dm.ids[:, p0].contiguous()
+            step_fn = lambda: dm.decode(cache, cache_seq, dec_tok, dec_pos, logits=dec_logits)
+            eager_ms = time_launches(step_fn, 20, stream, graph=False)
+            graph_ms = time_launches(step_fn, 20, stream, graph=True)
+            dm.check_decode_flags()
+            dbytes = accounting.decode_bytes(cfg, B, p0 + 1)
+            extras["decode"] = {
+                "batch": B, "context": p0 + 1, "cache_seq": cache_seq,
+                "ms_per_step_graph": round(graph_ms, 4), "ms_per_step_eager": round(eager_ms, 4),
+                "tokens_per_s": round(B / (graph_ms / 1e3), 1),
+                "hbm_bytes_per_step": int(dbytes["total"]),
+                "GB/s": round(dbytes["total"] / (graph_ms / 1e3) / 1e9, 1),
+                "frac_hbm": round(dbytes["total"] / (graph_ms / 1e3) / PEAK_HBM, 4)}
+            log(f"decode B={B} context {p0 + 1}: {graph_ms * 1e3:.1f} us/step in a graph "
+                f"({eager_ms * 1e3:.1f} eager), {extras['decode']['GB/s']} GB/s algorithmic")
+            del cache
 
-        # MFMA utilisation of the GEMM and attention kernels over one step
-        L_ = cfg.n_layers
-        gemm_f = L_ * (flops_gemm(3 * qd, D) + flops_gemm(D, qd) + flops_gemm(2 * F, D)
-                       + flops_gemm(D, F)) + flops_gemm(V, D)
-        gemm_ms = L_ * (kernels["gemm_qkv_rope"]["ms"] + kernels["gemm_out_residual"]["ms"]
-                        + kernels["swiglu_ffn"]["ms"]) + kernels["gemm_lm_head"]["ms"]
-        mfma_util = {"gemm": round(gemm_f / (gemm_ms / 1e3) / PEAK_BF16, 4),
-                     "attention": kernels["attention"]["frac_mfma"]}
-
-    train = None
-    if not args.no_kernels:
-        # training step on the same batch: forward keeping activations, backward, global-norm
-        # clipping and AdamW (it rewrites the weights, so it runs after every other leg)
-        tr = tfm.Trainer(dm, lr=1e-4, weight_decay=0.1, max_norm=1.0)
-        t_tg = tfm.next_token_targets(dm.ids)
-        loss0 = float(tr.step(dm.ids, t_tg).item())
-        train_ms = time_launches(lambda: tr.step(dm.ids, t_tg), 5, stream, graph=False)
-        fw = accounting.forward_flops(cfg)["total"]
-        train = {"ms_per_step": round(train_ms, 3), "tokens_per_s": round(M / (train_ms / 1e3), 1),
-                 "loss_first_step": round(loss0, 4),
-                 "model_TFLOP/s": round(3 * fw / (train_ms / 1e3) / 1e12, 1),
-                 "flops_note": "3 x forward (causal) per step"}
-        log(f"training step: {train_ms:.2f} ms, {M / (train_ms / 1e3) / 1e3:.1f} k tokens/s")
-        del tr
+            # training step on the same batch: forward keeping activations, backward,
+            # global-norm clipping and AdamW (it rewrites the weights, so it runs last)
+            trn = tfm.Trainer(dm, lr=1e-4, weight_decay=0.1, max_norm=1.0)
+            t_tg = tfm.next_token_targets(dm.ids)
+            loss0 = float(trn.step(dm.ids, t_tg).item())
+            train_ms = time_launches(lambda: trn.step(dm.ids, t_tg), 5, stream, graph=False)
+            fw = flops["total"]
+            extras["train_step"] = {
+                "ms_per_step": round(train_ms, 3), "tokens_per_s": round(M / (train_ms / 1e3), 1),
+                "loss_first_step": round(loss0, 4),
+                "model_TFLOP/s": round(3 * fw / (train_ms / 1e3) / 1e12, 1),
+                "flops_note": "3 x forward (causal) per step"}
+            log(f"training step: {train_ms:.2f} ms, {M / (train_ms / 1e3) / 1e3:.1f} k tokens/s")
+            del trn
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle, budget {args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(cfg, inputs, args.cpu_budget)
-        log(f"cpu baseline {cpu['value']:.2f} tokens/s ({cpu['sample']}, {cpu['seconds']} s)")
+        host = host_cpu()
+        log(f"cpu baseline: oracle on {host['nproc']} usable threads ({host['model']}), "
+            f"budget {args.cpu_budget:.0f} s per thread count")
+        cpu = cpu_baseline(cfg, inputs, args.cpu_budget, host["nproc"])
+        one = cpu_baseline(cfg, inputs, args.cpu_budget, 1)
+        cpu["sample"] += f", fp64 oracle with {host['nproc']} OpenMP threads"
+        cpu["host"] = host
+        cpu["one_thread"] = {"value": one["value"], "sample": one["sample"],
+                             "seconds": one["seconds"]}
+        log(f"cpu baseline {cpu['value']:.2f} tokens/s on {host['nproc']} threads "
+            f"({cpu['sample']}); {one['value']:.2f} tokens/s on 1 thread ({one['sample']})")
 
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded uniform ids, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "batch": B, "seq_len": S, "n_layers": cfg.n_layers,
-                   "d_model": cfg.d_model, "n_heads": cfg.n_heads, "d_ff": cfg.d_ff,
-                   "vocab": cfg.vocab, "logits_dtype": args.logits, "ld_logits": ld_logits,
+                   "d_model": cfg.d_model, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "d_head": cfg.d_head, "d_ff": cfg.d_ff, "vocab": cfg.vocab,
+                   "logits_dtype": "f32" if lbytes == 4 else "bf16", "ld_logits": ld_logits,
                    "parallelism": "single GPU"},
         "end_to_end": {"flops_per_step_causal": int(flops["total"]),
                        "TFLOP/s": round(flops["total"] / (ms / 1e3) / 1e12, 1),
-                       "frac_mfma": round(flops["total"] / (ms / 1e3) / PEAK_BF16, 4),
+                       "frac_mfma": round(flops["total"] / (ms / 1e3) / peak_mfma, 4),
                        "frac_mfma_sustained": (round(flops["total"] / (ms / 1e3) / 1e12
-                                                     / mfma_sustained["TFLOP/s"], 4)
-                                               if mfma_sustained else None)},
-        "mfma_sustained": mfma_sustained,
+                                                     / extras["mfma_sustained"]["TFLOP/s"], 4)
+                                               if "mfma_sustained" in extras else None)},
         "roofline": roofline,
+        "roofline_lm_head": roofline_lm,
+        "traced_ms_per_step": round(traced_ms, 4),
+        "step_kernels": step_kernels,
         "mfma_util": mfma_util,
-        "kernels": kernels,
-        "loss_forward": loss_forward,
-        "decode": decode,
-        "train_step": train,
+        "rmsnorm_hbm": rmsnorm_hbm,
+        **extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

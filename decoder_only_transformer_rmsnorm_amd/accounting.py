@@ -70,3 +70,72 @@ def decode_bytes(cfg, batch: int, context: int, elt: int = 2) -> dict:
     cache_write = L * 2 * batch * kvd * elt
     total = weights + embed + cache_read + cache_write
     return {"weights": weights, "kv_cache_read": cache_read, "total": total}
+
+
+RIDGE_BF16 = 2.5e15 / 8.0e12   # flop per HBM byte where the bf16 MFMA and HBM rooflines meet
+
+
+def norm_split(cfg) -> bool:
+    """Whether the forward splits each block's RMSNorms across the products that write and read
+    the residual (bf16 models with d_model <= 768, the width whose row partials one tile row of
+    the residual product holds)."""
+    return cfg.dtype == "bf16" and cfg.d_model <= 768
+
+
+def step_kernels(cfg, batch: int | None = None, seq: int | None = None,
+                 logits_bytes: int | None = None) -> dict:
+    """Algorithmic work of each kernel of one forward, per launch: {label: {"launches",
+    "flops", "bytes"}}, the labels those of the library's launch trace. Bytes read every input
+    element once and write every output element once (weights included, the residual read and
+    written by the residual products); FLOPs follow forward_flops. Where launches of one label
+    differ (the last down projection writes no split RMSNorm), the figures are the mean over
+    its launches."""
+    B = cfg.batch if batch is None else batch
+    S = cfg.seq if seq is None else seq
+    M = B * S
+    D, F, V, L = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_layers
+    e = 2 if cfg.dtype == "bf16" else 4
+    lb = e if logits_bytes is None else logits_bytes
+    qd, kvd = cfg.n_heads * cfg.d_head, cfg.n_kv_heads * cfg.d_head
+    W = qd + 2 * kvd
+    split = norm_split(cfg)
+    parts = -(-D // 192)                  # row partials of the split RMSNorm per row
+    part_b = M * parts * 4
+    rms = rmsnorm_bytes(M, D, 4, e)
+    window = getattr(cfg, "window", 0)
+    k = {}
+    k["fill_flags"] = {"launches": 1, "flops": 0, "bytes": 8}
+    k["embed"] = {"launches": 1, "flops": 0, "bytes": M * 4 + M * D * e + M * D * 4}
+    k["rmsnorm"] = {"launches": 2 if split else 2 * L + 1, "flops": 0, "bytes": rms + D * e}
+    rope_table = S * cfg.d_head * 4       # (cos, sin) of every position 0..S-1
+    k["gemm_qkv_rope"] = {"launches": L, "flops": 2 * M * D * W,
+                          "bytes": M * D * e + W * D * e + M * W * e + rope_table
+                          + (part_b * (L - 1) / L if split else 0)}
+    full_layers = L
+    if window:
+        fe = getattr(cfg, "full_every", 0)
+        full_layers = sum(1 for l in range(L) if fe > 0 and l % fe == fe - 1)
+    att_bytes = M * qd * e + 2 * M * kvd * e + M * qd * e
+    if full_layers:
+        k["attention"] = {"launches": full_layers,
+                          "flops": attention_flops(B, S, cfg.n_heads, cfg.d_head),
+                          "bytes": att_bytes}
+    if full_layers < L:
+        k["attention_window"] = {"launches": L - full_layers,
+                                 "flops": attention_flops(B, S, cfg.n_heads, cfg.d_head, window),
+                                 "bytes": att_bytes}
+    res_rw = 2 * M * D * 4
+    k["gemm_out_residual"] = {"launches": L, "flops": 2 * M * qd * D,
+                              "bytes": M * qd * e + qd * D * e + res_rw
+                              + ((M * D * e + part_b) if split else 0)}
+    k["gemm_swiglu"] = {"launches": L, "flops": 2 * M * D * 2 * F,
+                        "bytes": M * D * e + 2 * F * D * e + M * F * e + (part_b if split else 0)}
+    k["gemm_down_residual"] = {"launches": L, "flops": 2 * M * F * D,
+                               "bytes": M * F * e + F * D * e + res_rw
+                               + ((M * D * e + part_b) * (L - 1) / L if split else 0)}
+    k["gemm_lm_head"] = {"launches": 1, "flops": 2 * M * D * V,
+                         "bytes": M * D * e + V * D * e + M * V * lb}
+    for v in k.values():
+        v["bytes"] = int(round(v["bytes"]))
+        v["bound"] = "mfma" if v["flops"] > RIDGE_BF16 * v["bytes"] else "hbm"
+    return k

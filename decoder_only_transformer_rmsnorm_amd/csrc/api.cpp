@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "internal.h"
 #include "tfm.h"
@@ -29,6 +30,31 @@ int hip_status(hipError_t e) {
   } while (0)
 
 #define TFM_HIP(expr) TFM_TRY(hip_status(expr))
+
+// Launch trace (tfm_trace_begin / tfm_trace_end / tfm_trace_read): while it is on, the forward
+// path records a HIP event on its stream after each launch, with the kernel's label, so a
+// caller can time every kernel inside a real step.
+struct Trace {
+  std::vector<hipEvent_t> ev;      // ev[0] recorded at begin, ev[i] after launch i
+  std::vector<const char *> label; // label[i] of launch i (label[0] unused)
+  int n = 0;                       // events recorded so far
+  bool on = false;
+};
+thread_local Trace g_trace;
+
+int mark(hipStream_t s, const char *label) {
+  Trace &t = g_trace;
+  if (!t.on || t.n >= (int)t.ev.size()) return TFM_OK;
+  t.label[t.n] = label;
+  return hip_status(hipEventRecord(t.ev[t.n++], s));
+}
+
+// A launch of the forward path followed by its trace mark.
+#define TFM_LAUNCH(label, expr)   \
+  do {                            \
+    TFM_HIP(expr);                \
+    TFM_TRY(mark(s, label));      \
+  } while (0)
 
 bool valid_dt(int dt) { return dt == TFM_F32 || dt == TFM_BF16; }
 size_t elt(int dt) { return dt == TFM_BF16 ? 2 : 4; }
@@ -170,7 +196,7 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
     g.nrm_g = gain; g.nrm_y = xn; g.nrm_part = nrm;
   };
 
-  if (!norm_in) TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
+  if (!norm_in) TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
 
   GemmArgs g{};
   g.a = xn; g.lda = D; g.w0 = w->wq; g.w1 = w->wk; g.w2 = w->wv; g.n0 = qd; g.n1 = kvd;
@@ -178,34 +204,36 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
   g.positions = positions; g.cos_sin = cos_sin; g.S = S; g.d_head = c->d_head;
   g.max_seq = c->max_seq_len;
   if (norm_in) scale_rows(g);
-  TFM_HIP(launch_gemm(EPI_QKV_ROPE, dt, g, s));
+  TFM_LAUNCH("gemm_qkv_rope", launch_gemm(EPI_QKV_ROPE, dt, g, s));
   if (lc.k)   // prefill: rotated k and v rows into the cache slots of their positions
-    TFM_HIP(launch_kv_store(qkv, qkv_w, qd, kvd, c->d_head, c->n_kv_heads, B, S, positions,
-                            lc.k, lc.v, lc.seq, (int32_t *)(ws + p.flag) + 1, s));
+    TFM_LAUNCH("kv_store", launch_kv_store(qkv, qkv_w, qd, kvd, c->d_head, c->n_kv_heads, B, S,
+                                           positions, lc.k, lc.v, lc.seq,
+                                           (int32_t *)(ws + p.flag) + 1, s));
 
-  TFM_HIP(launch_attention(qkv, qkv_w, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e,
-                           qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt, window,
-                           s));
+  TFM_LAUNCH(window > 0 ? "attention_window" : "attention",
+             launch_attention(qkv, qkv_w, qkv + (size_t)qd * e, qkv + (size_t)(qd + kvd) * e,
+                              qkv_w, o, qd, B, S, c->n_heads, c->n_kv_heads, c->d_head, dt,
+                              window, s));
 
   g = GemmArgs{};
   g.a = o; g.lda = qd; g.w0 = w->wo; g.M = M; g.N = D; g.K = qd; g.y = x; g.ldy = D;
   g.y_dt = DT_F32; g.residual = x;
   if (split) emit_norm(g, w->g_ffn);
-  TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
+  TFM_LAUNCH("gemm_out_residual", launch_gemm(EPI_RESIDUAL, dt, g, s));
 
-  if (!split) TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_ffn, dt, xn, dt, M, D, c->eps, s));
+  if (!split) TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_ffn, dt, xn, dt, M, D, c->eps, s));
 
   g = GemmArgs{};
   g.a = xn; g.lda = D; g.w0 = w->w1; g.w1 = w->w3; g.n0 = c->d_ff; g.M = M; g.N = c->d_ff;
   g.K = D; g.y = u; g.ldy = c->d_ff; g.y_dt = dt;
   if (split) scale_rows(g);
-  TFM_HIP(launch_gemm(EPI_SWIGLU, dt, g, s));
+  TFM_LAUNCH("gemm_swiglu", launch_gemm(EPI_SWIGLU, dt, g, s));
 
   g = GemmArgs{};
   g.a = u; g.lda = c->d_ff; g.w0 = w->w2; g.M = M; g.N = D; g.K = c->d_ff; g.y = x; g.ldy = D;
   g.y_dt = DT_F32; g.residual = x;
   if (split && g_next) emit_norm(g, g_next);
-  TFM_HIP(launch_gemm(EPI_RESIDUAL, dt, g, s));
+  TFM_LAUNCH("gemm_down_residual", launch_gemm(EPI_RESIDUAL, dt, g, s));
   return TFM_OK;
 }
 
@@ -223,9 +251,9 @@ int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t
                   const WsPlan &p, hipStream_t s, void *kv_cache = nullptr, int cache_seq = 0) {
   const int64_t M = (int64_t)B * S;
   float *x = (float *)(wsb + p.x);
-  TFM_HIP(launch_fill_i32((int32_t *)(wsb + p.flag), 2, 0, s));   // token and position flags
-  TFM_HIP(launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
-                       (int32_t *)(wsb + p.flag), s));
+  TFM_LAUNCH("fill_flags", launch_fill_i32((int32_t *)(wsb + p.flag), 2, 0, s));   // token and position flags
+  TFM_LAUNCH("embed", launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
+                                   (int32_t *)(wsb + p.flag), s));
   const bool split = norm_split(c);
   for (int l = 0; l < c->n_layers; ++l) {
     const void *g_next = split && l + 1 < c->n_layers ? w->layers[l + 1].g_attn : nullptr;
@@ -233,8 +261,8 @@ int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t
                           layer_window(c, l), s, layer_cache(c, kv_cache, B, cache_seq, l),
                           split && l > 0, g_next));
   }
-  TFM_HIP(launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M, c->d_model,
-                         c->eps, s));
+  TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M,
+                                       c->d_model, c->eps, s));
   return TFM_OK;
 }
 
@@ -276,8 +304,9 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
   g.x_max = (float *)(wsb + xp.x_max);
   g.x_sum = (float *)(wsb + xp.x_sum);
   g.x_tgt = (float *)(wsb + xp.x_tgt);
-  TFM_HIP(launch_gemm(EPI_XENT, DT_BF16, g, s));
-  TFM_HIP(launch_xent_reduce(g.x_max, g.x_sum, g.x_tgt, targets, xp.parts, M, V, loss, mean, s));
+  TFM_LAUNCH("gemm_lm_head_xent", launch_gemm(EPI_XENT, DT_BF16, g, s));
+  TFM_LAUNCH("xent_reduce", launch_xent_reduce(g.x_max, g.x_sum, g.x_tgt, targets, xp.parts, M, V,
+                                               loss, mean, s));
   return TFM_OK;
 }
 
@@ -619,7 +648,7 @@ int tfm_model_forward(const tfm_config *cfg, const tfm_model_weights *w, const i
   GemmArgs g{};
   g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = (int64_t)B * S;
   g.N = cfg->vocab; g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
-  TFM_HIP(launch_gemm(EPI_STORE, cfg->dtype, g, s));
+  TFM_LAUNCH("gemm_lm_head", launch_gemm(EPI_STORE, cfg->dtype, g, s));
   return TFM_OK;
 }
 
@@ -709,7 +738,7 @@ int tfm_model_prefill(const tfm_config *cfg, const tfm_model_weights *w, const i
   GemmArgs g{};
   g.a = wsb + p.xn; g.lda = cfg->d_model; g.w0 = w->lm_head; g.M = (int64_t)B * S;
   g.N = cfg->vocab; g.K = cfg->d_model; g.y = logits; g.ldy = ld_logits; g.y_dt = logits_dt;
-  TFM_HIP(launch_gemm(EPI_STORE, cfg->dtype, g, s));
+  TFM_LAUNCH("gemm_lm_head", launch_gemm(EPI_STORE, cfg->dtype, g, s));
   return TFM_OK;
 }
 
@@ -1029,3 +1058,55 @@ int tfm_adamw_step_multi(float *const *params, void *const *params_bf16,
 }
 
 }  // extern "C"
+
+
+// ---- launch trace
+
+int tfm_trace_begin(int capacity, void *stream) {
+  if (capacity <= 0 || capacity > (1 << 20)) return TFM_ERR_SHAPE;
+  tfm_trace_free();
+  Trace &t = g_trace;
+  t.ev.assign((size_t)capacity + 1, nullptr);
+  t.label.assign((size_t)capacity + 1, nullptr);
+  for (auto &e : t.ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      tfm_trace_free();
+      return hip_status(r);
+    }
+  }
+  t.n = 0;
+  t.on = true;
+  return mark((hipStream_t)stream, "begin");
+}
+
+int tfm_trace_end(int *n_launches) {
+  Trace &t = g_trace;
+  t.on = false;
+  if (n_launches) *n_launches = t.n > 0 ? t.n - 1 : 0;
+  return TFM_OK;
+}
+
+int tfm_trace_read(float *ms, const char **labels, int n) {
+  Trace &t = g_trace;
+  if (t.on) return TFM_ERR_SHAPE;
+  if (n < 0 || n > t.n - 1) return TFM_ERR_SHAPE;
+  if (n > 0 && (!ms || !labels)) return TFM_ERR_NULL;
+  if (t.n > 0) TFM_HIP(hipEventSynchronize(t.ev[t.n - 1]));
+  for (int i = 0; i < n; ++i) {
+    TFM_HIP(hipEventElapsedTime(&ms[i], t.ev[i], t.ev[i + 1]));
+    labels[i] = t.label[i + 1];
+  }
+  return TFM_OK;
+}
+
+void tfm_trace_free(void) {
+  Trace &t = g_trace;
+  for (auto e : t.ev)
+    if (e) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.label.clear();
+  t.n = 0;
+  t.on = false;
+}

@@ -30,7 +30,8 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
            "tfm_train_workspace_bytes", "tfm_model_backward", "tfm_clip_workspace_bytes",
            "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_adamw_step_multi",
-           "tfm_check_device_flags", "tfm_mfma_rate"]
+           "tfm_check_device_flags", "tfm_mfma_rate", "tfm_trace_begin", "tfm_trace_end",
+           "tfm_trace_read", "tfm_trace_free"]
 
 
 class TfmError(RuntimeError):
@@ -144,6 +145,11 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                              ctypes.c_float, ctypes.c_float, c_int, c_p, c_p]),
             "tfm_check_device_flags": (c_int, [c_p, c_p]),
+            "tfm_trace_begin": (c_int, [c_int, c_p]),
+            "tfm_trace_end": (c_int, [ctypes.POINTER(c_int)]),
+            "tfm_trace_read": (c_int, [ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_char_p), c_int]),
+            "tfm_trace_free": (None, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -623,6 +629,33 @@ def tfm_decode_attention(q, k_cache, v_cache, positions, n_heads: int, n_kv_head
                                       n_kv_heads, d_head, cache_seq, window, _dev(ws), ws.numel(),
                                       _stream(stream))
     return o
+
+
+class LaunchTrace:
+    """Times every kernel launch of the forward path inside real steps (tfm_trace_begin /
+    tfm_trace_end / tfm_trace_read): inside the `with` block each launch records a HIP event
+    on its stream; afterwards `records` lists (label, milliseconds) in launch order."""
+
+    def __init__(self, capacity: int, stream=None):
+        self.capacity, self.stream, self.records = capacity, stream, []
+
+    def __enter__(self):
+        _call("tfm_trace_begin", self.capacity, _stream(self.stream))
+        return self
+
+    def __exit__(self, *exc):
+        L = lib()
+        n = c_int(0)
+        L.tfm_trace_end(ctypes.byref(n))
+        try:
+            if exc[0] is None and n.value > 0:
+                ms = (ctypes.c_float * n.value)()
+                labels = (ctypes.c_char_p * n.value)()
+                _check(L.tfm_trace_read(ms, labels, n.value), "tfm_trace_read")
+                self.records = [(labels[i].decode(), float(ms[i])) for i in range(n.value)]
+        finally:
+            L.tfm_trace_free()
+        return False
 
 
 def tfm_block_forward(dm: DeviceModel, layer: int, x, positions=None, stream=None):

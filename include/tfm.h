@@ -333,6 +333,26 @@ int tfm_adamw_step_multi(float *const *params, void *const *params_bf16,
                          float eps, float weight_decay, int step, const float *coef,
                          void *stream);
 
+/* ---- Launch trace (measurement): while a trace is on for the calling thread, every kernel
+ * launch of tfm_block_forward, tfm_model_forward, tfm_model_loss and tfm_model_prefill records
+ * a HIP event on the call's stream right after it, labelled with the kernel's step
+ * ("embed", "rmsnorm", "gemm_qkv_rope", "attention", "attention_window", "gemm_out_residual",
+ * "gemm_swiglu", "gemm_down_residual", "gemm_lm_head", "gemm_lm_head_xent", "xent_reduce",
+ * "kv_store", "fill_flags"), so each launch's time inside a real step is the elapsed time
+ * between consecutive events (the launch plus any gap before it). Launches beyond `capacity`
+ * are not recorded. The library creates the events (no device memory) and keeps them until
+ * tfm_trace_free or the next tfm_trace_begin.
+ * tfm_trace_begin: starts a trace of up to `capacity` launches and records the first event on
+ *   `stream`; TFM_ERR_SHAPE for capacity outside [1, 2^20].
+ * tfm_trace_end: stops recording; *n_launches (nullable) = launches recorded.
+ * tfm_trace_read: after tfm_trace_end, waits for the last event and writes, for launch i < n,
+ *   ms[i] = its time in milliseconds and labels[i] = its label (static strings); n at most the
+ *   launches recorded (TFM_ERR_SHAPE otherwise, or while the trace is on). */
+int tfm_trace_begin(int capacity, void *stream);
+int tfm_trace_end(int *n_launches);
+int tfm_trace_read(float *ms, const char **labels, int n);
+void tfm_trace_free(void);
+
 /* Waits for `stream`, then returns TFM_ERR_TOKEN if the last whole-model call that used this
  * workspace saw an out-of-range token id, TFM_ERR_POSITION if it saw a position outside the
  * KV cache or the RoPE table (prefill / decode), else TFM_OK. */

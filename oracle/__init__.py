@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_model.argtypes = [ctypes.POINTER(OracleCfg), _p, ctypes.POINTER(OracleLayer),
                                    _p, _p, _p, _p, c_int, c_int, _p, _p, c_i64, _p]
         L.oracle_num_threads.restype = c_int
+        L.oracle_set_num_threads.argtypes = [c_int]
+        L.oracle_set_num_threads.restype = None
         L.oracle_model_grads.argtypes = [ctypes.POINTER(OracleCfg), ctypes.POINTER(OracleParamsD),
                                          _p, _p, _p, c_int, c_int, ctypes.POINTER(OracleParamsD)]
         L.oracle_model_grads.restype = c_double
@@ -108,6 +110,11 @@ def _ptr(a) -> int | None:
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops (from the next call on)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def embedding(ids, E) -> np.ndarray:

@@ -18,6 +18,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the following parallel loops use (timing of the baseline at several counts). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* [T1 5.2 Embedding]: a table lookup, row id of E. */
 int oracle_embedding(const int32_t *ids, int64_t n, const float *E, int vocab, int d, double *x) {
   for (int64_t r = 0; r < n; ++r)

@@ -118,6 +118,7 @@ double oracle_cross_entropy(const double *logits, int64_t rows, int V, const int
 
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 /* ---- training step (oracle_train.c)  [T2 Optimize: Loss, AdamW; T3 12 training]. All
  * parameters and gradients in double. lm_head may equal embed (tied); then the gradient

@@ -28,3 +28,21 @@ def test_forward_flops_follow_the_weight_shapes():
     assert f["lm_head"] == 2 * M * inp.lm_head.size
     assert f["attn"] == cfg.n_layers * accounting.attention_flops(cfg.batch, cfg.seq, cfg.n_heads,
                                                                    cfg.d_head)
+
+
+@pytest.mark.parametrize("name", ["TINY_F32", "SMALL_BF16", "GPT2S_BF16", "XL_BF16", "LONG_GQA_BF16"])
+def test_step_kernels_add_up_to_the_forward(name):
+    """The per-kernel work the benchmark rates each launch by sums, over the launches of one
+    forward, to the whole forward's FLOPs; the RMSNorm launches and their bytes follow whether
+    the norms are split across the products."""
+    cfg = getattr(synth, name)
+    k = accounting.step_kernels(cfg)
+    total = sum(v["flops"] * v["launches"] for v in k.values())
+    assert total == accounting.forward_flops(cfg)["total"]
+    split = accounting.norm_split(cfg)
+    assert k["rmsnorm"]["launches"] == (2 if split else 2 * cfg.n_layers + 1)
+    M, D = cfg.tokens, cfg.d_model
+    e = 2 if cfg.dtype == "bf16" else 4
+    assert k["gemm_lm_head"]["bytes"] == M * D * e + cfg.vocab * D * e + M * cfg.vocab * e
+    for v in k.values():
+        assert v["bound"] == ("mfma" if v["flops"] > accounting.RIDGE_BF16 * v["bytes"] else "hbm")
