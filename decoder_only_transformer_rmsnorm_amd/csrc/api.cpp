@@ -814,10 +814,12 @@ size_t tfm_decode_attention_workspace_bytes(int B, int Hq, int d_head, int cache
   return round256((size_t)B * Hq * decode_chunks(cache_seq) * (2 + d_head) * 4);
 }
 
-int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
-                         const void *v_cache, const int32_t *positions, void *o,
-                         int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
-                         int window, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+// Checks shared by the decode attention entry points (everything but the workspace).
+int check_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
+                           const void *v_cache, const int32_t *positions, const void *o,
+                           int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
+                           int window) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || cache_seq <= 0 || window < 0)
     return TFM_ERR_SHAPE;
   if (q_stride < (int64_t)Hq * d_head || o_stride < (int64_t)Hq * d_head) return TFM_ERR_SHAPE;
@@ -825,15 +827,46 @@ int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
       cache_seq > decode_max_cache())
     return TFM_ERR_UNSUPPORTED;
   if (B == 0) return TFM_OK;
-  if (!q || !k_cache || !v_cache || !positions || !o || !ws) return TFM_ERR_NULL;
+  if (!q || !k_cache || !v_cache || !positions || !o) return TFM_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-      !aligned16(ws) || q_stride % 8 != 0 || o_stride % 8 != 0)
+      q_stride % 8 != 0 || o_stride % 8 != 0)
     return TFM_ERR_ALIGN;
+  return TFM_OK;
+}
+}  // namespace
+
+int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
+                         const void *v_cache, const int32_t *positions, void *o,
+                         int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
+                         int window, void *ws, size_t ws_bytes, void *stream) {
+  TFM_TRY(check_decode_attention(q, q_stride, k_cache, v_cache, positions, o, o_stride, B, Hq,
+                                 Hkv, d_head, cache_seq, window));
+  if (B == 0) return TFM_OK;
+  if (!ws) return TFM_ERR_NULL;
+  if (!aligned16(ws)) return TFM_ERR_ALIGN;
   if (ws_bytes < tfm_decode_attention_workspace_bytes(B, Hq, d_head, cache_seq))
     return TFM_ERR_WORKSPACE;
   return hip_status(launch_decode_attention(q, q_stride, k_cache, v_cache, positions, B, Hq,
                                             Hkv, d_head, cache_seq, window, (float *)ws, o,
                                             o_stride, (hipStream_t)stream));
+}
+
+size_t tfm_decode_attention_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int tfm_decode_attention_noalloc(const void *q, int64_t q_stride, const void *k_cache,
+                                 const void *v_cache, const int32_t *positions, void *o,
+                                 int64_t o_stride, int B, int Hq, int Hkv, int d_head,
+                                 int cache_seq, int window, void *stream) {
+  TFM_TRY(check_decode_attention(q, q_stride, k_cache, v_cache, positions, o, o_stride, B, Hq,
+                                 Hkv, d_head, cache_seq, window));
+  if (B == 0) return TFM_OK;
+  if (tfm_decode_attention_workspace_bytes(B, Hq, d_head, cache_seq) > kNoAllocScratchBytes)
+    return TFM_ERR_WORKSPACE;
+  float *part = nullptr;
+  TFM_HIP(noalloc_scratch((hipStream_t)stream, &part));
+  return hip_status(launch_decode_attention(q, q_stride, k_cache, v_cache, positions, B, Hq,
+                                            Hkv, d_head, cache_seq, window, part, o, o_stride,
+                                            (hipStream_t)stream));
 }
 
 

@@ -26,11 +26,19 @@
 //    into the cache slots of their positions.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
 
 namespace tfm {
+
+// Split records of the allocation-free decode attention entry point. One copy per GPU, held
+// until the process ends; every call on a GPU shares it (concurrent calls on one GPU race).
+// Host code never uses this name as an address: it passes the device address that
+// hipGetSymbolAddress returns for the device running the call.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int kDecMaxGroup = 8;      // query heads per kv head supported by the decode kernel
@@ -518,6 +526,37 @@ hipError_t run_dec_attn_g(const void *q, int64_t q_stride, const void *kc, const
 }  // namespace
 
 int decode_chunks(int cache_seq) { return std::min(kMaxSplits, (cache_seq + 63) / 64); }
+
+hipError_t noalloc_scratch(hipStream_t stream, float **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float *addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // the symbol's address on `dev`, looked up with that device current
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = (float *)p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 int decode_max_cache() { return kDecMaxCache; }
 bool decode_group_supported(int Hq, int Hkv) { return Hq % Hkv == 0 && Hq / Hkv <= kDecMaxGroup; }
 

@@ -134,6 +134,11 @@ hipError_t launch_decode_attention(const void *q, int64_t q_stride, const void *
                                    const void *v_cache, const int32_t *positions, int B, int Hq,
                                    int Hkv, int d_head, int cache_seq, int window, float *part,
                                    void *o, int64_t o_stride, hipStream_t s);
+// Size of the static device scratch of the allocation-free decode attention entry point, and
+// its device address on the GPU that runs `stream` (looked up once per device with
+// hipGetSymbolAddress, never allocated).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, float **ptr);
 // Copies the k and v columns of B*S qkv rows into the cache slots positions[r] (or r % S).
 hipError_t launch_kv_store(const void *qkv, int64_t ld, int qd, int kvd, int d_head, int Hkv,
                            int B, int S, const int32_t *positions, void *k_cache, void *v_cache,

@@ -28,6 +28,7 @@ EXPORTS = ["tfm_status_string", "tfm_last_hip_error", "tfm_version", "tfm_rope_t
            "tfm_sliding_window_attention", "tfm_kv_cache_bytes", "tfm_model_prefill",
            "tfm_decode_workspace_bytes", "tfm_model_decode",
            "tfm_decode_attention_workspace_bytes", "tfm_decode_attention",
+           "tfm_decode_attention_noalloc_max_bytes", "tfm_decode_attention_noalloc",
            "tfm_train_workspace_bytes", "tfm_model_backward", "tfm_clip_workspace_bytes",
            "tfm_grad_clip_coef", "tfm_adamw_step", "tfm_adamw_step_multi",
            "tfm_check_device_flags", "tfm_mfma_rate", "tfm_trace_begin", "tfm_trace_end",
@@ -129,6 +130,9 @@ def lib() -> ctypes.CDLL:
             "tfm_decode_attention_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
             "tfm_decode_attention": (c_int, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_int, c_int,
                                              c_int, c_int, c_int, c_int, c_p, c_size, c_p]),
+            "tfm_decode_attention_noalloc_max_bytes": (c_size, []),
+            "tfm_decode_attention_noalloc": (c_int, [c_p, c_i64, c_p, c_p, c_p, c_p, c_i64, c_int,
+                                                     c_int, c_int, c_int, c_int, c_int, c_p]),
             "tfm_train_workspace_bytes": (c_size, [ctypes.POINTER(Config), c_int, c_int]),
             "tfm_model_backward": (c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights),
                                            c_p, c_p, c_p, c_p, ctypes.POINTER(ModelGrads), c_int,
@@ -628,6 +632,25 @@ def tfm_decode_attention(q, k_cache, v_cache, positions, n_heads: int, n_kv_head
                                       o.stride(0), B, n_heads,
                                       n_kv_heads, d_head, cache_seq, window, _dev(ws), ws.numel(),
                                       _stream(stream))
+    return o
+
+
+def tfm_decode_attention_noalloc(q, k_cache, v_cache, positions, n_heads: int, n_kv_heads: int,
+                                 d_head: int, window: int = 0, o=None, stream=None):
+    """tfm_decode_attention with its split records in the library's static device scratch
+    (no workspace, nothing allocated by the library). Concurrent calls on one GPU race."""
+    torch = _torch()
+    B, cache_seq = q.shape[0], k_cache.shape[2]
+    if o is None:
+        o = torch.empty((B, n_heads * d_head), dtype=q.dtype, device=q.device)
+    bf, cache_n = torch.bfloat16, B * n_kv_heads * cache_seq * d_head
+    _call("tfm_decode_attention_noalloc",
+          _dev_rows(q, "q", bf, B, n_heads * d_head, q.stride(0)), q.stride(0),
+          _dev(k_cache, "k_cache", bf, cache_n, exact=True),
+          _dev(v_cache, "v_cache", bf, cache_n, exact=True),
+          _dev(positions, "positions", _int32(), B, exact=True),
+          _dev_rows(o, "o", bf, B, n_heads * d_head, o.stride(0)), o.stride(0), B, n_heads,
+          n_kv_heads, d_head, cache_seq, window, _stream(stream))
     return o
 
 

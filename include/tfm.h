@@ -274,6 +274,24 @@ int tfm_decode_attention(const void *q, int64_t q_stride, const void *k_cache,
                          int64_t o_stride, int B, int Hq, int Hkv, int d_head, int cache_seq,
                          int window, void *ws, size_t ws_bytes, void *stream);
 
+/* Decode attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): tfm_decode_attention with
+ * the same arguments, kernels and results, but its split records live in a static device
+ * array of tfm_decode_attention_noalloc_max_bytes() bytes (4 MiB) that each GPU holds until the
+ * process ends, instead of a caller workspace. Allocates nothing: no hipMalloc, no hipFree. The
+ * first call on a device looks up the array's address on the device of `stream` (once per
+ * device). A call whose records would exceed the array, i.e. whose
+ * tfm_decode_attention_workspace_bytes(B, Hq, d_head, cache_seq) is larger, returns
+ * TFM_ERR_WORKSPACE before any launch. Every call on one GPU uses the same array, so calls that
+ * overlap on one GPU (on different streams, or from different threads) race; calls on one
+ * stream are ordered. Nothing in the array needs to start at zero: each call writes every
+ * record it reads. */
+size_t tfm_decode_attention_noalloc_max_bytes(void);
+int tfm_decode_attention_noalloc(const void *q, int64_t q_stride, const void *k_cache,
+                                 const void *v_cache, const int32_t *positions, void *o,
+                                 int64_t o_stride, int B, int Hq, int Hkv, int d_head,
+                                 int cache_seq, int window, void *stream);
+
 /* ---- Training step  [T2 Optimize: Loss, Optimizer - AdamW, Gradient Clip; T3 12 training
  * loop: loss, backward, clip, step]. fp32 gradients; fp32 master weights and moments. */
 typedef struct {

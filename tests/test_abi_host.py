@@ -394,6 +394,28 @@ def test_decode_attention_validation(L):
     assert call(nb=need - 1) == WS
 
 
+def test_decode_attention_noalloc_validation(L):
+    """The allocation-free variant checks like tfm_decode_attention and refuses, before any
+    device call, a call whose split records exceed its static scratch array."""
+    f = L.tfm_decode_attention_noalloc
+    cap = L.tfm_decode_attention_noalloc_max_bytes()
+    assert cap == 4 << 20
+    call = lambda q=P, qs=512, o=P, os=512, B=2, Hq=8, Hkv=2, dh=64, cs=300, W=0: f(
+        q, qs, P, P, P, o, os, B, Hq, Hkv, dh, cs, W, None)
+    assert call(Hkv=3) == SHAPE
+    assert call(cs=0) == SHAPE
+    assert call(cs=131073) == UNSUP
+    assert call(W=-1) == SHAPE
+    assert call(dh=48, qs=384, os=384) == UNSUP
+    assert call(B=0) == OK
+    assert call(q=None) == NULL
+    assert call(o=PM) == ALIGN
+    # 64 sequences x 32 heads x 64 chunks of 130 floats: 68 MB of records > 4 MiB
+    big = dict(B=64, Hq=32, Hkv=4, dh=128, qs=4096, os=4096, cs=4096)
+    assert L.tfm_decode_attention_workspace_bytes(64, 32, 128, 4096) > cap
+    assert call(**big) == WS
+
+
 def test_training_entry_points_validation(L):
     """Every call fails validation (or is empty) before any launch."""
     c = _cfg()
