@@ -57,6 +57,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
+
 // Buffer resources exist only for the device target; the host pass sees the kernels'
 // signatures (to emit launch stubs) but not their bodies.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -217,6 +218,65 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, f32x16_t (&acc)[NBN]
           }
           store_out(g, m, n, v, g.N);
         }
+      }
+    }
+  }
+}
+
+// Epilogue of the SwiGLU product's 16 x 16 blocks, written from registers. Block (bn, bm) of
+// the lane holds rows m = m0 + wm WM + 16 bm + l32 and virtual weight rows n0 + wn WN + 16 bn
+// + 4 h .. + 3; in every 64-row group of virtual rows, gate block gb and up block gb + 2 hold
+// the same hidden units, and the output column is the hidden unit. Rows are first scaled by
+// 1 / rms(x) when the RMSNorm is split across the products.
+template <int NBM, int NBN, int WM, int WN, typename Acc>
+__device__ __forceinline__ void swiglu_direct_epilogue(const GemmArgs &g, Acc (&acc)[NBN][NBM],
+                                                       int64_t m0, int n0, int wm, int wn, int h,
+                                                       int l32) {
+  const int ncols = g.n0;   // d_ff
+  const bool vec = (g.ldy & 3) == 0;
+  float rsv[NBM];
+#pragma unroll
+  for (int bm = 0; bm < NBM; ++bm) rsv[bm] = 1.f;
+  if (g.rs_part) {
+    f32x4_t pr[NBM];
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      const int64_t m = m0 + wm * WM + bm * 16 + l32;
+      pr[bm] = *(const f32x4_t *)(g.rs_part + (m < g.M ? m : g.M - 1) * kNormParts);
+    }
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < kNormParts; ++t) ss += t < g.rs_parts ? pr[bm][t] : 0.f;
+      rsv[bm] = rsqrtf(ss / (float)g.rs_d + g.rs_eps);
+    }
+  }
+  bf16_t *y = (bf16_t *)g.y;
+#pragma unroll
+  for (int bm = 0; bm < NBM; ++bm) {
+    const int64_t m = m0 + wm * WM + bm * 16 + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int bn = 0; bn < NBN / 2; ++bn) {
+      const int gb = 4 * (bn >> 1) + (bn & 1), ub = gb + 2;
+      const int col = (n0 + wn * WN) / 2 + bn * 16 + 4 * h;
+      float v[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        // SiLU(a) b = a b / (1 + 2^(-a log2 e)) with the hardware exp2 and reciprocal (about 1
+        // ulp each, far inside the bf16 rounding that follows); a very negative a gives
+        // 2^(+big) = inf, a reciprocal of 0 and SiLU = -0
+        const float a = acc[gb][bm][x] * rsv[bm], b = acc[ub][bm][x] * rsv[bm];
+        v[x] = a * b * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+      }
+      bf16_t *p = y + m * g.ldy + col;
+      if (vec && col + 3 < ncols) {
+        *(u32x2_t *)p = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (col + x < ncols) p[x] = f32_to_bf16(v[x]);
       }
     }
   }
@@ -552,6 +612,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  }
+  // 16 x 16 blocks of the SwiGLU product leave the accumulators straight to global memory (each
+  // lane holds 4 consecutive hidden units of one row), without staging the tile in LDS. The
+  // large plain-store output (the logits) must leave in whole 128-byte lines: written from
+  // registers in 32-byte row pieces it took 1.4x as long (measured), so it and the QKV
+  // product stage through LDS.
+  if constexpr (MS == 16 && EPI == EPI_SWIGLU) {
+    swiglu_direct_epilogue<NBM, NBN, WM, WN>(g, acc, m0, n0, wm, wn, h, l32);
+    return;
   }
   __syncthreads();  // every wave is done with the ring: reuse it to stage the output
 
@@ -893,6 +962,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     }
     if (p + 1 < passes) __syncthreads();
   }
+
 #endif
 }
 
