@@ -77,9 +77,9 @@ RIDGE_BF16 = 2.5e15 / 8.0e12   # flop per HBM byte where the bf16 MFMA and HBM r
 
 def norm_split(cfg) -> bool:
     """Whether the forward splits each block's RMSNorms across the products that write and read
-    the residual (bf16 models with d_model <= 768, the width whose row partials one tile row of
-    the residual product holds)."""
-    return cfg.dtype == "bf16" and cfg.d_model <= 768
+    the residual (bf16 models with d_model <= 3072: at most 16 column tiles of 192, the row
+    partials one row of the partials buffer holds)."""
+    return cfg.dtype == "bf16" and cfg.d_model <= 3072
 
 
 def step_kernels(cfg, batch: int | None = None, seq: int | None = None,

@@ -223,6 +223,43 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, f32x16_t (&acc)[NBN]
   }
 }
 
+// 1 / rms(x) of each of a lane's NBM rows (rows m0 + wm WM + MS bm + l32) from the producer's
+// per-column-tile sums of squares, added in tile order (deterministic); four partials are
+// loaded per step while the previous four are added. Rows past M read row M - 1 (their
+// outputs are never stored).
+template <int NBM, int MS, int WM>
+__device__ __forceinline__ void split_norm_scales(const GemmArgs &g, int64_t m0, int wm, int l32,
+                                                  float (&rsv)[NBM]) {
+  constexpr int NV = kNormParts / 4;
+  const float *rowp[NBM];
+  float ss[NBM];
+  f32x4_t cur[NBM], nxt[NBM];
+#pragma unroll
+  for (int bm = 0; bm < NBM; ++bm) {
+    const int64_t m = m0 + wm * WM + bm * MS + l32;
+    rowp[bm] = g.rs_part + (m < g.M ? m : g.M - 1) * kNormParts;
+    cur[bm] = *(const f32x4_t *)rowp[bm];
+    ss[bm] = 0.f;
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const bool more = v + 1 < NV && 4 * (v + 1) < g.rs_parts;
+    if (more) {
+#pragma unroll
+      for (int bm = 0; bm < NBM; ++bm) nxt[bm] = *(const f32x4_t *)(rowp[bm] + 4 * (v + 1));
+    }
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ss[bm] += 4 * v + t < g.rs_parts ? cur[bm][t] : 0.f;
+    if (!more) break;
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) cur[bm] = nxt[bm];
+  }
+#pragma unroll
+  for (int bm = 0; bm < NBM; ++bm) rsv[bm] = rsqrtf(ss[bm] / (float)g.rs_d + g.rs_eps);
+}
+
 // Epilogue of the SwiGLU product's 16 x 16 blocks, written from registers. Block (bn, bm) of
 // the lane holds rows m = m0 + wm WM + 16 bm + l32 and virtual weight rows n0 + wn WN + 16 bn
 // + 4 h .. + 3; in every 64-row group of virtual rows, gate block gb and up block gb + 2 hold
@@ -237,21 +274,7 @@ __device__ __forceinline__ void swiglu_direct_epilogue(const GemmArgs &g, Acc (&
   float rsv[NBM];
 #pragma unroll
   for (int bm = 0; bm < NBM; ++bm) rsv[bm] = 1.f;
-  if (g.rs_part) {
-    f32x4_t pr[NBM];
-#pragma unroll
-    for (int bm = 0; bm < NBM; ++bm) {
-      const int64_t m = m0 + wm * WM + bm * 16 + l32;
-      pr[bm] = *(const f32x4_t *)(g.rs_part + (m < g.M ? m : g.M - 1) * kNormParts);
-    }
-#pragma unroll
-    for (int bm = 0; bm < NBM; ++bm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int t = 0; t < kNormParts; ++t) ss += t < g.rs_parts ? pr[bm][t] : 0.f;
-      rsv[bm] = rsqrtf(ss / (float)g.rs_d + g.rs_eps);
-    }
-  }
+  if (g.rs_part) split_norm_scales<NBM, 16, WM>(g, m0, wm, l32, rsv);
   bf16_t *y = (bf16_t *)g.y;
 #pragma unroll
   for (int bm = 0; bm < NBM; ++bm) {
@@ -756,21 +779,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) rsv[bm] = 1.f;
       if constexpr (EPI == EPI_QKV_ROPE || EPI == EPI_SWIGLU) {
-        if (g.rs_part) {
-          f32x4_t pr[NBM];
-#pragma unroll
-          for (int bm = 0; bm < NBM; ++bm) {
-            const int64_t m = m0 + wm * WM + bm * MS + l32;
-            pr[bm] = *(const f32x4_t *)(g.rs_part + (m < g.M ? m : g.M - 1) * kNormParts);
-          }
-#pragma unroll
-          for (int bm = 0; bm < NBM; ++bm) {
-            float ss = 0.f;
-#pragma unroll
-            for (int t = 0; t < kNormParts; ++t) ss += t < g.rs_parts ? pr[bm][t] : 0.f;
-            rsv[bm] = rsqrtf(ss / (float)g.rs_d + g.rs_eps);
-          }
-        }
+        if (g.rs_part) split_norm_scales<NBM, MS, WM>(g, m0, wm, l32, rsv);
       }
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {

@@ -65,19 +65,20 @@ struct GemmArgs {
   // (1/rms(x)) ((x * g) W^T), the per-row factor commutes with the product).
   // EPI_RESIDUAL with nrm_y (bf16 only): besides x it writes nrm_y = bf16(x * nrm_g) (row
   // stride ldy) and the sum of squares of the tile's columns of x, row m, column tile t, into
-  // nrm_part[4 m + t] (at most kNormParts column tiles, i.e. N <= gemm_norm_max_cols()).
+  // nrm_part[kNormParts m + t] (at most kNormParts column tiles: N <= gemm_norm_max_cols()).
   const void *nrm_g;
   void *nrm_y;
   float *nrm_part;
   // EPI_QKV_ROPE / EPI_SWIGLU with rs_part (bf16 only): the activations a are bf16(x * g);
-  // every output row m is scaled by 1 / sqrt(sum_{t < rs_parts} rs_part[4 m + t] / rs_d + rs_eps)
+  // every output row m is scaled by 1 / sqrt(sum_{t < rs_parts} rs_part[kNormParts m + t] / rs_d
+  // + rs_eps)
   // in fp32 before the rest of the epilogue.
   const float *rs_part;
   int rs_parts, rs_d;
   float rs_eps;
 };
 
-constexpr int kNormParts = 4;   // column tiles whose row partials one row of nrm_part holds
+constexpr int kNormParts = 16;  // column tiles whose row partials one row of nrm_part holds
 // Column tiles of the bf16 residual product over N columns, and the largest N whose row
 // partials fit in nrm_part.
 int gemm_residual_col_tiles(int N);

@@ -153,8 +153,8 @@ def test_workspace_bytes_plan(L):
     n = L.tfm_workspace_bytes(ctypes.byref(c), B, S)
     M, D, F, e = B * S, 512, 1344, 2
     # plus the per-row partial sums of squares of the RMSNorm split across products (bf16,
-    # d_model <= 768): 4 floats per row
-    expect = 256 + M * D * 4 + M * D * e + M * 3 * D * e + M * D * e + M * F * e + M * 4 * 4
+    # d_model <= 3072): 16 floats per row
+    expect = 256 + M * D * 4 + M * D * e + M * 3 * D * e + M * D * e + M * F * e + M * 16 * 4
     assert n == expect
     assert L.tfm_workspace_bytes(ctypes.byref(_cfg(n_kv_heads=5)), B, S) == 0
     assert L.tfm_workspace_bytes(ctypes.byref(c), B, 257) == 0    # S > max_seq_len

@@ -163,19 +163,24 @@ def _swap_gain(inp, layer: int, field: str, src_layer: int, src_field: str):
     return bad
 
 
-@pytest.mark.parametrize("case", ["d256_gqa", "d768_mha"])
+@pytest.mark.parametrize("case", ["d256_gqa", "d768_mha", "d1600_mha", "d2048_gqa"])
 def test_model_split_norm_nonunit_gains(case):
-    """bf16 models with d <= 768 split each block's RMSNorms across two products ("Transformer
-    篇" (dujian.net) 5.6, the per-dimension gain g): block l's down projection writes
-    bf16(x * g_attn of block l + 1) and the row sums of squares, and block l + 1's QKV product
-    rescales its rows by 1 / rms(x). With gains 1 + N(0, 0.1) every logit is compared with the
+    """bf16 models with d <= 3072 split each block's RMSNorms across two products
+    ("Transformer 篇" (dujian.net) 5.6, the per-dimension gain g): block l's down projection
+    writes bf16(x * g_attn of block l + 1) and the sums of squares of each 192-column tile of
+    every row, and block l + 1's QKV product adds them in tile order and rescales its rows by
+    1 / rms(x). With gains 1 + N(0, 0.1) every logit is compared with the
     oracle. The same oracle run with one gain taken from the wrong place (block 1's FFN gain,
     block 0's attention gain, or block 1's attention gain as block 0's FFN gain) differs from
     the reference by more than the bar, so none of those choices on the GPU could pass."""
     if case == "d256_gqa":
         cfg = small("bf16", n_layers=3, seq=160, batch=3)
-    else:
+    elif case == "d768_mha":
         cfg = synth.GPT2S_BF16.replace(name="d768_L2", n_layers=2, batch=2, seq=256)
+    elif case == "d1600_mha":   # 9 column tiles of row partials (the XL width)
+        cfg = synth.XL_BF16.replace(name="d1600_L2", n_layers=2, batch=1, seq=160, vocab=4000)
+    else:                       # 11 column tiles, grouped-query heads of 128 (long-GQA width)
+        cfg = synth.LONG_GQA_BF16.replace(name="d2048_L2", n_layers=2, batch=1, seq=192, vocab=4000)
     say(f"model split RMSNorm gains {case}: L={cfg.n_layers} d={cfg.d_model} B={cfg.batch} S={cfg.seq}")
     inp = synth.make_inputs(cfg, seed=11, gamma_std=GAIN_STD)
     assert np.abs(inp.layers[1].g_attn - 1).max() > 0.1
