@@ -126,18 +126,23 @@ def cpu_baseline(cfg, inputs, budget_s: float, threads: int):
     import numpy as np
     import oracle
     oracle.set_num_threads(threads)
-    p0 = min(64, cfg.seq)
+    p0 = min(16, cfg.seq)          # probe; 64 tokens when 16 take under a tenth of the budget
     t0 = time.perf_counter()
     logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :p0])
-    t64 = time.perf_counter() - t0
-    if t64 > 0.4 * budget_s:      # the probe alone is a long enough sample
+    tp = time.perf_counter() - t0
+    if tp < 0.1 * budget_s and cfg.seq > p0:
+        p0 = min(64, cfg.seq)
+        t0 = time.perf_counter()
+        logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :p0])
+        tp = time.perf_counter() - t0
+    if tp > 0.4 * budget_s:      # the probe alone is a long enough sample
         assert np.isfinite(logits).all()
         sample = (f"sequence 0 of {cfg.batch}, positions 0..{p0 - 1} ({p0} tokens), all "
                   f"{cfg.vocab} logits per token")
-        return {"value": round(p0 / t64, 2), "unit": "tokens/s", "cores": threads,
-                "kind": "oracle", "sample": sample, "seconds": round(t64, 2)}
-    if t64 * (cfg.seq / p0) * 1.15 > budget_s:
-        prefix = max(64, int(64 * budget_s / max(t64, 1e-9) / 1.15) // 64 * 64)
+        return {"value": round(p0 / tp, 2), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle", "sample": sample, "seconds": round(tp, 2)}
+    if tp * (cfg.seq / p0) * 1.15 > budget_s:
+        prefix = max(p0, int(p0 * budget_s / max(tp, 1e-9) / 1.15) // 16 * 16)
         t0 = time.perf_counter()
         logits = oracle.model(cfg, inputs, ids=inputs.ids[:1, :prefix])
         dt = time.perf_counter() - t0
@@ -160,7 +165,8 @@ def cpu_baseline(cfg, inputs, budget_s: float, threads: int):
 
 
 def rate_entry(label: str, w: dict, avg_ms: float, peak_mfma: float) -> dict:
-    """A kernel family against its binding roofline; both fractions are given."""
+    """A kernel family against its binding roofline (avg_ms: its launch duration in the step);
+    both fractions are given."""
     s = avg_ms / 1e3
     e = {"kernel": label, "bound": w["bound"], "avg_launch_us": round(avg_ms * 1e3, 2),
          "flops_per_launch": int(w["flops"]), "bytes_per_launch": int(w["bytes"]),
@@ -182,7 +188,8 @@ def roofline_of(entry: dict, peak_mfma: float, traffic) -> dict:
             "flops_per_launch": entry["flops_per_launch"],
             "bytes_per_launch": entry["bytes_per_launch"],
             "avg_launch_us": entry["avg_launch_us"],
-            "timing": "HIP events around every launch inside the traced steps, launch stream"}
+            "timing": "HIP events around every launch inside the traced steps on the launch "
+                      "stream, less the trace's own cost per launch"}
 
 
 def main() -> int:
@@ -295,22 +302,30 @@ def main() -> int:
         a = agg.setdefault(label, [0, 0.0])
         a[0] += 1
         a[1] += t
+    # An event pair brackets a launch plus the gap before it, and recording the events costs
+    # time of its own; that cost per launch is the traced step's excess over the untraced one
+    # divided by the step's launches, and is taken off every launch's average.
+    launches = len(tr.records) / args.steps
+    trace_cost = max(0.0, traced_ms - ms) / launches
     step_kernels = {}
     for label, (n, tot) in agg.items():
         w = work.get(label)
-        avg = tot / n
+        avg_gap = tot / n
+        avg = max(avg_gap - trace_cost, 1e-6)
         e = rate_entry(label, w, avg, peak_mfma) if w else {"kernel": label,
                                                             "avg_launch_us": round(avg * 1e3, 2)}
+        e["avg_launch_us_with_gap"] = round(avg_gap * 1e3, 2)
         e["launches_per_step"] = n // args.steps
-        e["us_per_step"] = round(tot / args.steps * 1e3, 1)
-        e["share_of_step"] = round(tot / args.steps / traced_ms, 4)
+        e["us_per_step"] = round(avg * n / args.steps * 1e3, 1)
+        e["share_of_step"] = round(avg * n / args.steps / ms, 4)
         step_kernels[label] = e
     order = sorted(step_kernels, key=lambda k: -step_kernels[k]["us_per_step"])
     for k in order:
         e = step_kernels[k]
         log(f"in-step {k}: {e['launches_per_step']} x {e['avg_launch_us']} us = {e['us_per_step']} "
             f"us/step ({e['share_of_step']:.1%})" + (f", {e['bound']} frac {e['frac']}" if "frac" in e else ""))
-    log(f"traced steps: {traced_ms:.3f} ms/step (untraced {ms:.3f})")
+    log(f"traced steps: {traced_ms:.3f} ms/step (untraced {ms:.3f}; trace cost "
+        f"{trace_cost * 1e3:.2f} us per launch, taken off each launch)")
     dominant = next(k for k in order if k in work)
     roofline = roofline_of(step_kernels[dominant], peak_mfma,
                            traffic_from_profiles(cfg.name, dominant))
@@ -435,6 +450,7 @@ def main() -> int:
         "roofline": roofline,
         "roofline_lm_head": roofline_lm,
         "traced_ms_per_step": round(traced_ms, 4),
+        "trace_cost_us_per_launch": round(trace_cost * 1e3, 3),
         "step_kernels": step_kernels,
         "mfma_util": mfma_util,
         "rmsnorm_hbm": rmsnorm_hbm,
