@@ -28,8 +28,12 @@
 // in the scalar offset, so a fill costs no vector arithmetic. Buffer resources cover
 // exactly the rows a tile may read, so rows past M or N (and K chunks past K) read as zero
 // without branches. A ring of 2-6 stages runs ahead of the MFMAs, refilled between them.
-// The 8-wave ping-pong variant splits the waves into two groups half a step apart, so one
-// group's LDS reads and fills overlap the other's MFMAs on every SIMD. Tiles are assigned
+// Main loops: the cross-stage pipeline (the products whose K is a multiple of 64) reads the
+// fragments of the next 32-deep k step while the MFMAs of the current one run, across the
+// stage barrier too, with two waves per SIMD; the classic loop (ragged K, split K) reads a
+// stage's first fragments after its barrier; the 8-wave ping-pong variant (SwiGLU with ragged
+// K) splits the waves into two groups half a step apart, so one group's LDS reads and fills
+// overlap the other's MFMAs on every SIMD. Tiles are assigned
 // to XCDs in contiguous runs (workgroup b runs on XCD b % 8) and ordered in groups of 8
 // tile-rows, so the workgroups an XCD runs at once share activation and weight row-blocks
 // in its L2.
@@ -57,6 +61,27 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
+
+template <int N>
+using ic2 = std::integral_constant<int, N>;
+
+// 16-byte LDS read at addr + IMM, issued as written: the compiler's own wait insertion cannot
+// tell which LDS bytes an in-flight buffer->LDS fill writes, so fragment reads are inline and
+// waited for explicitly.
+template <int IMM>
+__device__ __forceinline__ void ds_read16(u32x4_t &dst, uint32_t addr) {
+  static_assert(IMM >= 0 && IMM < 65536, "LDS offset immediate");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(IMM) : "memory");
+}
+
+// f(integral_constant<int, I>) for I = B .. E - 1, each index a constant expression
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(ic2<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Buffer resources exist only for the device target; the host pass sees the kernels'
 // signatures (to emit launch stubs) but not their bodies.
@@ -357,8 +382,11 @@ struct BfTile {
 // MS: matrix-core block, 32 (v_mfma_f32_32x32x16_bf16) or 16 (v_mfma_f32_16x16x32_bf16). The
 // 16x16 form moves less accumulator and operand data through the register file per flop,
 // which pays under the chip's power limit.
+// XS (cross-stage pipeline): the KM-deep k steps run as one flat sequence and the fragments of
+// step s + 1 are read while the MFMAs of step s run, also across a stage boundary, so no wave
+// waits on LDS at the start of a stage (see the main loop).
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2, bool PP = false, int MS = 32>
+          int WGN = 2, bool PP = false, int MS = 32, bool XS = false>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g0, int tiles_m,
                                                                         int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -560,8 +588,125 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   // other waves at the barrier (after which the stage consumed one iteration earlier is
   // free and gets refilled, interleaved with this stage's MFMAs), then multiplies, reading
   // the next k step's fragments while the current step's MFMAs run.
-  static_assert(NBM + NBN <= 15, "fragment reads exceed the lgkmcnt range");
-  if constexpr (PP) {
+  static_assert(XS || NBM + NBN <= 15, "fragment reads exceed the lgkmcnt range");
+  if constexpr (XS) {
+    // Cross-stage pipeline (one wave per SIMD, K a multiple of BK, two 32-deep k slices per
+    // stage). Slice step s multiplies fragments read during step s - 1 while it reads those
+    // of step s + 1, one fragment between every few MFMAs. Before the second slice of a stage
+    // each wave waits for its own fills of the next stage and meets the others at the
+    // barrier: after it the next stage is complete in LDS (its first fragments are read
+    // during this slice) and every wave has finished reading the current stage (its last
+    // fragments are in registers), so the current stage's slot is refilled at once with the
+    // stage NST ahead, the fills spread between this slice's MFMAs. Fragment reads never wait
+    // on a barrier.
+    static_assert(!PP && MS == 16 && KK == 2, "cross-stage pipeline layout");
+    constexpr int NR = NBM + NBN;                        // fragment reads per slice
+    constexpr int MFN = NBN * NBM;                       // MFMAs per slice
+    constexpr int RG = (3 * MFN / 4) / NR > 0 ? (3 * MFN / 4) / NR : 1;   // MFMAs per read
+    constexpr int FG = MFN / LOADS > 0 ? MFN / LOADS : 1;                 // MFMAs per fill
+    // Per-lane LDS read addresses within a stage slot. The chunk swizzle depends on row bits
+    // 1..4 only, and bit 4 of a block's rows is the parity of its 16-row block index, so one
+    // base per (parity, k slice) serves every block; the block's row offset is the read's
+    // immediate and the slot's offset is added once per slice.
+    uint32_t ra[2][KK], rb[2][KK];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int rowa = wm * WM + q * MS + l32, rowb = BM + wn * WN + q * MS + l32;
+        ra[q][kk] = lds_base + (rowa - q * MS) * RB + ((((KM / 8) * kk + h) ^ swz_rb<RB>(rowa)) << 4);
+        rb[q][kk] = lds_base + (rowb - q * MS) * RB + ((((KM / 8) * kk + h) ^ swz_rb<RB>(rowb)) << 4);
+      }
+    u32x4_t fa[2][NBM], fb[2][NBN];
+    // fragment R (activation block R, then weight block R - NBM) into buffer BU
+    auto rd = [&](const uint32_t (&ba)[2], const uint32_t (&bb)[2], auto r_, auto buf_) {
+      constexpr int R = decltype(r_)::value, BU = decltype(buf_)::value;
+      if constexpr (R < NBM)
+        ds_read16<R * MS * RB>(fa[BU][R], ba[R & 1]);
+      else
+        ds_read16<(R - NBM) * MS * RB>(fb[BU][R - NBM], bb[(R - NBM) & 1]);
+    };
+    // fill J of a stage into `slot`; koff past the last stage puts every lane out of range
+    // (zeros land in a slot nobody reads again)
+    auto fill_one = [&](uint32_t koff, int slot, auto j_) {
+      constexpr int J = decltype(j_)::value;
+      uint8_t *base = lds + slot * STAGE;
+      if constexpr (J < A_INS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_void_t *)(base + (wid * A_INS + J) * FR * RB), 16, a_off[J], koff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            b_rsrc[J - A_INS], (lds_void_t *)(base + (BM + (wid * B_INS + J - A_INS) * FR) * RB),
+            16, b_off[J - A_INS], koff, 0, 0);
+    };
+    // slice KS of stage st; NEXT: read the fragments of the following slice during it
+    auto slice = [&](int st, auto ks_, auto next_) {
+      constexpr int KS = decltype(ks_)::value, C = KS, N = KS ^ 1;
+      constexpr bool NEXT = decltype(next_)::value;
+      constexpr bool LAST = KS == KK - 1;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int bm = 0; bm < NBM; ++bm) asm volatile("" : "+v"(fa[C][bm]));
+#pragma unroll
+      for (int bn = 0; bn < NBN; ++bn) asm volatile("" : "+v"(fb[C][bn]));
+      uint32_t koff = kOOB;
+      int slot = 0;
+      if constexpr (LAST && NEXT) {
+        wait_fills(min(NST - 2, nk - 2 - st));
+        asm volatile("s_barrier" ::: "memory");
+        koff = st + NST < nk ? (uint32_t)((st + NST) * BK * 2) : kOOB;
+        slot = st % NST;
+      }
+      // read bases of the following slice: same stage, next k slice; or next stage, slice 0
+      constexpr int NKS = LAST ? 0 : KS + 1;
+      const uint32_t soff = (uint32_t)(((LAST ? st + 1 : st) % NST) * STAGE);
+      uint32_t ba[2], bb[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        ba[q] = ra[q][NKS] + soff;
+        bb[q] = rb[q][NKS] + soff;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, MFN>([&](auto i_) {
+        constexpr int I = decltype(i_)::value;
+        constexpr int BN_ = I / NBM, BM_ = I % NBM;
+        acc[BN_][BM_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, fb[C][BN_]), __builtin_bit_cast(bf16x8_t, fa[C][BM_]),
+            acc[BN_][BM_], 0, 0, 0);
+        if constexpr (NEXT && I % RG == 0 && I / RG < NR) {
+          rd(ba, bb, ic2<I / RG>{}, ic2<N>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (LAST && NEXT && I % FG == FG / 2 && I / FG < LOADS) {
+          fill_one(koff, slot, ic2<I / FG>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      if constexpr (NEXT) {   // reads the MFMAs ran out before
+        static_for<(MFN + RG - 1) / RG, NR>([&](auto r) { rd(ba, bb, r, ic2<N>{}); });
+      }
+      if constexpr (LAST && NEXT) {   // fills the MFMAs ran out before
+        static_for<(MFN - FG / 2 + FG - 1) / FG, LOADS>([&](auto j) { fill_one(koff, slot, j); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s0 = 0; s0 < NST && s0 < nk; ++s0)
+      static_for<0, LOADS>([&](auto j) { fill_one((uint32_t)(s0 * BK * 2), s0, j); });
+    wait_fills(min(NST - 1, nk - 1));
+    asm volatile("s_barrier" ::: "memory");
+    {
+      uint32_t ba[2] = {ra[0][0], ra[1][0]}, bb[2] = {rb[0][0], rb[1][0]};
+      static_for<0, NR>([&](auto r) { rd(ba, bb, r, ic2<0>{}); });
+    }
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    for (int st = 0; st + 1 < nk; ++st) {
+      slice(st, ic2<0>{}, T_{});
+      slice(st, ic2<1>{}, T_{});
+    }
+    slice(nk - 1, ic2<0>{}, T_{});
+    slice(nk - 1, ic2<1>{}, F_{});
+  } else if constexpr (PP) {
     // Phases alternate memory / matrix work; group 1 runs one phase behind group 0, and
     // every phase ends at a barrier of all 8 waves. Fills run D = NST-1 stages ahead: the
     // memory phase of step kt reads all of stage kt's fragments into registers and issues
@@ -1100,13 +1245,13 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
 }
 
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2, bool PP = false, int MS = 32>
+          int WGN = 2, bool PP = false, int MS = 32, bool XS = false>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS, XS>),
                      dim3((unsigned)(tm * tn), g.kparts > 1 ? g.kparts : 1), dim3(64 * WGM * WGN), 0,
                      s, g, (int)tm, (int)tn);
   return hipGetLastError();
@@ -1135,11 +1280,28 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // 192 x 128 16x16 tiles of the plain store: 3.24 against 3.38 ms per step (QKV 47 against
     // 54 us); residual products on those tiles: 3.62 ms, SwiGLU on them: no gain. Residual
     // products on 16x16 blocks of the same 128 x 192 tiles: 3.179 against 3.197 ms.
-    case EPI_STORE: return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
+    // The cross-stage pipeline (K a multiple of 64, not split), same-box A/B over three
+    // alternating rounds of the d768 step: LM head 582 against 597 us, SwiGLU (8 waves, plain
+    // order instead of ping-pong) 57.6 against 60.6, down / out projections 38.0 / 24.8
+    // against 39.3 / 25.3; step 2.795 against 2.868 ms. With one wave per SIMD (256 x 256 and
+    // 256 x 288 tiles, one workgroup per CU) the same loop was slower (LM head 747-829 us):
+    // nothing covers a wave's memory stalls there.
+    case EPI_STORE:
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<192, 128, 64, 2, EPI_STORE, 2, false, 2, 2, false, 16, true>(g, s);
+      return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
     case EPI_RESIDUAL:
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<128, kResidualBN, 64, 4, EPI_RESIDUAL, 1, false, 4, 2, false, 16, true>(g, s);
       return run_bf16<128, kResidualBN, 64, 4, EPI_RESIDUAL, 1, true, 4, 2, false, 16>(g, s);
-    case EPI_QKV_ROPE: return run_bf16<192, 128, 64, 2, EPI_QKV_ROPE, 2, true, 2, 2, false, 16>(g, s);
-    case EPI_SWIGLU: return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
+    case EPI_QKV_ROPE:
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<192, 128, 64, 2, EPI_QKV_ROPE, 2, false, 2, 2, false, 16, true>(g, s);
+      return run_bf16<192, 128, 64, 2, EPI_QKV_ROPE, 2, true, 2, 2, false, 16>(g, s);
+    case EPI_SWIGLU:
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<256, 256, 64, 2, EPI_SWIGLU, 1, false, 2, 4, false, 16, true>(g, s);
+      return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
   }
   return hipErrorInvalidValue;
