@@ -376,6 +376,386 @@ __global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_kernel(
 #endif
 }
 
+// bf16 kernel for d_head 128, software pipelined. Its 456 registers per lane leave one wave
+// per SIMD, so no other wave hides the serial chain scores -> softmax -> P V of a tile; the
+// wave itself overlaps them instead. Step t computes the scores of tile t + 1 on the matrix
+// core between the exponentials of tile t, then tile t's P V products with tile t + 1's mask
+// and row maximum between them. K therefore runs one tile ahead of V in the LDS ring, and
+// every wave runs every step of its workgroup (tiles outside a wave's queries are masked).
+// Layouts, fills, swizzles and the lazy reference are those of attn_bf16_kernel.
+template <int DH>
+__global__ __launch_bounds__(kThreads, AttnTile<DH>::OCC) void attn_bf16_pipe_kernel(
+    const bf16_t *__restrict__ q, int64_t q_stride, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, int64_t kv_stride, bf16_t *__restrict__ o, int64_t o_stride,
+    int B, int S, int Hq, int Hkv, int n_qt, float scale_log2, int cus, int window,
+    float *__restrict__ lse) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using T = AttnTile<DH>;
+  constexpr int RB = T::RB, CPR = T::CPR, FR = T::FR, TILE = T::TILE, INS = T::INS;
+  constexpr int LOADS = T::LOADS, STAGE = T::STAGE, NST = T::NST;
+  constexpr int NKB = kBKV / 32;              // 32-key score blocks per tile
+  constexpr int NDB = DH / 32;                // 32-dim output blocks
+  constexpr int QK_STEPS = DH / 16;           // k-steps of the score MFMA
+  constexpr int PV_STEPS = kBKV / 16;         // k-steps of the PV MFMA
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bh_count = B * Hq;
+  // Work items in order of decreasing length (query tile n_qt-1 of every head first). Blocks
+  // take them in a snake over rounds of `cus` blocks (one per CU when the grid is dispatched
+  // in order): a CU's blocks of rounds 0, 1, 2 get long, shorter and short items.
+  const int round = (int)(blockIdx.x / cus), in_round = (int)(blockIdx.x % cus);
+  int item = (round & 1) ? round * cus + (cus - 1 - in_round) : (int)blockIdx.x;
+  if (item >= (int)gridDim.x) item = (int)blockIdx.x;   // partial last round: keep in order
+  const int qt = n_qt - 1 - item / bh_count;
+  const int bh = item % bh_count;
+  const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
+  const int q0 = qt * kBQ, qw0 = q0 + wid * 32;
+  const uint32_t kvsb = (uint32_t)(kv_stride * 2);   // bytes between key rows
+
+  // K and V rows 0..S-1 of this (b, kv head); rows at or past S read as zero.
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(k + (int64_t)b * S * kv_stride + (int64_t)hkv * DH), 0,
+      (int)(S * kvsb), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(v + (int64_t)b * S * kv_stride + (int64_t)hkv * DH), 0,
+      (int)(S * kvsb), kRsrcWord3);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query qw0 + l32, dims 16*kk + 8h .. +7.
+  //      The empty statements make the compiler finish these loads here, so it does not wait
+  //      for them (and for every fill issued after them) inside the loop.
+  u32x4_t qf[QK_STEPS];
+  {
+    const int qi = qw0 + l32;
+    const bf16_t *qp = q + ((int64_t)b * S + (qi < S ? qi : 0)) * q_stride + (int64_t)hq * DH;
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk)
+      qf[kk] = qi < S ? *(const u32x4_t *)(qp + 16 * kk + 8 * h) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) asm volatile("" : "+v"(qf[kk]));
+  }
+
+  const int kv_end = min(q0 + kBQ, S);
+  const int n_tiles = (kv_end + kBKV - 1) / kBKV;
+  // sliding window ("LLM 2" sliding window): query s sees keys s - window + 1 .. s
+  const int j_lo = window > 0 ? max(0, q0 - window + 1) / kBKV : 0;
+
+  // ---- fills: lane l of a fill lands at base + 16 l, i.e. row frow, chunk slot fchunk; it
+  //      fetches the global chunk that the swizzle places in that slot.
+  const int frow = lane / CPR, fchunk = lane % CPR;
+  uint32_t k_off[INS], v_off[INS];
+#pragma unroll
+  for (int i = 0; i < INS; ++i) {
+    const int r = (wid * INS + i) * FR + frow;
+    k_off[i] = (uint32_t)r * kvsb + (uint32_t)((fchunk ^ swz_k<DH>(r)) << 4);
+    v_off[i] = (uint32_t)r * kvsb + (uint32_t)((fchunk ^ swz_v<DH>(r)) << 4);
+  }
+  // The scores of tile t + 1 are computed while the softmax of tile t runs, so K runs one tile
+  // ahead of V: stage t (t = j_lo - 1 .. n_tiles - 1) holds the K rows of tile t + 1 and the
+  // V rows of tile t (clamped into j_lo .. n_tiles - 1 at the two ends, where that half is not
+  // read), and step t reads only stage t.
+  auto issue = [&](int t, auto slot) {
+    uint8_t *base = lds + decltype(slot)::value * STAGE;
+    const uint32_t tk = (uint32_t)(min(t + 1, n_tiles - 1) * kBKV) * kvsb;
+    const uint32_t tv = (uint32_t)(max(t, j_lo) * kBKV) * kvsb;
+#pragma unroll
+    for (int i = 0; i < INS; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          k_rsrc, (lds_void_t *)(base + (wid * INS + i) * 1024), 16, tk + k_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (lds_void_t *)(base + TILE + (wid * INS + i) * 1024), 16, tv + v_off[i], 0,
+          0, 0);
+    }
+  };
+  auto wait_fills = [&](int stages_after) {
+    if (NST >= 3 && stages_after >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // ---- LDS read addresses: a per-lane register plus an immediate for the slot and step.
+  //      The reads are inline so the compiler does not wait for every in-flight fill before
+  //      them; each is waited for explicitly before its first use.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t *)lds;
+  uint32_t k_rd[NKB][QK_STEPS];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) {
+      const int row = kb * 32 + l32;
+      k_rd[kb][kk] = lds_base + row * RB + (((2 * kk + h) ^ swz_k<DH>(row)) << 4);
+    }
+  // V^T fragment of dims 32 db .. +31, key step ks: lane (group g = lane / 16, i = lane % 16)
+  // addresses row 16 ks + 4 (g / 2) + 8 half + i / 4, dims d0 + 4 (i % 4) with
+  // d0 = 32 db + 16 (g % 2); the transpose read returns to lane i of the group the four keys
+  // of dim d0 + i.
+  const int tg = lane >> 4, ti = lane & 15;
+  uint32_t v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int row = 4 * (tg >> 1) + (ti >> 2);          // row bits the swizzle reads
+    const int chunk = ((db * 32 + 16 * (tg & 1)) >> 3) + ((ti & 3) >> 1);
+    v_rd[db] = lds_base + TILE + row * RB + ((chunk ^ swz_v<DH>(row)) << 4) + 8 * (ti & 1);
+  }
+
+  f32x16_t oacc[NDB], lacc;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  // all-ones A operand: the row sums of P come out of the matrix core with the P V product
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  float m_run = -__builtin_inff();
+  const int my_q = qw0 + l32;
+  float mc = 0.f;   // m_run in the exponent's units (scale_log2 folded in)
+
+  // ---- scores of tile t: S^T = K Q^T from the K fragments, as products into s
+  auto qk_mfma = [&](f32x16_t &s, const u32x4_t &kfr, int kk) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kfr),
+                                                __builtin_bit_cast(bf16x8_t, qf[kk]),
+                                                kk == 0 ? f32x16_t{} : s, 0, 0, 0);
+  };
+  // ---- masks of tile t on its scores: keys after the query (diagonal tile, and every tile
+  //      past the wave's queries) and, with a window, keys older than the band
+  auto mask = [&](f32x16_t (&s)[NKB], int t) {
+    const int kv0 = t * kBKV;
+    if (kv0 + kBKV - 1 > qw0) {
+      const int lim = my_q - kv0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -__builtin_inff();
+    }
+    if (window > 0 && kv0 < qw0 + 31 - window + 1) {
+      const int lo = my_q - window + 1 - kv0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 8 * (e >> 2) + (e & 3) < lo) s[kb][e] = -__builtin_inff();
+    }
+  };
+  // ---- the tile's row maximum against the running reference. The reference only moves when
+  //      the tile's maximum exceeds it by more than 2^8 in probability (log2 units): exp2(s -
+  //      ref) then stays below 256, and the result does not depend on which reference is used
+  //      (the same one scales the row sum), so the running output is rescaled rarely instead
+  //      of on almost every tile. Returns whether some row's reference moved.
+  auto row_max = [&](const f32x16_t (&s)[NKB], float &alpha) -> bool {
+    float mt0 = s[0][0], mt1 = s[NKB - 1][1];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        mt0 = fmaxf(mt0, s[kb][e]);
+        mt1 = fmaxf(mt1, s[kb][e + 1]);
+      }
+    float mt = fmaxf(mt0, mt1);
+    {   // lanes l and l ^ 32 hold the two key halves of one query
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool move = (mt - m_run) * scale_log2 > kLazyLog2;
+    const float m_new = move ? fmaxf(m_run, mt) : m_run;
+    // a lane that has seen no visible key yet (possible at a window's edge) keeps zero weight
+    const float mc_new = m_new == -__builtin_inff() ? 0.f : m_new * scale_log2;
+    alpha = m_new == m_run ? 1.f : fast_exp2(m_run * scale_log2 - mc_new);
+    m_run = m_new;
+    mc = mc_new;
+    return __any(move);
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    lacc[0] *= alpha;
+  };
+  // ---- exponentials of 8 keys per lane (chunk c = key block c / 2, half c % 2) of the scores
+  //      in s, packed to bf16 into pf[c], and their row sums on the matrix core
+  auto expo = [&](const f32x16_t (&s)[NKB], int c, u32x4_t (&pf)[PV_STEPS]) {
+    const int kb = c >> 1, half = c & 1;
+    u32x4_t w;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = 8 * half + 2 * x;
+      w[x] = pack_bf16x2(fast_exp2(__builtin_fmaf(s[kb][e], scale_log2, -mc)),
+                         fast_exp2(__builtin_fmaf(s[kb][e + 1], scale_log2, -mc)));
+    }
+    pf[c] = w;
+    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ones),
+                                                   __builtin_bit_cast(bf16x8_t, w), lacc, 0, 0, 0);
+  };
+  constexpr int KR = NKB * QK_STEPS;   // K fragment reads of a tile
+  constexpr int PER = QK_STEPS / 2;    // score products per exponential chunk
+  static_assert(PER >= 1 && 2 * PER == QK_STEPS, "chunking");
+
+  // Step j. On entry sc holds tile j's masked scores and mc its reference; the step issues
+  // tile j + 1's K reads, then tile j's exponentials with tile j + 1's score products
+  // (into sn) between them, then tile j's P V products with tile j + 1's mask and row maximum
+  // between them; a moved reference rescales the output after tile j's products.
+  auto body = [&](int j, auto soff, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+    constexpr int SOFF = decltype(soff)::value;
+    u32x4_t kf[NKB][QK_STEPS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < QK_STEPS; ++kk) ds_read16<SOFF>(kf[kb][kk], k_rd[kb][kk]);
+    u32x4_t pf[PV_STEPS];
+    u32x2_t vf[NDB][2 * PV_STEPS];
+    // key block 0 of tile j (chunks 0, 1) with the products of key block 0 of tile j + 1
+    if constexpr (KR / 2 <= 15) asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(KR / 2) : "memory");
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) asm volatile("" : "+v"(kf[0][kk]));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) qk_mfma(sn[0], kf[0][c * PER + x], c * PER + x);
+      expo(sc, c, pf);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 20 / (PER + 1), 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 20 - PER * (20 / (PER + 1)), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // key block 1 likewise; tile j's V fragments go out first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < QK_STEPS; ++kk) asm volatile("" : "+v"(kf[NKB - 1][kk]));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < PV_STEPS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                       : "=v"(vf[db][2 * ks + half])
+                       : "v"(v_rd[db]), "i"(SOFF + (16 * ks + 8 * half) * RB) : "memory");
+#pragma unroll
+    for (int c = 2; c < 4; ++c) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) qk_mfma(sn[NKB - 1], kf[NKB - 1][(c - 2) * PER + x], (c - 2) * PER + x);
+      expo(sc, c, pf);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 20 / (PER + 1), 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 20 - PER * (20 / (PER + 1)), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // tile j + 1's masks (a branch taken on few tiles), then tile j's P V products with tile
+    // j + 1's row maximum between them
+    mask(sn, j + 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int x = 0; x < 2 * PV_STEPS; ++x) asm volatile("" : "+v"(vf[db][x]));
+#pragma unroll
+    for (int ks = 0; ks < PV_STEPS; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x4_t a = {vf[db][2 * ks][0], vf[db][2 * ks][1], vf[db][2 * ks + 1][0],
+                           vf[db][2 * ks + 1][1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, pf[ks]), oacc[db],
+            0, 0, 0);
+      }
+    float alpha;
+    const bool moved = row_max(sn, alpha);
+    if (moved) rescale(alpha);
+  };
+
+  // stages j_lo - 1 .. j_lo + NST - 3 go out first; the first step (stage j_lo - 1) computes
+  // tile j_lo's scores, mask and reference, and sends stage j_lo + NST - 2
+  f32x16_t sa[NKB], sb[NKB];
+  issue(j_lo - 1, ic<0>{});
+  if constexpr (NST > 2) issue(j_lo, ic<1>{});   // j_lo <= n_tiles - 1 always
+  wait_fills(NST - 2);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (j_lo + NST - 2 < n_tiles) issue(j_lo + NST - 2, ic<(NST - 1) % NST>{});
+  {
+    u32x4_t kf[NKB][QK_STEPS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < QK_STEPS; ++kk) ds_read16<0>(kf[kb][kk], k_rd[kb][kk]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < QK_STEPS; ++kk) {
+        asm volatile("" : "+v"(kf[kb][kk]));
+        qk_mfma(sa[kb], kf[kb][kk], kk);
+      }
+    mask(sa, j_lo);
+    float alpha;
+    row_max(sa, alpha);   // the output is still zero: nothing to rescale
+  }
+  // Step j reads stage j from slot (j - j_lo + 1) % NST. Every wave runs every step of the
+  // workgroup: on a tile outside a wave's queries (after its last query or, with a window,
+  // before its band) the masks give every key zero weight, and the last step's scores (of
+  // the clamped tile, past every query) are all masked. This keeps the loop to one path.
+  auto step = [&](int j, auto slot, f32x16_t (&sc)[NKB], f32x16_t (&sn)[NKB]) {
+    constexpr int SL = decltype(slot)::value;
+    wait_fills(min(NST - 2, n_tiles - 1 - j));
+    // every wave's fills of stage j are in LDS; every wave is done reading stage j - 1's slot
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + NST - 1 < n_tiles) issue(j + NST - 1, ic<(SL + NST - 1) % NST>{});
+    body(j, ic<SL * STAGE>{}, sc, sn);
+  };
+  // unrolled over lcm(NST, 2) steps so the score buffers alternate without copies
+  constexpr int PERIOD = NST > 2 ? 6 : 2;
+  static_assert(NST == 2 || NST == 3, "ring depth");
+  for (int j0 = j_lo; j0 < n_tiles; j0 += PERIOD) {
+    step(j0, ic<1 % NST>{}, sa, sb);
+    if (j0 + 1 >= n_tiles) break;
+    step(j0 + 1, ic<2 % NST>{}, sb, sa);
+    if constexpr (NST > 2) {
+      if (j0 + 2 >= n_tiles) break;
+      step(j0 + 2, ic<0>{}, sa, sb);
+      if (j0 + 3 >= n_tiles) break;
+      step(j0 + 3, ic<1>{}, sb, sa);
+      if (j0 + 4 >= n_tiles) break;
+      step(j0 + 4, ic<2>{}, sa, sb);
+      if (j0 + 5 >= n_tiles) break;
+      step(j0 + 5, ic<0>{}, sb, sa);
+    }
+  }
+  if (my_q < S) {
+    // row logsumexp of the scaled scores (kept for the backward): max + log(sum)
+    if (lse && h == 0)
+      lse[((int64_t)b * S + my_q) * Hq + hq] = m_run * (scale_log2 / kLog2e) + logf(lacc[0]);
+    const float inv = 1.0f / lacc[0];
+    bf16_t *op = o + ((int64_t)b * S + my_q) * o_stride + (int64_t)hq * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t r;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) r[x] = oacc[db][4 * g + x] * inv;
+        store4(op + 32 * db + 8 * g + 4 * h, r);
+      }
+  }
+#endif
+}
+
 template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ q, int64_t q_stride,
                                                       const float *__restrict__ k,
@@ -421,9 +801,14 @@ hipError_t run_bf16(const void *q, int64_t qs, const void *k, const void *v, int
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff || !attention_fits(DT_BF16, S, kvs)) return hipErrorInvalidValue;
   const float sl2 = kLog2e / sqrtf((float)DH);
-  attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
-      (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S, Hq,
-      Hkv, n_qt, sl2, compute_units(), window, lse);
+  if constexpr (DH >= 128)
+    attn_bf16_pipe_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+        (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S,
+        Hq, Hkv, n_qt, sl2, compute_units(), window, lse);
+  else
+    attn_bf16_kernel<DH><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+        (const bf16_t *)q, qs, (const bf16_t *)k, (const bf16_t *)v, kvs, (bf16_t *)o, os, B, S,
+        Hq, Hkv, n_qt, sl2, compute_units(), window, lse);
   return hipGetLastError();
 }
 

@@ -34,6 +34,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
 }
 
+// 16-byte LDS read at addr + IMM, issued as written: the compiler's own wait insertion cannot
+// tell which LDS bytes an in-flight buffer->LDS fill writes, so fragment reads are inline and
+// waited for explicitly (s_waitcnt lgkmcnt) before first use.
+template <int IMM>
+__device__ __forceinline__ void ds_read16(u32x4_t &dst, uint32_t addr) {
+  static_assert(IMM >= 0 && IMM < 65536, "LDS offset immediate");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(IMM) : "memory");
+}
+
 template <typename T> struct Elt;
 template <> struct Elt<float> {
   static constexpr int bytes = 4;

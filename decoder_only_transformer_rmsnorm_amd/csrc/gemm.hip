@@ -65,15 +65,6 @@ __device__ __forceinline__ int swz(int row) { return row & 7; }
 template <int N>
 using ic2 = std::integral_constant<int, N>;
 
-// 16-byte LDS read at addr + IMM, issued as written: the compiler's own wait insertion cannot
-// tell which LDS bytes an in-flight buffer->LDS fill writes, so fragment reads are inline and
-// waited for explicitly.
-template <int IMM>
-__device__ __forceinline__ void ds_read16(u32x4_t &dst, uint32_t addr) {
-  static_assert(IMM >= 0 && IMM < 65536, "LDS offset immediate");
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(IMM) : "memory");
-}
-
 // f(integral_constant<int, I>) for I = B .. E - 1, each index a constant expression
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
