@@ -317,7 +317,8 @@ struct TrainPlan {
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
-  int Vp;        // vocabulary padded to a multiple of 8 (K of the head's input-gradient GEMM)
+  int Vp;        // vocabulary padded to a multiple of 64: the K of the head's input-gradient
+                 // product, which then runs the cross-stage main loop
   int64_t Mp;    // tokens padded to a multiple of 8 (K of the weight-gradient GEMMs)
   size_t total;
 };
@@ -328,11 +329,18 @@ struct TrainPlan {
 // summed in part order (deterministic).
 constexpr int64_t kSplitTarget = 512;
 constexpr int kSplitMax = 16;
-int splitk_parts(int dt, int64_t M, int N, int64_t K) {
-  const int64_t tiles = gemm_store_tiles(dt, M, N);
+int splitk_parts_of(int64_t tiles, int64_t K) {
   int64_t parts = (kSplitTarget + tiles - 1) / tiles;
   parts = std::min<int64_t>(parts, std::max<int64_t>(1, K / 512));
   return (int)std::min<int64_t>(parts, kSplitMax);
+}
+int splitk_parts(int dt, int64_t M, int N, int64_t K) {
+  return splitk_parts_of(gemm_store_tiles(dt, M, N), K);
+}
+// the K-major product's 128 x 128 tiles: at least as many as the plain store's, so never
+// more parts (the workspace sized by splitk_bytes holds them)
+int splitk_parts_kmajor(int64_t M, int N, int64_t K) {
+  return splitk_parts_of(((M + 127) / 128) * ((N + 127) / 128), K);
 }
 size_t splitk_bytes(int dt, int64_t M, int N, int64_t K) {
   const int parts = splitk_parts(dt, M, N, K);
@@ -345,7 +353,7 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   const size_t D = c->d_model, F = c->d_ff, V = c->vocab;
   const size_t qd = (size_t)c->n_heads * c->d_head, kvd = (size_t)c->n_kv_heads * c->d_head;
   const size_t W = qd + 2 * kvd;
-  p.Vp = (int)((V + 7) / 8 * 8);
+  p.Vp = (int)((V + 63) / 64 * 64);
   p.Mp = (int64_t)((M + 7) / 8 * 8);
   const size_t Vp = p.Vp, Mp = p.Mp;
   size_t off = 0;
@@ -438,6 +446,28 @@ int gemm_wgrad(int dt, const void *a, int64_t lda, const void *w, int64_t M, int
   g.y = part; g.ldy = N; g.y_dt = DT_F32;
   g.kparts = n; g.kpart = ks; g.ypart = M * N;
   TFM_HIP(launch_gemm(EPI_STORE, dt, g, s));
+  return hip_status(launch_sum_parts(part, n, M, N, y, ldy, s));
+}
+
+// The same product with both operands as the forward keeps them (bf16, tokens as rows):
+// y (M, N) = sum over t < K of a[t lda + m] b[t ldb + n], on the K-major product, so no
+// activation is transposed. Returns TFM_ERR_UNSUPPORTED where that product does not take the
+// operands (the caller then transposes them).
+int gemm_wgrad_rows(const void *a, int64_t lda, const void *b, int64_t ldb, int64_t M, int N,
+                    int K, float *y, int64_t ldy, float *part, hipStream_t s) {
+  if (!gemm_kmajor_ok(a, lda, b, ldb, M, N, K)) return TFM_ERR_UNSUPPORTED;
+  const int parts = splitk_parts_kmajor(M, N, K);
+  GemmArgs g{};
+  g.a = a; g.lda = lda; g.w0 = b; g.ldw = ldb; g.M = M; g.N = N; g.K = K; g.y_dt = DT_F32;
+  if (parts <= 1) {
+    g.y = y; g.ldy = ldy;
+    return hip_status(launch_gemm_kmajor(g, s));
+  }
+  const int ks = ((K + parts - 1) / parts + 63) / 64 * 64;
+  const int n = (K + ks - 1) / ks;
+  g.y = part; g.ldy = N;
+  g.kparts = n; g.kpart = ks; g.ypart = M * N;
+  TFM_HIP(launch_gemm_kmajor(g, s));
   return hip_status(launch_sum_parts(part, n, M, N, y, ldy, s));
 }
 }  // namespace
@@ -925,6 +955,11 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   float *dhp = (float *)(wb + p.dh), *du = (float *)(wb + p.du);
   float *rpart = (float *)(wb + p.rms_part);
   float *skp = (float *)(wb + p.splitk);
+  // bf16 weight gradients read the stored activations K-major (tokens as rows); the others
+  // transpose them first
+  auto kmok = [&](const void *a, int64_t lda, const void *b, int64_t ldb, int64_t m, int n) {
+    return dt == DT_BF16 && gemm_kmajor_ok(a, lda, b, ldb, m, n, M);
+  };
 
   // ---- forward, keeping each layer's activations ("Transformer 篇" 5.7)
   TFM_HIP(launch_fill_i32(flags, 2, 0, s));
@@ -962,12 +997,16 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   // ---- LM head and final RMSNorm
   TFM_HIP(launch_transpose(w->lm_head, dt, D, wT, dt, Vp, Vp, V, D, s));
   TFM_TRY(gemm(EPI_STORE, dt, dlog, Vp, wT, M, D, Vp, dhp, D, DT_F32, nullptr, s));
-  // all Vp columns (the cross-entropy backward zeroes [V, Vp)), so the transpose takes the
-  // 16-byte path; rows [V, Vp) of dlogT are zeros the weight-gradient product never reads
-  TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, Vp, s));
-  TFM_HIP(launch_transpose(xf, dt, D, xfT, dt, Mp, Mp, M, D, s));
   float *g_lm = tied ? gr->embed : gr->lm_head;
-  TFM_TRY(gemm_wgrad(dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, skp, s));
+  if (kmok(dlog, Vp, xf, D, V, D)) {
+    TFM_TRY(gemm_wgrad_rows(dlog, Vp, xf, D, V, D, (int)M, g_lm, D, skp, s));
+  } else {
+    // all Vp columns (the cross-entropy backward zeroes [V, Vp)), so the transpose takes the
+    // 16-byte path; rows [V, Vp) of dlogT are zeros the weight-gradient product never reads
+    TFM_HIP(launch_transpose(dlog, dt, Vp, dlogT, dt, Mp, Mp, M, Vp, s));
+    TFM_HIP(launch_transpose(xf, dt, D, xfT, dt, Mp, Mp, M, D, s));
+    TFM_TRY(gemm_wgrad(dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, skp, s));
+  }
   TFM_HIP(launch_fill_f32(dx, M * D, 0.f, s));
   TFM_HIP(launch_rms_backward(X(NL), w->g_final, dt, dhp, dx, gr->g_final, 0, rpart, M, D, eps, s));
 
@@ -981,29 +1020,42 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     void *a = LA(l, p.l_a), *c = LA(l, p.l_c), *u = LA(l, p.l_u);
     // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
     TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
-    TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
     TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
-    TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
-    TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, skp, s));
+    if (kmok(dxb, D, u, F, D, F)) {
+      TFM_TRY(gemm_wgrad_rows(dxb, D, u, F, D, F, (int)M, lg->w2, F, skp, s));
+    } else {
+      TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
+      TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
+      TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, skp, s));
+    }
     TFM_HIP(launch_swiglu_backward(a, c, du, da, dc, dt, M * F, s));
     TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, F, F, F, D, s));
     TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
     TFM_HIP(launch_transpose(lw->w3, dt, D, wT, dt, F, F, F, D, s));
     TFM_TRY(gemm(EPI_RESIDUAL, dt, dc, F, wT, M, D, F, dhp, D, DT_F32, dhp, s));
-    TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
-    TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
-    TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
-    TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
-    TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
+    if (kmok(da, F, h2, D, F, D) && kmok(dc, F, h2, D, F, D)) {
+      TFM_TRY(gemm_wgrad_rows(da, F, h2, D, F, D, (int)M, lg->w1, D, skp, s));
+      TFM_TRY(gemm_wgrad_rows(dc, F, h2, D, F, D, (int)M, lg->w3, D, skp, s));
+    } else {
+      TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
+      TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
+      TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
+      TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
+      TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
+    }
     TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, lg->g_ffn, 0, rpart, M, D, eps, s));
     // attention output projection: xm = x + o Wo^T
     TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
-    TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
     TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
-    TFM_HIP(launch_transpose(o, dt, qd, actT, dt, Mp, Mp, M, qd, s));
-    TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, skp, s));
+    if (kmok(dxb, D, o, qd, D, qd)) {
+      TFM_TRY(gemm_wgrad_rows(dxb, D, o, qd, D, qd, (int)M, lg->wo, qd, skp, s));
+    } else {
+      TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
+      TFM_HIP(launch_transpose(o, dt, qd, actT, dt, Mp, Mp, M, qd, s));
+      TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, skp, s));
+    }
     // attention, then back through the rotations of q and k
     TFM_HIP(launch_attention_backward(qkv, W, o, qd, dout, qd, dqkv, B, S, Hq, Hkv, dh, dt,
                                       layer_window(cfg, l), (const float *)LA(l, p.l_lse),
@@ -1017,13 +1069,20 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_transpose(lw->wv, dt, D, (uint8_t *)wT + (size_t)(qd + kvd) * e, dt, W, kvd, kvd,
                              D, s));
     TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wT, M, D, W, dhp, D, DT_F32, nullptr, s));
-    TFM_HIP(launch_transpose(dqkv, dt, W, dqkvT, dt, Mp, Mp, M, W, s));
-    TFM_HIP(launch_transpose(h1, dt, D, hT, dt, Mp, Mp, M, D, s));
-    TFM_TRY(gemm_wgrad(dt, dqkvT, Mp, hT, qd, D, (int)Mp, lg->wq, D, skp, s));
-    TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)qd * Mp * e, Mp, hT, kvd, D, (int)Mp,
-                       lg->wk, D, skp, s));
-    TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
-                       (int)Mp, lg->wv, D, skp, s));
+    const uint8_t *dk = (const uint8_t *)dqkv + (size_t)qd * e, *dv = dk + (size_t)kvd * e;
+    if (kmok(dqkv, W, h1, D, qd, D) && kmok(dk, W, h1, D, kvd, D) && kmok(dv, W, h1, D, kvd, D)) {
+      TFM_TRY(gemm_wgrad_rows(dqkv, W, h1, D, qd, D, (int)M, lg->wq, D, skp, s));
+      TFM_TRY(gemm_wgrad_rows(dk, W, h1, D, kvd, D, (int)M, lg->wk, D, skp, s));
+      TFM_TRY(gemm_wgrad_rows(dv, W, h1, D, kvd, D, (int)M, lg->wv, D, skp, s));
+    } else {
+      TFM_HIP(launch_transpose(dqkv, dt, W, dqkvT, dt, Mp, Mp, M, W, s));
+      TFM_HIP(launch_transpose(h1, dt, D, hT, dt, Mp, Mp, M, D, s));
+      TFM_TRY(gemm_wgrad(dt, dqkvT, Mp, hT, qd, D, (int)Mp, lg->wq, D, skp, s));
+      TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)qd * Mp * e, Mp, hT, kvd, D, (int)Mp,
+                         lg->wk, D, skp, s));
+      TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
+                         (int)Mp, lg->wv, D, skp, s));
+    }
     TFM_HIP(launch_rms_backward(x, lw->g_attn, dt, dhp, dx, lg->g_attn, 0, rpart, M, D, eps, s));
   }
   // ---- embedding rows (a tied head's gradient is already in gr->embed)

@@ -39,6 +39,7 @@
 // in its L2.
 // f32 kernel (the small fp32 model): the same tile logic with register-staged loads and
 // v_mfma_f32_32x32x2_f32.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -103,14 +104,15 @@ __device__ __forceinline__ int64_t wstride(const GemmArgs &g) { return g.ldw > 0
 
 // The arguments of K part blockIdx.y of a split product: operands advanced to the part's first
 // k (the weight rows keep their full stride), K cut to the part, output advanced to its slab.
-template <typename T>
+template <typename T, bool KMAJ = false>
 __device__ __forceinline__ GemmArgs k_part(const GemmArgs &g0) {
   GemmArgs g = g0;
   if (g0.kparts > 1) {
     const int64_t k0 = (int64_t)blockIdx.y * g0.kpart;
     g.ldw = wstride(g0);
-    g.a = (const T *)g0.a + k0;
-    g.w0 = (const T *)g0.w0 + k0;
+    // K-major operands (row k of both is one k): the part starts k0 rows in
+    g.a = (const T *)g0.a + (KMAJ ? k0 * g0.lda : k0);
+    g.w0 = (const T *)g0.w0 + (KMAJ ? k0 * g.ldw : k0);
     g.K = (int)min((int64_t)g0.kpart, (int64_t)g0.K - k0);
     g.y = (uint8_t *)g0.y + (size_t)blockIdx.y * g0.ypart * (g0.y_dt == DT_F32 ? 4 : 2);
   }
@@ -376,12 +378,19 @@ struct BfTile {
 // XS (cross-stage pipeline): the KM-deep k steps run as one flat sequence and the fragments of
 // step s + 1 are read while the MFMAs of step s run, also across a stage boundary, so no wave
 // waits on LDS at the start of a stage (see the main loop).
+// KMAJ (the weight-gradient products, K = tokens): both operands are K-major, element (m, k)
+// of the activations at a[k lda + m] and (n, k) of the weights at w0[k ldw + n], as the
+// row-major activations of the forward are read when the sum runs over tokens. A stage then
+// holds BK rows of k, each BM (or BN) contiguous elements, and every MFMA fragment (8
+// consecutive k of one row m) comes from two LDS transpose reads (ds_read_b64_tr_b16: each
+// lane of a 16-lane group reads 4 elements of one k row, and lane i receives the 4 k values
+// of column i). No operand is ever transposed in memory.
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2, bool PP = false, int MS = 32, bool XS = false>
+          int WGN = 2, bool PP = false, int MS = 32, bool XS = false, bool KMAJ = false>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g0, int tiles_m,
                                                                         int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const GemmArgs g = k_part<bf16_t>(g0);
+  const GemmArgs g = k_part<bf16_t, KMAJ>(g0);
   constexpr int NT = 64 * WGM * WGN;
   using T = BfTile<BM, BN, BK, NST, WGM * WGN>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
@@ -402,6 +411,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   static_assert(LDS * OCC <= kLdsBytes, "LDS does not allow the requested occupancy");
   static_assert(EPI != EPI_SWIGLU || (NBN % 2) == 0, "SwiGLU needs gate/up block pairs");
   using acc_t = std::conditional_t<MS == 32, f32x16_t, f32x4_t>;
+  static_assert(!KMAJ || (!XS && !PP && MS == 32 && BK == 64 && BM == 128 && BN == 128 &&
+                          EPI == EPI_STORE),
+                "K-major operands: 128 x 128 tiles of 32 x 32 blocks, classic loop, plain store");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
 
@@ -419,15 +431,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   const int frow = lane / (RB / 16), fchunk = lane % (RB / 16);  // lane's slot in a fill
 
   // Activation rows m0 .. m0+BM-1: one resource; rows past M read as zero.
+  // K-major: the resource starts at column m0 and ends with the operand's last element
+  // (column M - 1 of row K - 1), so rows past K read as zero and nothing past the operand is
+  // read; columns past M inside earlier rows only feed outputs that are never stored.
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      make_rsrc((const bf16_t *)g.a + m0 * g.lda, min((int64_t)BM, g.M - m0) * g.lda * 2);
+      KMAJ ? make_rsrc((const bf16_t *)g.a + m0, ((int64_t)(g.K - 1) * g.lda + g.M - m0) * 2)
+           : make_rsrc((const bf16_t *)g.a + m0 * g.lda, min((int64_t)BM, g.M - m0) * g.lda * 2);
+  // K-major fills: a 1 KB fill covers 4 k rows of 128 elements; lane l lands in row l / 16,
+  // 16-byte slot l % 16, which holds chunk (l % 16) ^ 4 (row % 4) of the row (the swizzle
+  // the transpose reads need).
+  const int krow = lane >> 4, kslot = lane & 15;
   uint32_t a_off[A_INS];
   int a_k[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = (wid * A_INS + i) * FR + frow;
-    a_k[i] = (fchunk ^ swz_rb<RB>(r)) * 8;
-    a_off[i] = (uint32_t)(r * g.lda * 2 + a_k[i] * 2);
+    if constexpr (KMAJ) {
+      const int r = (wid * A_INS + i) * 4 + krow;
+      a_k[i] = 0;
+      a_off[i] = (uint32_t)(r * g.lda * 2 + ((kslot ^ (4 * krow)) << 4));
+    } else {
+      const int r = (wid * A_INS + i) * FR + frow;
+      a_k[i] = (fchunk ^ swz_rb<RB>(r)) * 8;
+      a_off[i] = (uint32_t)(r * g.lda * 2 + a_k[i] * 2);
+    }
   }
   // Weight rows: one resource per fill group (a group never straddles two sources).
   __amdgpu_buffer_rsrc_t b_rsrc[B_INS];
@@ -435,12 +461,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   int b_k[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r0 = (wid * B_INS + i) * FR;
-    int rows_left;
-    const bf16_t *src = weight_rows<EPI, bf16_t>(g, n0 + r0, rows_left);
-    b_rsrc[i] = make_rsrc(src, (int64_t)min(rows_left, FR) * wstride(g) * 2);
-    b_k[i] = (fchunk ^ swz_rb<RB>(r0 + frow)) * 8;
-    b_off[i] = (uint32_t)(frow * wstride(g) * 2 + b_k[i] * 2);
+    if constexpr (KMAJ) {
+      const int r = (wid * B_INS + i) * 4 + krow;
+      b_rsrc[i] = make_rsrc((const bf16_t *)g.w0 + n0, ((int64_t)(g.K - 1) * g.ldw + g.N - n0) * 2);
+      b_k[i] = 0;
+      b_off[i] = (uint32_t)(r * g.ldw * 2 + ((kslot ^ (4 * krow)) << 4));
+    } else {
+      const int r0 = (wid * B_INS + i) * FR;
+      int rows_left;
+      const bf16_t *src = weight_rows<EPI, bf16_t>(g, n0 + r0, rows_left);
+      b_rsrc[i] = make_rsrc(src, (int64_t)min(rows_left, FR) * wstride(g) * 2);
+      b_k[i] = (fchunk ^ swz_rb<RB>(r0 + frow)) * 8;
+      b_off[i] = (uint32_t)(frow * wstride(g) * 2 + b_k[i] * 2);
+    }
   }
 
   // Residual epilogue: the fp32 residual tile is read into registers before the main loop,
@@ -476,26 +509,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   // The k offset of a stage travels in the scalar offset of the load, so a fill costs no
   // vector arithmetic. Only a ragged last stage (K % BK != 0) switches each lane to its
   // precomputed tail offset: out of range (reads zero) where its chunk lies past K.
-  const int tail_kt = K % BK != 0 ? nk - 1 : -1;
+  const int tail_kt = K % BK != 0 && !KMAJ ? nk - 1 : -1;
   uint32_t a_toff[A_INS], b_toff[B_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) a_toff[i] = (nk - 1) * BK + a_k[i] >= K ? kOOB : a_off[i];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) b_toff[i] = (nk - 1) * BK + b_k[i] >= K ? kOOB : b_off[i];
   // Fill number `idx` (A fills first, then B fills) of stage `kt`.
+  // the stage's k offset in bytes: along the row, or (K-major) whole rows
+  const uint32_t kstep_a = KMAJ ? (uint32_t)(BK * g.lda * 2) : (uint32_t)(BK * 2);
+  const uint32_t kstep_b = KMAJ ? (uint32_t)(BK * wstride(g) * 2) : (uint32_t)(BK * 2);
   auto issue_one = [&](int kt, int idx) {
-    const int koff = kt * BK * 2;
     uint8_t *base = lds + (kt % NST) * STAGE;
     if (idx < A_INS) {
       const uint32_t off = kt == tail_kt ? a_toff[idx] : a_off[idx];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_void_t *)(base + (wid * A_INS + idx) * FR * RB), 16, off, koff, 0, 0);
+          a_rsrc, (lds_void_t *)(base + (wid * A_INS + idx) * FR * RB), 16, off, kt * kstep_a,
+          0, 0);
     } else {
       const int i = idx - A_INS;
       const uint32_t off = kt == tail_kt ? b_toff[i] : b_off[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc[i], (lds_void_t *)(base + (BM + (wid * B_INS + i) * FR) * RB), 16, off, koff,
-          0, 0);
+          b_rsrc[i], (lds_void_t *)(base + (BM + (wid * B_INS + i) * FR) * RB), 16, off,
+          kt * kstep_b, 0, 0);
     }
   };
   auto issue = [&](int kt) {
@@ -525,8 +561,53 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   // fills of the stage being read are already complete (wait_fills + barrier); the reads
   // are waited for explicitly (wait_frags) before the MFMAs that use them.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t *)lds;
+  // K-major fragment of 32 rows (block j of the operand tile) for k rows 16 kk .. +15: lane
+  // (group q = lane / 16, i = lane % 16) addresses k row 16 kk + 8 (q / 2) + 4 t + i / 4 and
+  // columns 32 j + 16 (q % 2) + 4 (i % 4) .. +3 (read t = 0, 1), so it receives k values
+  // 8 (q / 2) + 4 t .. +3 of column 32 j + 16 (q % 2) + i: lane l holds row l % 32 and k
+  // 8 (l / 32) .. +7, the MFMA operand layout. Per lane and block: one base address.
+  uint32_t kmA[KMAJ ? NBM : 1], kmB[KMAJ ? NBN : 1];
+  if constexpr (KMAJ) {
+    const int q = lane >> 4, i = lane & 15;
+    const int rowl = 8 * (q >> 1) + (i >> 2);   // row within the 16-row k step (t = 0)
+    auto col_off = [&](int j) {
+      const int chunk = 4 * j + 2 * (q & 1) + ((i & 3) >> 1);
+      return (uint32_t)(((chunk ^ (4 * (i >> 2))) << 4) + 8 * (i & 1));
+    };
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm)
+      kmA[bm] = lds_base + rowl * (BM * 2) + col_off(wm * NBM + bm);
+#pragma unroll
+    for (int bn = 0; bn < NBN; ++bn)
+      kmB[bn] = lds_base + BK * BM * 2 + rowl * (BN * 2) + col_off(wn * NBN + bn);
+  }
+  auto read_km = [](uint32_t addr, auto imm_c, u32x4_t &f) {
+    constexpr int IMM = decltype(imm_c)::value;
+    u32x2_t lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(IMM) : "memory");
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(addr), "i"(IMM + 4 * BM * 2) : "memory");
+    f = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
   auto read_frags = [&](int stage, int kk, u32x4_t (&fa)[NBM], u32x4_t (&fb)[NBN]) {
     const uint32_t st = lds_base + stage * STAGE;
+    if constexpr (KMAJ) {
+      static_assert(BM == BN, "one row pitch for both K-major operands");
+      const uint32_t so = stage * STAGE;
+      // kk is a compile-time value in the unrolled loop; the immediate needs it as one
+      static_for<0, KK>([&](auto kc) {
+        if (kc.value == kk) {
+#pragma unroll
+          for (int bm = 0; bm < NBM; ++bm)
+            read_km(kmA[bm] + so, ic2<decltype(kc)::value * 16 * BM * 2>{}, fa[bm]);
+#pragma unroll
+          for (int bn = 0; bn < NBN; ++bn)
+            read_km(kmB[bn] + so, ic2<decltype(kc)::value * 16 * BN * 2>{}, fb[bn]);
+        }
+      });
+      (void)st;
+      return;
+    }
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
       const int row = wm * WM + bm * MS + l32;
@@ -579,7 +660,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   // other waves at the barrier (after which the stage consumed one iteration earlier is
   // free and gets refilled, interleaved with this stage's MFMAs), then multiplies, reading
   // the next k step's fragments while the current step's MFMAs run.
-  static_assert(XS || NBM + NBN <= 15, "fragment reads exceed the lgkmcnt range");
+  constexpr int NRD = (KMAJ ? 2 : 1) * (NBM + NBN);   // LDS reads of one k step's fragments
+  static_assert(XS || NRD <= 15, "fragment reads exceed the lgkmcnt range");
   if constexpr (XS) {
     // Cross-stage pipeline (one wave per SIMD, K a multiple of BK, two 32-deep k slices per
     // stage). Slice step s multiplies fragments read during step s - 1 while it reads those
@@ -760,7 +842,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) {
         read_frags(stage, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        wait_frags(std::integral_constant<int, NBM + NBN>{}, fa[kk & 1], fb[kk & 1]);
+        wait_frags(std::integral_constant<int, NRD>{}, fa[kk & 1], fb[kk & 1]);
       } else {
         wait_frags(std::integral_constant<int, 0>{}, fa[kk & 1], fb[kk & 1]);
       }
@@ -1236,13 +1318,13 @@ void grid_for(const GemmArgs &g, int64_t &tm, int64_t &tn) {
 }
 
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
-          int WGN = 2, bool PP = false, int MS = 32, bool XS = false>
+          int WGN = 2, bool PP = false, int MS = 32, bool XS = false, bool KMAJ = false>
 hipError_t run_bf16(const GemmArgs &g, hipStream_t s) {
   int64_t tm, tn;
   grid_for<BM, BN, EPI>(g, tm, tn);
   if (tm * tn == 0) return hipSuccess;
   if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS, XS>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS, XS, KMAJ>),
                      dim3((unsigned)(tm * tn), g.kparts > 1 ? g.kparts : 1), dim3(64 * WGM * WGN), 0,
                      s, g, (int)tm, (int)tn);
   return hipGetLastError();
@@ -1324,6 +1406,19 @@ int64_t gemm_store_tiles(int dt, int64_t M, int N) {
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s) {
   if (g.M == 0) return hipSuccess;
   return dt == DT_BF16 ? dispatch_bf16(epi, g, s) : dispatch_f32(epi, g, s);
+}
+
+bool gemm_kmajor_ok(const void *a, int64_t lda, const void *w, int64_t ldw, int64_t M, int N,
+                    int64_t K) {
+  // 16-byte chunks of every row; every offset of a part (k rows x row stride) in 32 bits
+  return ((uintptr_t)a & 15) == 0 && ((uintptr_t)w & 15) == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
+         lda >= M && ldw >= N && K * std::max(lda, ldw) * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_kmajor(const GemmArgs &g, hipStream_t s) {
+  if (g.M == 0) return hipSuccess;
+  if (g.ldw <= 0) return hipErrorInvalidValue;
+  return run_bf16<128, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 32, false, true>(g, s);
 }
 
 }  // namespace tfm

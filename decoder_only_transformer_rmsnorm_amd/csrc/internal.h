@@ -88,6 +88,13 @@ int gemm_norm_max_cols();
 int gemm_xent_parts(int N);
 
 hipError_t launch_gemm(int epi, int dt, const GemmArgs &g, hipStream_t s);
+// y (M, N) = sum over k of a[k lda + m] w0[k ldw + n] (bf16, both operands K-major: the
+// weight-gradient products over tokens read the row-major activations as they are), fp32 or
+// bf16 output, split K like launch_gemm (kparts / kpart / ypart). g.ldw must be set.
+hipError_t launch_gemm_kmajor(const GemmArgs &g, hipStream_t s);
+// whether launch_gemm_kmajor takes these operands (alignment, strides, 32-bit offsets)
+bool gemm_kmajor_ok(const void *a, int64_t lda, const void *w, int64_t ldw, int64_t M, int N,
+                    int64_t K);
 // Workgroups of a plain-store GEMM of M x N outputs.
 int64_t gemm_store_tiles(int dt, int64_t M, int N);
 
