@@ -982,9 +982,16 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
                              (float *)LA(l, p.l_lse)));
     TFM_TRY(gemm(EPI_RESIDUAL, dt, o, qd, lw->wo, M, D, qd, xm, D, DT_F32, x, s));
     TFM_HIP(launch_rmsnorm(xm, DT_F32, lw->g_ffn, dt, h2, dt, M, D, eps, s));
-    TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w1, M, F, D, a, F, dt, nullptr, s));
-    TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w3, M, F, D, c, F, dt, nullptr, s));
-    TFM_HIP(launch_swiglu_fwd(a, c, u, dt, M * F, s));
+    if (dt == DT_BF16) {   // one product: gate and up rows interleaved, u, a and c written
+      GemmArgs gs{};
+      gs.a = h2; gs.lda = D; gs.w0 = lw->w1; gs.w1 = lw->w3; gs.n0 = F; gs.M = M; gs.N = F;
+      gs.K = D; gs.y = u; gs.ldy = F; gs.y_dt = dt; gs.keep_a = a; gs.keep_c = c;
+      TFM_HIP(launch_gemm(EPI_SWIGLU, dt, gs, s));
+    } else {
+      TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w1, M, F, D, a, F, dt, nullptr, s));
+      TFM_TRY(gemm(EPI_STORE, dt, h2, D, lw->w3, M, F, D, c, F, dt, nullptr, s));
+      TFM_HIP(launch_swiglu_fwd(a, c, u, dt, M * F, s));
+    }
     TFM_TRY(gemm(EPI_RESIDUAL, dt, u, F, lw->w2, M, D, F, X(l + 1), D, DT_F32, xm, s));
   }
   TFM_HIP(launch_rmsnorm(X(NL), DT_F32, w->g_final, dt, xf, dt, M, D, eps, s));
@@ -1008,7 +1015,10 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_TRY(gemm_wgrad(dt, dlogT, Mp, xfT, V, D, (int)Mp, g_lm, D, skp, s));
   }
   TFM_HIP(launch_fill_f32(dx, M * D, 0.f, s));
-  TFM_HIP(launch_rms_backward(X(NL), w->g_final, dt, dhp, dx, gr->g_final, 0, rpart, M, D, eps, s));
+  // bf16: the norm backward also leaves the bf16 copy of dx the next products read
+  void *dxc = dt == DT_BF16 ? dxb : nullptr;
+  TFM_HIP(launch_rms_backward(X(NL), w->g_final, dt, dhp, dx, dxc, gr->g_final, 0, rpart, M, D, eps,
+                              s));
 
   // ---- blocks, last to first; dx holds the gradient of the block's output
   for (int l = NL - 1; l >= 0; --l) {
@@ -1019,7 +1029,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     void *h1 = LA(l, p.l_h1), *o = LA(l, p.l_o), *h2 = LA(l, p.l_h2);
     void *a = LA(l, p.l_a), *c = LA(l, p.l_c), *u = LA(l, p.l_u);
     // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
-    TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
+    if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
     TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
     if (kmok(dxb, D, u, F, D, F)) {
@@ -1044,9 +1054,9 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
       TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
       TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
     }
-    TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, lg->g_ffn, 0, rpart, M, D, eps, s));
+    TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, dxc, lg->g_ffn, 0, rpart, M, D, eps, s));
     // attention output projection: xm = x + o Wo^T
-    TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
+    if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
     TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
     if (kmok(dxb, D, o, qd, D, qd)) {
@@ -1083,7 +1093,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
       TFM_TRY(gemm_wgrad(dt, (uint8_t *)dqkvT + (size_t)(qd + kvd) * Mp * e, Mp, hT, kvd, D,
                          (int)Mp, lg->wv, D, skp, s));
     }
-    TFM_HIP(launch_rms_backward(x, lw->g_attn, dt, dhp, dx, lg->g_attn, 0, rpart, M, D, eps, s));
+    TFM_HIP(launch_rms_backward(x, lw->g_attn, dt, dhp, dx, dxc, lg->g_attn, 0, rpart, M, D, eps,
+                                s));
   }
   // ---- embedding rows (a tied head's gradient is already in gr->embed)
   if (!tied) TFM_HIP(launch_fill_f32(gr->embed, (int64_t)V * D, 0.f, s));

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__
                                                        const TG *__restrict__ g,
                                                        const float *__restrict__ dy,
                                                        float *__restrict__ dx,
+                                                       bf16_t *__restrict__ dxb,
                                                        float *__restrict__ dg_part, int64_t rows,
                                                        int d, float eps) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -278,7 +279,9 @@ __global__ __launch_bounds__(256) void rms_back_kernel(const float *__restrict__
     for (int i = 0; i < VPT; ++i) {
       const int gi = lane + 64 * i;
       if (gi < ng) {
-        store4(dx + r * d + 4 * gi, ov[i] + ri * gv[i] * dv[i] - xv[i] * c3);
+        const f32x4_t nv = ov[i] + ri * gv[i] * dv[i] - xv[i] * c3;
+        store4(dx + r * d + 4 * gi, nv);
+        if (dxb) store4(dxb + r * d + 4 * gi, nv);   // the bf16 operand of the next products
         gacc[i] += dv[i] * xv[i] * ri;
       }
     }
@@ -779,18 +782,18 @@ hipError_t launch_ce_backward(const float *z, int64_t ldz, const int32_t *target
 int rms_back_parts(int64_t rows) { return (int)nblk(rows, 4 * kRmsRows); }
 
 hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const float *dy, float *dx,
-                               float *dg, int accumulate_dg, float *dg_part, int64_t rows, int d,
-                               float eps, hipStream_t s) {
+                               void *dx_bf16, float *dg, int accumulate_dg, float *dg_part,
+                               int64_t rows, int d, float eps, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int ng = d / 4, vpt = (ng + 63) / 64;
   const unsigned nb = (unsigned)rms_back_parts(rows);
 #define TFM_RMSB(V)                                                                            \
   if (g_dt == DT_BF16)                                                                         \
-    rms_back_kernel<V, bf16_t><<<nb, 256, 0, s>>>(x, (const bf16_t *)g, dy, dx, dg_part, rows, \
-                                                  d, eps);                                     \
+    rms_back_kernel<V, bf16_t><<<nb, 256, 0, s>>>(x, (const bf16_t *)g, dy, dx,               \
+                                                  (bf16_t *)dx_bf16, dg_part, rows, d, eps);    \
   else                                                                                         \
-    rms_back_kernel<V, float><<<nb, 256, 0, s>>>(x, (const float *)g, dy, dx, dg_part, rows, d, \
-                                                 eps);
+    rms_back_kernel<V, float><<<nb, 256, 0, s>>>(x, (const float *)g, dy, dx,                 \
+                                                 (bf16_t *)dx_bf16, dg_part, rows, d, eps);
   switch (vpt) {
     case 1: TFM_RMSB(1) break;
     case 2: TFM_RMSB(2) break;

@@ -319,6 +319,26 @@ __device__ __forceinline__ void swiglu_direct_epilogue(const GemmArgs &g, Acc (&
         for (int x = 0; x < 4; ++x)
           if (col + x < ncols) p[x] = f32_to_bf16(v[x]);
       }
+      if (g.keep_a) {   // training: the gate and up values the backward reads
+        bf16_t *pa = (bf16_t *)g.keep_a + m * g.ldy + col, *pc = (bf16_t *)g.keep_c + m * g.ldy + col;
+        float a[4], c[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          a[x] = acc[gb][bm][x] * rsv[bm];
+          c[x] = acc[ub][bm][x] * rsv[bm];
+        }
+        if (vec && col + 3 < ncols) {
+          *(u32x2_t *)pa = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          *(u32x2_t *)pc = u32x2_t{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (col + x < ncols) {
+              pa[x] = f32_to_bf16(a[x]);
+              pc[x] = f32_to_bf16(c[x]);
+            }
+        }
+      }
     }
   }
 }

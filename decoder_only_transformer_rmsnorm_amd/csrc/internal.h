@@ -76,6 +76,9 @@ struct GemmArgs {
   const float *rs_part;
   int rs_parts, rs_d;
   float rs_eps;
+  // EPI_SWIGLU (bf16): also keep the gate and up values (bf16, same layout as y) for the
+  // backward, when not null
+  void *keep_a, *keep_c;
 };
 
 constexpr int kNormParts = 16;  // column tiles whose row partials one row of nrm_part holds
@@ -169,8 +172,8 @@ hipError_t launch_ce_backward(const float *z, int64_t ldz, const int32_t *target
 // dg_part: rms_back_parts(rows) * d floats of scratch.
 int rms_back_parts(int64_t rows);
 hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const float *dy, float *dx,
-                               float *dg, int accumulate_dg, float *dg_part, int64_t rows, int d,
-                               float eps, hipStream_t s);
+                               void *dx_bf16, float *dg, int accumulate_dg, float *dg_part,
+                               int64_t rows, int d, float eps, hipStream_t s);
 hipError_t launch_swiglu_fwd(const void *a, const void *c, void *u, int dt, int64_t n,
                              hipStream_t s);
 hipError_t launch_swiglu_backward(const void *a, const void *c, const float *du, void *da,
