@@ -313,7 +313,7 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
 
 // ---- training step: plan of the workspace and the enqueued forward / backward
 struct TrainPlan {
-  size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxT, dh, hT, du,
+  size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du,
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
@@ -374,6 +374,7 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.wT = take(wmax * e);
   p.dx = take(M * D * 4);
   p.dxb = take(M * D * e);
+  p.dxb2 = take(M * D * e);
   p.dxT = take(D * Mp * e);
   p.dh = take(M * D * 4);
   p.hT = take(D * Mp * e);
@@ -948,7 +949,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   auto X = [&](int l) { return l < NL ? (float *)LA(l, p.l_x) : (float *)(wb + p.xfinal); };
   int32_t *flags = (int32_t *)(wb + p.flag);
   void *xf = wb + p.xf, *dlog = wb + p.dlog, *dlogT = wb + p.dlogT, *xfT = wb + p.xfT;
-  void *wT = wb + p.wT, *dxb = wb + p.dxb, *dxT = wb + p.dxT, *hT = wb + p.hT;
+  void *wT = wb + p.wT, *dxb = wb + p.dxb, *dxb2 = wb + p.dxb2, *dxT = wb + p.dxT;
+  void *hT = wb + p.hT;
   void *da = wb + p.da, *dc = wb + p.dc, *daT = wb + p.daT, *dcT = wb + p.dcT;
   void *actT = wb + p.actT, *dout = wb + p.dout, *dqkv = wb + p.dqkv, *dqkvT = wb + p.dqkvT;
   float *logits = (float *)(wb + p.logits), *dx = (float *)(wb + p.dx);
@@ -1028,11 +1030,25 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     uint8_t *qkv = LA(l, p.l_qkv);
     void *h1 = LA(l, p.l_h1), *o = LA(l, p.l_o), *h2 = LA(l, p.l_h2);
     void *a = LA(l, p.l_a), *c = LA(l, p.l_c), *u = LA(l, p.l_u);
+    const uint8_t *dk = (const uint8_t *)dqkv + (size_t)qd * e, *dv = dk + (size_t)kvd * e;
+    // bf16: the layer's seven weight gradients run as one grouped launch once its input
+    // gradients are done (the gradient of the block output into the FFN stays in dxb, the one
+    // into the attention sublayer goes to dxb2)
+    const bool grouped = kmok(dxb, D, u, F, D, F) && kmok(da, F, h2, D, F, D) &&
+                         kmok(dc, F, h2, D, F, D) && kmok(dxb2, D, o, qd, D, qd) &&
+                         kmok(dqkv, W, h1, D, qd, D) && kmok(dk, W, h1, D, kvd, D) &&
+                         kmok(dv, W, h1, D, kvd, D);
+    WgradGroup wg{};
+    wg.K = (int)M;
+    auto job = [&](const void *ja, int64_t jlda, const void *jb, int64_t jldb, float *jy, int jm,
+                   int jn) { wg.job[wg.njobs++] = WgradJob{ja, jb, jy, jlda, jldb, jn, jm, jn}; };
     // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
     if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
     TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
     TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
-    if (kmok(dxb, D, u, F, D, F)) {
+    if (grouped) {
+      job(dxb, D, u, F, lg->w2, D, F);
+    } else if (kmok(dxb, D, u, F, D, F)) {
       TFM_TRY(gemm_wgrad_rows(dxb, D, u, F, D, F, (int)M, lg->w2, F, skp, s));
     } else {
       TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
@@ -1044,7 +1060,10 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
     TFM_HIP(launch_transpose(lw->w3, dt, D, wT, dt, F, F, F, D, s));
     TFM_TRY(gemm(EPI_RESIDUAL, dt, dc, F, wT, M, D, F, dhp, D, DT_F32, dhp, s));
-    if (kmok(da, F, h2, D, F, D) && kmok(dc, F, h2, D, F, D)) {
+    if (grouped) {
+      job(da, F, h2, D, lg->w1, F, D);
+      job(dc, F, h2, D, lg->w3, F, D);
+    } else if (kmok(da, F, h2, D, F, D) && kmok(dc, F, h2, D, F, D)) {
       TFM_TRY(gemm_wgrad_rows(da, F, h2, D, F, D, (int)M, lg->w1, D, skp, s));
       TFM_TRY(gemm_wgrad_rows(dc, F, h2, D, F, D, (int)M, lg->w3, D, skp, s));
     } else {
@@ -1054,12 +1073,16 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
       TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
       TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
     }
-    TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, dxc, lg->g_ffn, 0, rpart, M, D, eps, s));
+    void *dxo = grouped ? dxb2 : dxb;   // bf16 gradient into the attention sublayer
+    TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, dxc ? dxo : nullptr, lg->g_ffn, 0,
+                                rpart, M, D, eps, s));
     // attention output projection: xm = x + o Wo^T
-    if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
+    if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxo, dt, M * D, s));
     TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
-    if (kmok(dxb, D, o, qd, D, qd)) {
+    TFM_TRY(gemm(EPI_STORE, dt, dxo, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
+    if (grouped) {
+      job(dxo, D, o, qd, lg->wo, D, qd);
+    } else if (kmok(dxb, D, o, qd, D, qd)) {
       TFM_TRY(gemm_wgrad_rows(dxb, D, o, qd, D, qd, (int)M, lg->wo, qd, skp, s));
     } else {
       TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
@@ -1079,8 +1102,13 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_transpose(lw->wv, dt, D, (uint8_t *)wT + (size_t)(qd + kvd) * e, dt, W, kvd, kvd,
                              D, s));
     TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wT, M, D, W, dhp, D, DT_F32, nullptr, s));
-    const uint8_t *dk = (const uint8_t *)dqkv + (size_t)qd * e, *dv = dk + (size_t)kvd * e;
-    if (kmok(dqkv, W, h1, D, qd, D) && kmok(dk, W, h1, D, kvd, D) && kmok(dv, W, h1, D, kvd, D)) {
+    if (grouped) {
+      job(dqkv, W, h1, D, lg->wq, qd, D);
+      job(dk, W, h1, D, lg->wk, kvd, D);
+      job(dv, W, h1, D, lg->wv, kvd, D);
+      TFM_HIP(launch_gemm_wgrad_group(wg, s));
+    } else if (kmok(dqkv, W, h1, D, qd, D) && kmok(dk, W, h1, D, kvd, D) &&
+               kmok(dv, W, h1, D, kvd, D)) {
       TFM_TRY(gemm_wgrad_rows(dqkv, W, h1, D, qd, D, (int)M, lg->wq, D, skp, s));
       TFM_TRY(gemm_wgrad_rows(dk, W, h1, D, kvd, D, (int)M, lg->wk, D, skp, s));
       TFM_TRY(gemm_wgrad_rows(dv, W, h1, D, kvd, D, (int)M, lg->wv, D, skp, s));

@@ -407,10 +407,8 @@ struct BfTile {
 // of column i). No operand is ever transposed in memory.
 template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
           int WGN = 2, bool PP = false, int MS = 32, bool XS = false, bool KMAJ = false>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g0, int tiles_m,
-                                                                        int tiles_n) {
+__device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const GemmArgs g = k_part<bf16_t, KMAJ>(g0);
   constexpr int NT = 64 * WGM * WGN;
   using T = BfTile<BM, BN, BK, NST, WGM * WGN>;
   constexpr int RB = T::RB, FR = T::FILL_ROWS, A_INS = T::A_INS, B_INS = T::B_INS;
@@ -443,8 +441,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
   const int wm = PP ? wid / WGN : wid % WGM, wn = PP ? wid % WGN : wid / WGM;
   // lane -> (row of the block it reads / m of its outputs, k chunk it reads / n group it holds)
   const int h = lane / MS, l32 = lane % MS;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
   const int K = g.K;
@@ -1213,7 +1209,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs
 #endif
 }
 
+template <int BM, int BN, int BK, int NST, int EPI, int OCC = 1, bool EARLY = false, int WGM = 2,
+          int WGN = 2, bool PP = false, int MS = 32, bool XS = false, bool KMAJ = false>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(GemmArgs g0, int tiles_m,
+                                                                        int tiles_n) {
+  const GemmArgs g = k_part<bf16_t, KMAJ>(g0);
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  gemm_bf16_tile<BM, BN, BK, NST, EPI, OCC, EARLY, WGM, WGN, PP, MS, XS, KMAJ>(g, tm, tn);
+}
+
+// Several weight-gradient products over the same tokens in one launch, one 128 x 128 tile of
+// one product per workgroup and the whole token range per tile (no split, no partial sums):
+// a layer's products together launch enough tiles to fill the chip. Workgroup ids map to a
+// contiguous run of the concatenated tiles per XCD; inside a product the tiles go in the
+// grouped order of tile_coords.
+__global__ __launch_bounds__(256, 2) void gemm_wgrad_group_kernel(WgradGroup grp) {
+  const int T = grp.start[grp.njobs];
+  const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+  const int per = T >> 3, extra = T & 7;
+  const int logical = xcd * per + min(xcd, extra) + local;
+  GemmArgs g{};
+  int t0 = 0, tiles_m = 1;
+#pragma unroll
+  for (int j = 0; j < kWgradJobs; ++j) {
+    if (j < grp.njobs && logical >= grp.start[j]) {
+      const WgradJob &jb = grp.job[j];
+      g.a = jb.a; g.lda = jb.lda; g.w0 = jb.b; g.ldw = jb.ldb; g.M = jb.M; g.N = jb.N;
+      g.y = jb.y; g.ldy = jb.ldy;
+      t0 = grp.start[j];
+      tiles_m = (jb.M + 127) / 128;
+    }
+  }
+  g.K = grp.K;
+  g.y_dt = DT_F32;
+  const int tiles_n = (g.N + 127) / 128;
+  const int in = logical - t0;
+  const int group = in / (kGroupM * tiles_n), first_m = group * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m), r = in - group * kGroupM * tiles_n;
+  gemm_bf16_tile<128, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 32, false, true>(
+      g, first_m + r % gm, r / gm);
+}
+
 // ------------------------------------------------------------------ f32 kernel
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmArgs g0, int tiles_m,
                                                                int tiles_n) {
@@ -1435,7 +1474,26 @@ bool gemm_kmajor_ok(const void *a, int64_t lda, const void *w, int64_t ldw, int6
          lda >= M && ldw >= N && K * std::max(lda, ldw) * 2 < ((int64_t)1 << 31);
 }
 
+hipError_t launch_gemm_wgrad_group(const WgradGroup &grp, hipStream_t s) {
+  if (grp.njobs < 1 || grp.njobs > kWgradJobs || grp.K < 1) return hipErrorInvalidValue;
+  int64_t t = 0;
+  WgradGroup q = grp;
+  for (int j = 0; j < grp.njobs; ++j) {
+    const WgradJob &jb = grp.job[j];
+    if (jb.M < 1 || jb.N < 1 || !jb.y ||
+        !gemm_kmajor_ok(jb.a, jb.lda, jb.b, jb.ldb, jb.M, jb.N, grp.K))
+      return hipErrorInvalidValue;
+    q.start[j] = (int)t;
+    t += (int64_t)((jb.M + 127) / 128) * ((jb.N + 127) / 128);
+    if (t > 0x7fffffff) return hipErrorInvalidValue;
+  }
+  q.start[grp.njobs] = (int)t;
+  hipLaunchKernelGGL(gemm_wgrad_group_kernel, dim3((unsigned)t), dim3(256), 0, s, q);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_kmajor(const GemmArgs &g, hipStream_t s) {
+
   if (g.M == 0) return hipSuccess;
   if (g.ldw <= 0) return hipErrorInvalidValue;
   return run_bf16<128, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 32, false, true>(g, s);

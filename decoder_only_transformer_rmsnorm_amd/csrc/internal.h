@@ -98,6 +98,22 @@ hipError_t launch_gemm_kmajor(const GemmArgs &g, hipStream_t s);
 // whether launch_gemm_kmajor takes these operands (alignment, strides, 32-bit offsets)
 bool gemm_kmajor_ok(const void *a, int64_t lda, const void *w, int64_t ldw, int64_t M, int N,
                     int64_t K);
+// Up to kWgradJobs K-major products over the same K in one launch, unsplit, fp32 output:
+// job j writes y[m ldy + n] = sum over k < K of a[k lda + m] b[k ldb + n], m < M, n < N.
+// Every job must pass gemm_kmajor_ok; start[] is filled by the launcher.
+constexpr int kWgradJobs = 8;
+struct WgradJob {
+  const void *a, *b;
+  float *y;
+  int64_t lda, ldb, ldy;
+  int M, N;
+};
+struct WgradGroup {
+  WgradJob job[kWgradJobs];
+  int start[kWgradJobs + 1];
+  int njobs, K;
+};
+hipError_t launch_gemm_wgrad_group(const WgradGroup &grp, hipStream_t s);
 // Workgroups of a plain-store GEMM of M x N outputs.
 int64_t gemm_store_tiles(int dt, int64_t M, int N);
 
