@@ -313,7 +313,7 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
 
 // ---- training step: plan of the workspace and the enqueued forward / backward
 struct TrainPlan {
-  size_t flag, count, row_loss, xfinal, xf, logits, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du,
+  size_t flag, count, row_loss, xfinal, xf, logits, x_max, x_sum, x_tgt, x_lse, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du,
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
@@ -347,6 +347,12 @@ size_t splitk_bytes(int dt, int64_t M, int N, int64_t K) {
   return parts > 1 ? (size_t)parts * M * N * 4 : 0;
 }
 
+// bf16 models take the loss through the fused LM-head cross-entropy (no logits stored) and
+// recompute the logits for their gradient in the backward
+bool train_fused_xent(const tfm_config *c) {
+  return c->dtype == TFM_BF16 && c->d_model % 8 == 0;
+}
+
 TrainPlan plan_train(const tfm_config *c, int B, int S) {
   TrainPlan p;
   const size_t M = (size_t)B * S, e = elt(c->dtype);
@@ -363,7 +369,13 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.row_loss = take(M * 4);
   p.xfinal = take(M * D * 4);
   p.xf = take(M * D * e);
-  p.logits = take(M * Vp * 4);
+  const bool fx = train_fused_xent(c);
+  const size_t xparts = fx ? (size_t)gemm_xent_parts((int)V) : 0;
+  p.logits = take(fx ? 4 : M * Vp * 4);
+  p.x_max = take(std::max<size_t>(M * xparts * 4, 4));
+  p.x_sum = take(std::max<size_t>(M * xparts * 4, 4));
+  p.x_tgt = take(M * 4);
+  p.x_lse = take(M * 4);
   p.dlog = take(M * Vp * e);
   p.dlogT = take(Vp * Mp * e);
   p.xfT = take(D * Mp * e);
@@ -997,11 +1009,35 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_TRY(gemm(EPI_RESIDUAL, dt, u, F, lw->w2, M, D, F, X(l + 1), D, DT_F32, xm, s));
   }
   TFM_HIP(launch_rmsnorm(X(NL), DT_F32, w->g_final, dt, xf, dt, M, D, eps, s));
-  TFM_TRY(gemm(EPI_STORE, dt, xf, D, w->lm_head, M, V, D, logits, Vp, DT_F32, nullptr, s));
 
   // ---- loss and its gradient with respect to the logits ("LLM 2" Optimize / Loss)
-  TFM_HIP(launch_ce_backward(logits, Vp, targets, M, V, dlog, dt, Vp, (float *)(wb + p.row_loss),
-                             (int32_t *)(wb + p.count), loss_mean, s));
+  int32_t *count = (int32_t *)(wb + p.count);
+  float *row_loss = (float *)(wb + p.row_loss);
+  if (train_fused_xent(cfg)) {
+    // per-tile row maxima / sums of exp and the target logits, combined into each row's
+    // log-sum-exp and loss; the gradient product then recomputes the logits tile by tile
+    GemmArgs gx{};
+    gx.a = xf; gx.lda = D; gx.w0 = w->lm_head; gx.M = M; gx.N = V; gx.K = D;
+    gx.targets = targets;
+    gx.x_max = (float *)(wb + p.x_max);
+    gx.x_sum = (float *)(wb + p.x_sum);
+    gx.x_tgt = (float *)(wb + p.x_tgt);
+    TFM_HIP(launch_gemm(EPI_XENT, dt, gx, s));
+    TFM_HIP(launch_count_targets(targets, M, V, count, s));
+    float *x_lse = (float *)(wb + p.x_lse);
+    TFM_HIP(launch_xent_reduce(gx.x_max, gx.x_sum, gx.x_tgt, targets, gemm_xent_parts(V), M, V,
+                               row_loss, nullptr, s, x_lse, true));
+    TFM_HIP(launch_mean_rows(row_loss, M, count, loss_mean, s));
+    GemmArgs gg{};
+    gg.a = xf; gg.lda = D; gg.w0 = w->lm_head; gg.M = M; gg.N = V; gg.n0 = Vp; gg.K = D;
+    gg.y = dlog; gg.ldy = Vp; gg.y_dt = DT_BF16;
+    gg.targets = targets; gg.xg_lse = x_lse; gg.xg_count = count;
+    TFM_HIP(launch_gemm(EPI_XENT_GRAD, dt, gg, s));
+  } else {
+    TFM_TRY(gemm(EPI_STORE, dt, xf, D, w->lm_head, M, V, D, logits, Vp, DT_F32, nullptr, s));
+    TFM_HIP(launch_ce_backward(logits, Vp, targets, M, V, dlog, dt, Vp, row_loss, count,
+                               loss_mean, s));
+  }
 
   // ---- LM head and final RMSNorm
   TFM_HIP(launch_transpose(w->lm_head, dt, D, wT, dt, Vp, Vp, V, D, s));

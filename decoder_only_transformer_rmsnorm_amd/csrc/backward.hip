@@ -779,6 +779,18 @@ hipError_t launch_ce_backward(const float *z, int64_t ldz, const int32_t *target
   return hipGetLastError();
 }
 
+hipError_t launch_count_targets(const int32_t *targets, int64_t M, int V, int32_t *count,
+                                hipStream_t s) {
+  count_targets_kernel<<<1, 1024, 0, s>>>(targets, M, V, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_mean_rows(const float *row_loss, int64_t M, const int32_t *count, float *mean,
+                            hipStream_t s) {
+  mean_rows_kernel<<<1, 1024, 0, s>>>(row_loss, M, count, mean);
+  return hipGetLastError();
+}
+
 int rms_back_parts(int64_t rows) { return (int)nblk(rows, 4 * kRmsRows); }
 
 hipError_t launch_rms_backward(const float *x, const void *g, int g_dt, const float *dy, float *dx,

@@ -127,7 +127,7 @@ constexpr int kXentWaves = 8;
 __global__ __launch_bounds__(64 * kXentWaves) void xent_reduce_kernel(
     const float *__restrict__ x_max, const float *__restrict__ x_sum,
     const float *__restrict__ x_tgt, const int32_t *targets, int T, int64_t M, int V,
-    float *loss) {
+    float *loss, float *lse, bool oob_zero) {
   __shared__ float red[kXentWaves][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t m = (int64_t)blockIdx.x * 64 + lane;
@@ -153,9 +153,11 @@ __global__ __launch_bounds__(64 * kXentWaves) void xent_reduce_kernel(
 #pragma unroll
   for (int i = 0; i < kXentWaves; ++i) se += red[i][lane];
   const int t = targets[m];
-  if (t < 0) loss[m] = 0.f;
+  const float l = mx + logf(se);
+  if (lse) lse[m] = l;
+  if (t < 0 || (oob_zero && t >= V)) loss[m] = 0.f;
   else if (t >= V) loss[m] = __builtin_nanf("");
-  else loss[m] = mx + logf(se) - x_tgt[m];
+  else loss[m] = l - x_tgt[m];
 }
 
 // Mean over the rows with a target: one workgroup, strided fp64 partial sums in a fixed order
@@ -323,10 +325,10 @@ hipError_t launch_rope(void *x, int x_dt, int64_t row_stride, const int32_t *pos
 
 hipError_t launch_xent_reduce(const float *x_max, const float *x_sum, const float *x_tgt,
                               const int32_t *targets, int T, int64_t M, int V, float *loss,
-                              float *mean, hipStream_t s) {
+                              float *mean, hipStream_t s, float *lse, bool oob_zero) {
   if (M == 0) return hipSuccess;
   xent_reduce_kernel<<<blocks_for(M, 64), 64 * kXentWaves, 0, s>>>(x_max, x_sum, x_tgt, targets,
-                                                                   T, M, V, loss);
+                                                                   T, M, V, loss, lse, oob_zero);
   if (mean) mean_loss_kernel<<<1, kMeanThreads, 0, s>>>(loss, targets, M, mean);
   return hipGetLastError();
 }

@@ -446,6 +446,27 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
   const int K = g.K;
   const int frow = lane / (RB / 16), fchunk = lane % (RB / 16);  // lane's slot in a fill
 
+  // cross-entropy gradient: each of the lane's rows' exponent offset (log2 units: log-sum-exp
+  // plus log2 of the counted rows) and target (-1 for a row without one in [0, N)), read
+  // before the main loop so that their latency is hidden
+  constexpr int XR = EPI == EPI_XENT_GRAD ? NBM : 1;
+  float xl[XR], xinv = 0.f;
+  int xt[XR];
+  if constexpr (EPI == EPI_XENT_GRAD) {
+    const int cnt = max(g.xg_count[0], 1);
+    xinv = 1.0f / (float)cnt;
+    const float l2c = __builtin_amdgcn_logf((float)cnt);   // log2
+#pragma unroll
+    for (int bm = 0; bm < NBM; ++bm) {
+      const int64_t m = m0 + wm * WM + bm * MS + l32;
+      const int64_t mc = m < g.M ? m : g.M - 1;
+      const int t = g.targets[mc];
+      xt[bm] = t >= 0 && t < g.N ? t : -1;
+      xl[bm] = __builtin_fmaf(g.xg_lse[mc], 1.4426950408889634f, l2c);
+      asm volatile("" : "+v"(xl[bm]), "+v"(xt[bm]));
+    }
+  }
+
   // Activation rows m0 .. m0+BM-1: one resource; rows past M read as zero.
   // K-major: the resource starts at column m0 and ends with the operand's last element
   // (column M - 1 of row K - 1), so rows past K read as zero and nothing past the operand is
@@ -974,7 +995,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
   const int passes = kRes ? RES_PASSES : (BM * rb > LDS ? 2 : 1);
   static_assert(!kRes || RES_LDS == LDS, "residual pass split");
   const int prow = BM / passes;
-  const int ncols = EPI == EPI_SWIGLU ? g.n0 : g.N;
+  const int ncols = EPI == EPI_SWIGLU || EPI == EPI_XENT_GRAD ? g.n0 : g.N;
   const int nout0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;
   const bool vec_ok = ((g.ldy * ob) & 15) == 0;
 #pragma unroll
@@ -1015,6 +1036,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
       if constexpr (EPI == EPI_QKV_ROPE || EPI == EPI_SWIGLU) {
         if (g.rs_part) split_norm_scales<NBM, MS, WM>(g, m0, wm, l32, rsv);
       }
+      const bool xfull = n0 + BN <= g.N;   // cross-entropy gradient: no padded column here
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
         const int r = wm * WM + bm * MS + l32 - p * prow;
@@ -1060,6 +1082,30 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
                     const float nan = __builtin_nanf("");
                     v = f32x4_t{nan, nan, nan, nan};
                   }
+                }
+              }
+              if constexpr (EPI == EPI_XENT_GRAD) {
+                // (softmax(z) - onehot(t)) / count as 2^(z log2 e - xl) with the row's offset
+                // xl (log2 units) = lse log2 e + log2 count; the hardware exp2 (about 1 ulp) is
+                // far inside the bf16 rounding of the stored gradient. Rows without a target
+                // and padded columns store 0.
+                const int n = n0 + col;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                  const float e =
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(v[x], 1.4426950408889634f, -xl[bm]));
+                  v[x] = xt[bm] >= 0 ? e : 0.f;
+                }
+                const int tc = xt[bm] - n;
+                if ((unsigned)tc < 4u) {
+#pragma unroll
+                  for (int x = 0; x < 4; ++x)
+                    if (x == tc) v[x] -= xinv;
+                }
+                if (!xfull) {
+#pragma unroll
+                  for (int x = 0; x < 4; ++x)
+                    if (n + x >= g.N) v[x] = 0.f;
                 }
               }
             }
@@ -1165,7 +1211,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
         bf16_t *y = (bf16_t *)g.y + off;
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
         if (vec_ok && n + 8 <= ncols) {
-          if constexpr (EPI == EPI_STORE)   // logits: streamed out, not re-read here
+          if constexpr (EPI == EPI_STORE || EPI == EPI_XENT_GRAD)   // streamed out
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, raw), (u32x4_t *)y);
           else
             *(uint4 *)y = raw;
@@ -1173,7 +1219,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
           // row stride not a multiple of 8 elements: 4-byte stores on an even element
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            if constexpr (EPI == EPI_STORE)
+            if constexpr (EPI == EPI_STORE || EPI == EPI_XENT_GRAD)
               __builtin_nontemporal_store(w4[x], (uint32_t *)y + x);
             else
               ((uint32_t *)y)[x] = w4[x];
@@ -1193,7 +1239,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
         float *y = (float *)g.y + off;
         f32x4_t v = __builtin_bit_cast(f32x4_t, raw);
         if (vec_ok && n + 4 <= ncols) {
-          if constexpr (EPI == EPI_STORE)
+          if constexpr (EPI == EPI_STORE || EPI == EPI_XENT_GRAD)
             __builtin_nontemporal_store(v, (f32x4_t *)y);
           else
             *(f32x4_t *)y = v;
@@ -1435,6 +1481,13 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
         return run_bf16<256, 256, 64, 2, EPI_SWIGLU, 1, false, 2, 4, false, 16, true>(g, s);
       return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
+    case EPI_XENT_GRAD:
+      // the padded columns [N, n0) must lie inside the last column tile
+      if (g.n0 < g.N || g.n0 > (g.N + 127) / 128 * 128 || g.y_dt != DT_BF16)
+        return hipErrorInvalidValue;
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<192, 128, 64, 2, EPI_XENT_GRAD, 2, false, 2, 2, false, 16, true>(g, s);
+      return run_bf16<192, 128, 64, 2, EPI_XENT_GRAD, 2, true, 2, 2, false, 16>(g, s);
   }
   return hipErrorInvalidValue;
 }

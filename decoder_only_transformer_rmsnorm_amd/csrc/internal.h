@@ -23,9 +23,12 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // Next-token cross-entropy from the LM-head tile partials: loss[m] = max_m + log(sum_m) -
 // tgt[m] with max_m, sum_m combined over the T column tiles in a fixed order; negative
 // targets give 0, targets >= V give NaN. mean (optional) = mean over rows with target >= 0.
+// lse (M), when not null, receives each row's log-sum-exp; with oob_zero a target >= V gives
+// a zero loss (the training convention) instead of NaN.
 hipError_t launch_xent_reduce(const float *x_max, const float *x_sum, const float *x_tgt,
                               const int32_t *targets, int T, int64_t M, int V, float *loss,
-                              float *mean, hipStream_t s);
+                              float *mean, hipStream_t s, float *lse = nullptr,
+                              bool oob_zero = false);
 
 // ---- GEMM family (gemm.hip): y = a w^T with a fused epilogue.
 enum GemmEpi {
@@ -35,7 +38,10 @@ enum GemmEpi {
   EPI_SWIGLU = 3,    // gate rows from w1, up rows from w3; y = SiLU(gate) * up
   EPI_XENT = 4,      // no y: per row and column tile, max and sum of exp of the tile's
                      // logits, plus the logit of the row's target column (bf16 only)
-  EPI_QKV_CACHE = 5  // decode only: q -> y with RoPE; k (RoPE) and v -> KV cache slot
+  EPI_QKV_CACHE = 5, // decode only: q -> y with RoPE; k (RoPE) and v -> KV cache slot
+  EPI_XENT_GRAD = 6  // bf16 only: the logits recomputed and turned into the cross-entropy
+                     // gradient y = (exp(z - lse[m]) - [n == t_m]) / count for rows with a
+                     // target in [0, N), 0 elsewhere; columns [N, n0) are stored as zeros
 };
 
 struct GemmArgs {
@@ -79,6 +85,10 @@ struct GemmArgs {
   // EPI_SWIGLU (bf16): also keep the gate and up values (bf16, same layout as y) for the
   // backward, when not null
   void *keep_a, *keep_c;
+  // EPI_XENT_GRAD: each row's log-sum-exp (M) and the number of rows with a target (one int);
+  // the targets come in `targets`
+  const float *xg_lse;
+  const int32_t *xg_count;
 };
 
 constexpr int kNormParts = 16;  // column tiles whose row partials one row of nrm_part holds
@@ -184,6 +194,12 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_ce_backward(const float *z, int64_t ldz, const int32_t *targets, int64_t M,
                               int V, void *dz, int dz_dt, int64_t ldd, float *row_loss,
                               int32_t *count, float *mean, hipStream_t s);
+// count[0] = rows with a target in [0, V); mean[0] = sum of row_loss / count[0] (fp64, fixed
+// order; 0 without targets)
+hipError_t launch_count_targets(const int32_t *targets, int64_t M, int V, int32_t *count,
+                                hipStream_t s);
+hipError_t launch_mean_rows(const float *row_loss, int64_t M, const int32_t *count, float *mean,
+                            hipStream_t s);
 // dx += RMSNorm backward of rows x with gain g (d <= 2048); dg = (or +=) gain gradient.
 // dg_part: rms_back_parts(rows) * d floats of scratch.
 int rms_back_parts(int64_t rows);
