@@ -1465,6 +1465,11 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
     // 256 x 288 tiles, one workgroup per CU) the same loop was slower (LM head 747-829 us):
     // nothing covers a wave's memory stalls there.
     case EPI_STORE:
+      // narrow outputs (the backward's input-gradient products, N = d_model): 128 x 96 tiles
+      // launch twice the workgroups of 192 x 128 ones, two per CU at M = 8192, N = 768
+      // (alone: 28 against 40 us at K = 2048, 696 against 799 us at K = 50304)
+      if (g.K % 64 == 0 && g.kparts <= 1 && g.N <= 1024)
+        return run_bf16<128, 96, 64, 2, EPI_STORE, 2, false, 2, 2, false, 16, true>(g, s);
       if (g.K % 64 == 0 && g.kparts <= 1)
         return run_bf16<192, 128, 64, 2, EPI_STORE, 2, false, 2, 2, false, 16, true>(g, s);
       return run_bf16<192, 128, 64, 2, EPI_STORE, 2, true, 2, 2, false, 16>(g, s);
