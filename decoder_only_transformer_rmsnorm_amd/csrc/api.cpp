@@ -313,7 +313,7 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
 
 // ---- training step: plan of the workspace and the enqueued forward / backward
 struct TrainPlan {
-  size_t flag, count, row_loss, xfinal, xf, logits, x_max, x_sum, x_tgt, x_lse, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du,
+  size_t flag, count, row_loss, xfinal, xf, logits, x_max, x_sum, x_tgt, x_lse, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du, dac,
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
@@ -380,7 +380,7 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.dlogT = take(Vp * Mp * e);
   p.xfT = take(D * Mp * e);
   size_t wmax = D * Vp;
-  wmax = std::max(wmax, F * D);
+  wmax = std::max(wmax, 2 * F * D);
   wmax = std::max(wmax, D * W);
   wmax = std::max(wmax, qd * D);
   p.wT = take(wmax * e);
@@ -392,6 +392,7 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   p.hT = take(D * Mp * e);
   p.du = take(M * F * 4);
   p.da = take(M * F * e);
+  p.dac = take(M * 2 * F * e);
   p.dc = take(M * F * e);
   p.daT = take(F * Mp * e);
   p.dcT = take(F * Mp * e);
@@ -963,6 +964,7 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
   void *xf = wb + p.xf, *dlog = wb + p.dlog, *dlogT = wb + p.dlogT, *xfT = wb + p.xfT;
   void *wT = wb + p.wT, *dxb = wb + p.dxb, *dxb2 = wb + p.dxb2, *dxT = wb + p.dxT;
   void *hT = wb + p.hT;
+  void *dac = wb + p.dac, *dacF = wb + p.dac + (size_t)F * e;
   void *da = wb + p.da, *dc = wb + p.dc, *daT = wb + p.daT, *dcT = wb + p.dcT;
   void *actT = wb + p.actT, *dout = wb + p.dout, *dqkv = wb + p.dqkv, *dqkvT = wb + p.dqkvT;
   float *logits = (float *)(wb + p.logits), *dx = (float *)(wb + p.dx);
@@ -1070,8 +1072,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     // bf16: the layer's seven weight gradients run as one grouped launch once its input
     // gradients are done (the gradient of the block output into the FFN stays in dxb, the one
     // into the attention sublayer goes to dxb2)
-    const bool grouped = kmok(dxb, D, u, F, D, F) && kmok(da, F, h2, D, F, D) &&
-                         kmok(dc, F, h2, D, F, D) && kmok(dxb2, D, o, qd, D, qd) &&
+    const bool grouped = kmok(dxb, D, u, F, D, F) && kmok(dac, 2 * F, h2, D, F, D) &&
+                         kmok(dacF, 2 * F, h2, D, F, D) && kmok(dxb2, D, o, qd, D, qd) &&
                          kmok(dqkv, W, h1, D, qd, D) && kmok(dk, W, h1, D, kvd, D) &&
                          kmok(dv, W, h1, D, kvd, D);
     WgradGroup wg{};
@@ -1081,33 +1083,45 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
     if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
     TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
     if (grouped) {
+      // du never leaves the registers: the product's epilogue applies the SwiGLU backward and
+      // writes da | dc side by side (rows of 2 F), so one product over K = 2 F against
+      // [W1^T | W3^T] gives the input gradient
+      GemmArgs gb{};
+      gb.a = dxb; gb.lda = D; gb.w0 = wT; gb.M = M; gb.N = F; gb.K = D;
+      gb.y = dac; gb.ldy = 2 * (int64_t)F; gb.y_dt = dt; gb.keep_a = a; gb.keep_c = c;
+      TFM_HIP(launch_gemm(EPI_SWIGLU_BACK, dt, gb, s));
       job(dxb, D, u, F, lg->w2, D, F);
-    } else if (kmok(dxb, D, u, F, D, F)) {
-      TFM_TRY(gemm_wgrad_rows(dxb, D, u, F, D, F, (int)M, lg->w2, F, skp, s));
+      TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, 2 * F, F, F, D, s));
+      TFM_HIP(launch_transpose(lw->w3, dt, D, (uint8_t *)wT + (size_t)F * e, dt, 2 * F, F, F, D,
+                               s));
+      TFM_TRY(gemm(EPI_STORE, dt, dac, 2 * F, wT, M, D, 2 * F, dhp, D, DT_F32, nullptr, s));
+      job(dac, 2 * F, h2, D, lg->w1, F, D);
+      job(dacF, 2 * F, h2, D, lg->w3, F, D);
     } else {
-      TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
-      TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
-      TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, skp, s));
-    }
-    TFM_HIP(launch_swiglu_backward(a, c, du, da, dc, dt, M * F, s));
-    TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, F, F, F, D, s));
-    TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
-    TFM_HIP(launch_transpose(lw->w3, dt, D, wT, dt, F, F, F, D, s));
-    TFM_TRY(gemm(EPI_RESIDUAL, dt, dc, F, wT, M, D, F, dhp, D, DT_F32, dhp, s));
-    if (grouped) {
-      job(da, F, h2, D, lg->w1, F, D);
-      job(dc, F, h2, D, lg->w3, F, D);
-    } else if (kmok(da, F, h2, D, F, D) && kmok(dc, F, h2, D, F, D)) {
-      TFM_TRY(gemm_wgrad_rows(da, F, h2, D, F, D, (int)M, lg->w1, D, skp, s));
-      TFM_TRY(gemm_wgrad_rows(dc, F, h2, D, F, D, (int)M, lg->w3, D, skp, s));
-    } else {
-      TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
-      TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
-      TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
-      TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
-      TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
+      TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
+      if (kmok(dxb, D, u, F, D, F)) {
+        TFM_TRY(gemm_wgrad_rows(dxb, D, u, F, D, F, (int)M, lg->w2, F, skp, s));
+      } else {
+        TFM_HIP(launch_transpose(dxb, dt, D, dxT, dt, Mp, Mp, M, D, s));
+        TFM_HIP(launch_transpose(u, dt, F, actT, dt, Mp, Mp, M, F, s));
+        TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, F, (int)Mp, lg->w2, F, skp, s));
+      }
+      TFM_HIP(launch_swiglu_backward(a, c, du, da, dc, dt, M * F, s));
+      TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, F, F, F, D, s));
+      TFM_TRY(gemm(EPI_STORE, dt, da, F, wT, M, D, F, dhp, D, DT_F32, nullptr, s));
+      TFM_HIP(launch_transpose(lw->w3, dt, D, wT, dt, F, F, F, D, s));
+      TFM_TRY(gemm(EPI_RESIDUAL, dt, dc, F, wT, M, D, F, dhp, D, DT_F32, dhp, s));
+      if (kmok(da, F, h2, D, F, D) && kmok(dc, F, h2, D, F, D)) {
+        TFM_TRY(gemm_wgrad_rows(da, F, h2, D, F, D, (int)M, lg->w1, D, skp, s));
+        TFM_TRY(gemm_wgrad_rows(dc, F, h2, D, F, D, (int)M, lg->w3, D, skp, s));
+      } else {
+        TFM_HIP(launch_transpose(da, dt, F, daT, dt, Mp, Mp, M, F, s));
+        TFM_HIP(launch_transpose(dc, dt, F, dcT, dt, Mp, Mp, M, F, s));
+        TFM_HIP(launch_transpose(h2, dt, D, hT, dt, Mp, Mp, M, D, s));
+        TFM_TRY(gemm_wgrad(dt, daT, Mp, hT, F, D, (int)Mp, lg->w1, D, skp, s));
+        TFM_TRY(gemm_wgrad(dt, dcT, Mp, hT, F, D, (int)Mp, lg->w3, D, skp, s));
+      }
     }
     void *dxo = grouped ? dxb2 : dxb;   // bf16 gradient into the attention sublayer
     TFM_HIP(launch_rms_backward(xm, lw->g_ffn, dt, dhp, dx, dxc ? dxo : nullptr, lg->g_ffn, 0,

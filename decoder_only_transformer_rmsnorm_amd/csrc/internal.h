@@ -39,9 +39,13 @@ enum GemmEpi {
   EPI_XENT = 4,      // no y: per row and column tile, max and sum of exp of the tile's
                      // logits, plus the logit of the row's target column (bf16 only)
   EPI_QKV_CACHE = 5, // decode only: q -> y with RoPE; k (RoPE) and v -> KV cache slot
-  EPI_XENT_GRAD = 6  // bf16 only: the logits recomputed and turned into the cross-entropy
+  EPI_XENT_GRAD = 6, // bf16 only: the logits recomputed and turned into the cross-entropy
                      // gradient y = (exp(z - lse[m]) - [n == t_m]) / count for rows with a
                      // target in [0, N), 0 elsewhere; columns [N, n0) are stored as zeros
+  EPI_SWIGLU_BACK = 7// bf16 only: acc is du, the gradient of u = SiLU(a) c; with the forward's a
+                     // and c in keep_a / keep_c ((M, N), row stride N) it stores
+                     // da = du c s (1 + a (1 - s)), s = sigmoid(a), at y[m ldy + n] and
+                     // dc = du a s at y[m ldy + N + n] (ldy >= 2 N)
 };
 
 struct GemmArgs {
