@@ -278,71 +278,6 @@ __device__ __forceinline__ void split_norm_scales(const GemmArgs &g, int64_t m0,
   for (int bm = 0; bm < NBM; ++bm) rsv[bm] = rsqrtf(ss[bm] / (float)g.rs_d + g.rs_eps);
 }
 
-// Epilogue of the SwiGLU backward on 16 x 16 blocks, from registers: block (bn, bm) of the lane
-// holds du for row m = m0 + wm WM + 16 bm + l32 and hidden units n = n0 + wn WN + 16 bn + 4 h
-// .. + 3; the forward's gate a and up c of those units are read (8 bytes each) and da, dc
-// written side by side in one row of y (dc N columns after da).
-template <int NBM, int NBN, int WM, int WN, typename Acc>
-__device__ __forceinline__ void swiglu_back_epilogue(const GemmArgs &g, Acc (&acc)[NBN][NBM],
-                                                     int64_t m0, int n0, int wm, int wn, int h,
-                                                     int l32) {
-  const int N = g.N;
-  const bool vec = (N & 3) == 0 && (g.ldy & 3) == 0;
-  const bf16_t *ka = (const bf16_t *)g.keep_a, *kc = (const bf16_t *)g.keep_c;
-  bf16_t *y = (bf16_t *)g.y;
-#pragma unroll
-  for (int bm = 0; bm < NBM; ++bm) {
-    const int64_t m = m0 + wm * WM + bm * 16 + l32;
-    if (m >= g.M) continue;
-#pragma unroll
-    for (int bn = 0; bn < NBN; ++bn) {
-      const int n = n0 + wn * WN + bn * 16 + 4 * h;
-      if (n >= N) continue;
-      const int64_t ko = m * N + n;
-      float a[4], c[4];
-      if (vec && n + 3 < N) {
-        const u32x2_t av = *(const u32x2_t *)(ka + ko), cv = *(const u32x2_t *)(kc + ko);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          a[2 * x] = __uint_as_float(av[x] << 16);
-          a[2 * x + 1] = __uint_as_float(av[x] & 0xffff0000u);
-          c[2 * x] = __uint_as_float(cv[x] << 16);
-          c[2 * x + 1] = __uint_as_float(cv[x] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          a[x] = n + x < N ? bf16_to_f32(ka[ko + x]) : 0.f;
-          c[x] = n + x < N ? bf16_to_f32(kc[ko + x]) : 0.f;
-        }
-      }
-      float da[4], dc[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        // sigmoid with the hardware exp2 and reciprocal (about 1 ulp each, inside the bf16
-        // rounding that follows)
-        const float sg =
-            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a[x] * 1.4426950408889634f));
-        const float du = acc[bn][bm][x];
-        da[x] = du * c[x] * sg * (1.0f + a[x] * (1.0f - sg));
-        dc[x] = du * a[x] * sg;
-      }
-      bf16_t *pa = y + m * g.ldy + n, *pc = pa + N;
-      if (vec && n + 3 < N) {
-        *(u32x2_t *)pa = u32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
-        *(u32x2_t *)pc = u32x2_t{pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3])};
-      } else {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          if (n + x < N) {
-            pa[x] = f32_to_bf16(da[x]);
-            pc[x] = f32_to_bf16(dc[x]);
-          }
-      }
-    }
-  }
-}
-
 // Epilogue of the SwiGLU product's 16 x 16 blocks, written from registers. Block (bn, bm) of
 // the lane holds rows m = m0 + wm WM + 16 bm + l32 and virtual weight rows n0 + wn WN + 16 bn
 // + 4 h .. + 3; in every 64-row group of virtual rows, gate block gb and up block gb + 2 hold
@@ -965,11 +900,6 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
     swiglu_direct_epilogue<NBM, NBN, WM, WN>(g, acc, m0, n0, wm, wn, h, l32);
     return;
   }
-  if constexpr (EPI == EPI_SWIGLU_BACK) {
-    static_assert(MS == 16, "16 x 16 blocks");
-    swiglu_back_epilogue<NBM, NBN, WM, WN>(g, acc, m0, n0, wm, wn, h, l32);
-    return;
-  }
   __syncthreads();  // every wave is done with the ring: reuse it to stage the output
 
   if constexpr (EPI == EPI_XENT) {
@@ -1059,7 +989,8 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
   // ---- epilogue: final values -> LDS (output dtype, row-major tile) -> coalesced rows.
   //      Lane holds acc[bn][bm][4q + r] for m = m0 + wm*WM + bm*MS + l32 and
   //      n = n0 + wn*WN + bn*MS + 8q + 4h + r (MS = 32, q < 4) or + 4h + r (MS = 16).
-  const bool out_bf16 = EPI == EPI_RESIDUAL ? false : g.y_dt == DT_BF16;
+  // the SwiGLU backward stages du in fp32 and writes bf16 da, dc from the coalesced pass
+  const bool out_bf16 = EPI == EPI_RESIDUAL || EPI == EPI_SWIGLU_BACK ? false : g.y_dt == DT_BF16;
   const int ob = out_bf16 ? 2 : 4;
   const int rb = OUT_COLS * ob;
   const int passes = kRes ? RES_PASSES : (BM * rb > LDS ? 2 : 1);
@@ -1195,7 +1126,59 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
     __syncthreads();
     // coalesced stores: consecutive threads take consecutive 16-byte chunks of a row
     const int cpr = rb >> 4, epc = 16 / ob;
-    if constexpr (kRes) {
+    if constexpr (EPI == EPI_SWIGLU_BACK) {
+      // SwiGLU backward: a thread takes 16-byte chunks (4 du values) of the staged rows, reads
+      // the forward's gate a and up c of those hidden units (8 bytes each, all loads issued
+      // before any is used) and writes da = du c s (1 + a (1 - s)), dc = du a s, s =
+      // sigmoid(a), side by side in one row of y (dc N columns after da). N is a multiple
+      // of 4, so a chunk is whole or past N.
+      constexpr int CPR = BN / 4;
+      constexpr int SB_PASSES = BM * BN * 4 > LDS ? 2 : 1;
+      constexpr int SB_ROWS = BM / SB_PASSES, IT = SB_ROWS * CPR / NT;
+      static_assert(IT * NT == SB_ROWS * CPR, "SwiGLU backward chunk split");
+      constexpr int IB = 4;   // chunks whose loads are in flight together
+      static_assert(IT % IB == 0, "SwiGLU backward batches");
+      const bf16_t *ka = (const bf16_t *)g.keep_a, *kc = (const bf16_t *)g.keep_c;
+#pragma unroll
+      for (int i0 = 0; i0 < IT; i0 += IB) {
+        f32x4_t dv[IB];
+        u32x2_t av[IB], cv[IB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+          const int idx = tid + (i0 + i) * NT, r = idx / CPR, cc = idx % CPR;
+          const int64_t m = m0 + p * SB_ROWS + r;
+          const int n = n0 + 4 * cc;
+          const int64_t ko = m < g.M && n < g.N ? m * g.N + n : 0;
+          av[i] = *(const u32x2_t *)(ka + ko);
+          cv[i] = *(const u32x2_t *)(kc + ko);
+          dv[i] = *(const f32x4_t *)(lds + stage_off(r, cc * 16, rb));
+        }
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+          const int idx = tid + (i0 + i) * NT, r = idx / CPR, cc = idx % CPR;
+          const int64_t m = m0 + p * SB_ROWS + r;
+          const int n = n0 + 4 * cc;
+          if (m >= g.M || n >= g.N) continue;
+          float da[4], dc[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t aw = av[i][x >> 1], cw = cv[i][x >> 1];
+            const float a = __uint_as_float((x & 1) ? (aw & 0xffff0000u) : (aw << 16));
+            const float c = __uint_as_float((x & 1) ? (cw & 0xffff0000u) : (cw << 16));
+            // sigmoid with the hardware exp2 and reciprocal (about 1 ulp each, inside the
+            // bf16 rounding that follows)
+            const float sg =
+                __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f));
+            da[x] = dv[i][x] * c * sg * (1.0f + a * (1.0f - sg));
+            dc[x] = dv[i][x] * a * sg;
+          }
+          bf16_t *pa = (bf16_t *)g.y + m * g.ldy + n;
+          *(u32x2_t *)pa = u32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+          *(u32x2_t *)(pa + g.N) =
+              u32x2_t{pack_bf16x2(dc[0], dc[1]), pack_bf16x2(dc[2], dc[3])};
+        }
+      }
+    } else if constexpr (kRes) {
       // a fresh copy of the thread id: without it the compiler keeps every chunk's address
       // from the prefetch alive through the main loop (and spills)
       int tid_e = tid;
@@ -1557,7 +1540,8 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
       return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
     case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
     case EPI_SWIGLU_BACK:
-      if (g.y_dt != DT_BF16 || !g.keep_a || !g.keep_c || g.ldy < 2 * (int64_t)g.N)
+      if (g.y_dt != DT_BF16 || !g.keep_a || !g.keep_c || g.ldy < 2 * (int64_t)g.N ||
+          g.N % 4 != 0 || g.ldy % 4 != 0)
         return hipErrorInvalidValue;
       if (g.K % 64 == 0 && g.kparts <= 1)
         return run_bf16<192, 128, 64, 2, EPI_SWIGLU_BACK, 2, false, 2, 2, false, 16, true>(g, s);

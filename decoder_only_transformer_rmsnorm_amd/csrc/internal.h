@@ -45,7 +45,7 @@ enum GemmEpi {
   EPI_SWIGLU_BACK = 7// bf16 only: acc is du, the gradient of u = SiLU(a) c; with the forward's a
                      // and c in keep_a / keep_c ((M, N), row stride N) it stores
                      // da = du c s (1 + a (1 - s)), s = sigmoid(a), at y[m ldy + n] and
-                     // dc = du a s at y[m ldy + N + n] (ldy >= 2 N)
+                     // dc = du a s at y[m ldy + N + n] (ldy >= 2 N; N, ldy multiples of 4)
 };
 
 struct GemmArgs {
