@@ -313,7 +313,7 @@ int enqueue_xent(const void *x, const void *w, const int32_t *targets, float *lo
 
 // ---- training step: plan of the workspace and the enqueued forward / backward
 struct TrainPlan {
-  size_t flag, count, row_loss, xfinal, xf, logits, x_max, x_sum, x_tgt, x_lse, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du, dac,
+  size_t flag, count, row_loss, xfinal, xf, logits, x_max, x_sum, x_tgt, x_lse, dlog, dlogT, xfT, wT, dx, dxb, dxb2, dxT, dh, hT, du, dac, wTl,
       da, dc, daT, dcT, actT, dout, dqkv, dqkvT, lse, dsum, rms_part, splitk;
   size_t layers, layer_bytes;
   size_t l_x, l_h1, l_qkv, l_o, l_lse, l_xm, l_h2, l_a, l_c, l_u;   // within a layer block
@@ -384,6 +384,9 @@ TrainPlan plan_train(const tfm_config *c, int B, int S) {
   wmax = std::max(wmax, D * W);
   wmax = std::max(wmax, qd * D);
   p.wT = take(wmax * e);
+  // a layer's transposed weights, all made by one launch before its backward:
+  // W2^T (F, D) | [W1^T | W3^T] (D, 2F) | Wo^T (qd, D) | [Wq; Wk; Wv]^T (D, W)
+  p.wTl = take((3 * F * D + qd * D + D * W) * e);
   p.dx = take(M * D * 4);
   p.dxb = take(M * D * e);
   p.dxb2 = take(M * D * e);
@@ -1080,25 +1083,35 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     wg.K = (int)M;
     auto job = [&](const void *ja, int64_t jlda, const void *jb, int64_t jldb, float *jy, int jm,
                    int jn) { wg.job[wg.njobs++] = WgradJob{ja, jb, jy, jlda, jldb, jn, jm, jn}; };
+    uint8_t *wT2 = wb + p.wTl, *wT13 = wT2 + (size_t)F * D * e;
+    uint8_t *wTo = wT13 + (size_t)2 * F * D * e, *wTqkv = wTo + (size_t)qd * D * e;
+    if (grouped) {
+      const TransposeJob tj[7] = {
+          {lw->w2, wT2, F, D, D, F},
+          {lw->w1, wT13, D, 2 * F, F, D},
+          {lw->w3, wT13 + (size_t)F * e, D, 2 * F, F, D},
+          {lw->wo, wTo, qd, D, D, qd},
+          {lw->wq, wTqkv, D, W, qd, D},
+          {lw->wk, wTqkv + (size_t)qd * e, D, W, kvd, D},
+          {lw->wv, wTqkv + (size_t)(qd + kvd) * e, D, W, kvd, D}};
+      TFM_HIP(launch_transpose_multi(tj, 7, s));
+    }
     // SwiGLU FFN: out = xm + u W2^T, u = SiLU(a) c, a = h2 W1^T, c = h2 W3^T
     if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxb, dt, M * D, s));
-    TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
     if (grouped) {
       // du never leaves the registers: the product's epilogue applies the SwiGLU backward and
       // writes da | dc side by side (rows of 2 F), so one product over K = 2 F against
       // [W1^T | W3^T] gives the input gradient
       GemmArgs gb{};
-      gb.a = dxb; gb.lda = D; gb.w0 = wT; gb.M = M; gb.N = F; gb.K = D;
+      gb.a = dxb; gb.lda = D; gb.w0 = wT2; gb.M = M; gb.N = F; gb.K = D;
       gb.y = dac; gb.ldy = 2 * (int64_t)F; gb.y_dt = dt; gb.keep_a = a; gb.keep_c = c;
       TFM_HIP(launch_gemm(EPI_SWIGLU_BACK, dt, gb, s));
       job(dxb, D, u, F, lg->w2, D, F);
-      TFM_HIP(launch_transpose(lw->w1, dt, D, wT, dt, 2 * F, F, F, D, s));
-      TFM_HIP(launch_transpose(lw->w3, dt, D, (uint8_t *)wT + (size_t)F * e, dt, 2 * F, F, F, D,
-                               s));
-      TFM_TRY(gemm(EPI_STORE, dt, dac, 2 * F, wT, M, D, 2 * F, dhp, D, DT_F32, nullptr, s));
+      TFM_TRY(gemm(EPI_STORE, dt, dac, 2 * F, wT13, M, D, 2 * F, dhp, D, DT_F32, nullptr, s));
       job(dac, 2 * F, h2, D, lg->w1, F, D);
       job(dacF, 2 * F, h2, D, lg->w3, F, D);
     } else {
+      TFM_HIP(launch_transpose(lw->w2, dt, F, wT, dt, D, D, D, F, s));
       TFM_TRY(gemm(EPI_STORE, dt, dxb, D, wT, M, F, D, du, F, DT_F32, nullptr, s));
       if (kmok(dxb, D, u, F, D, F)) {
         TFM_TRY(gemm_wgrad_rows(dxb, D, u, F, D, F, (int)M, lg->w2, F, skp, s));
@@ -1128,8 +1141,8 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
                                 rpart, M, D, eps, s));
     // attention output projection: xm = x + o Wo^T
     if (!dxc) TFM_HIP(launch_convert(dx, DT_F32, dxo, dt, M * D, s));
-    TFM_HIP(launch_transpose(lw->wo, dt, qd, wT, dt, D, D, D, qd, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dxo, D, wT, M, qd, D, dout, qd, dt, nullptr, s));
+    if (!grouped) TFM_HIP(launch_transpose(lw->wo, dt, qd, wTo, dt, D, D, D, qd, s));
+    TFM_TRY(gemm(EPI_STORE, dt, dxo, D, wTo, M, qd, D, dout, qd, dt, nullptr, s));
     if (grouped) {
       job(dxo, D, o, qd, lg->wo, D, qd);
     } else if (kmok(dxb, D, o, qd, D, qd)) {
@@ -1147,11 +1160,13 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
     TFM_HIP(launch_rope_inverse((uint8_t *)dqkv + (size_t)qd * e, dt, W, positions, M, S, Hkv, dh,
                                 cos_sin, cfg->max_seq_len, s));
     // q, k, v projections: one GEMM against [Wq; Wk; Wv]^T for the input gradient
-    TFM_HIP(launch_transpose(lw->wq, dt, D, wT, dt, W, qd, qd, D, s));
-    TFM_HIP(launch_transpose(lw->wk, dt, D, (uint8_t *)wT + (size_t)qd * e, dt, W, kvd, kvd, D, s));
-    TFM_HIP(launch_transpose(lw->wv, dt, D, (uint8_t *)wT + (size_t)(qd + kvd) * e, dt, W, kvd, kvd,
-                             D, s));
-    TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wT, M, D, W, dhp, D, DT_F32, nullptr, s));
+    if (!grouped) {
+      TFM_HIP(launch_transpose(lw->wq, dt, D, wTqkv, dt, W, qd, qd, D, s));
+      TFM_HIP(launch_transpose(lw->wk, dt, D, wTqkv + (size_t)qd * e, dt, W, kvd, kvd, D, s));
+      TFM_HIP(launch_transpose(lw->wv, dt, D, wTqkv + (size_t)(qd + kvd) * e, dt, W, kvd, kvd, D,
+                               s));
+    }
+    TFM_TRY(gemm(EPI_STORE, dt, dqkv, W, wTqkv, M, D, W, dhp, D, DT_F32, nullptr, s));
     if (grouped) {
       job(dqkv, W, h1, D, lg->wq, qd, D);
       job(dk, W, h1, D, lg->wk, kvd, D);

@@ -63,15 +63,12 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI *__restrict__ s
 // of 8 elements): a 64 x 64 tile, each thread reads 8 consecutive elements of a source row
 // (two rows per thread) into LDS (pitch 66 elements, so the 8 threads that later read one
 // column segment hit distinct banks) and writes 8 consecutive elements of a destination row.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
-                                                             int64_t lds,
-                                                             uint16_t *__restrict__ dst,
-                                                             int64_t ldd, int64_t R,
-                                                             int64_t R_valid, int C) {
+__device__ __forceinline__ void transpose_bf16_tile(const uint16_t *__restrict__ src, int64_t lds,
+                                                    uint16_t *__restrict__ dst, int64_t ldd,
+                                                    int64_t R, int64_t R_valid, int C,
+                                                    int64_t r0, int c0) {
   constexpr int P = 66;
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
   const int tid = threadIdx.x, g8 = tid & 7, row = tid >> 3;
 #pragma unroll
   for (int ps = 0; ps < 2; ++ps) {
@@ -96,6 +93,34 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
              ((uint32_t)tile[(8 * g8 + 2 * k + 1) * P + oc] << 16);
     if (c < C && r < R) *(uint4 *)(dst + (int64_t)c * ldd + r) = uint4{w[0], w[1], w[2], w[3]};
   }
+}
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ src,
+                                                             int64_t lds,
+                                                             uint16_t *__restrict__ dst,
+                                                             int64_t ldd, int64_t R,
+                                                             int64_t R_valid, int C) {
+  transpose_bf16_tile(src, lds, dst, ldd, R, R_valid, C, (int64_t)blockIdx.y * 64,
+                      blockIdx.x * 64);
+}
+
+// Several bf16 transposes in one launch (a layer's weights before its backward): workgroups
+// [start[j], start[j + 1]) take the 64 x 64 tiles of job j, row-major over its tile grid.
+struct TransposeBatch {
+  TransposeJob job[kTransposeJobs];
+  int start[kTransposeJobs + 1];
+  int n;
+};
+__global__ __launch_bounds__(256) void transpose_bf16_multi_kernel(TransposeBatch b) {
+  const int bid = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kTransposeJobs; ++i)
+    if (i < b.n && bid >= b.start[i]) j = i;
+  const TransposeJob &t = b.job[j];
+  const int tc = (t.C + 63) / 64, in = bid - b.start[j];
+  transpose_bf16_tile((const uint16_t *)t.src, t.lds, (uint16_t *)t.dst, t.ldd, t.R, t.R, t.C,
+                      (int64_t)(in / tc) * 64, (in % tc) * 64);
 }
 
 template <typename TI, typename TO>
@@ -741,6 +766,30 @@ hipError_t launch_transpose(const void *src, int src_dt, int64_t lds, void *dst,
     transpose_kernel<float, float><<<grid, 256, 0, s>>>((const float *)src, lds, (float *)dst, ldd, R, R_valid, C);
   else
     transpose_kernel<bf16_t, float><<<grid, 256, 0, s>>>((const bf16_t *)src, lds, (float *)dst, ldd, R, R_valid, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_multi(const TransposeJob *jobs, int n, hipStream_t s) {
+  TransposeBatch b{};
+  int64_t t = 0;
+  for (int j = 0; j < n; ++j) {
+    const TransposeJob &q = jobs[j];
+    const bool vec = ((q.lds | q.ldd | q.R | q.C) & 7) == 0 &&
+                     (((uintptr_t)q.src | (uintptr_t)q.dst) & 15) == 0;
+    if (!vec || b.n == kTransposeJobs) {   // the general kernel, one launch
+      const hipError_t e = launch_transpose(q.src, DT_BF16, q.lds, q.dst, DT_BF16, q.ldd, q.R, q.R,
+                                            (int)q.C, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    b.job[b.n] = q;
+    b.start[b.n++] = (int)t;
+    t += ((q.R + 63) / 64) * ((q.C + 63) / 64);
+    if (t > 0x7fffffff) return hipErrorInvalidValue;
+  }
+  if (b.n == 0 || t == 0) return hipSuccess;
+  b.start[b.n] = (int)t;
+  transpose_bf16_multi_kernel<<<(unsigned)t, 256, 0, s>>>(b);
   return hipGetLastError();
 }
 

@@ -192,6 +192,16 @@ hipError_t launch_transpose(const void *src, int src_dt, int64_t lds, void *dst,
                             int64_t ldd, int64_t R, int64_t R_valid, int C, hipStream_t s);
 hipError_t launch_convert(const void *src, int src_dt, void *dst, int dst_dt, int64_t n,
                           hipStream_t s);
+// Up to kTransposeJobs bf16 transposes dst[c ldd + r] = src[r lds + c] (r < R, c < C) in one
+// launch; a job whose strides, sizes or pointers do not allow 16-byte accesses (or one past
+// the limit) gets a launch of its own.
+constexpr int kTransposeJobs = 8;
+struct TransposeJob {
+  const void *src;
+  void *dst;
+  int64_t lds, ldd, R, C;
+};
+hipError_t launch_transpose_multi(const TransposeJob *jobs, int n, hipStream_t s);
 hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 // dz = d mean-loss / d z for fp32 logits z (M, ldz), written (M, ldd) with zero padding past
 // V; row_loss (M); count = rows with a target in [0, V); mean = mean loss over them.
