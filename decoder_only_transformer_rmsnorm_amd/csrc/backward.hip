@@ -622,13 +622,40 @@ __global__ void embed_back_kernel(const int32_t *__restrict__ ids, int64_t n, in
 
 // ---- gradient clipping ("LLM 2" Gradient Clip) and AdamW ("LLM 2" Optimizer)
 constexpr int kSumsqBlocks = 256;   // partial sums per tensor
+
+__device__ __forceinline__ double sq4(f32x4_t v) {
+  return ((double)v[0] * v[0] + (double)v[1] * v[1]) + ((double)v[2] * v[2] + (double)v[3] * v[3]);
+}
+
+// Workgroup blk's share of sum g[i]^2 (fp64): 16-byte loads, four in flight per thread when g
+// is 16-byte aligned; the partition and the order of the adds are fixed by (blk, thread).
+__device__ __forceinline__ double sumsq_share(const float *__restrict__ g, int64_t n, int blk) {
+  const int tid = threadIdx.x;
+  const int64_t step = (int64_t)kSumsqBlocks * 256;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int64_t j0 = 0;   // first element left to the scalar loop
+  if (((uintptr_t)g & 15) == 0) {
+    const int64_t nv = n >> 2;
+    const f32x4_t *gv = (const f32x4_t *)g;
+    int64_t i = (int64_t)blk * 256 + tid;
+    for (; i + 3 * step < nv; i += 4 * step) {
+      const f32x4_t a = gv[i], b = gv[i + step], c = gv[i + 2 * step], d = gv[i + 3 * step];
+      s0 += sq4(a);
+      s1 += sq4(b);
+      s2 += sq4(c);
+      s3 += sq4(d);
+    }
+    for (; i < nv; i += step) s0 += sq4(gv[i]);
+    j0 = 4 * nv;
+  }
+  for (int64_t j = j0 + (int64_t)blk * 256 + tid; j < n; j += step) s1 += (double)g[j] * (double)g[j];
+  return (s0 + s1) + (s2 + s3);
+}
+
 __global__ __launch_bounds__(256) void sumsq_kernel(const float *__restrict__ g, int64_t n,
                                                     double *__restrict__ part) {
   __shared__ double red[256];
-  double s = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)kSumsqBlocks * 256)
-    s += (double)g[i] * (double)g[i];
-  red[threadIdx.x] = s;
+  red[threadIdx.x] = sumsq_share(g, n, blockIdx.x);
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
@@ -642,9 +669,17 @@ __global__ __launch_bounds__(256) void clip_coef_kernel(const double *__restrict
                                                         float *__restrict__ coef,
                                                         float *__restrict__ norm) {
   __shared__ double red[256];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += 256) s += part[i];
-  red[threadIdx.x] = s;
+  // four independent sums per thread, so four loads are in flight
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int i = threadIdx.x;
+  for (; i + 768 < nparts; i += 1024) {
+    s0 += part[i];
+    s1 += part[i + 256];
+    s2 += part[i + 512];
+    s3 += part[i + 768];
+  }
+  for (; i < nparts; i += 256) s0 += part[i];
+  red[threadIdx.x] = (s0 + s1) + (s2 + s3);
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
@@ -670,19 +705,15 @@ struct AdamwBatch {
   float *m[kBatch], *v[kBatch];
   int64_t n[kBatch];
   int64_t blk0[kBatch + 1];   // first block of each tensor; blk0[count] = total blocks
+  bool vec[kBatch];           // 16-byte aligned p, g, m, v and 8-byte aligned pb (or none)
   int count;
 };
 
 // sumsq_kernel for tensor blockIdx.y of a batch, partials at part + blockIdx.y * kSumsqBlocks
 __global__ __launch_bounds__(256) void sumsq_multi_kernel(SumsqBatch bt, double *__restrict__ part) {
   const int t = blockIdx.y;
-  const float *g = bt.g[t];
-  const int64_t n = bt.n[t];
   __shared__ double red[256];
-  double s = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)kSumsqBlocks * 256)
-    s += (double)g[i] * (double)g[i];
-  red[threadIdx.x] = s;
+  red[threadIdx.x] = sumsq_share(bt.g[t], bt.n[t], blockIdx.x);
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
@@ -726,10 +757,31 @@ __global__ __launch_bounds__(256) void adamw_multi_kernel(AdamwBatch bt, float l
   const int64_t b = blockIdx.x;
   int t = 0;
   while (t + 1 < bt.count && bt.blk0[t + 1] <= b) ++t;
-  const int64_t i = (b - bt.blk0[t]) * 256 + threadIdx.x;
-  if (i >= bt.n[t]) return;
-  adamw_elem(bt.p[t], bt.pb[t], bt.g[t], bt.m[t], bt.v[t], i, lr, b1, b2, eps, wd, c1, c2,
-             coef ? coef[0] : 1.0f);
+  // 4 consecutive elements per thread, with 16-byte accesses where the tensor allows them
+  const int64_t i = ((b - bt.blk0[t]) * 256 + threadIdx.x) * 4;
+  const int64_t n = bt.n[t];
+  if (i >= n) return;
+  const float cf = coef ? coef[0] : 1.0f;
+  float *p = bt.p[t], *m = bt.m[t], *v = bt.v[t];
+  const float *g = bt.g[t];
+  bf16_t *pb = bt.pb[t];
+  if (bt.vec[t] && i + 4 <= n) {
+    const f32x4_t gg = load4(g + i) * cf, m0 = load4(m + i), v0 = load4(v + i), th = load4(p + i);
+    f32x4_t mi, vi, nw;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      mi[x] = b1 * m0[x] + (1.0f - b1) * gg[x];
+      vi[x] = b2 * v0[x] + (1.0f - b2) * gg[x] * gg[x];
+      nw[x] = th[x] - lr * (mi[x] / c1) / (sqrtf(vi[x] / c2) + eps) - lr * wd * th[x];
+    }
+    store4(m + i, mi);
+    store4(v + i, vi);
+    store4(p + i, nw);
+    if (pb) store4(pb + i, nw);
+  } else {
+    for (int64_t j = i; j < i + 4 && j < n; ++j)
+      adamw_elem(p, pb, g, m, v, j, lr, b1, b2, eps, wd, c1, c2, cf);
+  }
 }
 
 template <typename T, int DH>
@@ -972,8 +1024,10 @@ hipError_t launch_adamw_multi(float *const *p, void *const *pb, const float *con
       bt.m[c] = m[t];
       bt.v[c] = v[t];
       bt.n[c] = n[t];
+      bt.vec[c] = (((uintptr_t)p[t] | (uintptr_t)g[t] | (uintptr_t)m[t] | (uintptr_t)v[t]) & 15) == 0 &&
+                  ((uintptr_t)bt.pb[c] & 7) == 0;
       bt.blk0[c] = blocks;
-      blocks += nblk(n[t], 256);
+      blocks += nblk(n[t], 1024);
       ++c;
     }
     if (c == 0) break;
