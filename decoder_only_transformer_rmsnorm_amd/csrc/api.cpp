@@ -1152,13 +1152,11 @@ int tfm_model_backward(const tfm_config *cfg, const tfm_model_weights *w, const 
       TFM_HIP(launch_transpose(o, dt, qd, actT, dt, Mp, Mp, M, qd, s));
       TFM_TRY(gemm_wgrad(dt, dxT, Mp, actT, D, qd, (int)Mp, lg->wo, qd, skp, s));
     }
-    // attention, then back through the rotations of q and k
+    // attention, and back through the rotations of q and k (applied as dq, dk are stored)
     TFM_HIP(launch_attention_backward(qkv, W, o, qd, dout, qd, dqkv, B, S, Hq, Hkv, dh, dt,
                                       layer_window(cfg, l), (const float *)LA(l, p.l_lse),
-                                      (float *)(wb + p.dsum), s));
-    TFM_HIP(launch_rope_inverse(dqkv, dt, W, positions, M, S, Hq, dh, cos_sin, cfg->max_seq_len, s));
-    TFM_HIP(launch_rope_inverse((uint8_t *)dqkv + (size_t)qd * e, dt, W, positions, M, S, Hkv, dh,
-                                cos_sin, cfg->max_seq_len, s));
+                                      (float *)(wb + p.dsum), positions, cos_sin,
+                                      cfg->max_seq_len, s));
     // q, k, v projections: one GEMM against [Wq; Wk; Wv]^T for the input gradient
     if (!grouped) {
       TFM_HIP(launch_transpose(lw->wq, dt, D, wTqkv, dt, W, qd, qd, D, s));

@@ -118,6 +118,20 @@ __device__ __forceinline__ int snake_item(int bid, int n, int cus) {
   return item < n ? item : bid;   // partial last round: keep in order
 }
 
+// The backward of RoPE: the (cos, sin) pairs of a row's position, or null without a table or
+// for a position outside it (the gradient then stays unrotated) ...
+template <int DH>
+__device__ __forceinline__ const float *rope_row(const float *cs, int p, int max_seq) {
+  return cs && p >= 0 && p < max_seq ? cs + (int64_t)p * DH : nullptr;
+}
+// ... and two adjacent pairs (v0, v1), (v2, v3) rotated by the opposite angles, with
+// c = (cos0, sin0, cos1, sin1)
+__device__ __forceinline__ f32x4_t rope_back4(f32x4_t v, const float *c) {
+  const f32x4_t t = *(const f32x4_t *)c;
+  return f32x4_t{v[0] * t[0] + v[1] * t[1], v[1] * t[0] - v[0] * t[1],
+                 v[2] * t[2] + v[3] * t[3], v[3] * t[2] - v[2] * t[3]};
+}
+
 // ---------------------------------------------------------------- dQ (and D)
 // grid ceil(S / 128) * Hq * B, query tiles longest first (the last tile sees every key)
 template <int DH>
@@ -125,7 +139,8 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dq_mfma_kernel(
     const bf16_t *__restrict__ qkv, int64_t ld, const bf16_t *__restrict__ o, int64_t ldo,
     const bf16_t *__restrict__ dout, int64_t lddo, bf16_t *__restrict__ dqkv, int S, int Hq,
     int Hkv, int window, float scale, const float *__restrict__ lse_in,
-    float *__restrict__ dsum_out, int B, int cus) {
+    float *__restrict__ dsum_out, int B, int cus, const int32_t *__restrict__ pos,
+    const float *__restrict__ cs, int max_seq) {
   constexpr int KS = DH / 16, NDB = DH / 32;
   using TL = BTile<DH>;
   __shared__ __attribute__((aligned(16))) uint8_t kt[TL::BYTES];
@@ -232,6 +247,8 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dq_mfma_kernel(
   }
   if (live) {
     bf16_t *op = dqkv + rq * ld + (int64_t)hq * DH;
+    const int p = pos ? pos[rq] : my_q;
+    const float *csr = rope_row<DH>(cs, p, max_seq);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -239,6 +256,7 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dq_mfma_kernel(
         f32x4_t r;
 #pragma unroll
         for (int x = 0; x < 4; ++x) r[x] = dq[db][4 * gq + x] * scale;
+        if (csr) r = rope_back4(r, csr + 32 * db + 8 * gq + 4 * h);
         store4(op + 32 * db + 8 * gq + 4 * h, r);
       }
   }
@@ -251,7 +269,8 @@ template <int DH>
 __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
     const bf16_t *__restrict__ qkv, int64_t ld, const bf16_t *__restrict__ dout, int64_t lddo,
     bf16_t *__restrict__ dqkv, int S, int Hq, int Hkv, int window, float scale,
-    const float *__restrict__ lse_in, const float *__restrict__ dsum_in, int B, int cus) {
+    const float *__restrict__ lse_in, const float *__restrict__ dsum_in, int B, int cus,
+    const int32_t *__restrict__ pos, const float *__restrict__ cs, int max_seq) {
   constexpr int KS = DH / 16, NDB = DH / 32;
   using TL = BTile<DH>;
   __shared__ __attribute__((aligned(16))) uint8_t qt[TL::BYTES];
@@ -372,6 +391,8 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
   if (live) {
     bf16_t *kp = dqkv + rk * ld + qd + (int64_t)g * DH;
     bf16_t *vp = kp + kvd;
+    const int p = pos ? pos[rk] : my_k;
+    const float *csr = rope_row<DH>(cs, p, max_seq);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -382,6 +403,7 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
           rkv[x] = dk[db][4 * gq + x] * scale;
           rvv[x] = dv[db][4 * gq + x];
         }
+        if (csr) rkv = rope_back4(rkv, csr + 32 * db + 8 * gq + 4 * h);
         store4(kp + 32 * db + 8 * gq + 4 * h, rkv);
         store4(vp + 32 * db + 8 * gq + 4 * h, rvv);
       }
@@ -391,17 +413,18 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
 template <int DH>
 hipError_t run(const void *qkv, int64_t ld, const void *o, int64_t ldo, const void *dout,
                int64_t lddo, void *dqkv, int B, int S, int Hq, int Hkv, int window,
-               const float *lse, float *dsum, hipStream_t s) {
+               const float *lse, float *dsum, const int32_t *pos, const float *cs,
+               int max_seq, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)DH);
   const int64_t nb = (S + kRows - 1) / kRows;
   if (nb * Hq * B > 0x7fffffff) return hipErrorInvalidValue;
   const int cus = compute_units();
   attn_dq_mfma_kernel<DH><<<dim3((unsigned)(nb * Hq * B)), 256, 0, s>>>(
       (const bf16_t *)qkv, ld, (const bf16_t *)o, ldo, (const bf16_t *)dout, lddo,
-      (bf16_t *)dqkv, S, Hq, Hkv, window, scale, lse, dsum, B, cus);
+      (bf16_t *)dqkv, S, Hq, Hkv, window, scale, lse, dsum, B, cus, pos, cs, max_seq);
   attn_dkdv_mfma_kernel<DH><<<dim3((unsigned)(nb * Hkv * B)), 256, 0, s>>>(
       (const bf16_t *)qkv, ld, (const bf16_t *)dout, lddo, (bf16_t *)dqkv, S, Hq, Hkv, window,
-      scale, lse, dsum, B, cus);
+      scale, lse, dsum, B, cus, pos, cs, max_seq);
   return hipGetLastError();
 }
 
@@ -411,12 +434,17 @@ hipError_t launch_attention_backward_bf16(const void *qkv, int64_t ld, const voi
                                           int64_t ldo, const void *dout, int64_t lddo,
                                           void *dqkv, int B, int S, int Hq, int Hkv, int d_head,
                                           int window, const float *lse, float *dsum,
-                                          hipStream_t s) {
+                                          const int32_t *positions, const float *cos_sin,
+                                          int max_seq, hipStream_t s) {
+#define TFM_RUN(D)                                                                             \
+  return run<D>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, window, lse, dsum, positions, \
+                cos_sin, max_seq, s);
   switch (d_head) {
-    case 32: return run<32>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, window, lse, dsum, s);
-    case 64: return run<64>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, window, lse, dsum, s);
-    case 128: return run<128>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, window, lse, dsum, s);
+    case 32: TFM_RUN(32)
+    case 64: TFM_RUN(64)
+    case 128: TFM_RUN(128)
   }
+#undef TFM_RUN
   return hipErrorInvalidValue;
 }
 

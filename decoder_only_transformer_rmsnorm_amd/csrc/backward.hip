@@ -970,25 +970,28 @@ bool attention_backward_supported(int d_head) {
 hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o, int64_t ldo,
                                      const void *dout, int64_t lddo, void *dqkv, int B, int S,
                                      int Hq, int Hkv, int d_head, int dt, int window,
-                                     const float *lse, float *dsum, hipStream_t s) {
+                                     const float *lse, float *dsum, const int32_t *positions,
+                                     const float *cos_sin, int max_seq, hipStream_t s) {
   if ((int64_t)B * S == 0) return hipSuccess;
   if (B > 65535 || Hq > 65535) return hipErrorInvalidValue;
   const int w = window > 0 && window < S ? window : 0;
-#define TFM_AB(T, D)                                                                          \
-  return run_attn_back<T, D>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s);
-  if (dt == DT_BF16) {
+  if (dt == DT_BF16)
     return launch_attention_backward_bf16(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv,
-                                          d_head, w, lse, dsum, s);
-  } else {
-    switch (d_head) {
-      case 16: TFM_AB(float, 16)
-      case 32: TFM_AB(float, 32)
-      case 64: TFM_AB(float, 64)
-      case 128: TFM_AB(float, 128)
-    }
+                                          d_head, w, lse, dsum, positions, cos_sin, max_seq, s);
+  hipError_t e = hipErrorInvalidValue;
+  switch (d_head) {
+    case 16: e = run_attn_back<float, 16>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s); break;
+    case 32: e = run_attn_back<float, 32>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s); break;
+    case 64: e = run_attn_back<float, 64>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s); break;
+    case 128: e = run_attn_back<float, 128>(qkv, ld, o, ldo, dout, lddo, dqkv, B, S, Hq, Hkv, w, lse, dsum, s); break;
   }
-#undef TFM_AB
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || !cos_sin) return e;
+  const int64_t qd = (int64_t)Hq * d_head;
+  e = launch_rope_inverse(dqkv, dt, ld, positions, (int64_t)B * S, S, Hq, d_head, cos_sin, max_seq,
+                          s);
+  if (e != hipSuccess) return e;
+  return launch_rope_inverse((float *)dqkv + qd, dt, ld, positions, (int64_t)B * S, S, Hkv,
+                             d_head, cos_sin, max_seq, s);
 }
 
 hipError_t launch_sumsq_multi(const float *const *g, const int64_t *n, int count, double *part,

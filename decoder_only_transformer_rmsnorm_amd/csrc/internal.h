@@ -230,16 +230,22 @@ hipError_t launch_rope_inverse(void *x, int dt, int64_t row_stride, const int32_
 bool attention_backward_supported(int d_head);
 // dq, dk, dv into the q | k | v columns of dqkv (same layout as qkv); lse: (B*S, Hq) row
 // logsumexp kept by the forward (launch_attention's lse); dsum: (B*S, Hq) fp32 scratch.
+// With cos_sin, dq and dk are then rotated back by their rows' positions (the backward of
+// the forward's RoPE; positions NULL -> row % S; a position outside [0, max_seq) is left
+// unrotated).
 hipError_t launch_attention_backward(const void *qkv, int64_t ld, const void *o, int64_t ldo,
                                      const void *dout, int64_t lddo, void *dqkv, int B, int S,
                                      int Hq, int Hkv, int d_head, int dt, int window,
-                                     const float *lse, float *dsum, hipStream_t s);
-// The bf16 path of launch_attention_backward (attn_back.hip): d_head 32, 64 or 128.
+                                     const float *lse, float *dsum, const int32_t *positions,
+                                     const float *cos_sin, int max_seq, hipStream_t s);
+// The bf16 path of launch_attention_backward (attn_back.hip): d_head 32, 64 or 128; the
+// rotation is applied to the gradients before they are stored.
 hipError_t launch_attention_backward_bf16(const void *qkv, int64_t ld, const void *o,
                                           int64_t ldo, const void *dout, int64_t lddo,
                                           void *dqkv, int B, int S, int Hq, int Hkv, int d_head,
                                           int window, const float *lse, float *dsum,
-                                          hipStream_t s);
+                                          const int32_t *positions, const float *cos_sin,
+                                          int max_seq, hipStream_t s);
 // The sum-of-squares partials of `count` tensors (host arrays of device pointers and sizes),
 // tensor t at part + t * sumsq_parts(), in launches of up to 32 tensors.
 hipError_t launch_sumsq_multi(const float *const *g, const int64_t *n, int count, double *part,
