@@ -54,9 +54,8 @@ __device__ __forceinline__ u32x4_t ld16(const bf16_t *p) { return *(const u32x4_
 
 // Rotates the adjacent pairs (n, n+1), (n+2, n+3) of a q or k head by the angles of position
 // pos ("Transformer 篇" 5.5; "LLM 2" RoPE); n is the column within the head.
-__device__ __forceinline__ f32x4_t rope4(f32x4_t v, const float *cos_sin, int pos, int d_head,
-                                         int n) {
-  const f32x4_t cs = *(const f32x4_t *)(cos_sin + ((int64_t)pos * (d_head >> 1) + (n >> 1)) * 2);
+// cs = (cos, sin) of the two pairs' angles
+__device__ __forceinline__ f32x4_t rope4(f32x4_t v, f32x4_t cs) {
   const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
   return f32x4_t{x0 * cs[0] - x1 * cs[1], x0 * cs[1] + x1 * cs[0], x2 * cs[2] - x3 * cs[3],
                  x2 * cs[3] + x3 * cs[2]};
@@ -93,9 +92,6 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
       wrow[a] = (const bf16_t *)g.w0 + (int64_t)(wok[a] ? n : 0) * g.K;
     }
   }
-  const int mr = m0 + r16;
-  const bool xok = mr < g.M;
-  const bf16_t *xrow = (const bf16_t *)g.x + (int64_t)(xok ? mr : 0) * g.ldx;
   const int nks = (g.K + 31) / 32;   // 32-wide k steps; wave w takes steps w, w + NWV, ...
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   u32x4_t wa[U][NA];
@@ -110,59 +106,144 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
   };
   load_w(w);   // the first weights are in flight while the norm is computed
 
-  // fused RMSNorm ("Transformer 篇" 5.6): 1 / rms of each of the 16 rows (NT / 16 threads
-  // per row); the operand is then x * inv * g, rounded once to bf16
-  __shared__ float inv_rms[16];
-  const bool fuse = g.norm_x != nullptr;
-  const float *nrow = fuse ? g.norm_x + (int64_t)(xok ? mr : 0) * g.ldx : nullptr;
-  if (fuse) {
-    constexpr int TPR = NT / 16;
-    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    const int m = m0 + row;
-    float ss = 0.f;
-    if (m < g.M) {
-      const float *xr = g.norm_x + (int64_t)m * g.ldx;
-#pragma unroll 2
-      for (int k = 4 * part; k < g.K; k += 4 * TPR) {
-        const f32x4_t v = load4(xr + k);
-        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  // Wave 0 writes the block's outputs: the operands its epilogue reads besides the products
+  // (the residual, the token's position and its rotation angles) are requested now, so their
+  // latency hides behind the weight stream.
+  const int m_out = m0 + r16, n_out = nb0 + 4 * kc;
+  f32x4_t y_pre = {0.f, 0.f, 0.f, 0.f}, cs_pre = {0.f, 0.f, 0.f, 0.f};
+  int pos_pre = 0;
+  if (w == 0 && m_out < g.M) {
+    if constexpr (EPI == EPI_RESIDUAL) {
+      const float *yr = (const float *)g.y + (int64_t)m_out * g.ldy + n_out;
+      if (n_out + 3 < g.N && (g.ldy & 3) == 0) {
+        y_pre = load4(yr);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y_pre[r] = n_out + r < g.N ? yr[r] : 0.f;
+      }
+    } else if constexpr (EPI == EPI_QKV_CACHE) {
+      pos_pre = g.positions[m_out];
+      if (n_out < g.n0 + g.n1 && pos_pre >= 0 && pos_pre < g.max_seq) {
+        const int j = n_out < g.n0 ? n_out : n_out - g.n0;
+        cs_pre = *(const f32x4_t *)(g.cos_sin +
+                                    ((int64_t)pos_pre * (g.d_head >> 1) + ((j % g.d_head) >> 1)) * 2);
       }
     }
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (part == 0) inv_rms[row] = rsqrtf(ss / (float)g.K + g.eps);
-    // LDS only: the weight loads above stay in flight across this barrier
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  const float rinv = fuse ? inv_rms[r16] : 0.f;
-  auto x_chunk = [&](int k) -> u32x4_t {   // 8 activations of row mr from column k
-    if (!fuse) return ld16(xrow + k);
-    const f32x4_t a = load4(nrow + k), b = load4(nrow + k + 4);
-    const f32x4_t ga = load4((const bf16_t *)g.norm_g + k), gb = load4((const bf16_t *)g.norm_g + k + 4);
-    const f32x4_t ya = a * rinv * ga, yb = b * rinv * gb;
-    return u32x4_t{pack_bf16x2(ya[0], ya[1]), pack_bf16x2(ya[2], ya[3]),
-                   pack_bf16x2(yb[0], yb[1]), pack_bf16x2(yb[2], yb[3])};
-  };
 
+  const bool fuse = g.norm_x != nullptr;
+  const int mr = m_out;
+  const bool xok = mr < g.M;
   f32x4_t acc[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) acc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int ks0 = w; ks0 < nks; ks0 += NWV * U) {
-    u32x4_t xa[U];
+
+  // (the gate and up weights of 8 steps leave no registers for a whole row: SwiGLU with 8
+  // steps per wave takes the general path)
+  constexpr bool kOnePass = !(NA == 2 && U > 4);
+  if (kOnePass && fuse && nks <= NWV * U) {
+    // fused RMSNorm ("Transformer 篇" 5.6) with the whole row in one batch of chunks: the
+    // chunks of row r16 over the block's lanes (waves w, k pieces kc, steps u) cover its K
+    // columns once, so the row's sum of squares is summed from them (two lane exchanges, then
+    // the waves through LDS) and the row is read only once; the operand is x * inv * g,
+    // rounded once to bf16
+    __shared__ float ssp[NWV][16];
+    const float *nrow = g.norm_x + (int64_t)(xok ? mr : 0) * g.ldx;
+    f32x4_t xl[U], xh[U];
+    u32x4_t gr[U];   // 8 gains (bf16) per chunk
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (ks0 + NWV * u) * 32 + kc * 8;
-      const bool kok = ks0 + NWV * u < nks && k < g.K;
-      xa[u] = xok && kok ? x_chunk(k) : zero;
+      const int k = (w + NWV * u) * 32 + kc * 8;
+      const bool kok = xok && w + NWV * u < nks && k < g.K;
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      xl[u] = kok ? load4(nrow + k) : z;
+      xh[u] = kok ? load4(nrow + k + 4) : z;
+      gr[u] = kok ? ld16((const bf16_t *)g.norm_g + k) : zero;
     }
+    float ss = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
+      for (int e = 0; e < 4; ++e) ss += xl[u][e] * xl[u][e] + xh[u][e] * xh[u][e];
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (kc == 0) ssp[w][r16] = ss;
+    // LDS only: the weight loads stay in flight across this barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float tot = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) tot += ssp[v][r16];
+    const float rinv = rsqrtf(tot / (float)g.K + g.eps);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4_t gl, gh;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        gl[2 * e] = __uint_as_float(gr[u][e] << 16);
+        gl[2 * e + 1] = __uint_as_float(gr[u][e] & 0xffff0000u);
+        gh[2 * e] = __uint_as_float(gr[u][e + 2] << 16);
+        gh[2 * e + 1] = __uint_as_float(gr[u][e + 2] & 0xffff0000u);
+      }
+      const f32x4_t ya = xl[u] * rinv * gl, yb = xh[u] * rinv * gh;
+      const u32x4_t xa = {pack_bf16x2(ya[0], ya[1]), pack_bf16x2(ya[2], ya[3]),
+                          pack_bf16x2(yb[0], yb[1]), pack_bf16x2(yb[2], yb[3])};
+#pragma unroll
       for (int a = 0; a < NA; ++a)
         acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u][a]),
-                                                        __builtin_bit_cast(bf16x8_t, xa[u]),
+                                                        __builtin_bit_cast(bf16x8_t, xa),
                                                         acc[a], 0, 0, 0);
-    if (ks0 + NWV * U < nks) load_w(ks0 + NWV * U);
+    }
+  } else {
+    const bf16_t *xrow = (const bf16_t *)g.x + (int64_t)(xok ? mr : 0) * g.ldx;
+    // fused RMSNorm over several batches: 1 / rms of each of the 16 rows first (NT / 16
+    // threads per row)
+    __shared__ float inv_rms[16];
+    const float *nrow = fuse ? g.norm_x + (int64_t)(xok ? mr : 0) * g.ldx : nullptr;
+    if (fuse) {
+      constexpr int TPR = NT / 16;
+      const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+      const int m = m0 + row;
+      float ss = 0.f;
+      if (m < g.M) {
+        const float *xr = g.norm_x + (int64_t)m * g.ldx;
+#pragma unroll 8
+        for (int k = 4 * part; k < g.K; k += 4 * TPR) {
+          const f32x4_t v = load4(xr + k);
+          ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+      }
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      if (part == 0) inv_rms[row] = rsqrtf(ss / (float)g.K + g.eps);
+      // LDS only: the weight loads above stay in flight across this barrier
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    const float rinv = fuse ? inv_rms[r16] : 0.f;
+    auto x_chunk = [&](int k) -> u32x4_t {   // 8 activations of row mr from column k
+      if (!fuse) return ld16(xrow + k);
+      const f32x4_t a = load4(nrow + k), b = load4(nrow + k + 4);
+      const f32x4_t ga = load4((const bf16_t *)g.norm_g + k), gb = load4((const bf16_t *)g.norm_g + k + 4);
+      const f32x4_t ya = a * rinv * ga, yb = b * rinv * gb;
+      return u32x4_t{pack_bf16x2(ya[0], ya[1]), pack_bf16x2(ya[2], ya[3]),
+                     pack_bf16x2(yb[0], yb[1]), pack_bf16x2(yb[2], yb[3])};
+    };
+    for (int ks0 = w; ks0 < nks; ks0 += NWV * U) {
+      u32x4_t xa[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = (ks0 + NWV * u) * 32 + kc * 8;
+        const bool kok = ks0 + NWV * u < nks && k < g.K;
+        xa[u] = xok && kok ? x_chunk(k) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u][a]),
+                                                          __builtin_bit_cast(bf16x8_t, xa[u]),
+                                                          acc[a], 0, 0, 0);
+      if (ks0 + NWV * U < nks) load_w(ks0 + NWV * U);
+    }
   }
 
   // the waves' partial sums meet in LDS; wave 0 finishes
@@ -196,11 +277,15 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
       for (int r = 0; r < 4; ++r)
         if (n + r < g.N) y[r] = acc[0][r];
     }
-  } else if constexpr (EPI == EPI_RESIDUAL) {
+  } else if constexpr (EPI == EPI_RESIDUAL) {   // the residual was read ahead (y_pre)
     float *y = (float *)g.y + (int64_t)m * g.ldy + n;
+    if (n + 3 < g.N && (g.ldy & 3) == 0) {
+      store4(y, y_pre + acc[0]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n + r < g.N) y[r] += acc[0][r];
+      for (int r = 0; r < 4; ++r)
+        if (n + r < g.N) y[r] = y_pre[r] + acc[0][r];
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
     bf16_t *y = (bf16_t *)g.y + (int64_t)m * g.ldy + n;
 #pragma unroll
@@ -211,19 +296,19 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
       }
   } else {   // EPI_QKV_CACHE: row m is sequence m's new token at position positions[m]
     if (n >= g.N) return;
-    const int pos = g.positions[m];
+    const int pos = pos_pre;   // read ahead with the angles cs_pre of the lane's columns
     const bool ok = pos >= 0 && pos < g.cache_seq && pos < g.max_seq;
     if (!ok) g.pos_flag[0] = 1;
     f32x4_t v = acc[0];
     const int dh = g.d_head;
     if (n < g.n0) {   // q column: rotate, keep for the attention
       const float nan = __builtin_nanf("");
-      v = ok ? rope4(v, g.cos_sin, pos, dh, n % dh) : f32x4_t{nan, nan, nan, nan};
+      v = ok ? rope4(v, cs_pre) : f32x4_t{nan, nan, nan, nan};
       store4((bf16_t *)g.y + (int64_t)m * g.ldy + n, v);
     } else if (ok) {  // k (rotated) or v column: into the cache slot of the position
       const bool is_k = n < g.n0 + g.n1;
       const int j = n - g.n0 - (is_k ? 0 : g.n1);
-      if (is_k) v = rope4(v, g.cos_sin, pos, dh, j % dh);
+      if (is_k) v = rope4(v, cs_pre);
       const int grp = j / dh, d = j % dh;
       bf16_t *dst = (bf16_t *)(is_k ? g.k_cache : g.v_cache) +
                     (((int64_t)m * g.n_kv_heads + grp) * g.cache_seq + pos) * dh + d;
@@ -577,11 +662,13 @@ hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s) {
   const int cols = epi == EPI_SWIGLU ? g.n0 : g.N;
   const dim3 grid(grid1(cols, 16), grid1(g.M, 16));
   if (grid.y > 65535) return hipErrorInvalidValue;
-  // Few column blocks (the layers' projections): 8 waves split K with 8 steps each in flight,
-  // so one round of loads covers K <= 2048 on the few CUs that have work. Many blocks (the LM
-  // head) fill the chip anyway: 4 waves with 4 steps each keep the registers, and so the
-  // occupancy, of a streaming kernel.
+  // Few column blocks (the layers' projections): 8 waves split K with 4 or 8 steps each in
+  // flight, so one round of loads covers K <= 2048 on the few CUs that have work. Many blocks
+  // (the LM head) fill the chip anyway: 4 waves with 4 steps each keep the registers, and so
+  // the occupancy, of a streaming kernel.
   if ((int64_t)grid.x * grid.y >= 1024) return run_dgemm<4, 4>(epi, g, grid, s);
+  // 4 steps per wave when they cover K (K <= 1024): fewer registers held for steps past K
+  if (g.K <= 8 * 4 * 32) return run_dgemm<8, 4>(epi, g, grid, s);
   return run_dgemm<8, 8>(epi, g, grid, s);
 }
 
