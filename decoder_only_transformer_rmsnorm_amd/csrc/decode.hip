@@ -328,6 +328,34 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
 // and is summed over the row groups once at the end. The waves' (max, sum, output) meet in
 // LDS: with one split the workgroup writes the normalised output, otherwise a partial record
 // per query head that dec_combine_kernel merges in split order.
+// Lane exchanges without LDS: DPP moves inside 16-lane rows (quad permutations, the half-row
+// mirror, row rotations) and the row / half swaps of v_permlane16/32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// sum over each group of P consecutive lanes (P = 4, 8 or 16), in every lane of the group
+template <int P>
+__device__ __forceinline__ float group_sum(float d) {
+  d += dpp<0xB1>(d);                              // quad_perm [1,0,3,2]: lane ^ 1
+  d += dpp<0x4E>(d);                              // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P >= 8) d += dpp<0x141>(d);      // half-row mirror: the other quad of 8
+  if constexpr (P >= 16) d += dpp<0x128>(d);     // row rotate by 8: the other half row
+  return d;
+}
+// op over the lanes with the same lane % P (P = 4, 8 or 16), in every lane
+template <int P, typename Op>
+__device__ __forceinline__ float across_groups(float v, Op op) {
+  if constexpr (P <= 4) v = op(v, dpp<0x124>(v));   // row rotate by 4
+  if constexpr (P <= 8) v = op(v, dpp<0x128>(v));   // row rotate by 8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 constexpr int dec_regs(int dh, int g) { return 8 * g + dh + (dh / 8) * g + 8 * g + 24; }
 constexpr int dec_waves(int dh, int g) {
   return dec_regs(dh, g) <= 128 ? 16 : dec_regs(dh, g) <= 256 ? 8 : 4;
@@ -345,6 +373,22 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int nwv = blockDim.x >> 6;   // waves of this launch, <= NWV
   const int pc = lane % PPR, rg = lane / PPR;
+  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this kv head
+  // Full causal attention: the first chunk's rows do not depend on the position, so they are
+  // requested before it is read (rows clamped into the cache; rows past the position are
+  // masked below).
+  // (Kernels with many registers per lane skip this: the early rows would spill.)
+  const int c_first = split * cps + w;
+  const bool pre = dec_regs(DH, GM) <= 200 && window == 0 && 64 * c_first < cache_seq;
+  u32x4_t kr[NJ], vr[NJ];
+  if (pre) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      kr[j] = ld16(kc + (head + min(64 * c_first + RPI * j + rg, cache_seq - 1)) * DH + 8 * pc);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      vr[j] = ld16(vc + (head + min(64 * c_first + RPI * j + rg, cache_seq - 1)) * DH + 8 * pc);
+  }
   const int pos = positions[b];
   if (pos < 0 || pos >= cache_seq) {   // no cache slot: NaN output for the group's heads
     if (split == 0)
@@ -357,7 +401,6 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
   const int nch = (n - t0 + 63) / 64;
   const int c_end = min((split + 1) * cps, nch);
 
-  const int64_t head = ((int64_t)b * Hkv + grp) * cache_seq;   // first row of this kv head
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   // this lane's q pieces (raw bf16); converted inside the loop, so the first chunk's K / V
   // loads are issued before anything waits on q
@@ -373,17 +416,18 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  for (int c = split * cps + w; c < c_end; c += nwv) {
+  for (int c = c_first; c < c_end; c += nwv) {
     const int k0 = t0 + 64 * c;
     // rows past the last visible key load that key again (no branch around the loads) and
     // are zeroed afterwards
-    u32x4_t kr[NJ], vr[NJ];
+    if (!(pre && c == c_first)) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      kr[j] = ld16(kc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
+      for (int j = 0; j < NJ; ++j)
+        kr[j] = ld16(kc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      vr[j] = ld16(vc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
+      for (int j = 0; j < NJ; ++j)
+        vr[j] = ld16(vc + (head + min(k0 + RPI * j + rg, n - 1)) * DH + 8 * pc);
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       if (k0 + RPI * j + rg >= n) vr[j] = zero;
@@ -415,8 +459,7 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
-#pragma unroll
-        for (int x = 1; x < PPR; x <<= 1) d += __shfl_xor(d, x);
+        d = group_sum<PPR>(d);
         sc[j][h] = k0 + RPI * j + rg < n ? d : -__builtin_inff();
       }
     }
@@ -425,8 +468,7 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
       float mx = sc[0][h];
 #pragma unroll
       for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, sc[j][h]);
-#pragma unroll
-      for (int x = PPR; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+      mx = across_groups<PPR>(mx, [](float a, float b) { return fmaxf(a, b); });
       const float mn = fmaxf(m[h], mx);        // finite: the chunk has a visible key
       const float alpha = exp2f(m[h] - mn);    // 0 for the first chunk
       m[h] = mn;
@@ -450,14 +492,13 @@ __global__ __launch_bounds__(64 * NWV) void dec_attn_kernel(
     }
   }
   // sums over the row groups (lanes with the same piece)
+  const auto add = [](float a, float b) { return a + b; };
 #pragma unroll
-  for (int h = 0; h < GM; ++h)
+  for (int h = 0; h < GM; ++h) {
+    l[h] = across_groups<PPR>(l[h], add);
 #pragma unroll
-    for (int x = PPR; x < 64; x <<= 1) {
-      l[h] += __shfl_xor(l[h], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], x);
-    }
+    for (int e = 0; e < 8; ++e) acc[h][e] = across_groups<PPR>(acc[h][e], add);
+  }
 
   __shared__ float wm[NWV][GM], wl[NWV][GM];
   __shared__ __attribute__((aligned(16))) float wo[NWV][GM][DH];
