@@ -61,6 +61,34 @@ __device__ __forceinline__ f32x4_t rope4(f32x4_t v, f32x4_t cs) {
                  x2 * cs[3] + x3 * cs[2]};
 }
 
+// Lane exchanges without LDS: DPP moves inside 16-lane rows (quad permutations, the half-row
+// mirror, row rotations) and the row / half swaps of v_permlane16/32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// sum over each group of P consecutive lanes (P = 4, 8 or 16), in every lane of the group
+template <int P>
+__device__ __forceinline__ float group_sum(float d) {
+  d += dpp<0xB1>(d);                              // quad_perm [1,0,3,2]: lane ^ 1
+  d += dpp<0x4E>(d);                              // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P >= 8) d += dpp<0x141>(d);      // half-row mirror: the other quad of 8
+  if constexpr (P >= 16) d += dpp<0x128>(d);     // row rotate by 8: the other half row
+  return d;
+}
+// op over the lanes with the same lane % P (P = 4, 8 or 16), in every lane
+template <int P, typename Op>
+__device__ __forceinline__ float across_groups(float v, Op op) {
+  if constexpr (P <= 4) v = op(v, dpp<0x124>(v));   // row rotate by 4
+  if constexpr (P <= 8) v = op(v, dpp<0x128>(v));   // row rotate by 8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // NWV waves share the workgroup's 16 columns and split K; each wave keeps the loads of U
 // 32-wide k steps in flight together
 template <int EPI, int NWV, int U>
@@ -317,6 +345,95 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
   }
 }
 
+// Wide plain-store products (the LM head over the vocabulary): a workgroup of 4 waves owns 64
+// output columns and each wave streams 16 of them over the whole K, U 32-wide k steps in
+// flight. The block's activation rows (at most 16, `rows` of them held) are RMS-normalised
+// once per workgroup into LDS (bf16, rows padded by 16 bytes so the 16 rows of a fragment read
+// fall on distinct banks), instead of once per 16 columns. Row r is normalised by the 16
+// consecutive lanes of threads 16 r .. 16 r + 15 (a DPP row), which sum its squares without
+// LDS. Lanes of rows past `rows` read row rows - 1: their products are never stored.
+constexpr int kWideCols = 64;
+template <int U>
+__global__ __launch_bounds__(256) void dgemv_wide_kernel(DecodeGemmArgs g, int rows) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  bf16_t *xs = (bf16_t *)dyn_lds;
+  const int KP = g.K + 8;   // padded row pitch (elements)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kc = lane >> 4;
+  const int nb = blockIdx.x * kWideCols + w * 16;   // this wave's first output column
+  const int m0 = blockIdx.y * 16;
+  const int nks = (g.K + 31) / 32;
+  const bool wok = nb + r16 < g.N;
+  const bf16_t *wrow = (const bf16_t *)g.w0 + (int64_t)(wok ? nb + r16 : 0) * g.K;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  u32x4_t wa[U];
+  auto load_w = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + u) * 32 + kc * 8;
+      wa[u] = wok && s0 + u < nks && k < g.K ? ld16(wrow + k) : zero;
+    }
+  };
+  load_w(0);   // in flight while the activations are normalised
+
+  // activations: thread t handles row t / 16 of the block, 4 columns of every 64
+  {
+    const int row = tid >> 4, part = tid & 15;
+    const int m = m0 + row;
+    bf16_t *dst = xs + row * KP;
+    if (row >= rows) {
+    } else if (g.norm_x) {
+      const float *xr = g.norm_x + (int64_t)(m < g.M ? m : 0) * g.ldx;
+      float ss = 0.f;
+      for (int k = 4 * part; k < g.K; k += 64) {
+        const f32x4_t v = m < g.M ? load4(xr + k) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+      }
+      ss = group_sum<16>(ss);
+      const float rinv = rsqrtf(ss / (float)g.K + g.eps);
+      for (int k = 4 * part; k < g.K; k += 64) {
+        const f32x4_t v = m < g.M ? load4(xr + k) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const f32x4_t gg = load4((const bf16_t *)g.norm_g + k);
+        const f32x4_t y = v * rinv * gg;
+        *(u32x2_t *)(dst + k) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+    } else {
+      const bf16_t *xr = (const bf16_t *)g.x + (int64_t)(m < g.M ? m : 0) * g.ldx;
+      for (int k = 4 * part; k < g.K; k += 64)
+        *(u32x2_t *)(dst + k) = m < g.M ? *(const u32x2_t *)(xr + k) : u32x2_t{0u, 0u};
+    }
+  }
+  // LDS only: the weight loads stay in flight across this barrier
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16_t *xrow = xs + min(r16, rows - 1) * KP + kc * 8;
+  for (int s0 = 0; s0 < nks; s0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + u) * 32;
+      const u32x4_t xa = s0 + u < nks && k + kc * 8 < g.K ? *(const u32x4_t *)(xrow + k) : zero;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
+                                                   __builtin_bit_cast(bf16x8_t, xa), acc, 0, 0, 0);
+    }
+    if (s0 + U < nks) load_w(s0 + U);
+  }
+  // lane holds columns n .. n+3 of row m
+  const int m = m0 + r16, n = nb + 4 * kc;
+  if (m >= g.M) return;
+  if (g.y_dt == DT_BF16) {
+    bf16_t *y = (bf16_t *)g.y + (int64_t)m * g.ldy + n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < g.N) y[r] = f32_to_bf16(acc[r]);
+  } else {
+    float *y = (float *)g.y + (int64_t)m * g.ldy + n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < g.N) y[r] = acc[r];
+  }
+}
+
 // ---- decode attention
 // Workgroup = (split s, kv head grp, sequence b) with NWV waves; a wave takes 64-key chunks of
 // the visible keys (chunk c covers keys t0 + 64 c ..), chunks s*cps .. (s+1)*cps - 1 of the
@@ -328,34 +445,6 @@ __global__ __launch_bounds__(64 * NWV) void dgemm_kernel(DecodeGemmArgs g) {
 // and is summed over the row groups once at the end. The waves' (max, sum, output) meet in
 // LDS: with one split the workgroup writes the normalised output, otherwise a partial record
 // per query head that dec_combine_kernel merges in split order.
-// Lane exchanges without LDS: DPP moves inside 16-lane rows (quad permutations, the half-row
-// mirror, row rotations) and the row / half swaps of v_permlane16/32_swap.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-// sum over each group of P consecutive lanes (P = 4, 8 or 16), in every lane of the group
-template <int P>
-__device__ __forceinline__ float group_sum(float d) {
-  d += dpp<0xB1>(d);                              // quad_perm [1,0,3,2]: lane ^ 1
-  d += dpp<0x4E>(d);                              // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (P >= 8) d += dpp<0x141>(d);      // half-row mirror: the other quad of 8
-  if constexpr (P >= 16) d += dpp<0x128>(d);     // row rotate by 8: the other half row
-  return d;
-}
-// op over the lanes with the same lane % P (P = 4, 8 or 16), in every lane
-template <int P, typename Op>
-__device__ __forceinline__ float across_groups(float v, Op op) {
-  if constexpr (P <= 4) v = op(v, dpp<0x124>(v));   // row rotate by 4
-  if constexpr (P <= 8) v = op(v, dpp<0x128>(v));   // row rotate by 8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 constexpr int dec_regs(int dh, int g) { return 8 * g + dh + (dh / 8) * g + 8 * g + 24; }
 constexpr int dec_waves(int dh, int g) {
   return dec_regs(dh, g) <= 128 ? 16 : dec_regs(dh, g) <= 256 ? 8 : 4;
@@ -707,7 +796,18 @@ hipError_t launch_decode_gemm(int epi, const DecodeGemmArgs &g, hipStream_t s) {
   // flight, so one round of loads covers K <= 2048 on the few CUs that have work. Many blocks
   // (the LM head) fill the chip anyway: 4 waves with 4 steps each keep the registers, and so
   // the occupancy, of a streaming kernel.
-  if ((int64_t)grid.x * grid.y >= 1024) return run_dgemm<4, 4>(epi, g, grid, s);
+  if ((int64_t)grid.x * grid.y >= 1024) {
+    // plain stores over many columns (the LM head): the wide kernel when the block's
+    // activation rows fit in 64 KB of LDS
+    const int rows = g.M < 16 ? g.M : 16;
+    const size_t lds = (size_t)rows * (g.K + 8) * 2;
+    if (epi == EPI_STORE && g.K % 8 == 0 && lds <= 65536) {
+      const dim3 gw(grid1(g.N, kWideCols), grid1(g.M, 16));
+      dgemv_wide_kernel<8><<<gw, 256, lds, s>>>(g, rows);
+      return hipGetLastError();
+    }
+    return run_dgemm<4, 4>(epi, g, grid, s);
+  }
   // 4 steps per wave when they cover K (K <= 1024): fewer registers held for steps past K
   if (g.K <= 8 * 4 * 32) return run_dgemm<8, 4>(epi, g, grid, s);
   return run_dgemm<8, 8>(epi, g, grid, s);
