@@ -333,29 +333,28 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
     const int i0 = (i_lo + it % n_it) * kTile;
     if (i0 + kTile - 1 < kw0) continue;                                  // queries before keys
     if (window > 0 && i0 > kw0 + 31 + window - 1) continue;              // keys too old for all
-    // S and dP: lane = key, 16 queries per 32-query block
-    f32x16_t sa[2], pa[2];
+    // per 32-query block qb: S and dP (lane = key, 16 queries), then P and dS = P (dP - D)
+    // (queries that do not see this key, or past S, get 0), then dV^T += dO^T P and
+    // dK^T += Q^T dS over the block's 32 queries; one block at a time keeps the registers
+    // of a single pair of score accumulators
+    const bool edge = i0 < kw0 + 31 || (window > 0 && i0 + kTile - 1 > kw0 - 1 + window - 1) ||
+                      i0 + kTile > S;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      f32x16_t sa, pa;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sa[qb][e] = pa[qb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sa[e] = pa[e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const u32x4_t qa = frag_rows<DH>(qt, 32 * qb, kk, lane);
         const u32x4_t oa = frag_rows<DH>(ot, 32 * qb, kk, lane);
-        sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa),
-                                                         __builtin_bit_cast(bf16x8_t, kf[kk]),
-                                                         sa[qb], 0, 0, 0);
-        pa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, oa),
-                                                         __builtin_bit_cast(bf16x8_t, vf[kk]),
-                                                         pa[qb], 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa),
+                                                     __builtin_bit_cast(bf16x8_t, kf[kk]), sa,
+                                                     0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, oa),
+                                                     __builtin_bit_cast(bf16x8_t, vf[kk]), pa,
+                                                     0, 0, 0);
       }
-    }
-    // P and dS = P (dP - D); queries that do not see this key (or past S) get 0
-    const bool edge = i0 < kw0 + 31 || (window > 0 && i0 + kTile - 1 > kw0 - 1 + window - 1) ||
-                      i0 + kTile > S;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int qr = 32 * qb + 8 * x + 4 * h;   // first of the 4 query rows of group x
@@ -364,27 +363,28 @@ __global__ __launch_bounds__(256, DH >= 128 ? 1 : 2) void attn_dkdv_mfma_kernel(
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
           const int e = 4 * x + y, qi = i0 + qr + y;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[qb][e], sl2, -l4[y]));
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], sl2, -l4[y]));
           if (edge && (my_k > qi || qi >= S || (window > 0 && my_k < qi - window + 1))) p = 0.f;
-          sa[qb][e] = p;
-          pa[qb][e] = p * (pa[qb][e] - d4[y]);
+          sa[e] = p;
+          pa[e] = p * (pa[e] - d4[y]);
         }
       }
-    // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
-    for (int ks = 0; ks < kTile / 16; ++ks) {
-      const u32x4_t bp = pack_step(sa[ks >> 1], ks & 1);
-      const u32x4_t bd = pack_step(pa[ks >> 1], ks & 1);
+      for (int half = 0; half < 2; ++half) {
+        const int ks = 2 * qb + half;
+        const u32x4_t bp = pack_step(sa, half);
+        const u32x4_t bd = pack_step(pa, half);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x4_t ao = frag_tr<DH>(ot, db, ks, lane);
-        const u32x4_t aq = frag_tr<DH>(qt, db, ks, lane);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ao),
-                                                         __builtin_bit_cast(bf16x8_t, bp), dv[db],
-                                                         0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq),
-                                                         __builtin_bit_cast(bf16x8_t, bd), dk[db],
-                                                         0, 0, 0);
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4_t ao = frag_tr<DH>(ot, db, ks, lane);
+          const u32x4_t aq = frag_tr<DH>(qt, db, ks, lane);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ao),
+                                                           __builtin_bit_cast(bf16x8_t, bp),
+                                                           dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq),
+                                                           __builtin_bit_cast(bf16x8_t, bd),
+                                                           dk[db], 0, 0, 0);
+        }
       }
     }
   }
