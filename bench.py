@@ -25,7 +25,10 @@ Besides the step time it reports:
 With --counters it runs only what the hardware-counter passes need: a plain device copy of a
 known size (the scale reference for the HBM byte counters), then two traced forward steps
 (no warm-up) whose dispatches a counter summary attributes to kernel families by launch order;
-it prints the launch labels of one step and exits without a JSON line.
+it prints the launch labels of one step and exits without a JSON line. --attention-counters
+likewise runs only ten launches of the step's causal attention. --train-only N and
+--decode-only N run only the training leg or the decode leg (for kernel traces) and print
+their mean step time.
 """
 from __future__ import annotations
 
@@ -210,6 +213,15 @@ def main() -> int:
                          "is shared by two output tiles)")
     ap.add_argument("--counters", action="store_true",
                     help="only a 1 GiB copy and 2 forward steps, for rocprofv3 --pmc passes")
+    ap.add_argument("--attention-counters", action="store_true",
+                    help="only 10 launches of the step's causal attention (random q, k, v of "
+                         "the workload's shape), for rocprofv3 --pmc passes")
+    ap.add_argument("--train-only", type=int, default=0, metavar="N",
+                    help="only N training steps after 2 warm-up steps (for kernel traces of the "
+                         "training step); prints the mean step time")
+    ap.add_argument("--decode-only", type=int, default=0, metavar="N",
+                    help="only a prefill of S - 24 positions and N decode steps after 3 warm-up "
+                         "steps (for kernel traces of the decode step); prints the mean step time")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -246,6 +258,51 @@ def main() -> int:
     def step():
         dm.forward(logits=logits, ld_logits=ld_logits)
 
+    if args.attention_counters:   # counter-pass mode: the step's attention alone
+        qd, kvd = cfg.n_heads * cfg.d_head, cfg.n_kv_heads * cfg.d_head
+        W = qd + 2 * kvd
+        qkv = torch.randn((M, W), device="cuda").to(torch.bfloat16)
+        o = torch.empty((M, qd), dtype=torch.bfloat16, device="cuda")
+        for _ in range(10):
+            tfm.tfm_causal_attention(
+                qkv[:, :qd].view(B, S, qd), qkv[:, qd:qd + kvd].view(B, S, kvd),
+                qkv[:, qd + kvd:].view(B, S, kvd), cfg.n_heads, cfg.n_kv_heads, cfg.d_head,
+                o=o.view(B, S, qd), q_stride=W, kv_stride=W, o_stride=qd)
+        torch.cuda.synchronize()
+        log("attention counters run done: 10 launches")
+        return 0
+    if args.train_only > 0:   # kernel-trace mode: the training leg alone
+        trn = tfm.Trainer(dm, lr=1e-4, weight_decay=0.1, max_norm=1.0)
+        t_tg = tfm.next_token_targets(dm.ids)
+        for _ in range(2):
+            trn.step(dm.ids, t_tg)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.train_only):
+            trn.step(dm.ids, t_tg)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.train_only
+        print(json.dumps({"train_only": cfg.name, "steps": args.train_only,
+                          "ms_per_step": round(ms, 3)}), flush=True)
+        return 0
+    if args.decode_only > 0:   # kernel-trace mode: the decode leg alone (as timed below)
+        p0 = S - 24
+        cache = dm.kv_cache(B, S)
+        dm.prefill(cache, S, ids=dm.ids[:, :p0].contiguous(), logits=False)
+        dlg = torch.empty((B, cfg.vocab), dtype=torch.bfloat16, device="cuda")
+        dpos = torch.full((B,), p0, dtype=torch.int32, device="cuda")
+        dtok = dm.ids[:, p0].contiguous()
+        for _ in range(3):
+            dm.decode(cache, S, dtok, dpos, logits=dlg)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.decode_only):
+            dm.decode(cache, S, dtok, dpos, logits=dlg)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.decode_only
+        print(json.dumps({"decode_only": cfg.name, "context": p0 + 1, "steps": args.decode_only,
+                          "ms_per_step": round(ms, 4)}), flush=True)
+        return 0
     if args.counters:
         src = torch.randn(COPY_BYTES // 4, device="cuda")
         dst = torch.empty_like(src)
