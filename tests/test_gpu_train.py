@@ -67,7 +67,7 @@ def _compare(cfg, tr, grads_ref, rel_bar, cos_bar=None):
     return worst
 
 
-def _grad_case(cfg, seed, rel_bar, cos_bar=None, drop=()):
+def _grad_case(cfg, seed, rel_bar, cos_bar=None, drop=(), oob=()):
     tfm = tfm_mod()
     inp = synth.make_inputs(cfg, seed=seed, gamma_std=0.1)
     dm = tfm.DeviceModel(inp)
@@ -75,6 +75,8 @@ def _grad_case(cfg, seed, rel_bar, cos_bar=None, drop=()):
     t = oracle.next_token_targets(inp.ids)
     for b, s in drop:
         t[b, s] = -1
+    for b, s in oob:   # a target past the vocabulary counts as no target
+        t[b, s] = cfg.vocab + 3
     loss = tr.backward(dm.ids, torch.from_numpy(t).cuda())
     torch.cuda.synchronize()
     ref_loss, grads = oracle.model_grads(cfg, oracle.params_of(inp), inp.ids, t)
@@ -102,6 +104,15 @@ def test_gradients_bf16(kv, dh):
                             1000, 3, 100)
     say(f"gradients bf16 kv={kv} dh={dh}")
     _grad_case(cfg, 2, 2.5e-2, cos_bar=0.9995)
+
+
+def test_gradients_bf16_ignored_targets():
+    """bf16 loss through the fused cross-entropy and its recomputed gradient: rows without a
+    target (-1) and a row whose target lies past the vocabulary are not counted and get no
+    gradient."""
+    cfg = synth.ModelConfig("train_bf16_ign", "bf16", 2, 256, 4, 2, 64, 704, 1000, 3, 100)
+    say("gradients bf16 with ignored and out-of-range targets")
+    _grad_case(cfg, 5, 2.5e-2, cos_bar=0.9995, drop=[(0, 7), (2, 50)], oob=[(1, 20)])
 
 
 def test_gradients_bf16_split_k_weight_products():
