@@ -419,7 +419,6 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
   constexpr int WM = BM / WGM, WN = BN / WGN;      // wave sub-tile
   constexpr int NBM = WM / MS, NBN = WN / MS;      // MS x MS blocks per wave
   static_assert(NBM * MS * WGM == BM && NBN * MS * WGN == BN, "wave grid does not tile");
-  static_assert(EPI != EPI_XENT || MS == 32, "the cross-entropy epilogue pairs lanes l, l^32");
   static_assert(EPI != EPI_SWIGLU || MS == 32 || WN % 64 == 0,
                 "16x16 SwiGLU pairs gate/up blocks inside 64-row groups");
   static_assert(WGM % 2 == 0, "the two-pass epilogue splits the waves along M");
@@ -904,37 +903,49 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
 
   if constexpr (EPI == EPI_XENT) {
     // ---- cross-entropy partials ("LLM 2" Optimize / Loss: logsumexp with the max taken
-    //      out). Lane holds row m = m0 + wm*WM + bm*32 + l32 and the columns
-    //      n = n0 + wn*WN + bn*32 + 8q + 4h + r. Per row: max over the lane's columns, over
-    //      the two lane halves (permlane32 swap), then over the WGN waves along N (LDS);
-    //      the same for the sum of exp(logit - max). The logits stay in registers. Column
-    //      bounds are only checked in the last column tile.
+    //      out). Lane holds row m = m0 + wm*WM + bm*MS + l32 and the columns
+    //      n = n0 + wn*WN + bn*32 + 8q + 4h + r (32x32 blocks) or n0 + wn*WN + bn*16 + 4h + r
+    //      (16x16 blocks). Per row: max over the lane's columns, over the lanes that hold the
+    //      row's other columns (permlane swaps: the two lane halves, and for 16x16 blocks the
+    //      four 16-lane rows), then over the WGN waves along N (LDS); the same for the sum of
+    //      exp(logit - max). The logits stay in registers. Column bounds are only checked in
+    //      the last column tile.
     constexpr float kLog2e = 1.4426950408889634f;
     float *red = (float *)lds;   // [BM][WGN]
     const int nw0 = n0 + wn * WN;
     const bool full = n0 + BN <= g.N;
-    auto col_ok = [&](int bn, int e) {
-      return full || nw0 + bn * 32 + 8 * (e >> 2) + 4 * h + (e & 3) < g.N;
+    auto col_of = [&](int bn, int e) {   // column of element e of block bn, within the wave
+      return MS == 32 ? bn * 32 + 8 * (e >> 2) + 4 * h + (e & 3) : bn * 16 + 4 * h + e;
+    };
+    auto col_ok = [&](int bn, int e) { return full || nw0 + col_of(bn, e) < g.N; };
+    // the same op over the lanes holding the row's columns
+    auto lanes_op = [&](float v, auto op) {
+      if constexpr (MS == 16) {
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                          false, false);
+        v = op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      }
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+      return op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     };
     float rmax[NBM];
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
-      const int rt = wm * WM + bm * 32 + l32;
+      const int rt = wm * WM + bm * MS + l32;
       float mx = -__builtin_inff();
 #pragma unroll
       for (int bn = 0; bn < NBN; ++bn)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
+        for (int e = 0; e < AE; ++e)
           if (col_ok(bn, e)) mx = fmaxf(mx, acc[bn][bm][e]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mx = lanes_op(mx, [](float x, float y) { return fmaxf(x, y); });
       if (h == 0) red[rt * WGN + wn] = mx;
     }
     __syncthreads();
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
-      const int rt = wm * WM + bm * 32 + l32;
+      const int rt = wm * WM + bm * MS + l32;
       float mx = -__builtin_inff();
 #pragma unroll
       for (int w = 0; w < WGN; ++w) mx = fmaxf(mx, red[rt * WGN + w]);
@@ -943,29 +954,28 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
     __syncthreads();
 #pragma unroll
     for (int bm = 0; bm < NBM; ++bm) {
-      const int rt = wm * WM + bm * 32 + l32;
+      const int rt = wm * WM + bm * MS + l32;
       const int64_t m = m0 + rt;
       const float mc = rmax[bm] * kLog2e;
       float se = 0.f;
 #pragma unroll
       for (int bn = 0; bn < NBN; ++bn)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
+        for (int e = 0; e < AE; ++e)
           if (col_ok(bn, e)) se += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bn][bm][e], kLog2e, -mc));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(se), __float_as_uint(se),
-                                                       false, false);
-      se = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      se = lanes_op(se, [](float x, float y) { return x + y; });
       if (h == 0) red[rt * WGN + wn] = se;
       // the row's target logit, if its column is one of this wave's (rare: one column tile)
       const int tr = (m < g.M ? g.targets[m] : -1) - nw0;
-      const bool mine = tr >= 0 && tr < WN && ((tr >> 2) & 1) == h;
+      const int th = MS == 32 ? (tr >> 2) & 1 : (tr & 15) >> 2;   // lane group holding it
+      const bool mine = tr >= 0 && tr < WN && th == h;
       if (__any(mine)) {
         float tv = 0.f;
 #pragma unroll
         for (int bn = 0; bn < NBN; ++bn)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (tr == bn * 32 + 8 * (e >> 2) + 4 * h + (e & 3)) tv = acc[bn][bm][e];
+          for (int e = 0; e < AE; ++e)
+            if (tr == col_of(bn, e)) tv = acc[bn][bm][e];
         if (mine) g.x_tgt[m] = tv;
       }
     }
@@ -973,7 +983,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
     if (wn == 0 && h == 0) {
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm) {
-        const int rt = wm * WM + bm * 32 + l32;
+        const int rt = wm * WM + bm * MS + l32;
         const int64_t m = m0 + rt;
         if (m >= g.M) continue;
         float se = 0.f;
@@ -1538,7 +1548,10 @@ hipError_t dispatch_bf16(int epi, const GemmArgs &g, hipStream_t s) {
       if (g.K % 64 == 0 && g.kparts <= 1)
         return run_bf16<256, 256, 64, 2, EPI_SWIGLU, 1, false, 2, 4, false, 16, true>(g, s);
       return run_bf16<256, 256, 32, 4, EPI_SWIGLU, 1, false, 2, 4, true, 16>(g, s);
-    case EPI_XENT: return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
+    case EPI_XENT:
+      if (g.K % 64 == 0 && g.kparts <= 1)
+        return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, false, 2, 2, false, 16, true>(g, s);
+      return run_bf16<kXentBM, kXentBN, 64, 2, EPI_XENT, 2, true>(g, s);
     case EPI_SWIGLU_BACK:
       if (g.y_dt != DT_BF16 || !g.keep_a || !g.keep_c || g.ldy < 2 * (int64_t)g.N ||
           g.N % 4 != 0 || g.ldy % 4 != 0)
