@@ -74,10 +74,38 @@ __device__ __forceinline__ void store4(bf16_t *p, f32x4_t v) {
   *(uint2 *)p = u;
 }
 
+// Lane exchanges without LDS: DPP moves inside 16-lane rows (quad permutations, the half-row
+// mirror, row rotations) and the row / half swaps of v_permlane16/32_swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// sum over each group of P consecutive lanes (P = 4, 8 or 16), in every lane of the group
+template <int P>
+__device__ __forceinline__ float group_sum(float d) {
+  d += dpp<0xB1>(d);                              // quad_perm [1,0,3,2]: lane ^ 1
+  d += dpp<0x4E>(d);                              // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P >= 8) d += dpp<0x141>(d);      // half-row mirror: the other quad of 8
+  if constexpr (P >= 16) d += dpp<0x128>(d);     // row rotate by 8: the other half row
+  return d;
+}
+// op over the lanes with the same lane % P (P = 4, 8 or 16), in every lane
+template <int P, typename Op>
+__device__ __forceinline__ float across_groups(float v, Op op) {
+  if constexpr (P <= 4) v = op(v, dpp<0x124>(v));   // row rotate by 4
+  if constexpr (P <= 8) v = op(v, dpp<0x128>(v));   // row rotate by 8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// sum over the 64 lanes of the wave, in every lane (DPP and permlane swaps, no LDS)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = group_sum<16>(v);
+  return across_groups<16>(v, [](float a, float b) { return a + b; });
 }
 
 }  // namespace tfm

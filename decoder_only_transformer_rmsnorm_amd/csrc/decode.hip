@@ -61,34 +61,6 @@ __device__ __forceinline__ f32x4_t rope4(f32x4_t v, f32x4_t cs) {
                  x2 * cs[3] + x3 * cs[2]};
 }
 
-// Lane exchanges without LDS: DPP moves inside 16-lane rows (quad permutations, the half-row
-// mirror, row rotations) and the row / half swaps of v_permlane16/32_swap.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-// sum over each group of P consecutive lanes (P = 4, 8 or 16), in every lane of the group
-template <int P>
-__device__ __forceinline__ float group_sum(float d) {
-  d += dpp<0xB1>(d);                              // quad_perm [1,0,3,2]: lane ^ 1
-  d += dpp<0x4E>(d);                              // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (P >= 8) d += dpp<0x141>(d);      // half-row mirror: the other quad of 8
-  if constexpr (P >= 16) d += dpp<0x128>(d);     // row rotate by 8: the other half row
-  return d;
-}
-// op over the lanes with the same lane % P (P = 4, 8 or 16), in every lane
-template <int P, typename Op>
-__device__ __forceinline__ float across_groups(float v, Op op) {
-  if constexpr (P <= 4) v = op(v, dpp<0x124>(v));   // row rotate by 4
-  if constexpr (P <= 8) v = op(v, dpp<0x128>(v));   // row rotate by 8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // NWV waves share the workgroup's 16 columns and split K; each wave keeps the loads of U
 // 32-wide k steps in flight together
 template <int EPI, int NWV, int U>
