@@ -1019,13 +1019,15 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
       constexpr int NQ = EPI == EPI_QKV_ROPE ? NBN * (AE / 4) : 1;
       f32x4_t csr[2][NQ];
       bool pok[2] = {true, true};
-      auto load_cs = [&](int bm, f32x4_t (&c)[NQ], bool &ok) {
-        // rows fit in 32 bits here (M * row width < 2^31 elements); no 64-bit division
-        const int64_t m = m0 + wm * WM + bm * MS + l32;
-        const int mc = (int)(m < g.M ? m : g.M - 1);
-        int pos = g.positions ? g.positions[mc] : mc % g.S;
-        ok = pos >= 0 && pos < g.max_seq;
-        pos = ok ? pos : 0;
+      // The integer divisions are taken once per lane, not per row block: a column group's
+      // offset in a position's (cos, sin) row is the same for every row (its column within the
+      // head; columns come in groups of 4 and d_head is even, so it is the pair index times 2),
+      // and without a positions array the rows of block bm are tokens MS bm further on, i.e.
+      // the first block's position stepped with wrap-around at S. Rows fit in 32 bits here
+      // (M * row width < 2^31 elements).
+      int cso[NQ];
+      int pbase = 0;
+      if constexpr (EPI == EPI_QKV_ROPE) {
         const int dmask = g.d_head - 1;
         const bool pow2 = (g.d_head & dmask) == 0;
 #pragma unroll
@@ -1033,10 +1035,23 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
 #pragma unroll
           for (int q = 0; q < AE / 4; ++q) {
             const int n = n0 + wn * WN + bn * MS + (MS == 32 ? 8 * q + 4 * h : 4 * h);
-            const int i0 = (pow2 ? (n & dmask) : n % g.d_head) >> 1;
-            c[bn * (AE / 4) + q] =
-                *(const f32x4_t *)(g.cos_sin + ((int64_t)pos * (g.d_head >> 1) + i0) * 2);
+            cso[bn * (AE / 4) + q] = pow2 ? (n & dmask) : n % g.d_head;
           }
+        if (!g.positions) pbase = (int)(m0 + wm * WM + l32) % g.S;
+      }
+      auto load_cs = [&](int bm, f32x4_t (&c)[NQ], bool &ok) {
+        int pos;
+        if (g.positions) {
+          const int64_t m = m0 + wm * WM + bm * MS + l32;
+          pos = g.positions[m < g.M ? m : g.M - 1];
+        } else {
+          pos = pbase + bm * MS;
+          while (pos >= g.S) pos -= g.S;
+        }
+        ok = pos >= 0 && pos < g.max_seq;
+        const float *row = g.cos_sin + (int64_t)(ok ? pos : 0) * g.d_head;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) c[i] = *(const f32x4_t *)(row + cso[i]);
       };
       if constexpr (EPI == EPI_QKV_ROPE) load_cs(0, csr[0], pok[0]);
       // RMSNorm split across the products: each of the lane's rows gets 1 / rms(x) from the
