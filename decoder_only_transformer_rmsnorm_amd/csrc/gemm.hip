@@ -1135,7 +1135,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
                 }
               }
             }
-            uint8_t *dst = lds + stage_off(r, col * ob, rb);
+            // bf16: rows with bit 3 set keep the two 8-byte halves of their chunks swapped,
+            // so the 16 rows of one 8-byte store cover distinct banks (rows r and r ^ 8 would
+            // otherwise share them); the reading pass swaps them back
+            uint8_t *dst = lds + (stage_off(r, col * ob, rb) ^ (out_bf16 ? (r & 8) : 0));
             if (out_bf16) {
               uint2 u;
               u.x = pack_bf16x2(v[0], v[1]);
@@ -1283,7 +1286,8 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
       const int64_t m = m0 + p * prow + r;
       const int n = nout0 + c * epc;
       if (m >= g.M || n >= ncols) continue;
-      const uint4 raw = *(const uint4 *)(lds + stage_off(r, c * 16, rb));
+      uint4 raw = *(const uint4 *)(lds + stage_off(r, c * 16, rb));
+      if (out_bf16 && (r & 8)) raw = uint4{raw.z, raw.w, raw.x, raw.y};
       const int64_t off = m * g.ldy + n;
       if (out_bf16) {
         bf16_t *y = (bf16_t *)g.y + off;
