@@ -105,8 +105,11 @@ def step_kernels(cfg, batch: int | None = None, seq: int | None = None,
     window = getattr(cfg, "window", 0)
     k = {}
     k["fill_flags"] = {"launches": 1, "flops": 0, "bytes": 8}
-    k["embed"] = {"launches": 1, "flops": 0, "bytes": M * 4 + M * D * e + M * D * 4}
-    k["rmsnorm"] = {"launches": 2 if split else 2 * L + 1, "flops": 0, "bytes": rms + D * e}
+    # the embedding pass also writes the first block's normalised input (when there is a block)
+    k["embed"] = {"launches": 1, "flops": 0,
+                  "bytes": M * 4 + M * D * e + M * D * 4 + (M * D * e + D * e if L else 0)}
+    k["rmsnorm"] = {"launches": (1 if split else 2 * L) if L else 1, "flops": 0,
+                    "bytes": rms + D * e}
     rope_table = S * cfg.d_head * 4       # (cos, sin) of every position 0..S-1
     k["gemm_qkv_rope"] = {"launches": L, "flops": 2 * M * D * W,
                           "bytes": M * D * e + W * D * e + M * W * e + rope_table

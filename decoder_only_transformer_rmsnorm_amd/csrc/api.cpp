@@ -172,10 +172,11 @@ LayerCache layer_cache(const tfm_config *c, void *cache, int B, int cache_seq, i
 // norm_in: the previous block's down projection already left bf16(x * g_attn) in xn and
 // its row partials in nrm (split RMSNorm). g_next: the gain of the next block's first
 // RMSNorm, split into this block's down projection the same way (nullptr: not split).
+// xn_ready: xn already holds RMSNorm(x; g_attn) (the embedding pass wrote it).
 int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
                   const int32_t *positions, int B, int S, const float *cos_sin, uint8_t *ws,
                   const WsPlan &p, int window, hipStream_t s, const LayerCache &lc = {},
-                  bool norm_in = false, const void *g_next = nullptr) {
+                  bool norm_in = false, const void *g_next = nullptr, bool xn_ready = false) {
   const int64_t M = (int64_t)B * S;
   const int D = c->d_model, dt = c->dtype;
   const int qd = c->n_heads * c->d_head, kvd = c->n_kv_heads * c->d_head;
@@ -196,7 +197,8 @@ int enqueue_block(const tfm_config *c, const tfm_layer_weights *w, float *x,
     g.nrm_g = gain; g.nrm_y = xn; g.nrm_part = nrm;
   };
 
-  if (!norm_in) TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
+  if (!norm_in && !xn_ready)
+    TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_attn, dt, xn, dt, M, D, c->eps, s));
 
   GemmArgs g{};
   g.a = xn; g.lda = D; g.w0 = w->wq; g.w1 = w->wk; g.w2 = w->wv; g.n0 = qd; g.n1 = kvd;
@@ -252,14 +254,20 @@ int enqueue_trunk(const tfm_config *c, const tfm_model_weights *w, const int32_t
   const int64_t M = (int64_t)B * S;
   float *x = (float *)(wsb + p.x);
   TFM_LAUNCH("fill_flags", launch_fill_i32((int32_t *)(wsb + p.flag), 2, 0, s));   // token and position flags
-  TFM_LAUNCH("embed", launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
-                                   (int32_t *)(wsb + p.flag), s));
+  // the embedding pass also writes the first block's RMSNorm(x; g_attn) into xn
+  if (c->n_layers > 0)
+    TFM_LAUNCH("embed", launch_embed_rmsnorm(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
+                                             (int32_t *)(wsb + p.flag), w->layers[0].g_attn,
+                                             wsb + p.xn, c->eps, s));
+  else
+    TFM_LAUNCH("embed", launch_embed(ids, M, w->embed, c->dtype, c->vocab, c->d_model, x,
+                                     (int32_t *)(wsb + p.flag), s));
   const bool split = norm_split(c);
   for (int l = 0; l < c->n_layers; ++l) {
     const void *g_next = split && l + 1 < c->n_layers ? w->layers[l + 1].g_attn : nullptr;
     TFM_TRY(enqueue_block(c, &w->layers[l], x, positions, B, S, cos_sin, wsb, p,
                           layer_window(c, l), s, layer_cache(c, kv_cache, B, cache_seq, l),
-                          split && l > 0, g_next));
+                          split && l > 0, g_next, l == 0));
   }
   TFM_LAUNCH("rmsnorm", launch_rmsnorm(x, DT_F32, w->g_final, c->dtype, wsb + p.xn, c->dtype, M,
                                        c->d_model, c->eps, s));

@@ -86,6 +86,63 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX *__restrict__ x,
     store4(yr + 4 * gi, load4(xr + 4 * gi) * inv * load4(g + 4 * gi));
 }
 
+// Embedding followed by the first block's RMSNorm ("Transformer 篇" 5.2 and 5.6) in one pass:
+// one wave per token gathers its table row, writes it to the fp32 residual x and writes
+// y = RMSNorm(x; g) — the same loads, sum order and rounding as embed_kernel followed by
+// rmsnorm_kernel (the table values convert to fp32 exactly), without reading x back. A bad id
+// gives a NaN row (and NaN y) and sets the flag.
+template <int VPT, typename TT, typename TG, typename TY>
+__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const int32_t *__restrict__ ids,
+                                                            int64_t rows,
+                                                            const TT *__restrict__ table,
+                                                            int vocab, int d, float *__restrict__ x,
+                                                            int32_t *err, const TG *__restrict__ g,
+                                                            TY *__restrict__ y, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int id = ids[row];
+  const bool ok = id >= 0 && id < vocab;
+  if (!ok && lane == 0 && err) *err = 1;
+  const TT *tr = table + (int64_t)(ok ? id : 0) * d;
+  float *xr = x + row * d;
+  TY *yr = y + row * d;
+  const int ng = d >> 2;
+  const float nan = __builtin_nanf("");
+  const f32x4_t bad = {nan, nan, nan, nan};
+  f32x4_t c[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int gi = lane + 64 * i;
+    c[i] = load4(tr + 4 * (gi < ng ? gi : 0));
+    if (!ok) c[i] = bad;
+    if (gi >= ng) c[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < ng) store4(xr + 4 * gi, c[i]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
+  for (int gi = lane + 64 * VPT; gi < ng; gi += 64) {
+    const f32x4_t v = ok ? load4(tr + 4 * gi) : bad;
+    store4(xr + 4 * gi, v);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int gi = lane + 64 * i;
+    if (gi < ng) store4(yr + 4 * gi, c[i] * inv * load4(g + 4 * gi));
+  }
+  for (int gi = lane + 64 * VPT; gi < ng; gi += 64)
+    store4(yr + 4 * gi, (ok ? load4(tr + 4 * gi) : bad) * inv * load4(g + 4 * gi));
+}
+
 // RoPE in place ("Transformer 篇" 5.5; "Transformer篇" (fengye404.top) 7): each thread
 // rotates two adjacent pairs (4 elements) of one head of one token.
 template <typename T>
@@ -233,6 +290,29 @@ hipError_t rms1(const void *x, const void *g, int g_dt, void *y, int y_dt, int64
                          : rms2<TX, float>(x, g, y, y_dt, rows, d, eps, s);
 }
 
+template <int VPT, typename T>
+hipError_t er4(const int32_t *ids, int64_t rows, const void *table, int vocab, int d, float *x,
+               int32_t *err, const void *g, void *y, float eps, hipStream_t s) {
+  embed_rmsnorm_kernel<VPT, T, T, T><<<blocks_for(rows, 4), 256, 0, s>>>(
+      ids, rows, (const T *)table, vocab, d, x, err, (const T *)g, (T *)y, eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t er3(const int32_t *ids, int64_t rows, const void *table, int vocab, int d, float *x,
+               int32_t *err, const void *g, void *y, float eps, hipStream_t s) {
+  switch ((d + 255) / 256) {   // float4 steps per lane, as for rmsnorm_kernel
+    case 1: return er4<1, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 2: return er4<2, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 3: return er4<3, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 4: return er4<4, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 5: return er4<5, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 6: return er4<6, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    case 7: return er4<7, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+    default: return er4<kMaxVpt, T>(ids, rows, table, vocab, d, x, err, g, y, eps, s);
+  }
+}
+
 // Matrix-core rate probe (a measurement of the sustained bf16 MFMA rate, the second
 // denominator beside the published peak): each wave runs `iters` rounds of 8 independent
 // v_mfma_f32_16x16x32_bf16 on operands held in registers, filled with pseudo-random bf16
@@ -300,6 +380,14 @@ hipError_t launch_embed(const int32_t *ids, int64_t n, const void *table, int ta
     embed_kernel<float><<<blocks_for(total, 256), 256, 0, s>>>(ids, n, (const float *)table,
                                                                vocab, d, x, err_flag);
   return hipGetLastError();
+}
+
+hipError_t launch_embed_rmsnorm(const int32_t *ids, int64_t n, const void *table, int dt,
+                                int vocab, int d, float *x, int32_t *err_flag, const void *g,
+                                void *y, float eps, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return dt == DT_BF16 ? er3<bf16_t>(ids, n, table, vocab, d, x, err_flag, g, y, eps, s)
+                       : er3<float>(ids, n, table, vocab, d, x, err_flag, g, y, eps, s);
 }
 
 hipError_t launch_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,

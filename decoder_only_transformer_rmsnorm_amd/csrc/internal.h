@@ -12,6 +12,10 @@ hipError_t launch_rope_table(float *cos_sin, int max_seq, int d_head, double the
                              hipStream_t s);
 hipError_t launch_embed(const int32_t *ids, int64_t n, const void *table, int table_dt,
                         int vocab, int d, float *x, int32_t *err_flag, hipStream_t s);
+// embedding into x and y = RMSNorm(x; g) in one pass; table, g and y of dtype dt
+hipError_t launch_embed_rmsnorm(const int32_t *ids, int64_t n, const void *table, int dt,
+                                int vocab, int d, float *x, int32_t *err_flag, const void *g,
+                                void *y, float eps, hipStream_t s);
 // matrix-core rate probe: blocks x 4 waves x iters x 8 MFMAs of 16x16x32; sink: blocks x 4
 hipError_t launch_mfma_rate(int64_t iters, int blocks, float *sink, hipStream_t s);
 hipError_t launch_rmsnorm(const void *x, int x_dt, const void *g, int g_dt, void *y, int y_dt,
