@@ -1053,7 +1053,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
 #pragma unroll
         for (int i = 0; i < NQ; ++i) c[i] = *(const f32x4_t *)(row + cso[i]);
       };
-      if constexpr (EPI == EPI_QKV_ROPE) load_cs(0, csr[0], pok[0]);
+      // a tile of v columns only (a third of the tiles) rotates nothing: no table reads
+      const bool tile_rope = EPI == EPI_QKV_ROPE && n0 < g.n0 + g.n1;
+      if constexpr (EPI == EPI_QKV_ROPE)
+        if (tile_rope) load_cs(0, csr[0], pok[0]);
       // RMSNorm split across the products: each of the lane's rows gets 1 / rms(x) from the
       // producer's per-tile sums of squares (summed in tile order), all read up front
       float rsv[NBM];
@@ -1067,7 +1070,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs &g, int tm, int tn
       for (int bm = 0; bm < NBM; ++bm) {
         const int r = wm * WM + bm * MS + l32 - p * prow;
         if constexpr (EPI == EPI_QKV_ROPE)
-          if (bm + 1 < NBM) load_cs(bm + 1, csr[(bm + 1) & 1], pok[(bm + 1) & 1]);
+          if (tile_rope && bm + 1 < NBM) load_cs(bm + 1, csr[(bm + 1) & 1], pok[(bm + 1) & 1]);
 #pragma unroll
         for (int bn = 0; bn < (EPI == EPI_SWIGLU ? NBN / 2 : NBN); ++bn) {
 #pragma unroll
