@@ -163,7 +163,7 @@ def _swap_gain(inp, layer: int, field: str, src_layer: int, src_field: str):
     return bad
 
 
-@pytest.mark.parametrize("case", ["d256_gqa", "d768_mha", "d1600_mha", "d2048_gqa"])
+@pytest.mark.parametrize("case", ["d256_gqa", "d768_mha", "d1600_mha", "d2048_gqa", "d2304_gqa"])
 def test_model_split_norm_nonunit_gains(case):
     """bf16 models with d <= 3072 split each block's RMSNorms across two products
     ("Transformer 篇" (dujian.net) 5.6, the per-dimension gain g): block l's down projection
@@ -179,8 +179,11 @@ def test_model_split_norm_nonunit_gains(case):
         cfg = synth.GPT2S_BF16.replace(name="d768_L2", n_layers=2, batch=2, seq=256)
     elif case == "d1600_mha":   # 9 column tiles of row partials (the XL width)
         cfg = synth.XL_BF16.replace(name="d1600_L2", n_layers=2, batch=1, seq=160, vocab=4000)
-    else:                       # 11 column tiles, grouped-query heads of 128 (long-GQA width)
+    elif case == "d2048_gqa":   # 11 column tiles, grouped-query heads of 128 (long-GQA width)
         cfg = synth.LONG_GQA_BF16.replace(name="d2048_L2", n_layers=2, batch=1, seq=192, vocab=4000)
+    else:   # 12 column tiles; rows wider than 2048 take the embedding pass's second loop
+        cfg = synth.LONG_GQA_BF16.replace(name="d2304_L2", n_layers=2, d_model=2304, n_heads=18,
+                                          n_kv_heads=6, d_ff=3072, batch=1, seq=128, vocab=4000)
     say(f"model split RMSNorm gains {case}: L={cfg.n_layers} d={cfg.d_model} B={cfg.batch} S={cfg.seq}")
     inp = synth.make_inputs(cfg, seed=11, gamma_std=GAIN_STD)
     assert np.abs(inp.layers[1].g_attn - 1).max() > 0.1
